@@ -1,0 +1,256 @@
+"""Python binding of libmoe_dequant.so (the gfx950 MoE expert-path library).
+
+Argument marshalling only: every function here converts torch tensors / numpy arrays to the
+pointers and sizes of the C ABI declared in include/moe_dequant.h and calls it; all arithmetic
+runs in the library.  The names match the C entry points.  PyTorch is used for device memory
+and streams only.  Importing works without a GPU (the packer and the validation paths are
+host code); compute calls need the built library and a gfx950 device, and raise if either is
+missing -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_dequant.so")
+
+MOE_OK = 0
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OP_ROUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE = 1, 2, 3
+MOE_FLAG_RESIDUAL = 1
+GROUP = 64
+MAX_TOPK = 8
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_BITS",
+          5: "MOE_ERR_ALIGN", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_LAUNCH", 8: "MOE_ERR_UNSUPPORTED",
+          9: "MOE_ERR_BUFFER", 10: "MOE_ERR_DEVICE"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class moe_expert_desc(ctypes.Structure):
+    _fields_ = [("blob", ctypes.c_uint64), ("bits", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32)]
+
+
+class moe_layer(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("logit_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m bit_expert_dequant_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
+        sig = {
+            "moe_status_string": (ctypes.c_char_p, [I32]),
+            "moe_last_error": (ctypes.c_char_p, []),
+            "moe_version": (ctypes.c_char_p, []),
+            "moe_packed_codes_bytes": (SZ, [I32, I32, I32]),
+            "moe_packed_sb_bytes": (SZ, [I32, I32]),
+            "moe_packed_expert_bytes": (SZ, [I32, I32, I32]),
+            "moe_expert_plane_offsets": (I32, [I32, I32, I32, P]),
+            "moe_pack_matrix": (I32, [P, P, P, I32, I32, I32, P, SZ, P, SZ]),
+            "moe_unpack_matrix": (I32, [P, P, I32, I32, I32, P, P, P]),
+            "moe_pack_expert": (I32, [P, P, P, I32, I32, I32, P, SZ]),
+            "moe_check_experts": (I32, [P, I32]),
+            "moe_workspace_bytes": (SZ, [I32, P, I32, I32]),
+            "moe_route": (I32, [P, P, P, I32, I32, P, P, P, P, SZ, P]),
+            "moe_expert_ffn": (I32, [P, P, P, I32, I32, P, P, P, SZ, P]),
+            "moe_combine": (I32, [P, P, I32, I32, I32, P, P, P]),
+            "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> List[str]:
+    return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
+            "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
+            "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
+            "moe_expert_ffn", "moe_combine", "moe_layer_decode"]
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _tptr(t):
+    """Device pointer of a torch tensor (None -> NULL)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version() -> str:
+    return lib().moe_version().decode()
+
+
+# ----------------------------------------------------------------------------- format (host)
+def moe_packed_codes_bytes(rows: int, cols: int, bits: int) -> int:
+    return int(lib().moe_packed_codes_bytes(rows, cols, bits))
+
+
+def moe_packed_sb_bytes(rows: int, cols: int) -> int:
+    return int(lib().moe_packed_sb_bytes(rows, cols))
+
+
+def moe_packed_expert_bytes(hidden: int, inter: int, bits: int) -> int:
+    return int(lib().moe_packed_expert_bytes(hidden, inter, bits))
+
+
+def moe_expert_plane_offsets(hidden: int, inter: int, bits: int) -> List[int]:
+    off = (ctypes.c_size_t * 6)()
+    _check(lib().moe_expert_plane_offsets(hidden, inter, bits, off))
+    return list(off)
+
+
+def moe_pack_matrix(codes: np.ndarray, scale: np.ndarray, bias: np.ndarray, bits: int):
+    """codes uint8 [R, C]; scale, bias uint16 (bf16 bits) [R, C/64] -> (code plane, sb plane)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    R, C = codes.shape
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    if scale.size != R * (C // GROUP) or bias.size != scale.size:
+        raise ValueError("scale/bias must have R*C/64 entries")
+    cb, sb = max(moe_packed_codes_bytes(R, C, bits), 1), max(moe_packed_sb_bytes(R, C), 4)
+    co = np.zeros(cb, dtype=np.uint8)
+    so = np.zeros(sb // 2, dtype=np.uint16)
+    _check(lib().moe_pack_matrix(_np_ptr(codes), _np_ptr(scale), _np_ptr(bias), R, C, bits,
+                                 _np_ptr(co), co.nbytes, _np_ptr(so), so.nbytes))
+    return co, so
+
+
+def moe_unpack_matrix(code_plane: np.ndarray, sb_plane: np.ndarray, rows: int, cols: int, bits: int):
+    cp = np.ascontiguousarray(code_plane, dtype=np.uint8)
+    sp = np.ascontiguousarray(sb_plane, dtype=np.uint16)
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scale = np.zeros(rows * (cols // GROUP), dtype=np.uint16)
+    bias = np.zeros_like(scale)
+    _check(lib().moe_unpack_matrix(_np_ptr(cp), _np_ptr(sp), rows, cols, bits, _np_ptr(codes),
+                                   _np_ptr(scale), _np_ptr(bias)))
+    return codes, scale, bias
+
+
+def moe_pack_expert(mats: Sequence, hidden: int, inter: int, bits: int) -> np.ndarray:
+    """mats = [(codes, scale, bias)] for gate [I,H], up [I,H], down [H,I] -> packed blob (uint8)."""
+    arrs = []
+    for codes, scale, bias in mats:
+        arrs.append((np.ascontiguousarray(codes, dtype=np.uint8), np.ascontiguousarray(scale, dtype=np.uint16),
+                     np.ascontiguousarray(bias, dtype=np.uint16)))
+    P3 = ctypes.c_void_p * 3
+    cp = P3(*[a[0].ctypes.data for a in arrs])
+    sp = P3(*[a[1].ctypes.data for a in arrs])
+    bp = P3(*[a[2].ctypes.data for a in arrs])
+    n = moe_packed_expert_bytes(hidden, inter, bits)
+    out = np.zeros(max(n, 1), dtype=np.uint8)
+    _check(lib().moe_pack_expert(cp, sp, bp, hidden, inter, bits, _np_ptr(out), out.nbytes))
+    return out
+
+
+def moe_check_experts(table) -> None:
+    """Validate a device descriptor table (torch uint8/int64 tensor of E*16 bytes)."""
+    _check(lib().moe_check_experts(_tptr(table), table.numel() * table.element_size() // 16))
+
+
+# ----------------------------------------------------------------------------- device helpers
+def expert_table(blob_ptrs: Sequence[int], bits: Sequence[int], device="cuda"):
+    """Build the device descriptor table [E] from blob device addresses and widths."""
+    import torch
+    E = len(blob_ptrs)
+    host = np.zeros((E, 2), dtype=np.uint64)
+    host[:, 0] = np.asarray(blob_ptrs, dtype=np.uint64)
+    host[:, 1] = np.asarray(bits, dtype=np.uint64)       # bits in the low word, reserved = 0
+    return torch.from_numpy(host.view(np.int64).reshape(-1)).to(device)
+
+
+def make_dims(hidden: int, inter: int, n_experts: int, top_k: int) -> moe_dims:
+    return moe_dims(hidden, inter, n_experts, top_k)
+
+
+class Layer:
+    """Keeps the tensors of one layer alive and exposes the C struct."""
+
+    def __init__(self, router, experts, logit_bias=None, norm_w=None, norm_eps: float = 1e-6):
+        self.router, self.experts, self.logit_bias, self.norm_w = router, experts, logit_bias, norm_w
+        self.c = moe_layer(router.data_ptr(), _dtype_code(router), float(norm_eps),
+                           None if logit_bias is None else logit_bias.data_ptr(),
+                           None if norm_w is None else norm_w.data_ptr(), experts.data_ptr())
+
+
+def moe_workspace_bytes(op: int, dims: moe_dims, T: int = 1, n_layers: int = 1) -> int:
+    return int(lib().moe_workspace_bytes(op, ctypes.byref(dims), T, n_layers))
+
+
+def workspace(op: int, dims: moe_dims, T: int = 1, n_layers: int = 1, device="cuda"):
+    import torch
+    n = moe_workspace_bytes(op, dims, T, n_layers)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- compute
+def moe_route(dims: moe_dims, layer: Layer, x, idx, w, logits=None, ws=None, stream=None) -> None:
+    T = x.shape[0] if x.dim() == 2 else 1
+    _check(lib().moe_route(ctypes.byref(dims), ctypes.byref(layer.c), _tptr(x), _dtype_code(x), T, _tptr(idx),
+                           _tptr(w), _tptr(logits), _tptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_expert_ffn(dims: moe_dims, layer: Layer, x, idx, y, ws, stream=None) -> None:
+    T = x.shape[0] if x.dim() == 2 else 1
+    _check(lib().moe_expert_ffn(ctypes.byref(dims), ctypes.byref(layer.c), _tptr(x), _dtype_code(x), T,
+                                _tptr(idx), _tptr(y), _tptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_combine(y, w, out, residual=None, stream=None) -> None:
+    T, K, H = y.shape
+    _check(lib().moe_combine(_tptr(y), _tptr(w), T, K, H, _tptr(residual), _tptr(out), _stream(stream)))
+
+
+def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, w=None, residual: bool = False,
+                     ws=None, stream=None) -> None:
+    arr = (moe_layer * len(layers))(*[L.c for L in layers])
+    flags = MOE_FLAG_RESIDUAL if residual else 0
+    _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
+                                  _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream)))

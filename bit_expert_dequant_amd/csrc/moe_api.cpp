@@ -1,0 +1,354 @@
+// moe_api.cpp -- C ABI entry points: argument validation, the packed-format packer, workspace
+// sizing and kernel dispatch.  Every check runs before anything is enqueued, so a failing call
+// leaves the stream untouched.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "moe_dequant.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = std::string(moe_status_string(status)) + ": " + buf;
+    return status;
+}
+int ok() {
+    g_err.clear();
+    return MOE_OK;
+}
+
+size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool bits_ok(int b) { return b == 2 || b == 4; }
+bool dim_ok(int v) { return v >= 64 && v <= MOE_MAX_DIM && v % MOE_GROUP == 0; }
+
+int check_dims(const moe_dims *d) {
+    if (!d) return fail(MOE_ERR_NULL, "dims is NULL");
+    if (!dim_ok(d->hidden)) return fail(MOE_ERR_SHAPE, "hidden=%d must be a multiple of 64 in [64, %d]", d->hidden, MOE_MAX_DIM);
+    if (!dim_ok(d->inter)) return fail(MOE_ERR_SHAPE, "inter=%d must be a multiple of 64 in [64, %d]", d->inter, MOE_MAX_DIM);
+    if (d->n_experts < 1 || d->n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", d->n_experts, MOE_MAX_EXPERTS);
+    if (d->top_k < 1 || d->top_k > MOE_MAX_TOPK || d->top_k > d->n_experts)
+        return fail(MOE_ERR_SHAPE, "top_k=%d outside [1, min(n_experts, %d)]", d->top_k, MOE_MAX_TOPK);
+    if ((long)d->top_k * d->inter > MOE_MAX_K_TIMES_I)
+        return fail(MOE_ERR_UNSUPPORTED, "top_k*inter=%ld exceeds %d (LDS staging of the down projection)",
+                    (long)d->top_k * d->inter, MOE_MAX_K_TIMES_I);
+    return MOE_OK;
+}
+
+int check_dtype(int dt, const char *what) {
+    if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_DTYPE, "%s dtype %d is not MOE_F32 or MOE_BF16", what, dt);
+    return MOE_OK;
+}
+
+int check_layer(const moe_layer *L, int idx) {
+    if (!L) return fail(MOE_ERR_NULL, "layer %d is NULL", idx);
+    if (!L->router) return fail(MOE_ERR_NULL, "layer %d router is NULL", idx);
+    if (!L->experts) return fail(MOE_ERR_NULL, "layer %d experts is NULL", idx);
+    if (int s = check_dtype(L->router_dtype, "router")) return s;
+    if (!aligned(L->router, 16)) return fail(MOE_ERR_ALIGN, "layer %d router not 16-byte aligned", idx);
+    if (!aligned(L->experts, 16)) return fail(MOE_ERR_ALIGN, "layer %d experts table not 16-byte aligned", idx);
+    if (L->logit_bias && !aligned(L->logit_bias, 4)) return fail(MOE_ERR_ALIGN, "layer %d logit_bias not 4-byte aligned", idx);
+    if (L->norm_w && !aligned(L->norm_w, 2)) return fail(MOE_ERR_ALIGN, "layer %d norm_w not 2-byte aligned", idx);
+    if (L->norm_w && !(L->norm_eps >= 0.f && std::isfinite(L->norm_eps)))
+        return fail(MOE_ERR_SHAPE, "layer %d norm_eps must be finite and >= 0", idx);
+    return MOE_OK;
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+    if (need && !ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+    if (ws && !aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
+    return MOE_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+// Workspace carving (each region 256-byte aligned).
+struct Carve {
+    char *base;
+    size_t off = 0;
+    template <typename T>
+    T *take(size_t n) {
+        T *p = base ? (T *)(base + off) : nullptr;
+        off = r256(off + n * sizeof(T));
+        return p;
+    }
+};
+
+size_t route_ws(const moe_dims *d, int T) { return r256((size_t)T * d->n_experts * 4); }
+size_t ffn_ws(const moe_dims *d, int T) { return r256((size_t)T * d->top_k * d->inter * 4); }
+size_t decode_ws(const moe_dims *d) {
+    Carve c{nullptr};
+    c.take<float>(d->n_experts);
+    c.take<int32_t>(d->top_k);
+    c.take<float>(d->top_k);
+    c.take<float>((size_t)d->top_k * d->inter);
+    c.take<float>(2 * (size_t)d->hidden);
+    return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+        case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+        case MOE_ERR_BITS: return "MOE_ERR_BITS";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_BUFFER: return "MOE_ERR_BUFFER";
+        case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+const char *moe_version(void) { return "moe_dequant 0.1 (gfx950)"; }
+
+// ------------------------------------------------------------------------------- format
+size_t moe_packed_codes_bytes(int rows, int cols, int bits) {
+    if (rows < 1 || cols < 64 || cols % MOE_GROUP || !bits_ok(bits)) return 0;
+    return (size_t)rows * cols * bits / 8;
+}
+
+size_t moe_packed_sb_bytes(int rows, int cols) {
+    if (rows < 1 || cols < 64 || cols % MOE_GROUP) return 0;
+    return (size_t)rows * (cols / MOE_GROUP) * 4;
+}
+
+int moe_expert_plane_offsets(int hidden, int inter, int bits, size_t off[6]) {
+    if (!off) return fail(MOE_ERR_NULL, "off is NULL");
+    if (!bits_ok(bits)) return fail(MOE_ERR_BITS, "bits=%d", bits);
+    if (hidden < 64 || hidden % 64 || inter < 64 || inter % 64)
+        return fail(MOE_ERR_SHAPE, "hidden=%d inter=%d must be positive multiples of 64", hidden, inter);
+    const size_t sz[6] = {moe_packed_codes_bytes(inter, hidden, bits), moe_packed_sb_bytes(inter, hidden),
+                          moe_packed_codes_bytes(inter, hidden, bits), moe_packed_sb_bytes(inter, hidden),
+                          moe_packed_codes_bytes(hidden, inter, bits), moe_packed_sb_bytes(hidden, inter)};
+    size_t p = 0;
+    for (int i = 0; i < 6; ++i) {
+        off[i] = p;
+        p = r256(p + sz[i]);
+    }
+    return ok();
+}
+
+size_t moe_packed_expert_bytes(int hidden, int inter, int bits) {
+    size_t off[6];
+    if (moe_expert_plane_offsets(hidden, inter, bits, off) != MOE_OK) return 0;
+    return r256(off[5] + moe_packed_sb_bytes(hidden, inter));
+}
+
+int moe_pack_matrix(const uint8_t *codes, const uint16_t *scale, const uint16_t *bias, int rows, int cols,
+                    int bits, uint8_t *codes_out, size_t codes_out_bytes, uint16_t *sb_out, size_t sb_out_bytes) {
+    if (!codes || !scale || !bias || !codes_out || !sb_out) return fail(MOE_ERR_NULL, "NULL argument");
+    if (!bits_ok(bits)) return fail(MOE_ERR_BITS, "bits=%d", bits);
+    const size_t cb = moe_packed_codes_bytes(rows, cols, bits), sb = moe_packed_sb_bytes(rows, cols);
+    if (!cb || !sb) return fail(MOE_ERR_SHAPE, "rows=%d cols=%d", rows, cols);
+    if (codes_out_bytes < cb || sb_out_bytes < sb) return fail(MOE_ERR_BUFFER, "need %zu + %zu bytes", cb, sb);
+    const size_t n = (size_t)rows * cols;
+    const unsigned lim = 1u << bits;
+    for (size_t i = 0; i < n; ++i)
+        if (codes[i] >= lim) return fail(MOE_ERR_BITS, "code %u at %zu does not fit in %d bits", codes[i], i, bits);
+    std::memset(codes_out, 0, cb);
+    const size_t rowb = (size_t)cols * bits / 8;
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c) {
+            const size_t bit = (size_t)c * bits;
+            codes_out[(size_t)r * rowb + bit / 8] |= (uint8_t)(codes[(size_t)r * cols + c] << (bit % 8));
+        }
+    const size_t ng = (size_t)rows * (cols / MOE_GROUP);
+    for (size_t g = 0; g < ng; ++g) {
+        sb_out[2 * g] = scale[g];
+        sb_out[2 * g + 1] = bias[g];
+    }
+    return ok();
+}
+
+int moe_unpack_matrix(const uint8_t *codes_in, const uint16_t *sb_in, int rows, int cols, int bits, uint8_t *codes,
+                      uint16_t *scale, uint16_t *bias) {
+    if (!codes_in || !sb_in || !codes || !scale || !bias) return fail(MOE_ERR_NULL, "NULL argument");
+    if (!bits_ok(bits)) return fail(MOE_ERR_BITS, "bits=%d", bits);
+    if (!moe_packed_codes_bytes(rows, cols, bits)) return fail(MOE_ERR_SHAPE, "rows=%d cols=%d", rows, cols);
+    const size_t rowb = (size_t)cols * bits / 8;
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c) {
+            const size_t bit = (size_t)c * bits;
+            codes[(size_t)r * cols + c] = (codes_in[(size_t)r * rowb + bit / 8] >> (bit % 8)) & ((1u << bits) - 1);
+        }
+    const size_t ng = (size_t)rows * (cols / MOE_GROUP);
+    for (size_t g = 0; g < ng; ++g) {
+        scale[g] = sb_in[2 * g];
+        bias[g] = sb_in[2 * g + 1];
+    }
+    return ok();
+}
+
+int moe_pack_expert(const uint8_t *const codes[3], const uint16_t *const scale[3], const uint16_t *const bias[3],
+                    int hidden, int inter, int bits, void *blob_out, size_t blob_out_bytes) {
+    if (!codes || !scale || !bias || !blob_out) return fail(MOE_ERR_NULL, "NULL argument");
+    size_t off[6];
+    if (int s = moe_expert_plane_offsets(hidden, inter, bits, off)) return s;
+    const size_t total = moe_packed_expert_bytes(hidden, inter, bits);
+    if (blob_out_bytes < total) return fail(MOE_ERR_BUFFER, "blob needs %zu bytes", total);
+    std::memset(blob_out, 0, total);
+    uint8_t *b = (uint8_t *)blob_out;
+    const int R[3] = {inter, inter, hidden}, C[3] = {hidden, hidden, inter};
+    for (int m = 0; m < 3; ++m) {
+        if (!codes[m] || !scale[m] || !bias[m]) return fail(MOE_ERR_NULL, "matrix %d has a NULL array", m);
+        const size_t cb = moe_packed_codes_bytes(R[m], C[m], bits), sb = moe_packed_sb_bytes(R[m], C[m]);
+        if (int s = moe_pack_matrix(codes[m], scale[m], bias[m], R[m], C[m], bits, b + off[2 * m], cb,
+                                    (uint16_t *)(b + off[2 * m + 1]), sb))
+            return s;
+    }
+    return ok();
+}
+
+int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts) {
+    if (!experts_dev) return fail(MOE_ERR_NULL, "experts is NULL");
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "n_experts=%d", n_experts);
+    std::vector<moe_expert_desc> h(n_experts);
+    hipError_t e = hipMemcpy(h.data(), experts_dev, sizeof(moe_expert_desc) * n_experts, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "copying the descriptor table: %s", hipGetErrorString(e));
+    for (int i = 0; i < n_experts; ++i) {
+        if (!h[i].blob) return fail(MOE_ERR_NULL, "expert %d blob is NULL", i);
+        if (h[i].blob % MOE_BLOB_ALIGN) return fail(MOE_ERR_ALIGN, "expert %d blob not 256-byte aligned", i);
+        if (!bits_ok((int)h[i].bits)) return fail(MOE_ERR_BITS, "expert %d bits=%u", i, h[i].bits);
+        if (h[i].reserved) return fail(MOE_ERR_SHAPE, "expert %d reserved field is not 0", i);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------------------- workspace
+size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers) {
+    if (!dims || check_dims(dims) != MOE_OK || T < 1) return 0;
+    switch (op) {
+        case MOE_OP_ROUTE: return route_ws(dims, T);
+        case MOE_OP_EXPERT_FFN: return ffn_ws(dims, T);
+        case MOE_OP_LAYER_DECODE: return (n_layers >= 1 && T == 1) ? decode_ws(dims) : 0;
+        default: return 0;
+    }
+}
+
+// ------------------------------------------------------------------------------- compute
+int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T, int32_t *idx,
+              float *w, float *logits, void *ws, size_t ws_bytes, void *stream) {
+    if (int s = check_dims(dims)) return s;
+    if (int s = check_layer(layer, 0)) return s;
+    if (int s = check_dtype(x_dtype, "x")) return s;
+    if (!x || !idx || !w) return fail(MOE_ERR_NULL, "x, idx and w are required");
+    if (T < 1 || T > 65535) return fail(MOE_ERR_SHAPE, "T=%d outside [1, 65535]", T);
+    if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
+    if (!aligned(idx, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)))
+        return fail(MOE_ERR_ALIGN, "idx/w/logits not 4-byte aligned");
+    const size_t need = logits ? 0 : route_ws(dims, T);
+    if (int s = check_ws(ws, ws_bytes, need)) return s;
+    float *lg = logits ? logits : (float *)ws;
+    hipStream_t st = (hipStream_t)stream;
+    moe::RouterLaunch ra{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, layer->router,
+                         layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T};
+    if (int s = launched(moe::launch_router(ra, st), "router")) return s;
+    moe::TopkLaunch ta{lg, dims->n_experts, dims->top_k, T, idx, w};
+    if (int s = launched(moe::launch_topk(ta, st), "top-k")) return s;
+    return ok();
+}
+
+int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+                   const int32_t *idx, float *y, void *ws, size_t ws_bytes, void *stream) {
+    if (int s = check_dims(dims)) return s;
+    if (int s = check_layer(layer, 0)) return s;
+    if (int s = check_dtype(x_dtype, "x")) return s;
+    if (!x || !idx || !y) return fail(MOE_ERR_NULL, "x, idx and y are required");
+    if (T < 1 || T > 65535) return fail(MOE_ERR_SHAPE, "T=%d outside [1, 65535]", T);
+    if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
+    if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MOE_ERR_ALIGN, "idx/y not 4-byte aligned");
+    if (int s = check_ws(ws, ws_bytes, ffn_ws(dims, T))) return s;
+    hipStream_t st = (hipStream_t)stream;
+    float *h = (float *)ws;
+    moe::GateUpLaunch ga{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, nullptr, idx, nullptr, nullptr,
+                         nullptr, nullptr, layer->experts, h, dims->hidden, dims->inter, dims->n_experts, dims->top_k, T};
+    if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
+    moe::DownLaunch da{h, idx, nullptr, layer->experts, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter,
+                       dims->top_k, T};
+    if (int s = launched(moe::launch_down(da, dims->n_experts, st), "down")) return s;
+    return ok();
+}
+
+int moe_combine(const float *y, const float *w, int T, int K, int H, const float *residual, float *out,
+                void *stream) {
+    if (!y || !w || !out) return fail(MOE_ERR_NULL, "y, w and out are required");
+    if (T < 1 || K < 1 || K > MOE_MAX_TOPK || H < 1) return fail(MOE_ERR_SHAPE, "T=%d K=%d H=%d", T, K, H);
+    if (!aligned(y, 4) || !aligned(w, 4) || !aligned(out, 4) || (residual && !aligned(residual, 4)))
+        return fail(MOE_ERR_ALIGN, "arrays must be 4-byte aligned");
+    moe::CombineLaunch ca{y, w, residual, out, T, K, H};
+    if (int s = launched(moe::launch_combine(ca, (hipStream_t)stream), "combine")) return s;
+    return ok();
+}
+
+int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
+                     unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+    if (int s = check_dims(dims)) return s;
+    if (!layers) return fail(MOE_ERR_NULL, "layers is NULL");
+    if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_SHAPE, "n_layers=%d outside [1, 4096]", n_layers);
+    for (int l = 0; l < n_layers; ++l)
+        if (int s = check_layer(&layers[l], l)) return s;
+    if (int s = check_dtype(x_dtype, "x")) return s;
+    if (!x || !out) return fail(MOE_ERR_NULL, "x and out are required");
+    if ((idx == nullptr) != (w == nullptr)) return fail(MOE_ERR_NULL, "idx and w must both be given or both NULL");
+    if (flags & ~MOE_FLAG_RESIDUAL) return fail(MOE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_ALIGN, "x and out must be 16-byte aligned");
+    if ((idx && !aligned(idx, 4)) || (w && !aligned(w, 4))) return fail(MOE_ERR_ALIGN, "idx/w not 4-byte aligned");
+    if (out == x) return fail(MOE_ERR_SHAPE, "out must not alias x");
+    if (int s = check_ws(ws, ws_bytes, decode_ws(dims))) return s;
+
+    const int H = dims->hidden, I = dims->inter, E = dims->n_experts, K = dims->top_k;
+    Carve c{(char *)ws};
+    float *logits = c.take<float>(E);
+    int32_t *idx_ws = c.take<int32_t>(K);
+    float *w_ws = c.take<float>(K);
+    float *h = c.take<float>((size_t)K * I);
+    float *xbuf = c.take<float>(2 * (size_t)H);
+    hipStream_t st = (hipStream_t)stream;
+    const bool residual = flags & MOE_FLAG_RESIDUAL;
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer &L = layers[l];
+        const void *xl = l == 0 ? x : (const void *)(xbuf + (size_t)((l - 1) & 1) * H);
+        const int xdt = l == 0 ? x_dtype : MOE_F32;
+        float *ol = l == n_layers - 1 ? out : xbuf + (size_t)(l & 1) * H;
+        moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, logits, H, E, 1};
+        if (int s = launched(moe::launch_router(ra, st), "router")) return s;
+        moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, logits, nullptr,
+                             idx ? idx + (size_t)l * K : nullptr, w ? w + (size_t)l * K : nullptr, idx_ws, w_ws,
+                             L.experts, h, H, I, E, K, 1};
+        if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
+        moe::DownLaunch da{h, idx_ws, w_ws, L.experts, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
+        if (int s = launched(moe::launch_down(da, E, st), "down")) return s;
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// moe_internal.h -- launchers shared between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_dequant.h"
+
+namespace moe {
+
+constexpr int kGroup = 64;
+
+// Rows of the gate/up matrices one wavefront handles per work unit, for a given
+// input width (cols) at 4-bit; the 2-bit path covers the same rows.
+int gateup_rows_per_unit(int cols);
+// Output rows of the down projection one wavefront handles per work unit.
+int down_rows_per_unit(int cols);
+size_t gateup_lds_bytes(int H);
+size_t down_lds_bytes(int I, int K);
+
+struct RouterLaunch {
+    const void *x; int x_dtype; int x_stride;     // x [T][x_stride]
+    const uint16_t *norm_w; float eps;
+    const void *router; int router_dtype;
+    const float *logit_bias;
+    float *logits;                                 // [T][E]
+    int H, E, T;
+};
+hipError_t launch_router(const RouterLaunch &a, hipStream_t s);
+
+struct TopkLaunch {
+    const float *logits; int E, K, T;
+    int32_t *idx; float *w;                        // [T][K]
+};
+hipError_t launch_topk(const TopkLaunch &a, hipStream_t s);
+
+struct GateUpLaunch {
+    const void *x; int x_dtype; int x_stride;      // activation source [T][x_stride]
+    const uint16_t *norm_w; float eps;             // RMSNorm applied to x when norm_w != NULL
+    const float *logits;                           // [T][E]: top-K computed here when idx_in == NULL
+    const int32_t *idx_in;                         // [T][K] given routing, or NULL
+    int32_t *idx_out; float *w_out;                // [T][K] written when top-K is computed here (nullable)
+    int32_t *idx_ws; float *w_ws;                  // [T][K] copies for the down kernel (nullable)
+    const moe_expert_desc *experts;
+    float *h;                                      // [T][K][I]
+    int H, I, E, K, T;
+};
+hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s);
+
+struct DownLaunch {
+    const float *h;                                // [T][K][I]
+    const int32_t *idx;                            // [T][K]
+    const float *w;                                // [T][K] (combine) or NULL (per-expert output)
+    const moe_expert_desc *experts;
+    const void *residual; int residual_dtype; int residual_stride;   // [T][stride] or NULL
+    float *out;                                    // combine: [T][H]; else y [T][K][H]
+    int H, I, K, T;
+};
+hipError_t launch_down(const DownLaunch &a, int E, hipStream_t s);
+
+struct CombineLaunch {
+    const float *y; const float *w; const float *residual; float *out;
+    int T, K, H;
+};
+hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
+
+}  // namespace moe

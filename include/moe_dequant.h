@@ -1,0 +1,230 @@
+/*
+ * moe_dequant.h -- C ABI of a gfx950 (MI355X) library for the per-token Mixture-of-Experts
+ * expert computation over affine group-quantised weights.
+ *
+ * What it computes (per token, per layer):
+ *   n      = RMSNorm(x) if the layer has a norm weight, else x
+ *   logits = W_r n (+ logit_bias);  p = softmax(logits) over all E experts
+ *   idx    = the K largest logits (descending; equal logits -> lower index first)
+ *   w_k    = p[idx_k] / sum_j p[idx_j]
+ *   y_k    = W_down[idx_k] (silu(W_gate[idx_k] n) * (W_up[idx_k] n)),  silu(z) = z/(1+e^-z)
+ *   out    = sum_k w_k y_k (+ x with MOE_FLAG_RESIDUAL)
+ * with every expert weight stored as codes q (2 or 4 bits) and one bf16 (scale, bias)
+ * pair per group of 64 inputs, w = q * scale + bias.
+ *
+ * Sources.  The Flash-MoE web pages define the affine dequantisation (nibble*scale+bias)
+ * and its FMA rewrite fma(nibble, scale*x, bias*x), the 4-bit and 2-bit expert matvec
+ * kernels, the two-pass RMSNorm and the MoE combine as a weighted sum of expert outputs
+ * (lilting.ch, "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE", section "Metal
+ * Compute Shaders", kernel table and the paragraph after it); 512 experts per layer with
+ * 4 active per token (same page, model-architecture section); about 6.75 MB per 4-bit
+ * expert and 27 MB per token (same page, SSD expert streaming section); the tiered
+ * hot-4-bit / cold-2-bit expert store (nzkcom.pages.dev, "flash-moe-romance-vs-utility",
+ * adopted-optimisations table).  The pages leave the router normalisation, top-K rule,
+ * SwiGLU form, RMSNorm epsilon placement, group size, code order and scale dtype open;
+ * this library takes the plain readings written above and in the format section below.
+ *
+ * Conventions (all entry points):
+ *   - Every device buffer is allocated, owned and freed by the caller.  The library never
+ *     allocates device memory, never synchronises the stream and keeps no global state
+ *     apart from a thread-local error message.
+ *   - Compute calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  They validate every argument the host can see first; on any failure they
+ *     return a non-zero moe_status and enqueue nothing.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - "device" pointers must point to memory of the current HIP device; "host" pointers
+ *     to ordinary host memory.
+ *   - Supported shapes: hidden H and intermediate I are multiples of 64 with
+ *     64 <= H <= 8192 and 64 <= I <= 8192; 1 <= E <= 2048; 1 <= K <= min(E, 8); and the
+ *     down projection's staged activations must fit in LDS: K * I <= 36864.
+ */
+#ifndef MOE_DEQUANT_H
+#define MOE_DEQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_GROUP 64        /* quantisation group length along the input dimension */
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_EXPERTS 2048
+#define MOE_MAX_DIM 8192
+#define MOE_MAX_K_TIMES_I 36864
+#define MOE_BLOB_ALIGN 256  /* required alignment of expert blobs and plane offsets */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,       /* a dimension or count is outside the supported range */
+    MOE_ERR_DTYPE = 3,       /* unknown moe_dtype */
+    MOE_ERR_BITS = 4,        /* bits not in {2, 4} */
+    MOE_ERR_ALIGN = 5,       /* a pointer lacks the documented alignment */
+    MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes() */
+    MOE_ERR_LAUNCH = 7,      /* the HIP runtime refused a kernel launch */
+    MOE_ERR_UNSUPPORTED = 8, /* valid request this build does not implement */
+    MOE_ERR_BUFFER = 9,      /* a host output buffer is too small */
+    MOE_ERR_DEVICE = 10      /* no usable gfx950 device / HIP runtime error */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,   /* IEEE binary32 */
+    MOE_BF16 = 1   /* bfloat16 bits, uint16 little-endian */
+} moe_dtype;
+
+/* ------------------------------------------------------------------------------------
+ * Packed format.
+ *
+ * Matrix with R rows (outputs) and C columns (inputs), C a multiple of 64, bits b:
+ *   code plane : R*C*b/8 bytes, row-major.  Code (r, c) is in byte r*(C*b/8) + (c*b)/8
+ *                at bit offset (c*b) % 8: the lowest bits hold the lowest column.
+ *   sb plane   : R*(C/64) pairs of bf16; pair (r, g) at uint16 index 2*(r*(C/64) + g),
+ *                scale first, then bias.  w[r][c] = code(r,c) * scale(r, c/64) + bias(r, c/64).
+ * Expert blob (gate and up are I x H, down is H x I), planes in this order, each starting
+ * at an offset rounded up to 256 bytes, total size rounded up to 256 bytes:
+ *   gate.codes, gate.sb, up.codes, up.sb, down.codes, down.sb
+ * At H = 4096, I = 1024 a 4-bit blob is 7,077,888 bytes (6.75 MiB) and a 2-bit blob
+ * 3,932,160 bytes; no padding occurs at those shapes.
+ * ------------------------------------------------------------------------------------ */
+
+/* One entry per expert of a layer, in DEVICE memory (the kernels select experts there).
+ * blob: device address of the expert's packed blob, 256-byte aligned.
+ * bits: 2 or 4.  Experts of one layer may mix widths (tiered store).  A value other than
+ *       2 is read as 4; moe_check_experts() validates a table on the host. */
+typedef struct moe_expert_desc {
+    uint64_t blob;
+    uint32_t bits;
+    uint32_t reserved;   /* must be 0 */
+} moe_expert_desc;
+
+typedef struct moe_dims {
+    int32_t hidden;      /* H */
+    int32_t inter;       /* I (expert intermediate size) */
+    int32_t n_experts;   /* E */
+    int32_t top_k;       /* K */
+} moe_dims;
+
+/* One layer: a HOST struct holding DEVICE pointers. */
+typedef struct moe_layer {
+    const void *router;              /* device [E][H] row-major, router_dtype; 16-byte aligned */
+    int32_t router_dtype;            /* MOE_F32 or MOE_BF16 */
+    float norm_eps;                  /* RMSNorm epsilon, added to mean(x^2) inside the sqrt */
+    const float *logit_bias;         /* device [E] fp32 added to the logits, or NULL */
+    const uint16_t *norm_w;          /* device [H] bf16 RMSNorm weight, or NULL for no norm */
+    const moe_expert_desc *experts;  /* device [E] */
+} moe_layer;
+
+/* --------------------------------------------------------------------------- errors */
+
+/* Static string naming a status code. */
+const char *moe_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none).  Valid until the next
+ * call on this thread. */
+const char *moe_last_error(void);
+
+/* Library version string. */
+const char *moe_version(void);
+
+/* --------------------------------------------------------------------------- format (host only) */
+
+/* Bytes of one code plane / one sb plane / one expert blob; 0 for unsupported arguments
+ * (rows, cols or dims < 1, cols or dims not multiples of 64, bits not in {2,4}). */
+size_t moe_packed_codes_bytes(int rows, int cols, int bits);
+size_t moe_packed_sb_bytes(int rows, int cols);
+size_t moe_packed_expert_bytes(int hidden, int inter, int bits);
+
+/* Byte offsets of the six planes inside one expert blob, in the order listed above.
+ * off: host [6].  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_BITS. */
+int moe_expert_plane_offsets(int hidden, int inter, int bits, size_t off[6]);
+
+/* Pack one R x C matrix.  codes: host [R*C], one code per byte (must be < 2^bits);
+ * scale, bias: host [R*(C/64)] bf16.  Writes codes_out (host, codes_out_bytes >=
+ * moe_packed_codes_bytes) and sb_out (host, sb_out_bytes >= moe_packed_sb_bytes).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_BITS (also for a code >= 2^bits),
+ * MOE_ERR_BUFFER. */
+int moe_pack_matrix(const uint8_t *codes, const uint16_t *scale, const uint16_t *bias,
+                    int rows, int cols, int bits,
+                    uint8_t *codes_out, size_t codes_out_bytes,
+                    uint16_t *sb_out, size_t sb_out_bytes);
+
+/* Inverse of moe_pack_matrix (host buffers; codes [R*C], scale/bias [R*(C/64)]). */
+int moe_unpack_matrix(const uint8_t *codes_in, const uint16_t *sb_in, int rows, int cols, int bits,
+                      uint8_t *codes, uint16_t *scale, uint16_t *bias);
+
+/* Pack a whole expert: matrices in the order gate (I x H), up (I x H), down (H x I), each
+ * given as (codes, scale, bias) host arrays as for moe_pack_matrix.  Writes the blob,
+ * padding included, to blob_out (host, blob_out_bytes >= moe_packed_expert_bytes). */
+int moe_pack_expert(const uint8_t *const codes[3], const uint16_t *const scale[3],
+                    const uint16_t *const bias[3], int hidden, int inter, int bits,
+                    void *blob_out, size_t blob_out_bytes);
+
+/* Copy a device descriptor table to the host (synchronously, on the null stream) and
+ * check it: non-NULL, 256-byte aligned blobs, bits in {2,4}, reserved == 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_BITS, MOE_ERR_SHAPE, MOE_ERR_DEVICE. */
+int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts);
+
+/* --------------------------------------------------------------------------- workspace */
+
+#define MOE_OP_ROUTE 1
+#define MOE_OP_EXPERT_FFN 2
+#define MOE_OP_LAYER_DECODE 3
+
+/* Device workspace bytes needed by one call of `op` with these dims and T tokens
+ * (n_layers for MOE_OP_LAYER_DECODE).  0 for unsupported arguments.  The workspace is
+ * scratch: its contents need no initialisation and are undefined after the call.  Two
+ * calls that may run concurrently need separate workspaces. */
+size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers);
+
+/* --------------------------------------------------------------------------- compute */
+
+/* Router for T tokens: steps n, logits, softmax, top-K and renormalisation above.
+ *   x      device [T][H], x_dtype, 16-byte aligned
+ *   idx    device [T][K] int32, descending weight (ties: lower expert index first)
+ *   w      device [T][K] fp32 renormalised weights (each row sums to 1)
+ *   logits device [T][E] fp32 pre-softmax logits (bias included), or NULL
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE,
+ * MOE_ERR_LAUNCH. */
+int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+              int32_t *idx, float *w, float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFN for T tokens and the K experts each token selected:
+ *   y[t][k] = W_down[e] (silu(W_gate[e] n_t) * (W_up[e] n_t)),  e = idx[t][k]
+ *   x   device [T][H] x_dtype (normalised inside when the layer has a norm weight)
+ *   idx device [T][K] int32 in [0, E) (out-of-range entries produce undefined y rows)
+ *   y   device [T][K][H] fp32
+ * T == 1 runs the decode matvec kernels (all K experts in one launch per phase); T > 1
+ * groups the T*K (token, slot) pairs by expert and runs the grouped dequant-GEMM (MFMA)
+ * kernels.  Errors as moe_route. */
+int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+                   const int32_t *idx, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine: out[t][c] = sum_k w[t][k] * y[t][k][c] (+ residual[t][c]).
+ *   y device [T][K][H] fp32, w device [T][K] fp32, residual device [T][H] fp32 or NULL,
+ *   out device [T][H] fp32 (may alias residual).  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
+ *   MOE_ERR_LAUNCH. */
+int moe_combine(const float *y, const float *w, int T, int K, int H, const float *residual,
+                float *out, void *stream);
+
+#define MOE_FLAG_RESIDUAL 1u   /* out = x + MoE(x) (pre-norm residual block) */
+
+/* One decode token through n_layers layers (1 <= n_layers <= 4096); layer l's output is
+ * layer l+1's input.  Per layer: [RMSNorm] -> router -> top-K -> gate/up/SwiGLU for all K
+ * experts in one launch -> down projection + weighted combine (+ residual) in one launch.
+ *   layers host [n_layers]
+ *   x      device [H] x_dtype (input of the first layer), 16-byte aligned
+ *   out    device [H] fp32 output of the last layer
+ *   idx    device [n_layers][K] int32, or NULL
+ *   w      device [n_layers][K] fp32, or NULL
+ * Errors as moe_route. */
+int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
+                     int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
+                     void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DEQUANT_H */

@@ -212,16 +212,18 @@ class Workload:
     x_bf16: bool = True
     norm: bool = False              # RMSNorm (eps 1e-6) before each layer; residual stream
     norm_eps: float = 1e-6
+    n_hot: int = N_HOT              # tiered: experts of prior rank 1..n_hot keep 4-bit codes
+    seed_override: Optional[int] = None
 
     @property
     def seed(self) -> int:
-        return config_seed(self.cfg)
+        return self.seed_override if self.seed_override is not None else config_seed(self.cfg)
 
     def expert_bits(self) -> np.ndarray:
         bits = np.full(self.E, self.bits_default, dtype=np.int32)
         if self.tiered:
             bits[:] = 2
-            bits[hot_set(self.seed, self.E)] = 4
+            bits[hot_set(self.seed, self.E, min(self.n_hot, self.E))] = 4
         return bits
 
     def blob(self, layer: int, e: int) -> np.ndarray:

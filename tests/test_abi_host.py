@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU): exported symbols, the packer against the oracle's
+independent unpack, and argument validation (each failing call returns its status before
+anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_expert_dequant_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dequant.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return M.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(M.exported_symbols()) == names
+
+
+def test_version_and_status_strings(L):
+    assert b"gfx950" in L.moe_version()
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(6) == b"MOE_ERR_WORKSPACE"
+
+
+def test_sizes_match_oracle(orc):
+    for H, I, bits in [(4096, 1024, 4), (4096, 1024, 2), (512, 256, 4), (192, 320, 2), (3072, 768, 4)]:
+        off, tot = orc.blob_layout(H, I, bits)
+        assert M.moe_packed_expert_bytes(H, I, bits) == tot
+        assert M.moe_expert_plane_offsets(H, I, bits) == off
+        assert M.moe_packed_codes_bytes(I, H, bits) == orc.codes_bytes(I, H, bits)
+        assert M.moe_packed_sb_bytes(I, H) == orc.sb_bytes(I, H)
+    assert M.moe_packed_expert_bytes(4096, 1024, 4) == 7_077_888
+    assert M.moe_packed_expert_bytes(100, 64, 4) == 0
+    assert M.moe_packed_expert_bytes(128, 64, 3) == 0
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_matrix_matches_oracle_unpack(orc, bits):
+    rng = np.random.default_rng(20 + bits)
+    R, C = 7, 320
+    codes = rng.integers(0, 1 << bits, (R, C)).astype(np.uint8)
+    scale = rng.integers(0, 1 << 16, R * (C // 64)).astype(np.uint16)
+    bias = rng.integers(0, 1 << 16, R * (C // 64)).astype(np.uint16)
+    cp, sp = M.moe_pack_matrix(codes, scale, bias, bits)
+    for r in range(R):
+        for c in range(0, C, 7):
+            assert orc.code(cp, R, C, bits, r, c) == codes[r, c]
+    assert np.array_equal(sp[0::2], scale) and np.array_equal(sp[1::2], bias)
+    c2, s2, b2 = M.moe_unpack_matrix(cp, sp, R, C, bits)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scale) and np.array_equal(b2, bias)
+
+
+def test_pack_expert_matches_oracle_dequant(orc):
+    rng = np.random.default_rng(30)
+    H, I, bits = 192, 128, 4
+    mats = []
+    for R, C in [(I, H), (I, H), (H, I)]:
+        codes = rng.integers(0, 16, (R, C)).astype(np.uint8)
+        s = (rng.uniform(0.002, 0.02, R * C // 64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        b = (rng.uniform(-0.1, 0.1, R * C // 64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        mats.append((codes, s, b))
+    blob = M.moe_pack_expert(mats, H, I, bits)
+    Wg, Wu, Wd = orc.expert_matrices(blob, H, I, bits)
+    for W, (codes, s, b) in zip((Wg, Wu, Wd), mats):
+        sf = orc.bf16_to_f32(s).reshape(W.shape[0], -1)
+        bf = orc.bf16_to_f32(b).reshape(W.shape[0], -1)
+        ref = codes.astype(np.float32) * np.repeat(sf, 64, 1) + np.repeat(bf, 64, 1)
+        assert np.array_equal(W, ref)
+
+
+def test_pack_rejects_bad_codes_and_buffers(L):
+    codes = np.full((2, 64), 4, dtype=np.uint8)
+    s = np.zeros(2, dtype=np.uint16)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_pack_matrix(codes, s, s, 2)           # code 4 does not fit in 2 bits
+    assert e.value.status == 4
+    out = np.zeros(8, dtype=np.uint8)
+    sb = np.zeros(4, dtype=np.uint16)
+    rc = L.moe_pack_matrix(codes.ctypes.data, s.ctypes.data, s.ctypes.data, 2, 64, 4, out.ctypes.data, 8,
+                           sb.ctypes.data, 8)
+    assert rc == 9                                   # MOE_ERR_BUFFER
+    assert b"need" in L.moe_last_error()
+
+
+# ----------------------------------------------------------------------------- validation
+FAKE = 1 << 20        # a 1 MiB-aligned non-NULL address that is never dereferenced
+
+
+def dims(H=512, I=256, E=8, K=2):
+    return M.moe_dims(H, I, E, K)
+
+
+def layer(router=FAKE, experts=FAKE, dtype=M.MOE_F32, bias=None, norm=None, eps=1e-6):
+    return M.moe_layer(router, dtype, eps, bias, norm, experts)
+
+
+def call_route(L, d, lay, x=FAKE, xdt=M.MOE_F32, T=1, idx=FAKE, w=FAKE, logits=FAKE, ws=None, wsb=0):
+    return L.moe_route(ctypes.byref(d) if d is not None else None, ctypes.byref(lay) if lay is not None else None,
+                       x, xdt, T, idx, w, logits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("d,status", [
+    (dims(H=500), 2), (dims(H=0), 2), (dims(I=32), 2), (dims(H=16384), 2), (dims(E=0), 2),
+    (dims(E=4096), 2), (dims(K=0), 2), (dims(K=9, E=16), 2), (dims(K=5, E=4), 2),
+    (dims(I=8192, K=8), 8),
+])
+def test_route_rejects_bad_dims(L, d, status):
+    assert call_route(L, d, layer()) == status
+    assert L.moe_last_error().startswith(M.STATUS[status].encode())
+
+
+def test_route_rejects_bad_arguments(L):
+    d = dims()
+    assert call_route(L, None, layer()) == 1
+    assert call_route(L, d, None) == 1
+    assert call_route(L, d, layer(router=None)) == 1
+    assert call_route(L, d, layer(experts=None)) == 1
+    assert call_route(L, d, layer(dtype=7)) == 3
+    assert call_route(L, d, layer(), xdt=9) == 3
+    assert call_route(L, d, layer(router=FAKE + 4)) == 5
+    assert call_route(L, d, layer(), x=FAKE + 8) == 5
+    assert call_route(L, d, layer(), x=None) == 1
+    assert call_route(L, d, layer(), T=0) == 2
+    assert call_route(L, d, layer(norm=FAKE, eps=float("nan"))) == 2
+    # logits NULL -> the workspace must hold them
+    assert call_route(L, d, layer(), logits=None) == 6
+    assert call_route(L, d, layer(), logits=None, ws=FAKE, wsb=16) == 6
+    assert call_route(L, d, layer(), logits=None, ws=FAKE + 16, wsb=1 << 20) == 5
+
+
+def test_expert_ffn_and_decode_validation(L):
+    d = dims()
+    lay = layer()
+    need = M.moe_workspace_bytes(M.MOE_OP_EXPERT_FFN, d, 1, 1)
+    assert need == 2 * 256 * 4
+    assert L.moe_expert_ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 1, FAKE, FAKE, FAKE, need - 1,
+                            None) == 6
+    assert L.moe_expert_ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 1, None, FAKE, FAKE, need,
+                            None) == 1
+    need = M.moe_workspace_bytes(M.MOE_OP_LAYER_DECODE, d, 1, 3)
+    assert need > 0 and M.moe_workspace_bytes(M.MOE_OP_LAYER_DECODE, d, 2, 3) == 0
+    arr = (M.moe_layer * 3)(layer(), layer(router=None), layer())
+    rc = L.moe_layer_decode(ctypes.byref(d), arr, 3, FAKE, M.MOE_F32, 0, FAKE + 4096, None, None, FAKE, need, None)
+    assert rc == 1 and b"layer 1" in L.moe_last_error()
+    arr = (M.moe_layer * 1)(layer())
+    assert L.moe_layer_decode(ctypes.byref(d), arr, 1, FAKE, M.MOE_F32, 8, FAKE + 4096, None, None, FAKE, need,
+                              None) == 8
+    assert L.moe_layer_decode(ctypes.byref(d), arr, 1, FAKE, M.MOE_F32, 0, FAKE, None, None, FAKE, need, None) == 2
+    assert L.moe_layer_decode(ctypes.byref(d), arr, 1, FAKE, M.MOE_F32, 0, FAKE + 4096, FAKE, None, FAKE, need,
+                              None) == 1
+    assert L.moe_layer_decode(ctypes.byref(d), arr, 0, FAKE, M.MOE_F32, 0, FAKE + 4096, None, None, FAKE, need,
+                              None) == 2
+    assert L.moe_combine(None, FAKE, 1, 2, 64, None, FAKE, None) == 1
+    assert L.moe_combine(FAKE, FAKE, 1, 9, 64, None, FAKE, None) == 2
+    assert L.moe_check_experts(None, 4) == 1

@@ -1,0 +1,175 @@
+"""GPU parity of the decode path (T = 1 per call) against the CPU oracle, through the C ABI.
+
+Routing indices must match the oracle exactly; router weights, logits, per-expert outputs and
+layer outputs must satisfy max|gpu - oracle| <= 2e-3 * ||oracle||_2 / sqrt(n) per token."""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import bit_expert_dequant_amd as M  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from moe_cases import (MIN_MARGIN, act_f64, act_tensor, assert_close, build_layer, oracle_layer,  # noqa: E402
+                       small_workload)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_decode(dl, x, residual=False):
+    wl = dl.wl
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(wl.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(wl.K, dtype=torch.float32, device="cuda")
+    M.moe_layer_decode(d, [dl.L], x, out, idx, w, residual=residual, ws=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def check_token(wl, ol, xg, x64, out, idx, w, residual=False, what=""):
+    ref = oracle.layer_token(x64, ol, wl.H, wl.I, wl.K, residual=residual)
+    assert ref.margin > MIN_MARGIN, f"{what}: routing margin {ref.margin:.2e} too small to compare"
+    assert list(idx) == list(ref.idx), f"{what}: idx {list(idx)} != oracle {list(ref.idx)}"
+    assert_close(w, ref.w, f"{what} weights")
+    assert abs(float(np.sum(w)) - 1.0) < 4 * 2**-24 * wl.K
+    assert_close(out, ref.out, f"{what} out")
+    return ref
+
+
+SMALL = [
+    # name, H, I, E, K, bits, extra
+    ("h64_i64_e4_k2_4b", 64, 64, 4, 2, 4, {}),
+    ("h128_i192_e6_k3_2b", 128, 192, 6, 3, 2, {}),
+    ("h192_i320_e5_k1_4b_ragged", 192, 320, 5, 1, 4, {}),
+    ("h512_i256_e8_k2_fp32", 512, 256, 8, 2, 4, {"router_bf16": False, "x_bf16": False}),
+    ("h1024_i512_e16_k4_norm", 1024, 512, 16, 4, 4, {"norm": True}),
+    ("h2048_i768_e32_k8_4b", 2048, 768, 32, 8, 4, {}),
+    ("h3072_i1536_e12_k4_2b_zipf", 3072, 1536, 12, 4, 2, {"zipf": True}),
+    ("h4096_i1024_e20_k4_tiered", 4096, 1024, 20, 4, 4, {"tiered": True, "n_hot": 7, "zipf": True}),
+    ("h8192_i256_e9_k2_fp32x", 8192, 256, 9, 2, 4, {"x_bf16": False}),
+    ("h640_i1344_e7_k7_tiered_norm", 640, 1344, 7, 7, 4, {"tiered": True, "n_hot": 3, "norm": True}),
+    ("h256_i64_e1_k1", 256, 64, 1, 1, 2, {}),
+    ("h4096_i4096_e8_k8_4b", 4096, 4096, 8, 8, 4, {"x_bf16": False}),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_layer_decode_small_shapes(case):
+    name, H, I, E, K, bits, extra = case
+    say(f"[decode small] {name}")
+    wl = small_workload(name, 0xC0DE + H + I + E, H, I, E, K, bits, **extra)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    bank = wl.tokens_bank(3)
+    for t in range(3):
+        residual = t == 2
+        x = act_tensor(wl, bank[t])
+        out, idx, w = run_decode(dl, x, residual=residual)
+        check_token(wl, ol, x, act_f64(wl, bank[t]), out, idx, w, residual, f"{name} token {t}")
+
+
+@pytest.mark.parametrize("case", SMALL[:8], ids=[c[0] for c in SMALL[:8]])
+def test_route_ffn_combine_small_shapes(case):
+    """The separate C-ABI calls: moe_route (idx, w, logits), moe_expert_ffn (y per expert),
+    moe_combine (out)."""
+    name, H, I, E, K, bits, extra = case
+    say(f"[route/ffn/combine small] {name}")
+    wl = small_workload(name, 0xBEEF + H + I + E, H, I, E, K, bits, **extra)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    bank = wl.tokens_bank(2)
+    d = M.make_dims(H, I, E, K)
+    for t in range(2):
+        x = act_tensor(wl, bank[t]).reshape(1, H)
+        idx = torch.empty(1, K, dtype=torch.int32, device="cuda")
+        w = torch.empty(1, K, dtype=torch.float32, device="cuda")
+        logits = torch.empty(1, E, dtype=torch.float32, device="cuda")
+        M.moe_route(d, dl.L, x, idx, w, logits)
+        y = torch.empty(1, K, H, dtype=torch.float32, device="cuda")
+        ws = M.workspace(M.MOE_OP_EXPERT_FFN, d, 1)
+        M.moe_expert_ffn(d, dl.L, x, idx, y, ws)
+        out = torch.empty(1, H, dtype=torch.float32, device="cuda")
+        M.moe_combine(y, w, out)
+        torch.cuda.synchronize()
+        ref = oracle.layer_token(act_f64(wl, bank[t]), ol, H, I, K)
+        assert ref.margin > MIN_MARGIN
+        assert list(idx.cpu().numpy()[0]) == list(ref.idx)
+        assert_close(logits.cpu().numpy()[0], ref.logits, f"{name} logits")
+        assert_close(w.cpu().numpy()[0], ref.w, f"{name} w")
+        yk = y.cpu().numpy()[0]
+        for k in range(K):
+            assert_close(yk[k], ref.y[k], f"{name} y[{k}]")
+        assert_close(out.cpu().numpy()[0], ref.out, f"{name} out")
+
+
+def test_expert_ffn_given_routing_and_invalid_index():
+    """moe_expert_ffn with caller-chosen experts (not the router's), including an out-of-range
+    index, which yields a zero row."""
+    wl = small_workload("given", 77, 512, 256, 8, 3, 4)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    x64 = act_f64(wl, wl.tokens_bank(1)[0])
+    x = act_tensor(wl, wl.tokens_bank(1)).reshape(1, wl.H)
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    idx = torch.tensor([[5, 8, 0]], dtype=torch.int32, device="cuda")
+    y = torch.full((1, 3, wl.H), 7.0, dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(d, dl.L, x, idx, y, M.workspace(M.MOE_OP_EXPERT_FFN, d, 1))
+    torch.cuda.synchronize()
+    yk = y.cpu().numpy()[0]
+    for k, e in [(0, 5), (2, 0)]:
+        _, _, _, ref = oracle.expert(ol.blob(e), 4, wl.H, wl.I, x64)
+        assert_close(yk[k], ref, f"y[{k}] expert {e}")
+    assert np.all(yk[1] == 0.0)
+
+
+def test_decode_is_deterministic():
+    wl = small_workload("det", 99, 4096, 1024, 16, 4, 4, norm=True)
+    dl = build_layer(wl)
+    x = act_tensor(wl, wl.tokens_bank(1)[0])
+    a = run_decode(dl, x, residual=True)
+    b = run_decode(dl, x, residual=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_device_filler_matches_host_generator():
+    for bits in (4, 2):
+        H, I = 512, 256
+        stride = synth.blob_layout(H, I, bits)[1]
+        buf = torch.full((3 * stride,), 0xAB, dtype=torch.uint8, device="cuda")
+        synth.fill_blobs_device(buf.data_ptr(), stride, 3, 5, 2, 1234, H, I, bits,
+                                torch.cuda.current_stream().cuda_stream)
+        host = buf.cpu().numpy().reshape(3, stride)
+        for i in range(3):
+            assert np.array_equal(host[i], synth.expert_blob(1234, 2, 5 + i, H, I, bits))
+
+
+def test_two_layer_stack_small():
+    wl = small_workload("stack2", 4242, 1024, 512, 16, 4, 4, norm=True, n_layers=3, x_bf16=True)
+    dls = [build_layer(wl, l) for l in range(3)]
+    ols = [oracle_layer(wl, l) for l in range(3)]
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 3)
+    bank = wl.tokens_bank(2)
+    for t in range(2):
+        x = act_tensor(wl, bank[t])
+        out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(3, wl.K, dtype=torch.int32, device="cuda")
+        w = torch.empty(3, wl.K, dtype=torch.float32, device="cuda")
+        M.moe_layer_decode(d, [dl.L for dl in dls], x, out, idx, w, residual=True, ws=ws)
+        torch.cuda.synchronize()
+        ref_out, refs = oracle.stack_token(act_f64(wl, bank[t]), ols, wl.H, wl.I, wl.K, residual=True)
+        for l, r in enumerate(refs):
+            assert r.margin > MIN_MARGIN
+            assert list(idx.cpu().numpy()[l]) == list(r.idx), f"layer {l}"
+            assert_close(w.cpu().numpy()[l], r.w, f"layer {l} w")
+        assert_close(out.cpu().numpy(), ref_out, "stack out")
