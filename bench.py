@@ -1,0 +1,306 @@
+"""Benchmark of the MoE expert path on one MI355X.
+
+Default workload: one MoE layer at hidden 4096, expert intermediate 1024, 512 experts, top-4,
+4-bit group-64 affine experts (bf16 scale/bias), router bf16 512 x 4096, one decode token per
+step.  A step is one token through the whole path (router, softmax/top-K/renormalise, gate/up
++ SwiGLU for the 4 experts, down + weighted combine), issued as one moe_layer_decode call; the
+steps run back to back on one stream (each call is complete before the next starts) and are
+captured in HIP graphs.  Tokens rotate through a bank of 4096 distinct seeded activations so
+that routing, and the experts read, change every step (3.4 GiB of experts, far beyond the
+256 MB last-level cache).  Inputs are synthetic and already resident in HBM.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config {0,1,2,3,4}] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--warmup", type=int, default=512)
+    p.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    p.add_argument("--graph-steps", type=int, default=0, help="steps per captured graph (0: auto)")
+    p.add_argument("--no-graph", action="store_true", help="issue steps eagerly instead of via HIP graphs")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["moe_decode.hip", "moe_grouped.hip", "moe_api.cpp"]:
+        p = os.path.join(ROOT, "bit_expert_dequant_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload_key: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, valid only while the
+    kernel sources are unchanged since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(workload_key, {}).get(kernel)
+        if e and e.get("source_hash") == source_hash():
+            return e.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path runs on a single MI355X here "
+              "(see the sharding notes in DESIGN.md); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_expert_dequant_amd as M
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from moe_cases import act_f64, build_layer, oracle_layer, to_bf16_tensor
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[a.config]
+    H, I, E, K = wl.H, wl.I, wl.E, wl.K
+    d = M.make_dims(H, I, E, K)
+    batched = wl.tokens > 1
+    log(f"[bench] config {a.config}: {wl.name}")
+
+    t0 = time.time()
+    layers = [build_layer(wl, l) for l in range(wl.n_layers)]
+    torch.cuda.synchronize()
+    log(f"[bench] built {wl.n_layers} layer(s) in {time.time() - t0:.1f}s")
+    bits = wl.expert_bits()
+    blob_bytes = np.array([wl.blob_bytes(int(b)) for b in bits], dtype=np.int64)
+    gu_bytes = np.array([2 * (M.moe_expert_plane_offsets(H, I, int(b))[2]) for b in bits], dtype=np.int64)
+    router_bytes = E * H * (2 if wl.router_bf16 else 4)
+    norm_bytes = H * 2 if wl.norm else 0
+
+    n_bank = 4096 if not batched else 16 * wl.tokens
+    bank_np = wl.tokens_bank(n_bank)
+    bank = to_bf16_tensor(bank_np, dev) if wl.x_bf16 else torch.from_numpy(bank_np).to(dev)
+    L = [dl.L for dl in layers]
+
+    stream = torch.cuda.current_stream()
+    if not batched:
+        G = a.graph_steps or (256 if wl.n_layers == 1 else 16)
+        ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, wl.n_layers)
+        outs = torch.empty(G, H, dtype=torch.float32, device=dev)
+        idxs = torch.empty(n_bank, wl.n_layers, K, dtype=torch.int32, device=dev)
+        wts = torch.empty(n_bank, wl.n_layers, K, dtype=torch.float32, device=dev)
+        residual = wl.norm
+
+        def step(i, g):
+            M.moe_layer_decode(d, L, bank[i % n_bank], outs[g], idxs[i % n_bank], wts[i % n_bank],
+                               residual=residual, ws=ws)
+    else:
+        T = wl.tokens
+        G = a.graph_steps or 1
+        ws_r = M.workspace(M.MOE_OP_ROUTE, d, T)
+        ws_f = M.workspace(M.MOE_OP_EXPERT_FFN, d, T)
+        y = torch.empty(T, K, H, dtype=torch.float32, device=dev)
+        outs = torch.empty(T, H, dtype=torch.float32, device=dev)
+        idxs = torch.empty(n_bank // T, T, K, dtype=torch.int32, device=dev)
+        wts = torch.empty(n_bank // T, T, K, dtype=torch.float32, device=dev)
+        bank_b = bank.view(n_bank // T, T, H)
+
+        def step(i, g):
+            j = i % (n_bank // T)
+            M.moe_route(d, L[0], bank_b[j], idxs[j], wts[j], ws=ws_r)
+            M.moe_expert_ffn(d, L[0], bank_b[j], idxs[j], y, ws_f)
+            M.moe_combine(y, wts[j], outs)
+
+    # eager warm-up (also sets kernel attributes before any capture)
+    for i in range(min(8, a.warmup) or 1):
+        step(i, i % G)
+    torch.cuda.synchronize()
+
+    graphs = []
+    use_graph = not a.no_graph
+    n_cycle = n_bank if not batched else n_bank // wl.tokens
+    if use_graph:
+        n_graphs = max(1, n_cycle // G)
+        for gi in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(G):
+                    step(gi * G + s, s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"[bench] captured {len(graphs)} graph(s) of {G} step(s)")
+
+    def run(n_steps, offset=0):
+        if use_graph:
+            reps = max(1, n_steps // G)
+            for r in range(reps):
+                graphs[(offset // G + r) % len(graphs)].replay()
+            return reps * G
+        for i in range(n_steps):
+            step(offset + i, (offset + i) % G)
+        return n_steps
+
+    run(a.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    w0 = time.perf_counter()
+    done = run(a.steps, offset=0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / done
+    log(f"[bench] timed {done} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e3:.1f} ms)")
+
+    # exact weight bytes per step from the routing the timed steps used
+    idx_h = idxs.cpu().numpy()
+    steps_idx = [(i % (n_cycle)) for i in range(done)]
+    if not batched:
+        per_tok = np.array([sum(router_bytes + norm_bytes + blob_bytes[idx_h[t, l]].sum()
+                                for l in range(wl.n_layers)) for t in range(n_bank)], dtype=np.float64)
+        bytes_per_step = float(np.mean(per_tok[[s % n_bank for s in steps_idx]]))
+        tokens_per_step = 1
+    else:
+        per_b = []
+        for j in range(n_cycle):
+            sel = np.unique(idx_h[j].reshape(-1))
+            per_b.append(router_bytes + blob_bytes[sel].sum())
+        per_b = np.array(per_b, dtype=np.float64)
+        bytes_per_step = float(np.mean(per_b[[s % n_cycle for s in steps_idx]]))
+        tokens_per_step = wl.tokens
+    tok_s = tokens_per_step / (ms_per_step * 1e-3)
+    gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] {tok_s:,.0f} tok/s, {gbps:,.1f} GB/s of weights ({gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)")
+
+    # per-kernel durations (events on the library's stream, eager issue)
+    roof = None
+    kernel_us = {}
+    if not batched:
+        n_t = min(a.timing_steps, n_bank)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * wl.n_layers + 1)] for _ in range(n_t)]
+        for row in evs:          # torch creates the HIP event on first record
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for t in range(n_t):
+            M.moe_layer_decode_timed(d, L, bank[t], outs[t % G], evs[t], idxs[t], wts[t], residual=wl.norm, ws=ws)
+        torch.cuda.synchronize()
+        names = ["router", "gateup", "down"]
+        dur = {n: [] for n in names}
+        gu_b = []
+        for t in range(n_t):
+            for l in range(wl.n_layers):
+                for j, n in enumerate(names):
+                    dur[n].append(evs[t][3 * l + j].elapsed_time(evs[t][3 * l + j + 1]) * 1e3)
+                gu_b.append(gu_bytes[idx_h[t, l]].sum())
+        kernel_us = {n: float(np.mean(v)) for n, v in dur.items()}
+        gu_us = kernel_us["gateup"]
+        achieved = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU, all K experts)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic("k_gateup", f"config{a.config}"),
+                "bytes_per_launch": float(np.mean(gu_b)), "us_per_launch": round(gu_us, 3)}
+        log(f"[bench] kernel us: {kernel_us}; gate/up {achieved:,.1f} GB/s")
+
+    # CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    parity = None
+    if not a.no_cpu:
+        import oracle
+        cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        ols = [oracle_layer(wl, l) for l in range(wl.n_layers)]
+        x0 = act_f64(wl, bank_np[0])
+        # one token first to size the sample
+        t1 = time.perf_counter()
+        oracle.stack_token(x0, ols, H, I, K, residual=wl.norm) if wl.n_layers > 1 else \
+            oracle.layer_token(x0, ols[0], H, I, K)
+        per = time.perf_counter() - t1
+        n_s = max(1, min(256, int(a.cpu_seconds / max(per, 1e-3))))
+        if batched:
+            n_s = min(n_s, wl.tokens)
+        # pre-generate the expert blobs the sample needs, so that only the oracle is timed
+        sample = list(range(n_s))
+        for t in sample:
+            for l in range(wl.n_layers):
+                for e in (idx_h[t, l] if not batched else idx_h[0, t]):
+                    ols[l].blob(int(e))
+        t1 = time.perf_counter()
+        refs = []
+        for t in sample:
+            xt = act_f64(wl, bank_np[t])
+            if wl.n_layers > 1:
+                refs.append(oracle.stack_token(xt, ols, H, I, K, residual=wl.norm)[0])
+            else:
+                refs.append(oracle.layer_token(xt, ols[0], H, I, K).out)
+        cpu_s = time.perf_counter() - t1
+        cpu_tok_s = n_s / cpu_s
+        cpu = {"value": round(cpu_tok_s, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n_s} token(s) of this workload through the CPU oracle (fp32 dequant, fp64 "
+                         f"accumulation, OpenMP over output rows), timed after host generation of the "
+                         f"selected experts; {cpu_s:.1f} s",
+               "weight_GBps": round(cpu_tok_s * bytes_per_step / tokens_per_step / 1e9, 4)}
+        log(f"[bench] oracle: {cpu_tok_s:.3f} tok/s on {cores} threads ({n_s} tokens, {cpu_s:.1f}s)")
+        # parity of the same tokens (GPU eager call vs oracle)
+        if not batched:
+            errs = []
+            o = torch.empty(H, dtype=torch.float32, device=dev)
+            for t, ref in zip(sample, refs):
+                M.moe_layer_decode(d, L, bank[t], o, residual=wl.norm, ws=ws)
+                g = o.cpu().numpy().astype(np.float64)
+                errs.append(np.abs(g - ref).max() / (np.linalg.norm(ref) / math.sqrt(ref.size)))
+            parity = {"tokens": len(errs), "max_err_over_rms": float(max(errs)), "tolerance": 2e-3,
+                      "ok": bool(max(errs) <= 2e-3)}
+
+    cfg = {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": K,
+           "layers": wl.n_layers, "tokens_per_step": tokens_per_step, "bits": sorted(set(bits.tolist())),
+           "group": 64, "graph_steps": G if use_graph else 0, "bank_tokens": n_bank}
+    line = {
+        "metric": "MoE decode tok/s and weight GB/s (% of HBM peak), 4-bit, 512 experts top-4",
+        "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": done, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": cfg,
+        "weight_bytes_per_step": bytes_per_step, "weight_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

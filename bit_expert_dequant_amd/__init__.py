@@ -78,6 +78,7 @@ def lib():
             "moe_expert_ffn": (I32, [P, P, P, I32, I32, P, P, P, SZ, P]),
             "moe_combine": (I32, [P, P, I32, I32, I32, P, P, P]),
             "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
+            "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -91,7 +92,7 @@ def exported_symbols() -> List[str]:
     return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
-            "moe_expert_ffn", "moe_combine", "moe_layer_decode"]
+            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed"]
 
 
 def _check(status: int):
@@ -254,3 +255,18 @@ def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, 
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                   _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
+
+
+def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,
+                           residual: bool = False, ws=None, stream=None) -> None:
+    """As moe_layer_decode, recording ``events`` (3*len(layers)+1 torch.cuda.Event objects with
+    timing enabled) before the first kernel and after every kernel, on the library's stream."""
+    arr = (moe_layer * len(layers))(*[L.c for L in layers])
+    handles = [e.cuda_event for e in events]
+    if not all(handles):
+        raise ValueError("events must have been recorded once (torch creates HIP events lazily)")
+    ev = (ctypes.c_void_p * len(events))(*handles)
+    flags = MOE_FLAG_RESIDUAL if residual else 0
+    _check(lib().moe_layer_decode_timed(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
+                                        _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(stream), ev))

@@ -94,11 +94,16 @@ struct Carve {
 };
 
 size_t route_ws(const moe_dims *d, int T) { return r256((size_t)T * d->n_experts * 4); }
-size_t ffn_ws(const moe_dims *d, int T) { return r256((size_t)T * d->top_k * d->inter * 4); }
+size_t ffn_ws(const moe_dims *d, int T) {
+    Carve c{nullptr};
+    c.take<float>((size_t)T * d->top_k * d->inter);
+    c.take<uint64_t>((size_t)T * d->top_k);
+    return c.off;
+}
 size_t decode_ws(const moe_dims *d) {
     Carve c{nullptr};
     c.take<float>(d->n_experts);
-    c.take<int32_t>(d->top_k);
+    c.take<uint64_t>(d->top_k);
     c.take<float>(d->top_k);
     c.take<float>((size_t)d->top_k * d->inter);
     c.take<float>(2 * (size_t)d->hidden);
@@ -288,13 +293,14 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MOE_ERR_ALIGN, "idx/y not 4-byte aligned");
     if (int s = check_ws(ws, ws_bytes, ffn_ws(dims, T))) return s;
     hipStream_t st = (hipStream_t)stream;
-    float *h = (float *)ws;
+    Carve c{(char *)ws};
+    float *h = c.take<float>((size_t)T * dims->top_k * dims->inter);
+    uint64_t *sel = c.take<uint64_t>((size_t)T * dims->top_k);
     moe::GateUpLaunch ga{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, nullptr, idx, nullptr, nullptr,
-                         nullptr, nullptr, layer->experts, h, dims->hidden, dims->inter, dims->n_experts, dims->top_k, T};
+                         sel, nullptr, layer->experts, h, dims->hidden, dims->inter, dims->n_experts, dims->top_k, T};
     if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
-    moe::DownLaunch da{h, idx, nullptr, layer->experts, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter,
-                       dims->top_k, T};
-    if (int s = launched(moe::launch_down(da, dims->n_experts, st), "down")) return s;
+    moe::DownLaunch da{h, sel, nullptr, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter, dims->top_k, T};
+    if (int s = launched(moe::launch_down(da, st), "down")) return s;
     return ok();
 }
 
@@ -309,8 +315,20 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
     return ok();
 }
 
-int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
-                     unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+static int record(void *const *events, int i, hipStream_t st) {
+    if (!events) return MOE_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e == hipSuccess)
+        e = cs == hipStreamCaptureStatusActive ? hipEventRecordWithFlags((hipEvent_t)events[i], st, hipEventRecordExternal)
+                                               : hipEventRecord((hipEvent_t)events[i], st);
+    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "event %d: %s", i, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
+                             int x_dtype, unsigned flags, float *out, int32_t *idx, float *w, void *ws,
+                             size_t ws_bytes, void *stream, void *const *events) {
     if (int s = check_dims(dims)) return s;
     if (!layers) return fail(MOE_ERR_NULL, "layers is NULL");
     if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_SHAPE, "n_layers=%d outside [1, 4096]", n_layers);
@@ -328,12 +346,13 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
     const int H = dims->hidden, I = dims->inter, E = dims->n_experts, K = dims->top_k;
     Carve c{(char *)ws};
     float *logits = c.take<float>(E);
-    int32_t *idx_ws = c.take<int32_t>(K);
+    uint64_t *sel_ws = c.take<uint64_t>(K);
     float *w_ws = c.take<float>(K);
     float *h = c.take<float>((size_t)K * I);
     float *xbuf = c.take<float>(2 * (size_t)H);
     hipStream_t st = (hipStream_t)stream;
     const bool residual = flags & MOE_FLAG_RESIDUAL;
+    if (int s = record(events, 0, st)) return s;
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer &L = layers[l];
         const void *xl = l == 0 ? x : (const void *)(xbuf + (size_t)((l - 1) & 1) * H);
@@ -341,14 +360,31 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
         float *ol = l == n_layers - 1 ? out : xbuf + (size_t)(l & 1) * H;
         moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, logits, H, E, 1};
         if (int s = launched(moe::launch_router(ra, st), "router")) return s;
+        if (int s = record(events, 3 * l + 1, st)) return s;
         moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, logits, nullptr,
-                             idx ? idx + (size_t)l * K : nullptr, w ? w + (size_t)l * K : nullptr, idx_ws, w_ws,
+                             idx ? idx + (size_t)l * K : nullptr, w ? w + (size_t)l * K : nullptr, sel_ws, w_ws,
                              L.experts, h, H, I, E, K, 1};
         if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
-        moe::DownLaunch da{h, idx_ws, w_ws, L.experts, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
-        if (int s = launched(moe::launch_down(da, E, st), "down")) return s;
+        if (int s = record(events, 3 * l + 2, st)) return s;
+        moe::DownLaunch da{h, sel_ws, w_ws, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
+        if (int s = launched(moe::launch_down(da, st), "down")) return s;
+        if (int s = record(events, 3 * l + 3, st)) return s;
     }
     return ok();
+}
+
+int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
+                     unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
+                           unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes,
+                           void *stream, void *const *events) {
+    if (!events) return fail(MOE_ERR_NULL, "events is NULL");
+    for (int i = 0; i < 3 * (n_layers > 0 ? n_layers : 0) + 1 && n_layers <= 4096; ++i)
+        if (!events[i]) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
+    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -3,10 +3,10 @@
 // Kernels (one launch each, stream-ordered, no grid-wide barriers):
 //   k_router : [RMSNorm] + router matvec -> logits[T][E]
 //   k_topk   : softmax / top-K / renormalise (for moe_route)
-//   k_gateup : every workgroup recomputes top-K from the logits (no host round trip and no
-//              grid barrier), stages the activation once in LDS in the order the unpack
-//              consumes it, then streams the gate and up rows of all K selected experts in one
-//              launch and writes h = silu(g) * u
+//   k_gateup : every wavefront recomputes top-K from the logits (no host round trip, no grid
+//              barrier), stages the activation once in LDS in the order the unpack consumes it,
+//              and streams the gate and up rows of all K selected experts in one launch,
+//              writing h = silu(g) * u
 //   k_down   : down projection of all K experts for a block of output rows, combined with the
 //              routing weights (+ residual) in registers before a single cross-lane reduction
 //   k_combine: standalone weighted combine
@@ -29,6 +29,11 @@
 // wave covers several rows at once, lanes grouped by the row's slot count rounded up to a power
 // of two.  Both code widths share the geometry, so experts of different widths combine in
 // registers, and a lane's activation operands come from LDS once per work unit.
+//
+// Latency.  A decode step moves ~30 MB in a few microseconds, so each kernel is built to pay
+// about two memory latencies: all independent loads (logits, descriptor table, activation,
+// norm weight) are issued together; the first work unit's weight loads are issued before the
+// activation layouts are written to LDS, so they are in flight while the workgroup stages.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -38,6 +43,7 @@
 namespace moe {
 namespace {
 
+#define GLOBAL_AS __attribute__((address_space(1)))
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -46,6 +52,7 @@ constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both 16-bit halves
 constexpr int kBlock = 256;               // threads per workgroup (4 wavefronts)
 constexpr int kWaves = kBlock / 64;
 constexpr int kDPS = 16;                  // activation dwords per slot (32 columns, bf16 pairs)
+constexpr int kTabMax = 512;              // experts whose descriptors are prefetched into LDS
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
@@ -85,47 +92,78 @@ __host__ __device__ __forceinline__ int next_pow2(int v) {
 }
 __host__ __device__ __forceinline__ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// --------------------------------------------------------------------------- activation layout
-// Slot s covers columns 32s..32s+31.  4-bit: the slot's 16 bytes are 4 dwords of 8 codes and the
-// AND-OR at shift 4i pairs columns (8k+i, 8k+i+4) of dword k; 2-bit: 8 bytes = 2 dwords of 16
-// codes and shift 2i pairs (16k+i, 16k+i+8).  Activation dword d of slot s packs the same pair.
-template <int BITS>
-__device__ __forceinline__ int arr_col(int d, int hf) {
-    const int s = d >> 4, j = d & 15;
-    if (BITS == 4) return s * 32 + (j >> 2) * 8 + (j & 3) + 4 * hf;
-    return s * 32 + (j >> 3) * 16 + (j & 7) + 8 * hf;
+// Selected expert, packed for the down kernel: blob address (256-byte aligned) | code width.
+__device__ __forceinline__ uint64_t pack_sel(uint64_t blob, uint32_t bits) { return blob ? (blob | (bits == 2 ? 2u : 4u)) : 0; }
+__device__ __forceinline__ uint64_t sel_blob(uint64_t s) { return s & ~(uint64_t)255; }
+__device__ __forceinline__ int sel_bits(uint64_t s) { return (int)(s & 255u) == 2 ? 2 : 4; }
+
+// Packed selection of expert e (0 for an index outside [0, E)).
+__device__ __forceinline__ uint64_t lookup_sel(int e, int E, bool use_tab, const uint64_t *tab,
+                                               const moe_expert_desc *experts) {
+    if (e < 0 || e >= E) return 0;
+    if (use_tab) return tab[e];
+    const moe_expert_desc d = experts[e];
+    return pack_sel(d.blob, d.bits);
+}
+
+// --------------------------------------------------------------------------- activation staging
+// A thread stages "chunks" of 16 consecutive columns (two chunks per 32-column slot).
+// Slot s: 4-bit dword s*16 + 4k + i packs columns (8k+i, 8k+i+4), k < 4, i < 4; 2-bit dword
+// s*16 + 8k + i packs (16k+i, 16k+i+8), k < 2, i < 8.  Chunk m = 2s + half therefore owns the 8
+// contiguous dwords s*16 + 8*half .. +8 of both layouts.
+__device__ __forceinline__ void load_chunk16(const void *x, int dtype, int m, float v[16]) {
+    if (dtype == MOE_BF16) {
+        const u32x4 *p = (const u32x4 *)((const uint16_t *)x + 16 * (size_t)m);
+        const u32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_f32(a[j] & 0xFFFFu); v[2 * j + 1] = bf16_f32(a[j] >> 16);
+            v[8 + 2 * j] = bf16_f32(b[j] & 0xFFFFu); v[8 + 2 * j + 1] = bf16_f32(b[j] >> 16);
+        }
+    } else {
+        const u32x4 *p = (const u32x4 *)((const float *)x + 16 * (size_t)m);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 a = p[q];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(a[j]);
+        }
+    }
+}
+
+// Writes chunk m's dwords of one layout (BITS) and returns the chunk's sum of hi + lo.
+template <int BITS, bool SPLIT>
+__device__ __forceinline__ float write_chunk(int m, const float v[16], uint32_t *hi, uint32_t *lo) {
+    uint32_t hv[16], lv[16];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        hv[i] = bf16_rne(v[i]);
+        lv[i] = SPLIT ? bf16_rne(v[i] - bf16_f32(hv[i])) : 0u;
+        sum += bf16_f32(hv[i]) + (SPLIT ? bf16_f32(lv[i]) : 0.f);
+    }
+    uint32_t H[8], L[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int a = BITS == 4 ? (j >> 2) * 8 + (j & 3) : j;
+        const int b = a + (BITS == 4 ? 4 : 8);
+        H[j] = hv[a] | (hv[b] << 16);
+        L[j] = lv[a] | (lv[b] << 16);
+    }
+    const int d0 = (m >> 1) * kDPS + 8 * (m & 1);
+    *(u32x4 *)(hi + d0) = u32x4{H[0], H[1], H[2], H[3]};
+    *(u32x4 *)(hi + d0 + 4) = u32x4{H[4], H[5], H[6], H[7]};
+    if (SPLIT) {
+        *(u32x4 *)(lo + d0) = u32x4{L[0], L[1], L[2], L[3]};
+        *(u32x4 *)(lo + d0 + 4) = u32x4{L[4], L[5], L[6], L[7]};
+    }
+    return sum;
 }
 
 struct ActView {
     const uint32_t *hi, *lo;  // [cols/2] packed bf16 pairs (lo: bf16 of the remainder)
     const float *xs;          // [cols/32] sum over the slot of hi + lo
 };
-
-template <int BITS, bool SPLIT, typename F>
-__device__ void stage_layout(F value, int cols, uint32_t *hi, uint32_t *lo) {
-    for (int d = threadIdx.x; d < cols / 2; d += blockDim.x) {
-        const float v0 = value(arr_col<BITS>(d, 0)), v1 = value(arr_col<BITS>(d, 1));
-        const uint32_t h0 = bf16_rne(v0), h1 = bf16_rne(v1);
-        hi[d] = h0 | (h1 << 16);
-        if (SPLIT) lo[d] = bf16_rne(v0 - bf16_f32(h0)) | (bf16_rne(v1 - bf16_f32(h1)) << 16);
-    }
-}
-// Per-slot sums of the values the dot products actually see (hi + lo).
-template <bool SPLIT>
-__device__ void stage_sums(int cols, const uint32_t *hi, const uint32_t *lo, float *xs) {
-    for (int s = threadIdx.x; s < cols / 32; s += blockDim.x) {
-        float t = 0.f;
-        for (int j = 0; j < kDPS; ++j) {
-            const uint32_t h = hi[s * kDPS + j];
-            t += bf16_f32(h & 0xFFFFu) + bf16_f32(h >> 16);
-            if (SPLIT) {
-                const uint32_t l = lo[s * kDPS + j];
-                t += bf16_f32(l & 0xFFFFu) + bf16_f32(l >> 16);
-            }
-        }
-        xs[s] = t;
-    }
-}
 
 // --------------------------------------------------------------------------- slot dot products
 // s * sum(q x) + b * sum(x) over one slot, given its codes and (scale, bias) dword.
@@ -152,10 +190,13 @@ __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t *X, cons
     return s * acc + (b - 128.f * s) * xs;
 }
 
+typedef const GLOBAL_AS uint8_t *gbytes;
+typedef const GLOBAL_AS uint32_t *gwords;
+
 template <int BITS>
-__device__ __forceinline__ u32x4 load_slot(const uint8_t *row, int slot) {
-    if (BITS == 4) return *(const u32x4 *)(row + (size_t)slot * 16);
-    const u32x2 v = *(const u32x2 *)(row + (size_t)slot * 8);
+__device__ __forceinline__ u32x4 load_slot(gbytes row, int slot) {
+    if (BITS == 4) return *(const GLOBAL_AS u32x4 *)(row + (size_t)slot * 16);
+    const u32x2 v = *(const GLOBAL_AS u32x2 *)(row + (size_t)slot * 8);
     return u32x4{v.x, v.y, 0u, 0u};
 }
 
@@ -179,195 +220,316 @@ __device__ __forceinline__ Geo make_geo(int cols) {
     return g;
 }
 
+// Weight planes are read through global (address space 1) pointers: the blob addresses come from
+// the descriptor table as integers, and generic pointers would turn every load into a flat load.
 struct Planes {
-    const uint8_t *q; const uint32_t *sb;
+    gbytes q; gwords sb;
 };
-__device__ __forceinline__ void expert_planes(const uint8_t *blob, int H, int I, int bits, Planes p[3]) {
+__device__ __forceinline__ void expert_planes(uint64_t blob_addr, int H, int I, int bits, Planes p[3]) {
+    gbytes blob = (gbytes)blob_addr;
     const size_t cin = (size_t)I * H * bits / 8, sbin = (size_t)I * (H / 64) * 4;
     const size_t cout = (size_t)H * I * bits / 8;
     size_t off = 0;
     p[0].q = blob + off; off = round256(off + cin);
-    p[0].sb = (const uint32_t *)(blob + off); off = round256(off + sbin);
+    p[0].sb = (gwords)(blob + off); off = round256(off + sbin);
     p[1].q = blob + off; off = round256(off + cin);
-    p[1].sb = (const uint32_t *)(blob + off); off = round256(off + sbin);
+    p[1].sb = (gwords)(blob + off); off = round256(off + sbin);
     p[2].q = blob + off; off = round256(off + cout);
-    p[2].sb = (const uint32_t *)(blob + off);
+    p[2].sb = (gwords)(blob + off);
 }
 
 // --------------------------------------------------------------------------- top-K (one wave)
 // Largest K logits, descending, equal values -> lower index; NaN counts as -inf.  The weights are
 // the softmax over the selected logits, which equals the softmax over all E renormalised.
-// `lg` is the logit row in LDS (E <= MOE_MAX_EXPERTS, so a lane owns at most 32 entries).
-__device__ void wave_topk(const float *lg, int E, int K, int *s_idx, float *s_w) {
-    const int lane = threadIdx.x & 63;
-    const int nper = (E + 63) / 64;
-    uint32_t taken = 0;
-    float top[MOE_MAX_TOPK];
-    int topi[MOE_MAX_TOPK];
+//
+// A logit is compared through an order-preserving 32-bit key (its fp32 bits with the sign folded;
+// -0 is first canonicalised to +0 so that equal floats give equal keys).  Lane l owns logits
+// l, l+64, ... and keeps its best untaken key ("head").  A round takes the wave maximum of the
+// heads (DPP inside 16-lane rows, readlane across rows); the lanes holding it are found with a
+// ballot, and only when several lanes tie does a second reduction pick the lowest expert index.
+// The winning lane then recomputes its head from its NP registers.
+__device__ __forceinline__ uint32_t f32_order(float v) {
+    v = (v != v) ? -INFINITY : v + 0.0f;
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_f32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Wave-wide max / min (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp32<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = max(v, dpp32<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = max(v, dpp32<0x141>(v));    // row_half_mirror
+    v = max(v, dpp32<0x140>(v));    // row_mirror: each lane holds its 16-lane row maximum
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dpp32<0xB1>(v));
+    v = min(v, dpp32<0x4E>(v));
+    v = min(v, dpp32<0x141>(v));
+    v = min(v, dpp32<0x140>(v));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return min(min(r0, r1), min(r2, r3));
+}
+
+// Best untaken key of this lane (0 = none; every real key is > 0) and its slot.
+template <int NP>
+__device__ __forceinline__ void lane_head(const uint32_t (&ord)[NP], uint32_t taken, uint32_t &hv, int &ht) {
+    hv = 0;
+    ht = 0;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        top[k] = -INFINITY;
-        topi[k] = 0;
-        if (k < K) {
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
-            for (int t = 0; t < nper; ++t) {
-                const int e = lane + 64 * t;
-                if (e < E && !((taken >> t) & 1u)) {
-                    float v = lg[e];
-                    v = (v != v) ? -INFINITY : v;
-                    if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
-                }
-            }
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            top[k] = bv;
-            topi[k] = bi;
-        }
-    }
-    if (lane == 0) {
-        float z = 0.f;
-        float ex[MOE_MAX_TOPK];
-#pragma unroll
-        for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-            ex[k] = k < K ? expf(top[k] - top[0]) : 0.f;
-            z += ex[k];
-        }
-#pragma unroll
-        for (int k = 0; k < MOE_MAX_TOPK; ++k)
-            if (k < K) { s_idx[k] = topi[k]; s_w[k] = ex[k] / z; }
+    for (int t = 0; t < NP; ++t) {
+        const bool better = !((taken >> t) & 1u) && ord[t] > hv;    // strict: lower slot wins ties
+        hv = better ? ord[t] : hv;
+        ht = better ? t : ht;
     }
 }
 
-// Copy one token's logits into LDS (whole workgroup), for wave_topk.
-__device__ __forceinline__ void load_logits(const float *g, int E, float *lg) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) lg[e] = g[e];
+// `lg`: the logit row in LDS, E <= 64*NP.  Lane k < K returns selection k (index, weight).
+template <int NP>
+__device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int &my_idx, float &my_w) {
+    const int lane = threadIdx.x & 63;
+    uint32_t ord[NP];
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+        const int e = lane + 64 * t;
+        ord[t] = e < E ? f32_order(lg[e]) : 0u;
+    }
+    uint32_t taken = 0, hv;
+    int ht;
+    lane_head(ord, taken, hv, ht);
+    uint32_t my_key = 0;
+    my_idx = 0;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t m = wave_max_u32(hv);
+        const uint64_t bal = __ballot(hv == m);
+        int wl, wt;
+        if (__popcll(bal) == 1) {
+            wl = __ffsll((unsigned long long)bal) - 1;
+            wt = __builtin_amdgcn_readlane(ht, wl);
+        } else {    // equal keys in several lanes: lowest expert index
+            const uint32_t me = wave_min_u32(hv == m ? (uint32_t)(lane + 64 * ht) : 0xFFFFFFFFu);
+            wl = me & 63;
+            wt = me >> 6;
+        }
+        if (lane == k) { my_idx = wl + 64 * wt; my_key = m; }
+        if (lane == wl) {
+            taken |= 1u << wt;
+            lane_head(ord, taken, hv, ht);
+        }
+    }
+    const float val = order_f32(my_key);
+    const float top0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(val), 0));   // largest logit
+    const bool finite0 = top0 > -INFINITY;
+    const float ex = lane < K ? (finite0 ? expf(val - top0) : 1.f) : 0.f;
+    float z = 0.f;
+    for (int k = 0; k < K; ++k) z += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex), k));
+    my_w = ex / z;
 }
 
 // --------------------------------------------------------------------------- router
-template <int RDT>
-__global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a, int rows_per_wave) {
-    extern __shared__ float s_x[];  // [H] activation fed to the router
+// Row loads per batch and lane (16 bytes each).
+constexpr int kRouterBatch = 8;
+
+// bf16 router: the activation is staged as bf16 pairs (columns 2i, 2i+1) plus the bf16 remainder
+// when it is not exactly bf16, so a 16-byte chunk of 8 weights meets one 16-byte LDS read per part
+// and four v_dot2_f32_bf16.  fp32 router: fp32 activation, float4 LDS reads, fp32 FMAs.
+template <int RDT, bool SPLIT>
+__global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
+    extern __shared__ __align__(16) uint32_t s_r[];   // bf16: hi [H/2] + lo [H/2]; fp32: x [H]
     __shared__ float red[kWaves];
     const int t = blockIdx.y;
     const int H = a.H;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * kWaves + wave;
+    constexpr int EB = RDT == MOE_BF16 ? 2 : 4;           // bytes per weight
+    constexpr int EPL = 16 / EB;                          // weights per 16-byte load
+    const int nld = (H / EPL + 63) / 64;
+    const uint8_t *row = (const uint8_t *)a.router + (size_t)(e < a.E ? e : 0) * H * EB;
+    // 1. first batch of this wave's row, issued before the activation arrives
+    u32x4 wv[kRouterBatch];
+#pragma unroll
+    for (int j = 0; j < kRouterBatch; ++j) {
+        const int c = min((lane + 64 * j) * EPL, H - EPL);       // clamped; unused lanes ignore it
+        wv[j] = *(const u32x4 *)(row + (size_t)c * EB);
+    }
+    // 2. activation (+ RMSNorm) into LDS
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
+    const int nch = H / 16;
+    float v[2][16];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = threadIdx.x + kBlock * j;
+        if (m < nch) {
+            load_chunk16(x, a.x_dtype, m, v[j]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
+        }
+    }
     float inv = 1.f;
     if (a.norm_w) {
-        float ss = 0.f;
-        for (int c = threadIdx.x; c < H; c += blockDim.x) { const float v = load_act(x, a.x_dtype, c); ss += v * v; }
         ss = block_sum(ss, red);
         inv = 1.0f / sqrtf(ss / (float)H + a.eps);
     }
-    for (int c = threadIdx.x; c < H; c += blockDim.x) {
-        float v = load_act(x, a.x_dtype, c);
-        if (a.norm_w) v = v * inv * bf16_f32(a.norm_w[c]);
-        s_x[c] = v;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e0 = (blockIdx.x * kWaves + wave) * rows_per_wave;
-    for (int r = 0; r < rows_per_wave; ++r) {
-        const int e = e0 + r;
-        if (e >= a.E) break;
-        float acc = 0.f;
-        if (RDT == MOE_BF16) {
-            const uint8_t *row = (const uint8_t *)a.router + (size_t)e * H * 2;
-            for (int c = lane * 8; c < H; c += 512) {
-                const u32x4 v = *(const u32x4 *)(row + (size_t)c * 2);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc = fmaf(bf16_f32(v[j] & 0xFFFFu), s_x[c + 2 * j], acc);
-                    acc = fmaf(bf16_f32(v[j] >> 16), s_x[c + 2 * j + 1], acc);
-                }
+    for (int j = 0; j < 2; ++j) {
+        const int m = threadIdx.x + kBlock * j;
+        if (m < nch) {
+            if (a.norm_w) {
+                float w[16];
+                load_chunk16(a.norm_w, MOE_BF16, m, w);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
             }
-        } else {
-            const float *row = (const float *)a.router + (size_t)e * H;
-            for (int c = lane * 4; c < H; c += 256) {
-                const u32x4 v = *(const u32x4 *)(row + c);
+            if (RDT == MOE_BF16) {
+                uint32_t hv[16], lv[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc = fmaf(__uint_as_float(v[j]), s_x[c + j], acc);
+                for (int i = 0; i < 16; ++i) {
+                    hv[i] = bf16_rne(v[j][i]);
+                    lv[i] = SPLIT ? bf16_rne(v[j][i] - bf16_f32(hv[i])) : 0u;
+                }
+                uint32_t *hi = s_r + 8 * m, *lo = s_r + H / 2 + 8 * m;
+#pragma unroll
+                for (int q = 0; q < 8; q += 4) {
+                    *(u32x4 *)(hi + q) = u32x4{hv[2 * q] | (hv[2 * q + 1] << 16), hv[2 * q + 2] | (hv[2 * q + 3] << 16),
+                                               hv[2 * q + 4] | (hv[2 * q + 5] << 16), hv[2 * q + 6] | (hv[2 * q + 7] << 16)};
+                    if (SPLIT)
+                        *(u32x4 *)(lo + q) = u32x4{lv[2 * q] | (lv[2 * q + 1] << 16), lv[2 * q + 2] | (lv[2 * q + 3] << 16),
+                                                   lv[2 * q + 4] | (lv[2 * q + 5] << 16), lv[2 * q + 6] | (lv[2 * q + 7] << 16)};
+                }
+            } else {
+                float *xs = (float *)s_r + 16 * m;
+#pragma unroll
+                for (int q = 0; q < 16; q += 4)
+                    *(u32x4 *)(xs + q) = u32x4{__float_as_uint(v[j][q]), __float_as_uint(v[j][q + 1]),
+                                               __float_as_uint(v[j][q + 2]), __float_as_uint(v[j][q + 3])};
             }
         }
-        acc = group_sum(acc, 64);
-        if (lane == 0) a.logits[(size_t)t * a.E + e] = acc + (a.logit_bias ? a.logit_bias[e] : 0.f);
     }
+    __syncthreads();
+    if (e >= a.E) return;
+    // 3. dot product, further batches for long rows
+    float acc = 0.f, acc2 = 0.f;
+    for (int base = 0; base < nld; base += kRouterBatch) {
+        if (base > 0) {
+#pragma unroll
+            for (int j = 0; j < kRouterBatch; ++j) {
+                const int c = min((lane + 64 * (base + j)) * EPL, H - EPL);
+                wv[j] = *(const u32x4 *)(row + (size_t)c * EB);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kRouterBatch; ++j) {
+            const int c = (lane + 64 * (base + j)) * EPL;
+            if (base + j < nld && c < H) {
+                if (RDT == MOE_BF16) {
+                    const u32x4 xh = *(const u32x4 *)(s_r + c / 2);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = dot2(wv[j][q], xh[q], acc);
+                    if (SPLIT) {
+                        const u32x4 xl = *(const u32x4 *)(s_r + H / 2 + c / 2);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc2 = dot2(wv[j][q], xl[q], acc2);
+                    }
+                } else {
+                    const u32x4 xf = *(const u32x4 *)((const float *)s_r + c);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(wv[j][q]), __uint_as_float(xf[q]), acc);
+                }
+            }
+        }
+    }
+    acc = group_sum(acc + acc2, 64);
+    if (lane == 0) a.logits[(size_t)t * a.E + e] = acc + (a.logit_bias ? a.logit_bias[e] : 0.f);
 }
 
+template <int NP>
 __global__ void __launch_bounds__(64) k_topk(TopkLaunch a) {
-    __shared__ int s_idx[MOE_MAX_TOPK];
-    __shared__ float s_w[MOE_MAX_TOPK];
     __shared__ float s_lg[MOE_MAX_EXPERTS];
     const int t = blockIdx.x;
-    load_logits(a.logits + (size_t)t * a.E, a.E, s_lg);
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) s_lg[e] = a.logits[(size_t)t * a.E + e];
     __syncthreads();
-    wave_topk(s_lg, a.E, a.K, s_idx, s_w);
-    __syncthreads();
+    int my_idx;
+    float my_w;
+    wave_topk<NP>(s_lg, a.E, a.K, my_idx, my_w);
     if ((int)threadIdx.x < a.K) {
-        a.idx[(size_t)t * a.K + threadIdx.x] = s_idx[threadIdx.x];
-        a.w[(size_t)t * a.K + threadIdx.x] = s_w[threadIdx.x];
+        a.idx[(size_t)t * a.K + threadIdx.x] = my_idx;
+        a.w[(size_t)t * a.K + threadIdx.x] = my_w;
     }
 }
 
 // --------------------------------------------------------------------------- gate/up + SwiGLU
 // Instruction groups per work unit: enough loads in flight per lane (about 16 slots of gate+up).
 template <int NJ>
-__host__ __device__ constexpr int gu_rg() { return NJ >= 4 ? 2 : 8 / NJ; }
+__host__ __device__ constexpr int gu_rg() { return NJ >= 4 ? 1 : 4 / NJ; }
 
-// One work unit: RB consecutive rows of gate and up of one expert.
-template <int BITS, int NJ, int RG, bool SPLIT>
-__device__ void gateup_unit(const Planes *pl, const Geo &g, int H, int I, int r0, int RB, const ActView &av,
-                            float *hout) {
+template <int NJ, int RG>
+struct GULoads {
+    u32x4 qg[RG][NJ], qu[RG][NJ];
+    uint32_t sg[RG][NJ], su[RG][NJ];
+};
+
+// Issue the loads of one work unit: RB consecutive rows of gate and up of one expert.
+template <int BITS, int NJ, int RG>
+__device__ __forceinline__ void gu_issue(const Planes *pl, const Geo &g, int H, int I, int r0, int RB,
+                                         GULoads<NJ, RG> &L) {
+    // Branch-free: rows past the matrix and idle slots read a clamped, in-bounds address.  Their
+    // contribution vanishes (idle slots have zero activation operands and sum; rows past the
+    // block are never written), so nothing needs masking here.
     const int G = H / 64;
     const size_t rowb = (size_t)H * BITS / 8;
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+        const int r = min(r0 + gi * g.rpi + g.lrow, I - 1);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int slot = min(g.lsl + 64 * j, g.spr - 1);
+            L.qg[gi][j] = load_slot<BITS>(pl[0].q + (size_t)r * rowb, slot);
+            L.qu[gi][j] = load_slot<BITS>(pl[1].q + (size_t)r * rowb, slot);
+            const size_t sbi = (size_t)r * G + (slot >> 1);
+            L.sg[gi][j] = pl[0].sb[sbi];
+            L.su[gi][j] = pl[1].sb[sbi];
+        }
+    }
+}
+
+template <int BITS, int NJ, int RG, bool SPLIT>
+__device__ __forceinline__ void gu_finish(const Geo &g, int I, int r0, int RB, const ActView &av,
+                                          const GULoads<NJ, RG> &L, float *hout) {
     uint32_t X[NJ][kDPS], XL[NJ][SPLIT ? kDPS : 1];
     float XS[NJ];
-    bool sok[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int slot = g.lsl + 64 * j;
-        sok[j] = slot < g.spr;
-        const int ss = sok[j] ? slot : 0;
+        const bool ok = slot < g.spr;
+        const int ss = ok ? slot : 0;
 #pragma unroll
-        for (int i = 0; i < kDPS; ++i) {
-            X[j][i] = sok[j] ? av.hi[ss * kDPS + i] : 0u;
-            if (SPLIT) XL[j][i] = sok[j] ? av.lo[ss * kDPS + i] : 0u;
-        }
-        XS[j] = sok[j] ? av.xs[ss] : 0.f;
-    }
-    u32x4 qg[RG][NJ], qu[RG][NJ];
-    uint32_t sg[RG][NJ], su[RG][NJ];
-#pragma unroll
-    for (int gi = 0; gi < RG; ++gi) {
-        const int rr = gi * g.rpi + g.lrow;
-        const int r = r0 + rr;
-        const bool rok = rr < RB && r < I;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int slot = g.lsl + 64 * j;
-            if (rok && sok[j]) {
-                qg[gi][j] = load_slot<BITS>(pl[0].q + (size_t)r * rowb, slot);
-                qu[gi][j] = load_slot<BITS>(pl[1].q + (size_t)r * rowb, slot);
-                const size_t sbi = (size_t)r * G + (slot >> 1);
-                sg[gi][j] = pl[0].sb[sbi];
-                su[gi][j] = pl[1].sb[sbi];
-            } else {
-                qg[gi][j] = qu[gi][j] = u32x4{0u, 0u, 0u, 0u};
-                sg[gi][j] = su[gi][j] = 0u;
+        for (int i = 0; i < kDPS; i += 4) {
+            const u32x4 h = *(const u32x4 *)(av.hi + ss * kDPS + i);
+            X[j][i] = ok ? h.x : 0u; X[j][i + 1] = ok ? h.y : 0u; X[j][i + 2] = ok ? h.z : 0u; X[j][i + 3] = ok ? h.w : 0u;
+            if (SPLIT) {
+                const u32x4 l = *(const u32x4 *)(av.lo + ss * kDPS + i);
+                XL[j][i] = ok ? l.x : 0u; XL[j][i + 1] = ok ? l.y : 0u; XL[j][i + 2] = ok ? l.z : 0u; XL[j][i + 3] = ok ? l.w : 0u;
             }
         }
+        XS[j] = ok ? av.xs[ss] : 0.f;
     }
 #pragma unroll
     for (int gi = 0; gi < RG; ++gi) {
         float pg = 0.f, pu = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            pg += slot_dot<BITS, SPLIT>(qg[gi][j], X[j], XL[j], sg[gi][j], XS[j]);
-            pu += slot_dot<BITS, SPLIT>(qu[gi][j], X[j], XL[j], su[gi][j], XS[j]);
+            pg += slot_dot<BITS, SPLIT>(L.qg[gi][j], X[j], XL[j], L.sg[gi][j], XS[j]);
+            pu += slot_dot<BITS, SPLIT>(L.qu[gi][j], X[j], XL[j], L.su[gi][j], XS[j]);
         }
         pg = group_sum(pg, g.gsz);
         pu = group_sum(pu, g.gsz);
@@ -376,95 +538,150 @@ __device__ void gateup_unit(const Planes *pl, const Geo &g, int H, int I, int r0
     }
 }
 
-template <int NJ, bool SPLIT>
+template <int NJ, bool SPLIT, int NP>
 __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
-    extern __shared__ uint32_t lds[];
-    __shared__ int s_idx[MOE_MAX_TOPK];
-    __shared__ float s_w[MOE_MAX_TOPK];
-    __shared__ uint64_t s_blob[MOE_MAX_TOPK];
-    __shared__ int s_bits[MOE_MAX_TOPK];
-    __shared__ float red[kWaves];
+    extern __shared__ __align__(16) uint32_t lds[];
     __shared__ float s_lg[MOE_MAX_EXPERTS];
-    const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
-    const int lane = threadIdx.x & 63;
+    __shared__ uint64_t s_tab[kTabMax];
+    __shared__ float red[kWaves];
+    constexpr int RG = gu_rg<NJ>();
+    const int H = a.H, I = a.I, E = a.E, K = a.K, t = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool use_tab = E <= kTabMax;
 
-    // 1. routing of this token
+    // 1. independent loads, issued back to back (straight-line code: a loop here would make the
+    //    compiler wait for every outstanding load at its header): logits, descriptor table,
+    //    activation chunks
+    float lgv[MOE_MAX_EXPERTS / kBlock];
+    u32x4 dsc[kTabMax / kBlock];
     if (!a.idx_in) {
-        load_logits(a.logits + (size_t)t * a.E, a.E, s_lg);
-        __syncthreads();
-    }
-    if (a.idx_in) {
-        if ((int)threadIdx.x < K) s_idx[threadIdx.x] = a.idx_in[(size_t)t * K + threadIdx.x];
-    } else if (threadIdx.x < 64) {
-        wave_topk(s_lg, a.E, K, s_idx, s_w);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        if (blockIdx.x == 0 && lane < K) {
-            const size_t o = (size_t)t * K + lane;
-            if (a.idx_out) a.idx_out[o] = s_idx[lane];
-            if (a.w_out) a.w_out[o] = s_w[lane];
-            if (a.idx_ws) a.idx_ws[o] = s_idx[lane];
-            if (a.w_ws) a.w_ws[o] = s_w[lane];
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_EXPERTS / kBlock; ++j) {
+            const int e = threadIdx.x + kBlock * j;
+            lgv[j] = e < E ? a.logits[(size_t)t * E + e] : 0.f;
         }
     }
-
-    // 2. activation (RMSNorm when requested), staged in both code-width layouts
+    if (use_tab) {
+#pragma unroll
+        for (int j = 0; j < kTabMax / kBlock; ++j) {
+            const int e = threadIdx.x + kBlock * j;
+            dsc[j] = e < E ? *(const u32x4 *)(a.experts + e) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
+    const int nch = H / 16;
+    float v[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = min(threadIdx.x + kBlock * j, nch - 1);      // clamped; extra chunks unused
+        load_chunk16(x, a.x_dtype, m, v[j]);
+    }
+    if (!a.idx_in) {
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_EXPERTS / kBlock; ++j) {
+            const int e = threadIdx.x + kBlock * j;
+            if (e < E) s_lg[e] = lgv[j];
+        }
+    }
+    if (use_tab) {
+#pragma unroll
+        for (int j = 0; j < kTabMax / kBlock; ++j) {
+            const int e = threadIdx.x + kBlock * j;
+            if (e < E) s_tab[e] = pack_sel(((uint64_t)dsc[j].y << 32) | dsc[j].x, dsc[j].z);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if ((int)threadIdx.x + kBlock * j < nch) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
+        }
     float inv = 1.f;
     if (a.norm_w) {
-        float ss = 0.f;
-        for (int c = threadIdx.x; c < H; c += blockDim.x) { const float v = load_act(x, a.x_dtype, c); ss += v * v; }
-        ss = block_sum(ss, red);
+        ss = block_sum(ss, red);   // also makes s_lg / s_tab visible
         inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+    } else {
+        __syncthreads();
     }
-    const uint16_t *nw = a.norm_w;
-    const int xdt = a.x_dtype;
-    auto value = [&](int c) {
-        float v = load_act(x, xdt, c);
-        if (nw) v = v * inv * bf16_f32(nw[c]);
-        return v;
-    };
+
+    // 2. routing (each wave, identical results) and the first unit's weight loads
+    int my_idx = 0;
+    float my_w = 0.f;
+    if (a.idx_in) {
+        if (lane < K) my_idx = a.idx_in[(size_t)t * K + lane];
+    } else {
+        wave_topk<NP>(s_lg, E, K, my_idx, my_w);
+    }
+    if (blockIdx.x == 0 && wave == 0 && lane < K) {
+        const size_t o = (size_t)t * K + lane;
+        if (a.idx_out) a.idx_out[o] = my_idx;
+        if (a.w_out) a.w_out[o] = my_w;
+        if (a.w_ws) a.w_ws[o] = my_w;
+        a.sel_ws[o] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
+    }
+    const Geo g = make_geo(H);
+    const int RB = RG * g.rpi;
+    const int nblk = (I + RB - 1) / RB;
+    const int units = K * nblk;
+    int u = blockIdx.x * kWaves + wave;
+    GULoads<NJ, RG> L;
+    uint64_t sel = 0;
+    Planes pl[3];
+    if (u < units) {
+        const int k = u / nblk;
+        sel = lookup_sel(__shfl(my_idx, k), E, use_tab, s_tab, a.experts);
+        if (sel) {
+            expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+            if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
+            else gu_issue<4, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
+        }
+    }
+
+    // 3. activation layouts for both code widths, straight from registers
     uint32_t *h4 = lds, *l4 = lds + H / 2, *h2 = lds + H, *l2 = lds + 3 * H / 2;
     float *xs = (float *)(lds + 2 * H);
-    stage_layout<4, SPLIT>(value, H, h4, l4);
-    stage_layout<2, SPLIT>(value, H, h2, l2);
-    __syncthreads();
-    stage_sums<SPLIT>(H, h4, l4, xs);
-    if ((int)threadIdx.x < K) {
-        const int e = s_idx[threadIdx.x];
-        if (e >= 0 && e < a.E) {
-            const moe_expert_desc d = a.experts[e];
-            s_blob[threadIdx.x] = d.blob;
-            s_bits[threadIdx.x] = d.bits == 2 ? 2 : 4;
-        } else {
-            s_blob[threadIdx.x] = 0;
-            s_bits[threadIdx.x] = 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = threadIdx.x + kBlock * j;
+        float sum = 0.f;
+        if (m < nch) {
+            if (a.norm_w) {
+                float w[16];
+                load_chunk16(a.norm_w, MOE_BF16, m, w);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
+            }
+            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
+            write_chunk<2, SPLIT>(m, v[j], h2, l2);
         }
+        sum += __shfl_xor(sum, 1);                   // chunks 2s and 2s+1 sit in lanes l and l^1
+        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
     }
     __syncthreads();
     const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
 
-    // 3. work units: (expert, block of RB rows)
-    const Geo g = make_geo(H);
-    constexpr int RG = gu_rg<NJ>();
-    const int RB = RG * g.rpi;
-    const int nblk = (I + RB - 1) / RB;
-    const int units = K * nblk;
-    const int wave = threadIdx.x >> 6;
-    for (int u = blockIdx.x * kWaves + wave; u < units; u += gridDim.x * kWaves) {
+    // 4. work units
+    bool first = true;
+    for (; u < units; u += gridDim.x * kWaves) {
         const int k = u / nblk;
         const int r0 = (u - k * nblk) * RB;
         float *hout = a.h + ((size_t)t * K + k) * I;
-        const uint64_t blob = s_blob[k];
-        if (!blob) {
+        if (!first) {
+            sel = lookup_sel(__shfl(my_idx, k), E, use_tab, s_tab, a.experts);
+            if (sel) {
+                expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+                if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
+                else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
+            }
+        }
+        first = false;
+        if (!sel) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
         }
-        Planes pl[3];
-        expert_planes((const uint8_t *)blob, H, I, s_bits[k], pl);
-        if (s_bits[k] == 2) gateup_unit<2, NJ, RG, SPLIT>(pl, g, H, I, r0, RB, v2, hout);
-        else gateup_unit<4, NJ, RG, SPLIT>(pl, g, H, I, r0, RB, v4, hout);
+        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG, SPLIT>(g, I, r0, RB, v2, L, hout);
+        else gu_finish<4, NJ, RG, SPLIT>(g, I, r0, RB, v4, L, hout);
     }
 }
 
@@ -472,113 +689,148 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
 template <int NJ>
 __host__ __device__ constexpr int dn_rg() { return NJ >= 2 ? 1 : 2; }
 
-// Adds to part[gi] this lane's partial sums of RG instruction rows of one expert's down matrix.
-template <int BITS, int NJ, int RG>
-__device__ __forceinline__ void down_part(const Planes &pl, const Geo &g, int H, int I, int r0, int RB,
-                                          const ActView &av, float *part) {
+template <int NJ, int RG, int KM>
+struct DLoads {
+    u32x4 q[KM][RG][NJ];
+    uint32_t sb[KM][RG][NJ];
+};
+
+template <int BITS, int NJ, int RG, int KM>
+__device__ __forceinline__ void dn_issue(const Planes &pl, const Geo &g, int H, int I, int r0, int RB, int k,
+                                         DLoads<NJ, RG, KM> &L) {
     const int G = I / 64;
     const size_t rowb = (size_t)I * BITS / 8;
-    u32x4 q[RG][NJ];
-    uint32_t sb[RG][NJ];
 #pragma unroll
     for (int gi = 0; gi < RG; ++gi) {
-        const int rr = gi * g.rpi + g.lrow;
-        const int r = r0 + rr;
-        const bool rok = rr < RB && r < H;
+        const int r = min(r0 + gi * g.rpi + g.lrow, H - 1);     // clamped; see gu_issue
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int slot = g.lsl + 64 * j;
-            if (rok && slot < g.spr) {
-                q[gi][j] = load_slot<BITS>(pl.q + (size_t)r * rowb, slot);
-                sb[gi][j] = pl.sb[(size_t)r * G + (slot >> 1)];
-            } else {
-                q[gi][j] = u32x4{0u, 0u, 0u, 0u};
-                sb[gi][j] = 0u;
-            }
+            const int slot = min(g.lsl + 64 * j, g.spr - 1);
+            L.q[k][gi][j] = load_slot<BITS>(pl.q + (size_t)r * rowb, slot);
+            L.sb[k][gi][j] = pl.sb[(size_t)r * G + (slot >> 1)];
         }
     }
+}
+
+// Issue every selected expert's loads for one unit (output rows r0..r0+RB-1).
+template <int NJ, int RG, int KM>
+__device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, const Geo &g, int H, int I, int r0,
+                                             int RB, DLoads<NJ, RG, KM> &L) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int slot = g.lsl + 64 * j;
-        const bool ok = slot < g.spr;
-        const int ss = ok ? slot : 0;
-        uint32_t X[kDPS], XL[kDPS];
-#pragma unroll
-        for (int i = 0; i < kDPS; ++i) {
-            X[i] = ok ? av.hi[ss * kDPS + i] : 0u;
-            XL[i] = ok ? av.lo[ss * kDPS + i] : 0u;
+    for (int k = 0; k < KM; ++k) {
+        if (k < K && sel[k]) {
+            Planes pl[3];
+            expert_planes(sel_blob(sel[k]), H, I, sel_bits(sel[k]), pl);
+            if (sel_bits(sel[k]) == 2) dn_issue<2, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
+            else dn_issue<4, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
         }
-        const float xs = ok ? av.xs[ss] : 0.f;
-#pragma unroll
-        for (int gi = 0; gi < RG; ++gi) part[gi] += slot_dot<BITS, true>(q[gi][j], X, XL, sb[gi][j], xs);
     }
 }
 
 // LDS per expert: hi [I/2], lo [I/2], xs [I/32].
-__host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I + I / 32; }
+__host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I + ((I / 32 + 3) & ~3); }
 
-template <int NJ, bool COMBINE>
-__global__ void __launch_bounds__(kBlock) k_down(DownLaunch a, int E) {
-    extern __shared__ uint32_t lds[];
-    __shared__ uint64_t s_blob[MOE_MAX_TOPK];
-    __shared__ int s_bits[MOE_MAX_TOPK];
-    __shared__ float s_w[MOE_MAX_TOPK];
-    const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
-    if ((int)threadIdx.x < K) {
-        const int e = a.idx[(size_t)t * K + threadIdx.x];
-        if (e >= 0 && e < E) {
-            const moe_expert_desc d = a.experts[e];
-            s_blob[threadIdx.x] = d.blob;
-            s_bits[threadIdx.x] = d.bits == 2 ? 2 : 4;
-        } else {
-            s_blob[threadIdx.x] = 0;
-            s_bits[threadIdx.x] = 4;
-        }
-        s_w[threadIdx.x] = COMBINE ? a.w[(size_t)t * K + threadIdx.x] : 0.f;
-    }
-    __syncthreads();
-    const int per = down_lds_per_expert(I);
-    for (int k = 0; k < K; ++k) {
-        const float *hk = a.h + ((size_t)t * K + k) * I;
-        auto value = [&](int c) { return hk[c]; };
-        uint32_t *hi = lds + k * per, *lo = hi + I / 2;
-        if (s_bits[k] == 2) stage_layout<2, true>(value, I, hi, lo);
-        else stage_layout<4, true>(value, I, hi, lo);
-    }
-    __syncthreads();
-    for (int k = 0; k < K; ++k) {
-        uint32_t *hi = lds + k * per;
-        stage_sums<true>(I, hi, hi + I / 2, (float *)(hi + I));
-    }
-    __syncthreads();
-
-    const Geo g = make_geo(I);
+template <int NJ, bool COMBINE, int KM>
+__global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
+    extern __shared__ __align__(16) uint32_t lds[];
     constexpr int RG = dn_rg<NJ>();
+    const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // 1. selected experts (wave-uniform), routing weights, first unit's weight loads
+    uint64_t sel[KM];
+    float wk[KM];
+    uint32_t two_mask = 0;   // bit k: expert k has 2-bit codes
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        sel[k] = k < K ? a.sel[(size_t)t * K + k] : 0;
+        wk[k] = (COMBINE && k < K) ? a.w[(size_t)t * K + k] : 0.f;
+        if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
+    }
+    // h chunks of this thread (first pass), loaded alongside
+    const int per = down_lds_per_expert(I);
+    const int cpe = I / 16;                         // chunks per expert
+    const int nch = K * cpe;
+    const float *hrow = a.h + (size_t)t * K * I;
+    float v[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_chunk16(hrow, MOE_F32, min(threadIdx.x + kBlock * j, nch - 1), v[j]);
+    const Geo g = make_geo(I);
     const int RB = RG * g.rpi;
     const int nblk = (H + RB - 1) / RB;
-    const int wave = threadIdx.x >> 6;
+    int u = blockIdx.x * kWaves + wave;
+    DLoads<NJ, RG, KM> L;
+    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, RB, L);
+
+    // 2. stage h of every expert in its code width's layout.  The first pass is straight-line code
+    //    (the chunks loaded above), so the weight loads just issued stay in flight meanwhile.
+    auto stage = [&](int m, const float (&vv)[16]) {
+        float sum = 0.f;
+        int kk = 0, mm = 0;
+        if (m < nch) {
+            kk = m / cpe;
+            mm = m - kk * cpe;
+            uint32_t *hi = lds + kk * per, *lo = hi + I / 2;
+            sum = ((two_mask >> kk) & 1u) ? write_chunk<2, true>(mm, vv, hi, lo) : write_chunk<4, true>(mm, vv, hi, lo);
+        }
+        sum += __shfl_xor(sum, 1);
+        if (m < nch && !(mm & 1)) ((float *)(lds + kk * per + I))[mm >> 1] = sum;
+    };
+#pragma unroll
+    for (int j = 0; j < 2; ++j) stage(threadIdx.x + kBlock * j, v[j]);
+    for (int base = 2 * kBlock; base < nch; base += 2 * kBlock) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int m = base + threadIdx.x + kBlock * j;
+            if (m < nch) load_chunk16(hrow, MOE_F32, m, v[j]);
+            stage(m, v[j]);
+        }
+    }
+    __syncthreads();
+
+    // 3. units: all experts of a block of output rows
     const char *res = a.residual ? (const char *)a.residual + (size_t)t * a.residual_stride * (a.residual_dtype == MOE_BF16 ? 2 : 4) : nullptr;
-    for (int u = blockIdx.x * kWaves + wave; u < nblk; u += gridDim.x * kWaves) {
+    bool first = true;
+    for (; u < nblk; u += gridDim.x * kWaves) {
         const int r0 = u * RB;
+        if (!first) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, r0, RB, L);
+        first = false;
         float acc[RG];
 #pragma unroll
         for (int gi = 0; gi < RG; ++gi) acc[gi] = 0.f;
-        for (int k = 0; k < K; ++k) {
-            const uint64_t blob = s_blob[k];
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
             float part[RG];
 #pragma unroll
             for (int gi = 0; gi < RG; ++gi) part[gi] = 0.f;
-            if (blob) {
-                Planes pl[3];
-                expert_planes((const uint8_t *)blob, H, I, s_bits[k], pl);
+            if (sel[k]) {
                 const uint32_t *hi = lds + k * per;
-                const ActView v{hi, hi + I / 2, (const float *)(hi + I)};
-                if (s_bits[k] == 2) down_part<2, NJ, RG>(pl[2], g, H, I, r0, RB, v, part);
-                else down_part<4, NJ, RG>(pl[2], g, H, I, r0, RB, v, part);
+                const ActView av{hi, hi + I / 2, (const float *)(hi + I)};
+                const bool two = sel_bits(sel[k]) == 2;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int slot = g.lsl + 64 * j;
+                    const bool ok = slot < g.spr;
+                    const int ss = ok ? slot : 0;
+                    uint32_t X[kDPS], XL[kDPS];
+#pragma unroll
+                    for (int i = 0; i < kDPS; i += 4) {
+                        const u32x4 h = *(const u32x4 *)(av.hi + ss * kDPS + i);
+                        const u32x4 l = *(const u32x4 *)(av.lo + ss * kDPS + i);
+                        // idle lanes (slot past the row) read clamped codes: zero operands
+                        X[i] = ok ? h.x : 0u; X[i + 1] = ok ? h.y : 0u; X[i + 2] = ok ? h.z : 0u; X[i + 3] = ok ? h.w : 0u;
+                        XL[i] = ok ? l.x : 0u; XL[i + 1] = ok ? l.y : 0u; XL[i + 2] = ok ? l.z : 0u; XL[i + 3] = ok ? l.w : 0u;
+                    }
+                    const float xsv = ok ? av.xs[ss] : 0.f;
+#pragma unroll
+                    for (int gi = 0; gi < RG; ++gi)
+                        part[gi] += two ? slot_dot<2, true>(L.q[k][gi][j], X, XL, L.sb[k][gi][j], xsv)
+                                        : slot_dot<4, true>(L.q[k][gi][j], X, XL, L.sb[k][gi][j], xsv);
+                }
             }
             if (COMBINE) {
 #pragma unroll
-                for (int gi = 0; gi < RG; ++gi) acc[gi] += s_w[k] * part[gi];
+                for (int gi = 0; gi < RG; ++gi) acc[gi] += wk[k] * part[gi];
             } else {
 #pragma unroll
                 for (int gi = 0; gi < RG; ++gi) {
@@ -635,36 +887,48 @@ int down_rows_per_unit(int cols) {
 size_t gateup_lds_bytes(int H) { return ((size_t)2 * H + H / 32) * 4; }
 size_t down_lds_bytes(int I, int K) { return (size_t)K * down_lds_per_expert(I) * 4; }
 
-hipError_t launch_router(const RouterLaunch &a, hipStream_t s) {
-    const int rpw = a.T == 1 ? 1 : 4;
-    const int rows_per_block = rpw * kWaves;
-    dim3 grid((a.E + rows_per_block - 1) / rows_per_block, a.T);
+static hipError_t set_lds(const void *fn, size_t lds) {
+    if (lds <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int RDT, bool SPLIT>
+static hipError_t router_impl(const RouterLaunch &a, hipStream_t s) {
+    dim3 grid((a.E + kWaves - 1) / kWaves, a.T);
     const size_t lds = (size_t)a.H * 4;
-    if (a.router_dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_router<MOE_BF16>, grid, dim3(kBlock), lds, s, a, rpw);
-    else
-        hipLaunchKernelGGL(k_router<MOE_F32>, grid, dim3(kBlock), lds, s, a, rpw);
+    auto fn = k_router<RDT, SPLIT>;
+    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
+hipError_t launch_router(const RouterLaunch &a, hipStream_t s) {
+    if (a.router_dtype != MOE_BF16) return router_impl<MOE_F32, false>(a, s);
+    const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
+    return split ? router_impl<MOE_BF16, true>(a, s) : router_impl<MOE_BF16, false>(a, s);
+}
+
 hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3(a.T), dim3(64), 0, s, a);
+    if (a.E <= 512) hipLaunchKernelGGL(k_topk<8>, dim3(a.T), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_topk<32>, dim3(a.T), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int NJ, bool SPLIT, int NP>
+static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s) {
+    const int RB = gateup_rows_per_unit(a.H);
+    const int units = a.K * ((a.I + RB - 1) / RB);
+    dim3 grid((units + kWaves - 1) / kWaves, a.T);
+    const size_t lds = gateup_lds_bytes(a.H);
+    auto fn = k_gateup<NJ, SPLIT, NP>;
+    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
 template <int NJ, bool SPLIT>
 static hipError_t gateup_impl(const GateUpLaunch &a, hipStream_t s) {
-    const int RB = gateup_rows_per_unit(a.H);
-    const int units = a.K * ((a.I + RB - 1) / RB);
-    dim3 grid((units + kWaves - 1) / kWaves, a.T);
-    const size_t lds = gateup_lds_bytes(a.H);
-    auto fn = k_gateup<NJ, SPLIT>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-    return hipGetLastError();
+    return a.E <= 512 ? gateup_impl_np<NJ, SPLIT, 8>(a, s) : gateup_impl_np<NJ, SPLIT, 32>(a, s);
 }
 
 hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s) {
@@ -676,27 +940,31 @@ hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s) {
     }
 }
 
-template <int NJ, bool COMBINE>
-static hipError_t down_impl(const DownLaunch &a, int E, hipStream_t s) {
+template <int NJ, bool COMBINE, int KM>
+static hipError_t down_impl_k(const DownLaunch &a, hipStream_t s) {
     const int RB = down_rows_per_unit(a.I);
     const int units = (a.H + RB - 1) / RB;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = down_lds_bytes(a.I, a.K);
-    auto fn = k_down<NJ, COMBINE>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a, E);
+    auto fn = k_down<NJ, COMBINE, KM>;
+    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const DownLaunch &a, int E, hipStream_t s) {
+template <int NJ, bool COMBINE>
+static hipError_t down_impl(const DownLaunch &a, hipStream_t s) {
+    if (a.K <= 2) return down_impl_k<NJ, COMBINE, 2>(a, s);
+    if (a.K <= 4) return down_impl_k<NJ, COMBINE, 4>(a, s);
+    return down_impl_k<NJ, COMBINE, 8>(a, s);
+}
+
+hipError_t launch_down(const DownLaunch &a, hipStream_t s) {
     const bool comb = a.w != nullptr;
     switch (nj_for(a.I)) {
-        case 1: return comb ? down_impl<1, true>(a, E, s) : down_impl<1, false>(a, E, s);
-        case 2: return comb ? down_impl<2, true>(a, E, s) : down_impl<2, false>(a, E, s);
-        default: return comb ? down_impl<4, true>(a, E, s) : down_impl<4, false>(a, E, s);
+        case 1: return comb ? down_impl<1, true>(a, s) : down_impl<1, false>(a, s);
+        case 2: return comb ? down_impl<2, true>(a, s) : down_impl<2, false>(a, s);
+        default: return comb ? down_impl<4, true>(a, s) : down_impl<4, false>(a, s);
     }
 }
 

@@ -40,8 +40,9 @@ struct GateUpLaunch {
     const uint16_t *norm_w; float eps;             // RMSNorm applied to x when norm_w != NULL
     const float *logits;                           // [T][E]: top-K computed here when idx_in == NULL
     const int32_t *idx_in;                         // [T][K] given routing, or NULL
-    int32_t *idx_out; float *w_out;                // [T][K] written when top-K is computed here (nullable)
-    int32_t *idx_ws; float *w_ws;                  // [T][K] copies for the down kernel (nullable)
+    int32_t *idx_out; float *w_out;                // [T][K] routing results (nullable)
+    uint64_t *sel_ws;                              // [T][K] selected blob address | code width, for down
+    float *w_ws;                                   // [T][K] routing weights for down (nullable)
     const moe_expert_desc *experts;
     float *h;                                      // [T][K][I]
     int H, I, E, K, T;
@@ -50,14 +51,13 @@ hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s);
 
 struct DownLaunch {
     const float *h;                                // [T][K][I]
-    const int32_t *idx;                            // [T][K]
+    const uint64_t *sel;                           // [T][K] blob address | code width (0: no expert)
     const float *w;                                // [T][K] (combine) or NULL (per-expert output)
-    const moe_expert_desc *experts;
     const void *residual; int residual_dtype; int residual_stride;   // [T][stride] or NULL
     float *out;                                    // combine: [T][H]; else y [T][K][H]
     int H, I, K, T;
 };
-hipError_t launch_down(const DownLaunch &a, int E, hipStream_t s);
+hipError_t launch_down(const DownLaunch &a, hipStream_t s);
 
 struct CombineLaunch {
     const float *y; const float *w; const float *residual; float *out;

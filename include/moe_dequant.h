@@ -223,6 +223,19 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
                      int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_decode with per-kernel timing, the library's counterpart of the pages' per-layer
+ * timing breakdown (lilting.ch page, "遅延GPU実行" section, per-layer time table).
+ *   events  host array of 3*n_layers + 1 hipEvent_t (created by the caller on the current
+ *           device).  events[0] is recorded on `stream` before the first kernel and
+ *           events[3l+1], events[3l+2], events[3l+3] after layer l's router, gate/up and down
+ *           kernels, so hipEventElapsedTime(events[i], events[i+1]) spans one kernel (including
+ *           its dispatch).  When the stream is being captured the records become external event
+ *           nodes of the graph.
+ * Other arguments and errors as moe_layer_decode (MOE_ERR_NULL when events is NULL). */
+int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
+                           int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
+                           void *ws, size_t ws_bytes, void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

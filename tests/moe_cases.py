@@ -100,7 +100,7 @@ def build_layer(wl: synth.Workload, layer_id: int = 0, host_blobs: Optional[bool
     return DeviceLayer(wl, layer_id, store, stride, table, router, logit_bias, norm_w, L)
 
 
-@functools.lru_cache(maxsize=256)
+@functools.lru_cache(maxsize=512)
 def _cached_blob(seed, layer, e, H, I, bits) -> np.ndarray:
     return synth.expert_blob(seed, layer, e, H, I, bits)
 

@@ -149,7 +149,7 @@ def test_expert_ffn_and_decode_validation(L):
     d = dims()
     lay = layer()
     need = M.moe_workspace_bytes(M.MOE_OP_EXPERT_FFN, d, 1, 1)
-    assert need == 2 * 256 * 4
+    assert need == 2 * 256 * 4 + 256   # h [K][I] fp32, then the selected experts [K] (256-byte regions)
     assert L.moe_expert_ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 1, FAKE, FAKE, FAKE, need - 1,
                             None) == 6
     assert L.moe_expert_ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 1, None, FAKE, FAKE, need,

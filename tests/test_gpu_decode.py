@@ -59,6 +59,7 @@ SMALL = [
     ("h640_i1344_e7_k7_tiered_norm", 640, 1344, 7, 7, 4, {"tiered": True, "n_hot": 3, "norm": True}),
     ("h256_i64_e1_k1", 256, 64, 1, 1, 2, {}),
     ("h4096_i4096_e8_k8_4b", 4096, 4096, 8, 8, 4, {"x_bf16": False}),
+    ("h256_i128_e1000_k6", 256, 128, 1000, 6, 4, {}),
 ]
 
 
@@ -173,3 +174,43 @@ def test_two_layer_stack_small():
             assert list(idx.cpu().numpy()[l]) == list(r.idx), f"layer {l}"
             assert_close(w.cpu().numpy()[l], r.w, f"layer {l} w")
         assert_close(out.cpu().numpy(), ref_out, "stack out")
+
+
+@pytest.mark.parametrize("E", [40, 700])
+def test_route_ties_zeros_and_infinities(E):
+    """Top-K on logits with exact ties, +0/-0 and -inf: an fp32 router and a one-hot fp32 token
+    make each logit equal to one router entry, so the expected order is exact."""
+    K = 8
+    H = 64
+    rng = np.random.default_rng(E)
+    col = rng.choice([-1.5, -0.0, 0.0, 0.25, 2.0, 3.0], size=E).astype(np.float32)
+    col[E // 3] = -np.inf
+    col[E // 2] = 3.0
+    router = np.zeros((E, H), dtype=np.float32)
+    router[:, 0] = col
+    x = np.zeros((1, H), dtype=np.float32)
+    x[0, 0] = 1.0
+    d = M.make_dims(H, 64, E, K)
+    table = M.expert_table([1 << 20] * E, [4] * E)          # never dereferenced by moe_route
+    L = M.Layer(torch.from_numpy(router).cuda(), table)
+    idx = torch.empty(1, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(1, K, dtype=torch.float32, device="cuda")
+    logits = torch.empty(1, E, dtype=torch.float32, device="cuda")
+    M.moe_route(d, L, torch.from_numpy(x).cuda(), idx, w, logits)
+    torch.cuda.synchronize()
+    lg = col.astype(np.float64)
+    ri, rw, _ = oracle.route(lg, K)
+    assert list(idx.cpu().numpy()[0]) == list(ri)
+    assert_close(w.cpu().numpy()[0], rw, "tie weights")
+    # NaN counts as -inf: never chosen while finite logits remain
+    col2 = col.copy()
+    col2[:3] = np.nan
+    router[:, 0] = col2
+    L2 = M.Layer(torch.from_numpy(router).cuda(), table)
+    M.moe_route(d, L2, torch.from_numpy(x).cuda(), idx, w, logits)
+    torch.cuda.synchronize()
+    lg2 = col2.astype(np.float64)
+    lg2[np.isnan(lg2)] = -np.inf
+    ri2, rw2, _ = oracle.route(lg2, K)
+    assert list(idx.cpu().numpy()[0]) == list(ri2)
+    assert np.all(np.isfinite(w.cpu().numpy()))
