@@ -94,7 +94,29 @@ struct Carve {
 };
 
 size_t route_ws(const moe_dims *d, int T) { return r256((size_t)T * d->n_experts * 4); }
+// Batched path workspace: grouping tables, SwiGLU outputs in expert order, normalised rows.
+struct GroupedWs {
+    int32_t *off, *ntiles, *perm, *tiles;
+    float *hbuf, *xn;
+    size_t bytes;
+};
+GroupedWs grouped_ws(const moe_dims *d, int T, void *base) {
+    const int P = T * d->top_k;
+    Carve c{(char *)base};
+    GroupedWs g;
+    g.off = c.take<int32_t>((size_t)d->n_experts + 1);
+    g.ntiles = c.take<int32_t>(1);
+    g.perm = c.take<int32_t>(P);
+    g.tiles = c.take<int32_t>(2 * (size_t)moe::grouped_max_tiles(T, d->top_k, d->n_experts));
+    g.hbuf = c.take<float>((size_t)P * d->inter);
+    g.xn = c.take<float>((size_t)T * d->hidden);
+    g.bytes = c.off;
+    return g;
+}
+constexpr int kMaxGroupedPairs = 32768;   // the grouping kernel keeps every pair in LDS
+
 size_t ffn_ws(const moe_dims *d, int T) {
+    if (T >= 2) return grouped_ws(d, T, nullptr).bytes;
     Carve c{nullptr};
     c.take<float>((size_t)T * d->top_k * d->inter);
     c.take<uint64_t>((size_t)T * d->top_k);
@@ -291,8 +313,31 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     if (T < 1 || T > 65535) return fail(MOE_ERR_SHAPE, "T=%d outside [1, 65535]", T);
     if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
     if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MOE_ERR_ALIGN, "idx/y not 4-byte aligned");
+    if (T >= 2 && T * dims->top_k > kMaxGroupedPairs)
+        return fail(MOE_ERR_UNSUPPORTED, "T*top_k=%d exceeds %d for the grouped path", T * dims->top_k, kMaxGroupedPairs);
     if (int s = check_ws(ws, ws_bytes, ffn_ws(dims, T))) return s;
     hipStream_t st = (hipStream_t)stream;
+    if (T >= 2) {
+        // batched: group the (token, slot) pairs by expert, then the MFMA grouped dequant-GEMMs
+        GroupedWs g = grouped_ws(dims, T, ws);
+        const void *xa = x;
+        int xdt = x_dtype;
+        if (layer->norm_w) {
+            if (int s = launched(moe::launch_norm_rows(x, x_dtype, layer->norm_w, layer->norm_eps, dims->hidden, T,
+                                                       g.xn, st), "norm"))
+                return s;
+            xa = g.xn;
+            xdt = MOE_F32;
+        }
+        moe::GroupLaunch gl{idx, T, dims->top_k, dims->n_experts, g.off, g.perm, g.tiles, g.ntiles, y, dims->hidden};
+        if (int s = launched(moe::launch_group(gl, st), "group")) return s;
+        moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, g.off, g.perm,
+                              g.tiles, g.ntiles, g.hbuf, y};
+        if (int s = launched(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts), st),
+                             "grouped ffn"))
+            return s;
+        return ok();
+    }
     Carve c{(char *)ws};
     float *h = c.take<float>((size_t)T * dims->top_k * dims->inter);
     uint64_t *sel = c.take<uint64_t>((size_t)T * dims->top_k);

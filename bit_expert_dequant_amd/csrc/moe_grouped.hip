@@ -1,0 +1,434 @@
+// moe_grouped.hip -- batched (T > 1) expert FFN: token grouping and MFMA grouped dequant-GEMM.
+//
+//   k_group    : counting sort of the T*K (token, slot) pairs by expert -- histogram (LDS integer
+//                atomics), exclusive prefix sum, and a stable scatter (one wavefront per expert,
+//                ballot + popcount over the pairs in index order, so the order is deterministic and
+//                follows the token id); also emits the work list of (expert, 32-token tile).
+//   k_norm_rows: RMSNorm of every token row (only when the layer has a norm weight).
+//   k_gu_mfma  : per (expert, token tile, 128 rows of I): G = X W_g^T and U = X W_u^T with
+//                v_mfma_f32_32x32x16_bf16, then h = silu(G) * U.
+//   k_dn_mfma  : per (expert, token tile, 128 rows of H): Y = h W_d^T, each row written straight
+//                to y[token][slot] (the scatter back to token order; the weighted sum is
+//                moe_combine).
+//
+// Exactness.  The B operand is the 4-bit (or 2-bit) code OR-ed into the mantissa of bf16 128.0
+// (exact: 128 + q), the A operand is the bf16 activation (split into hi + lo bf16 parts when it
+// is not exactly bf16, e.g. h).  Each MFMA K-step stays inside one quantisation group of 64, so
+// after the four steps of a group the fp32 accumulator P holds sum_c (128 + q) x; the group's
+// scale and bias are then applied in fp32: acc += s * P + (b - 128 s) * S[token][group], with
+// S the token's sum of x over the group -- the affine form w = q*s + b summed per group (the FMA
+// rewrite on the lilting.ch page "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE", section
+// "Metal Compute Shaders").  The dequantised weight is never rounded to bf16.
+//
+// Operand layout of v_mfma_f32_32x32x16_bf16 (checked on the device): lane l supplies row (A) or
+// column (B) l % 32 and the 8 K-values 8*(l/32)..+8; accumulator element v of lane l is row
+// 8*(v/4) + 4*(l/32) + v%4, column l % 32.  Within a K-step the order of the 8 K-values only has
+// to agree between A and B; it follows the code unpack order (pairs (c, c+4) of a 4-bit dword,
+// (c, c+8) of a 2-bit dword), so the A operand is staged in the same pair order.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+#define GLOBAL_AS __attribute__((address_space(1)))
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const GLOBAL_AS uint8_t *gbytes;
+typedef const GLOBAL_AS uint32_t *gwords;
+
+constexpr uint32_t kMagic = 0x43004300u;
+constexpr int kTM = 32;          // tokens per tile
+constexpr int kTN = 128;         // output rows per workgroup (4 waves x 32)
+constexpr int kKC = 256;         // K columns staged per chunk (4 groups)
+constexpr int kRowDw = kKC / 2 + 4;   // LDS dwords per token row of a chunk (padded)
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ f32x16 mfma(const u32x4 a, const u32x4 b, const f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
+
+// B operand (8 bf16 = 128 + q) of K-step `step` for this lane's half h.
+template <int BITS>
+__device__ __forceinline__ u32x4 unpack_b(const u32x4 q, int step, int h) {
+    u32x4 r;
+    if (BITS == 4) {
+        const uint32_t v = q[step];     // lane half h loaded dwords 4h..4h+3 of the group
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ((v >> (4 * j)) & 0x000F000Fu) | kMagic;
+    } else {
+        const uint32_t v = q[step];     // 2-bit: the whole group (4 dwords); pairs 4h..4h+3 of dword `step`
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ((v >> (2 * (4 * h + j))) & 0x00030003u) | kMagic;
+    }
+    return r;
+}
+
+// LDS dword offset (within a token row of the chunk) of the A operand of group gl, step, half h.
+template <int BITS>
+__device__ __forceinline__ int a_offset(int gl, int step, int h) {
+    if (BITS == 4) return (2 * gl + h) * 16 + 4 * step;
+    return (2 * gl + (step >> 1)) * 16 + 8 * (step & 1) + 4 * h;
+}
+
+// Column pair packed by activation dword d of a 32-column slot (same orders as the decode path).
+template <int BITS>
+__device__ __forceinline__ int pair_col(int d, int hf) {
+    if (BITS == 4) return (d >> 2) * 8 + (d & 3) + 4 * hf;
+    return (d >> 3) * 16 + (d & 7) + 8 * hf;
+}
+
+__device__ __forceinline__ void planes_of(uint64_t blob_addr, int R0, int C0, int R2, int C2, int bits,
+                                          gbytes *q, gwords *sb) {
+    // gate (R0 x C0), up (R0 x C0), down (R2 x C2)
+    gbytes blob = (gbytes)blob_addr;
+    const size_t c0 = (size_t)R0 * C0 * bits / 8, s0 = (size_t)R0 * (C0 / 64) * 4;
+    const size_t c2 = (size_t)R2 * C2 * bits / 8;
+    size_t off = 0;
+    q[0] = blob + off; off = round256(off + c0);
+    sb[0] = (gwords)(blob + off); off = round256(off + s0);
+    q[1] = blob + off; off = round256(off + c0);
+    sb[1] = (gwords)(blob + off); off = round256(off + s0);
+    q[2] = blob + off; off = round256(off + c2);
+    sb[2] = (gwords)(blob + off);
+}
+
+// --------------------------------------------------------------------------- grouping
+__global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
+    extern __shared__ int s_all[];
+    const int P = a.T * a.K, E = a.E;
+    int *s_idx = s_all;                // [P]
+    int *s_cnt = s_idx + P;            // [E]
+    int *s_off = s_cnt + E;            // [E + 1]
+    int *s_toff = s_off + E + 1;       // [E + 1]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = a.idx[p];
+        s_idx[p] = (e >= 0 && e < E) ? e : -1;
+    }
+    for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x)
+        if (s_idx[p] >= 0) atomicAdd(&s_cnt[s_idx[p]], 1);
+    // pairs naming no valid expert get a zero output row (as in the decode path); such pairs are
+    // a caller error, so one thread per pair is enough
+    for (int p = tid; p < P; p += blockDim.x)
+        if (s_idx[p] < 0)
+            for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
+    __syncthreads();
+    if (tid == 0) {      // E <= 2048: a serial scan is a few microseconds at most
+        int acc = 0, tacc = 0;
+        for (int e = 0; e < E; ++e) {
+            s_off[e] = acc;
+            s_toff[e] = tacc;
+            acc += s_cnt[e];
+            tacc += (s_cnt[e] + kTM - 1) / kTM;
+        }
+        s_off[E] = acc;
+        s_toff[E] = tacc;
+        *a.ntiles = tacc;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += blockDim.x) a.off[e] = s_off[e];
+    // stable scatter, one wave per expert
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int e = wave; e < E; e += nw) {
+        const int n = s_cnt[e];
+        if (n == 0) continue;
+        int base = 0;
+        for (int c = 0; c < P && base < n; c += 64) {
+            const int p = c + lane;
+            const bool m = p < P && s_idx[p] == e;
+            const uint64_t mask = __ballot(m);
+            if (m) a.perm[s_off[e] + base + __popcll(mask & lt)] = p;
+            base += __popcll(mask);
+        }
+        for (int j = lane; j < (n + kTM - 1) / kTM; j += 64) {
+            a.tiles[2 * (s_toff[e] + j)] = e;
+            a.tiles[2 * (s_toff[e] + j) + 1] = j * kTM;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+                                                   int H, float *out) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < H; c += blockDim.x) {
+        const float v = x_dtype == MOE_BF16 ? bf16_f32(((const uint16_t *)x)[(size_t)t * H + c])
+                                             : ((const float *)x)[(size_t)t * H + c];
+        ss += v * v;
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int c = threadIdx.x; c < H; c += blockDim.x) {
+        const float v = x_dtype == MOE_BF16 ? bf16_f32(((const uint16_t *)x)[(size_t)t * H + c])
+                                             : ((const float *)x)[(size_t)t * H + c];
+        out[(size_t)t * H + c] = v * inv * bf16_f32(norm_w[c]);
+    }
+}
+
+// --------------------------------------------------------------------------- shared GEMM pieces
+// Stage K columns [kc, kc+kKC) of the tile's tokens: each of the 256 threads converts 32 columns
+// of one token (hi, and lo when SPLIT) into the pair order of BITS and the token's group sums.
+// src(row, c) returns the fp32 activation of tile row `row` (< kTM) at column c.
+template <int BITS, bool SPLIT, typename F>
+__device__ __forceinline__ void stage_chunk(F src, int kc, int K, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    const int row = threadIdx.x >> 3, slot = threadIdx.x & 7;     // 32 rows x 8 slots of 32 columns
+    const int c0 = kc + 32 * slot;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = src(row, min(c0 + i, K - 1));
+    uint32_t hv[32], lv[32];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float x = (c0 + i < K) ? v[i] : 0.f;
+        hv[i] = bf16_rne(x);
+        lv[i] = SPLIT ? bf16_rne(x - bf16_f32(hv[i])) : 0u;
+        sum += bf16_f32(hv[i]) + (SPLIT ? bf16_f32(lv[i]) : 0.f);
+    }
+    uint32_t *hi = s_hi + row * kRowDw + slot * 16, *lo = s_lo + row * kRowDw + slot * 16;
+#pragma unroll
+    for (int d = 0; d < 16; d += 4) {
+        u32x4 H4, L4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            H4[j] = hv[pair_col<BITS>(d + j, 0)] | (hv[pair_col<BITS>(d + j, 1)] << 16);
+            L4[j] = lv[pair_col<BITS>(d + j, 0)] | (lv[pair_col<BITS>(d + j, 1)] << 16);
+        }
+        *(u32x4 *)(hi + d) = H4;
+        if (SPLIT) *(u32x4 *)(lo + d) = L4;
+    }
+    sum += __shfl_xor(sum, 1);                                // two slots per group of 64
+    if (!(slot & 1)) s_sum[row * 5 + (slot >> 1)] = sum;      // [kTM][4 groups] (row stride 5)
+}
+
+// Loads of one chunk (4 groups) of weight row `r` for this lane half: codes and (scale, bias).
+template <int BITS>
+__device__ __forceinline__ void load_chunk_w(gbytes q, gwords sb, int r, int cols, int kc, int h, u32x4 (&qv)[4],
+                                             uint32_t (&sv)[4]) {
+    const size_t rowb = (size_t)cols * BITS / 8;
+    const int G = cols / 64;
+#pragma unroll
+    for (int gl = 0; gl < 4; ++gl) {
+        const int g = min(kc / 64 + gl, G - 1);
+        if (BITS == 4) qv[gl] = *(const GLOBAL_AS u32x4 *)(q + (size_t)r * rowb + (size_t)g * 32 + 16 * h);
+        else qv[gl] = *(const GLOBAL_AS u32x4 *)(q + (size_t)r * rowb + (size_t)g * 16);
+        sv[gl] = sb[(size_t)r * G + g];
+    }
+}
+
+// acc += s * P + (b - 128 s) * S[row][gl] over this lane's 16 accumulator rows.
+__device__ __forceinline__ void apply_group(f32x16 &acc, const f32x16 &P, uint32_t sbw, const float *s_sum, int gl,
+                                            int h) {
+    const float s = bf16_f32(sbw & 0xFFFFu), c = bf16_f32(sbw >> 16) - 128.f * s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+        acc[v] += s * P[v] + c * s_sum[m * 5 + gl];
+    }
+}
+
+// Tile bookkeeping shared by both GEMM kernels.
+struct TileInfo {
+    int e, m0, n, base;   // expert, first token of the tile within the expert, tokens in tile, offset of expert
+};
+__device__ __forceinline__ bool tile_info(const GroupedLaunch &a, TileInfo &ti) {
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return false;
+    ti.e = a.tiles[2 * tile];
+    ti.m0 = a.tiles[2 * tile + 1];
+    ti.base = a.off[ti.e];
+    ti.n = min(kTM, a.off[ti.e + 1] - ti.base - ti.m0);
+    return true;
+}
+
+// --------------------------------------------------------------------------- gate/up
+template <int BITS, bool SPLIT>
+__device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, gwords sg, gbytes qu, gwords su,
+                        const int *s_tok, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+    const int r = blockIdx.x * kTN + wave * 32 + (lane & 31);
+    const int rc = min(r, I - 1);
+    f32x16 accG = {}, accU = {};
+    const float *xf = (const float *)a.x;
+    const uint16_t *xb = (const uint16_t *)a.x;
+    const int xdt = a.x_dtype;
+    auto src = [&](int row, int c) -> float {
+        const int t = s_tok[row];
+        if (t < 0) return 0.f;
+        return xdt == MOE_BF16 ? bf16_f32(xb[(size_t)t * H + c]) : xf[(size_t)t * H + c];
+    };
+    for (int kc = 0; kc < H; kc += kKC) {
+        u32x4 q_g[4], q_u[4];
+        uint32_t s_g[4], s_u[4];
+        load_chunk_w<BITS>(qg, sg, rc, H, kc, h, q_g, s_g);
+        load_chunk_w<BITS>(qu, su, rc, H, kc, h, q_u, s_u);
+        __syncthreads();                        // previous chunk fully consumed
+        stage_chunk<BITS, SPLIT>(src, kc, H, s_hi, s_lo, s_sum);
+        __syncthreads();
+        const int m = lane & 31;
+#pragma unroll
+        for (int gl = 0; gl < 4; ++gl) {
+            if (kc + 64 * gl >= H) break;
+            f32x16 Pg = {}, Pu = {};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int off = m * kRowDw + a_offset<BITS>(gl, st, h);
+                const u32x4 A = *(const u32x4 *)(s_hi + off);
+                const u32x4 Bg = unpack_b<BITS>(q_g[gl], st, h), Bu = unpack_b<BITS>(q_u[gl], st, h);
+                Pg = mfma(A, Bg, Pg);
+                Pu = mfma(A, Bu, Pu);
+                if (SPLIT) {
+                    const u32x4 Al = *(const u32x4 *)(s_lo + off);
+                    Pg = mfma(Al, Bg, Pg);
+                    Pu = mfma(Al, Bu, Pu);
+                }
+            }
+            apply_group(accG, Pg, s_g[gl], s_sum, gl, h);
+            apply_group(accU, Pu, s_u[gl], s_sum, gl, h);
+        }
+    }
+    if (r < I) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+            if (m < ti.n) a.hbuf[(size_t)(ti.base + ti.m0 + m) * I + r] = silu(accG[v]) * accU[v];
+        }
+    }
+}
+
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) k_gu_mfma(GroupedLaunch a) {
+    __shared__ __align__(16) uint32_t s_hi[kTM * kRowDw];
+    __shared__ __align__(16) uint32_t s_lo[SPLIT ? kTM * kRowDw : 4];
+    __shared__ float s_sum[kTM * 5];
+    __shared__ int s_tok[kTM];
+    TileInfo ti;
+    if (!tile_info(a, ti)) return;
+    if (threadIdx.x < kTM) s_tok[threadIdx.x] = (int)threadIdx.x < ti.n ? a.perm[ti.base + ti.m0 + threadIdx.x] / a.K : -1;
+    const moe_expert_desc d = a.experts[ti.e];
+    gbytes q[3];
+    gwords sb[3];
+    const int bits = d.bits == 2 ? 2 : 4;
+    planes_of(d.blob, a.I, a.H, a.H, a.I, bits, q, sb);
+    __syncthreads();
+    if (bits == 2) gu_tile<2, SPLIT>(a, ti, q[0], sb[0], q[1], sb[1], s_tok, s_hi, s_lo, s_sum);
+    else gu_tile<4, SPLIT>(a, ti, q[0], sb[0], q[1], sb[1], s_tok, s_hi, s_lo, s_sum);
+}
+
+// --------------------------------------------------------------------------- down
+template <int BITS>
+__device__ void dn_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, gwords sd, const int *s_pair,
+                        uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+    const int r = blockIdx.x * kTN + wave * 32 + (lane & 31);
+    const int rc = min(r, H - 1);
+    f32x16 acc = {};
+    const float *hb = a.hbuf + (size_t)(ti.base + ti.m0) * I;
+    const int n = ti.n;
+    auto src = [&](int row, int c) -> float { return row < n ? hb[(size_t)row * I + c] : 0.f; };
+    for (int kc = 0; kc < I; kc += kKC) {
+        u32x4 qv[4];
+        uint32_t sv[4];
+        load_chunk_w<BITS>(qd, sd, rc, I, kc, h, qv, sv);
+        __syncthreads();
+        stage_chunk<BITS, true>(src, kc, I, s_hi, s_lo, s_sum);
+        __syncthreads();
+        const int m = lane & 31;
+#pragma unroll
+        for (int gl = 0; gl < 4; ++gl) {
+            if (kc + 64 * gl >= I) break;
+            f32x16 P = {};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int off = m * kRowDw + a_offset<BITS>(gl, st, h);
+                const u32x4 B = unpack_b<BITS>(qv[gl], st, h);
+                P = mfma(*(const u32x4 *)(s_hi + off), B, P);
+                P = mfma(*(const u32x4 *)(s_lo + off), B, P);
+            }
+            apply_group(acc, P, sv[gl], s_sum, gl, h);
+        }
+    }
+    if (r < H) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+            if (m < n) a.y[(size_t)s_pair[m] * H + r] = acc[v];
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_dn_mfma(GroupedLaunch a) {
+    __shared__ __align__(16) uint32_t s_hi[kTM * kRowDw];
+    __shared__ __align__(16) uint32_t s_lo[kTM * kRowDw];
+    __shared__ float s_sum[kTM * 5];
+    __shared__ int s_pair[kTM];
+    TileInfo ti;
+    if (!tile_info(a, ti)) return;
+    if (threadIdx.x < kTM) s_pair[threadIdx.x] = (int)threadIdx.x < ti.n ? a.perm[ti.base + ti.m0 + threadIdx.x] : 0;
+    const moe_expert_desc d = a.experts[ti.e];
+    gbytes q[3];
+    gwords sb[3];
+    const int bits = d.bits == 2 ? 2 : 4;
+    planes_of(d.blob, a.I, a.H, a.H, a.I, bits, q, sb);
+    __syncthreads();
+    if (bits == 2) dn_tile<2>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
+    else dn_tile<4>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------- launchers
+int grouped_max_tiles(int T, int K, int E) {
+    const int P = T * K;
+    return (P + kTM - 1) / kTM + (E < P ? E : P);
+}
+
+size_t group_lds_bytes(int T, int K, int E) { return ((size_t)T * K + 3 * (size_t)E + 2) * 4; }
+
+hipError_t launch_group(const GroupLaunch &a, hipStream_t s) {
+    const size_t lds = group_lds_bytes(a.T, a.K, a.E);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_group, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, float eps, int H, int T, float *out,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_norm_rows, dim3(T), dim3(256), 0, s, x, x_dtype, norm_w, eps, H, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, hipStream_t s) {
+    const bool split = a.x_dtype != MOE_BF16;
+    dim3 g1((a.I + kTN - 1) / kTN, max_tiles);
+    if (split) hipLaunchKernelGGL(k_gu_mfma<true>, g1, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_gu_mfma<false>, g1, dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return e;
+    dim3 g2((a.H + kTN - 1) / kTN, max_tiles);
+    hipLaunchKernelGGL(k_dn_mfma, g2, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

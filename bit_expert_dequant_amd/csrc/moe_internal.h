@@ -59,6 +59,31 @@ struct DownLaunch {
 };
 hipError_t launch_down(const DownLaunch &a, hipStream_t s);
 
+// Batched path (T > 1): grouping of the T*K (token, slot) pairs by expert, then grouped GEMMs.
+struct GroupLaunch {
+    const int32_t *idx; int T, K, E;
+    int32_t *off;                                  // [E+1] first sorted position of each expert
+    int32_t *perm;                                 // [T*K] pair index (t*K+k) in expert order
+    int32_t *tiles;                                // [2*max_tiles] (expert, first token) per tile
+    int32_t *ntiles;                               // [1]
+    float *y; int H;                               // rows of out-of-range pairs are zeroed
+};
+int grouped_max_tiles(int T, int K, int E);
+size_t group_lds_bytes(int T, int K, int E);
+hipError_t launch_group(const GroupLaunch &a, hipStream_t s);
+hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, float eps, int H, int T, float *out,
+                            hipStream_t s);
+
+struct GroupedLaunch {
+    const void *x; int x_dtype;                    // [T][H] activation fed to the experts
+    int H, I, K;
+    const moe_expert_desc *experts;
+    const int32_t *off, *perm, *tiles, *ntiles;
+    float *hbuf;                                   // [T*K][I] SwiGLU outputs in expert order
+    float *y;                                      // [T*K][H]
+};
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, hipStream_t s);
+
 struct CombineLaunch {
     const float *y; const float *w; const float *residual; float *out;
     int T, K, H;

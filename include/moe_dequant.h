@@ -193,7 +193,7 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
 /* Expert FFN for T tokens and the K experts each token selected:
  *   y[t][k] = W_down[e] (silu(W_gate[e] n_t) * (W_up[e] n_t)),  e = idx[t][k]
  *   x   device [T][H] x_dtype (normalised inside when the layer has a norm weight)
- *   idx device [T][K] int32 in [0, E) (out-of-range entries produce undefined y rows)
+ *   idx device [T][K] int32; an entry outside [0, E) gives a zero row of y
  *   y   device [T][K][H] fp32
  * T == 1 runs the decode matvec kernels (all K experts in one launch per phase); T > 1
  * groups the T*K (token, slot) pairs by expert and runs the grouped dequant-GEMM (MFMA)

@@ -267,7 +267,7 @@ _fill = None
 
 def build_device_filler(force: bool = True) -> str:
     if force or not os.path.exists(_FILL_LIB):
-        cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared",
+        cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=off",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                _FILL_SRC, "-o", _FILL_LIB + ".tmp"]
         subprocess.check_call(cmd, stderr=subprocess.DEVNULL)

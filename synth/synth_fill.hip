@@ -37,7 +37,10 @@ struct FillArgs {
   float s_lo, s_span, b_lo, b_span;
 };
 
+// Each step rounds to fp32 on its own, as the host generator's numpy float32 steps do: no fused
+// multiply-add may merge the product and the sum.
 __device__ inline uint32_t sb_pair(uint64_t key, uint64_t p, const FillArgs& a) {
+#pragma clang fp contract(off)
   uint64_t w = mix64(key + (p + 1) * kGamma);
   float hi = (float)(uint32_t)(w >> 40) * 5.9604644775390625e-08f;          // 2^-24, exact
   float lo = (float)(uint32_t)(w & 0xFFFFFFull) * 5.9604644775390625e-08f;

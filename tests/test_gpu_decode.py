@@ -142,16 +142,20 @@ def test_decode_is_deterministic():
         assert np.array_equal(u, v)
 
 
-def test_device_filler_matches_host_generator():
+@pytest.mark.parametrize("H,I,n", [(512, 256, 3), (4096, 1024, 2)])
+def test_device_filler_matches_host_generator(H, I, n):
+    """Every byte the device filler writes (codes and the fp32-derived scale/bias draws) equals the
+    host generator's, at the full expert shape too."""
     for bits in (4, 2):
-        H, I = 512, 256
         stride = synth.blob_layout(H, I, bits)[1]
-        buf = torch.full((3 * stride,), 0xAB, dtype=torch.uint8, device="cuda")
-        synth.fill_blobs_device(buf.data_ptr(), stride, 3, 5, 2, 1234, H, I, bits,
+        buf = torch.full((n * stride,), 0xAB, dtype=torch.uint8, device="cuda")
+        synth.fill_blobs_device(buf.data_ptr(), stride, n, 5, 2, 1234, H, I, bits,
                                 torch.cuda.current_stream().cuda_stream)
-        host = buf.cpu().numpy().reshape(3, stride)
-        for i in range(3):
-            assert np.array_equal(host[i], synth.expert_blob(1234, 2, 5 + i, H, I, bits))
+        host = buf.cpu().numpy().reshape(n, stride)
+        for i in range(n):
+            ref = synth.expert_blob(1234, 2, 5 + i, H, I, bits)
+            bad = np.flatnonzero(host[i] != ref)
+            assert bad.size == 0, f"bits {bits} expert {i}: {bad.size} bytes differ, first at {bad[:4]}"
 
 
 def test_two_layer_stack_small():
