@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -69,8 +71,27 @@ __device__ __forceinline__ float load_act(const void *x, int dtype, size_t i) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Sum over aligned groups of gs lanes (gs a power of two <= 64); every lane gets its group's sum.
+// Butterfly in registers: quad permutes and row mirrors (DPP) inside 16-lane rows, then the gfx950
+// row swaps (v_permlane16/32_swap) across rows.  After the steps below gs, every lane holds the sum
+// of its aligned group of gs lanes, and both partners of a step add the same two values, so all
+// lanes of a group hold identical bits.  Branch-free so that several sums interleave.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float group_sum(float v, int gs) {
-    for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    v += gs > 1 ? dppf<0xB1>(v) : 0.f;      // quad_perm [1,0,3,2]
+    v += gs > 2 ? dppf<0x4E>(v) : 0.f;      // quad_perm [2,3,0,1]
+    v += gs > 4 ? dppf<0x141>(v) : 0.f;     // row_half_mirror
+    v += gs > 8 ? dppf<0x140>(v) : 0.f;     // row_mirror
+    if (gs > 16) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    if (gs > 32) {
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    }
     return v;
 }
 
@@ -111,23 +132,31 @@ __device__ __forceinline__ uint64_t lookup_sel(int e, int E, bool use_tab, const
 // Slot s: 4-bit dword s*16 + 4k + i packs columns (8k+i, 8k+i+4), k < 4, i < 4; 2-bit dword
 // s*16 + 8k + i packs (16k+i, 16k+i+8), k < 2, i < 8.  Chunk m = 2s + half therefore owns the 8
 // contiguous dwords s*16 + 8*half .. +8 of both layouts.
-__device__ __forceinline__ void load_chunk16(const void *x, int dtype, int m, float v[16]) {
+// A chunk of 16 consecutive activations (32 bytes of bf16 or 64 of fp32) is loaded in two steps:
+// issue_chunk16 starts four 16-byte loads with no data-dependent branch (bf16 repeats its second
+// load), chunk16_f32 converts once the data is needed.  Keeping the conversion out of the issue
+// step lets every chunk a thread needs be in flight at once instead of one memory latency each.
+struct Chunk16 {
+    u32x4 q[4];
+};
+__device__ __forceinline__ void issue_chunk16(const void *x, int dtype, int m, Chunk16 &c) {
+    const int cb = dtype == MOE_BF16 ? 32 : 64;
+    const GLOBAL_AS uint8_t *p = (const GLOBAL_AS uint8_t *)x + (size_t)m * cb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.q[i] = *(const GLOBAL_AS u32x4 *)(p + min(16 * i, cb - 16));
+}
+__device__ __forceinline__ void chunk16_f32(const Chunk16 &c, int dtype, float v[16]) {
     if (dtype == MOE_BF16) {
-        const u32x4 *p = (const u32x4 *)((const uint16_t *)x + 16 * (size_t)m);
-        const u32x4 a = p[0], b = p[1];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            v[2 * j] = bf16_f32(a[j] & 0xFFFFu); v[2 * j + 1] = bf16_f32(a[j] >> 16);
-            v[8 + 2 * j] = bf16_f32(b[j] & 0xFFFFu); v[8 + 2 * j + 1] = bf16_f32(b[j] >> 16);
+            v[2 * j] = bf16_f32(c.q[0][j] & 0xFFFFu); v[2 * j + 1] = bf16_f32(c.q[0][j] >> 16);
+            v[8 + 2 * j] = bf16_f32(c.q[1][j] & 0xFFFFu); v[8 + 2 * j + 1] = bf16_f32(c.q[1][j] >> 16);
         }
     } else {
-        const u32x4 *p = (const u32x4 *)((const float *)x + 16 * (size_t)m);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4 a = p[q];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(a[j]);
-        }
+            for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(c.q[q][j]);
     }
 }
 
@@ -243,96 +272,126 @@ __device__ __forceinline__ void expert_planes(uint64_t blob_addr, int H, int I, 
 // the softmax over the selected logits, which equals the softmax over all E renormalised.
 //
 // A logit is compared through an order-preserving 32-bit key (its fp32 bits with the sign folded;
-// -0 is first canonicalised to +0 so that equal floats give equal keys).  Lane l owns logits
-// l, l+64, ... and keeps its best untaken key ("head").  A round takes the wave maximum of the
-// heads (DPP inside 16-lane rows, readlane across rows); the lanes holding it are found with a
-// ballot, and only when several lanes tie does a second reduction pick the lowest expert index.
-// The winning lane then recomputes its head from its NP registers.
-__device__ __forceinline__ uint32_t f32_order(float v) {
+// -0 is first canonicalised to +0 so that equal floats give equal keys); key 0 marks an absent
+// expert and is below every real key.  The experts are laid out lane-major: lane l holds experts
+// NP*l .. NP*l+NP-1 in registers, so among lanes whose best keys tie the lowest lane holds the lowest
+// index, and inside a lane the lowest slot does.  Each lane keeps its best two untaken keys.  A
+// round takes the wave maximum of the lane heads with DPP inside 16-lane rows and the gfx950 row
+// swaps across rows (every lane gets it, no scalar round trip), finds the lowest lane holding it
+// with one ballot, and promotes that lane's second key.  A lane that wins twice recomputes its
+// two best untaken keys.  The winner records its slot in a per-round bit field; lane k reads the
+// field of round k's winner once, after the last round.  Everything stays in registers: a round
+// is a short dependent chain, which is what bounds a single wave here.
+__device__ __forceinline__ uint32_t logit_key(float v) {
     v = (v != v) ? -INFINITY : v + 0.0f;
     const uint32_t u = __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
-__device__ __forceinline__ float order_f32(uint32_t o) {
+__device__ __forceinline__ float key_logit(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {   // DPP move; lanes without a source read 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
-// Wave-wide max / min (every lane gets the result).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp32<0xB1>(v));     // quad_perm [1,0,3,2]
-    v = max(v, dpp32<0x4E>(v));     // quad_perm [2,3,0,1]
-    v = max(v, dpp32<0x141>(v));    // row_half_mirror
-    v = max(v, dpp32<0x140>(v));    // row_mirror: each lane holds its 16-lane row maximum
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return max(max(r0, r1), max(r2, r3));
+// Wave-wide maximum, returned in every lane.
+__device__ __forceinline__ uint32_t wave_max_all(uint32_t v) {
+    v = max(v, dpp0<0xB1>(v));      // quad_perm [1,0,3,2]
+    v = max(v, dpp0<0x4E>(v));      // quad_perm [2,3,0,1]
+    v = max(v, dpp0<0x141>(v));     // row_half_mirror
+    v = max(v, dpp0<0x140>(v));     // row_mirror: the 16-lane row maximum
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);    // rows 0<->1, 2<->3
+    v = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);    // halves
+    return max(b[0], b[1]);
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, dpp32<0xB1>(v));
-    v = min(v, dpp32<0x4E>(v));
-    v = min(v, dpp32<0x141>(v));
-    v = min(v, dpp32<0x140>(v));
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return min(min(r0, r1), min(r2, r3));
+// The two best keys of this lane that are not in `taken` (ties: lower slot first).  Pairwise
+// tree: list A always comes from lower slots than list B.
+struct Top2 {
+    uint32_t h1, h2;
+    int s1, s2;
+};
+__device__ __forceinline__ Top2 top2_merge(const Top2 &A, const Top2 &B) {
+    const bool bw = B.h1 > A.h1;
+    Top2 r;
+    r.h1 = bw ? B.h1 : A.h1;
+    r.s1 = bw ? B.s1 : A.s1;
+    const bool a2 = bw ? (A.h1 >= B.h2) : (A.h2 >= B.h1);   // second: A's candidate wins ties
+    r.h2 = bw ? (a2 ? A.h1 : B.h2) : (a2 ? A.h2 : B.h1);
+    r.s2 = bw ? (a2 ? A.s1 : B.s2) : (a2 ? A.s2 : B.s1);
+    return r;
 }
-
-// Best untaken key of this lane (0 = none; every real key is > 0) and its slot.
-template <int NP>
-__device__ __forceinline__ void lane_head(const uint32_t (&ord)[NP], uint32_t taken, uint32_t &hv, int &ht) {
-    hv = 0;
-    ht = 0;
-#pragma unroll
-    for (int t = 0; t < NP; ++t) {
-        const bool better = !((taken >> t) & 1u) && ord[t] > hv;    // strict: lower slot wins ties
-        hv = better ? ord[t] : hv;
-        ht = better ? t : ht;
+template <int N>
+__device__ __forceinline__ Top2 top2_range(const uint32_t *key, uint32_t taken, int t0) {
+    if constexpr (N == 1) {
+        return Top2{((taken >> t0) & 1u) ? 0u : key[t0], 0u, t0, t0};
+    } else {
+        return top2_merge(top2_range<N / 2>(key, taken, t0), top2_range<N / 2>(key, taken, t0 + N / 2));
     }
 }
 
-// `lg`: the logit row in LDS, E <= 64*NP.  Lane k < K returns selection k (index, weight).
+// `key`: this lane's NP keys (experts NP*lane + t).  Lane k < K returns selection k.
 template <int NP>
-__device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int &my_idx, float &my_w) {
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[NP], int K, int &my_idx, float &my_w) {
+    constexpr int FW = NP <= 8 ? 3 : 5;                            // bits per recorded slot
+    typedef typename std::conditional<NP <= 8, uint32_t, uint64_t>::type rec_t;
     const int lane = threadIdx.x & 63;
-    uint32_t ord[NP];
-#pragma unroll
-    for (int t = 0; t < NP; ++t) {
-        const int e = lane + 64 * t;
-        ord[t] = e < E ? f32_order(lg[e]) : 0u;
-    }
-    uint32_t taken = 0, hv;
-    int ht;
-    lane_head(ord, taken, hv, ht);
-    uint32_t my_key = 0;
-    my_idx = 0;
+    Top2 c = top2_range<NP>(key, 0u, 0);
+    uint32_t taken = 0, my_key = 0, top = 0;
+    rec_t rec = 0;
+    int my_wl = 0;
+    uint64_t second_stale = 0;     // lanes whose second key was promoted and not yet recomputed
     for (int k = 0; k < K; ++k) {
-        const uint32_t m = wave_max_u32(hv);
-        const uint64_t bal = __ballot(hv == m);
-        int wl, wt;
-        if (__popcll(bal) == 1) {
-            wl = __ffsll((unsigned long long)bal) - 1;
-            wt = __builtin_amdgcn_readlane(ht, wl);
-        } else {    // equal keys in several lanes: lowest expert index
-            const uint32_t me = wave_min_u32(hv == m ? (uint32_t)(lane + 64 * ht) : 0xFFFFFFFFu);
-            wl = me & 63;
-            wt = me >> 6;
-        }
-        if (lane == k) { my_idx = wl + 64 * wt; my_key = m; }
-        if (lane == wl) {
-            taken |= 1u << wt;
-            lane_head(ord, taken, hv, ht);
+        const uint32_t m = wave_max_all(c.h1);
+        top = k == 0 ? m : top;
+        const int wl = __ffsll((unsigned long long)__ballot(c.h1 == m)) - 1;
+        const bool me = lane == wl;
+        rec |= me ? (rec_t)c.s1 << (FW * k) : (rec_t)0;
+        taken |= me ? 1u << c.s1 : 0u;
+        my_key = lane == k ? m : my_key;
+        my_wl = lane == k ? wl : my_wl;
+        if ((second_stale >> wl) & 1ull) {
+            const Top2 r = top2_range<NP>(key, taken, 0);
+            c.h1 = me ? r.h1 : c.h1; c.s1 = me ? r.s1 : c.s1;
+            c.h2 = me ? r.h2 : c.h2; c.s2 = me ? r.s2 : c.s2;
+            second_stale &= ~(1ull << wl);
+        } else {
+            c.h1 = me ? c.h2 : c.h1;
+            c.s1 = me ? c.s2 : c.s1;
+            second_stale |= 1ull << wl;
         }
     }
-    const float val = order_f32(my_key);
-    const float top0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(val), 0));   // largest logit
-    const bool finite0 = top0 > -INFINITY;
-    const float ex = lane < K ? (finite0 ? expf(val - top0) : 1.f) : 0.f;
-    float z = 0.f;
-    for (int k = 0; k < K; ++k) z += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex), k));
+    rec_t r;
+    if constexpr (NP <= 8) {
+        r = (rec_t)__shfl((int)rec, my_wl);
+    } else {
+        r = (rec_t)(uint32_t)__shfl((int)(uint32_t)rec, my_wl) | ((rec_t)(uint32_t)__shfl((int)(uint32_t)(rec >> 32), my_wl) << 32);
+    }
+    const int slot = lane < K ? (int)((r >> (FW * lane)) & ((1u << FW) - 1)) : 0;
+    my_idx = my_wl * NP + slot;
+    // weights: softmax over the K selected logits, max-subtracted; the sum runs over lanes 0..7
+    const float val = key_logit(my_key), top0 = key_logit(top);
+    const float ex = lane < K ? (top0 > -INFINITY ? expf(val - top0) : 1.f) : 0.f;
+    float z = ex;
+    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0xB1, 0xF, 0xF, true));
+    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x4E, 0xF, 0xF, true));
+    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x141, 0xF, 0xF, true));
     my_w = ex / z;
+}
+
+// Keys of this lane's experts NP*lane .. NP*lane+NP-1 from a logit row (absent experts: 0).  The
+// loads are branch-free (clamped address) so they are all in flight together.
+template <int NP>
+__device__ __forceinline__ void issue_logits(const float *row, int E, float (&lg)[NP]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < NP; ++t) lg[t] = ((const GLOBAL_AS float *)row)[min(NP * lane + t, E - 1)];
+}
+template <int NP>
+__device__ __forceinline__ void logit_keys(const float (&lg)[NP], int E, uint32_t (&key)[NP]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < NP; ++t) key[t] = NP * lane + t < E ? logit_key(lg[t]) : 0u;
 }
 
 // --------------------------------------------------------------------------- router
@@ -364,13 +423,19 @@ __global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
     // 2. activation (+ RMSNorm) into LDS
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
     const int nch = H / 16;
+    Chunk16 xc[2], nc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = min((int)threadIdx.x + kBlock * j, nch - 1);   // clamped; extra chunks unused
+        issue_chunk16(x, a.x_dtype, m, xc[j]);
+        if (a.norm_w) issue_chunk16(a.norm_w, MOE_BF16, m, nc[j]);
+    }
     float v[2][16];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int m = threadIdx.x + kBlock * j;
-        if (m < nch) {
-            load_chunk16(x, a.x_dtype, m, v[j]);
+        chunk16_f32(xc[j], a.x_dtype, v[j]);
+        if ((int)threadIdx.x + kBlock * j < nch) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
         }
@@ -386,7 +451,7 @@ __global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
         if (m < nch) {
             if (a.norm_w) {
                 float w[16];
-                load_chunk16(a.norm_w, MOE_BF16, m, w);
+                chunk16_f32(nc[j], MOE_BF16, w);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
             }
@@ -454,13 +519,14 @@ __global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
 
 template <int NP>
 __global__ void __launch_bounds__(64) k_topk(TopkLaunch a) {
-    __shared__ float s_lg[MOE_MAX_EXPERTS];
     const int t = blockIdx.x;
-    for (int e = threadIdx.x; e < a.E; e += blockDim.x) s_lg[e] = a.logits[(size_t)t * a.E + e];
-    __syncthreads();
+    float lg[NP];
+    issue_logits<NP>(a.logits + (size_t)t * a.E, a.E, lg);
+    uint32_t key[NP];
+    logit_keys<NP>(lg, a.E, key);
     int my_idx;
     float my_w;
-    wave_topk<NP>(s_lg, a.E, a.K, my_idx, my_w);
+    wave_topk<NP>(key, a.K, my_idx, my_w);
     if ((int)threadIdx.x < a.K) {
         a.idx[(size_t)t * a.K + threadIdx.x] = my_idx;
         a.w[(size_t)t * a.K + threadIdx.x] = my_w;
@@ -541,7 +607,6 @@ __device__ __forceinline__ void gu_finish(const Geo &g, int I, int r0, int RB, c
 template <int NJ, bool SPLIT, int NP>
 __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
-    __shared__ float s_lg[MOE_MAX_EXPERTS];
     __shared__ uint64_t s_tab[kTabMax];
     __shared__ float red[kWaves];
     constexpr int RG = gu_rg<NJ>();
@@ -550,39 +615,38 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     const bool use_tab = E <= kTabMax;
 
     // 1. independent loads, issued back to back (straight-line code: a loop here would make the
-    //    compiler wait for every outstanding load at its header): logits, descriptor table,
-    //    activation chunks
-    float lgv[MOE_MAX_EXPERTS / kBlock];
+    //    compiler wait for every outstanding load at its header): this lane's logits (first, so the
+    //    routing can start when they land), descriptor table, activation chunks
+    float lg[NP];
+    if (!a.idx_in) issue_logits<NP>(a.logits + (size_t)t * E, E, lg);
     u32x4 dsc[kTabMax / kBlock];
-    if (!a.idx_in) {
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_EXPERTS / kBlock; ++j) {
-            const int e = threadIdx.x + kBlock * j;
-            lgv[j] = e < E ? a.logits[(size_t)t * E + e] : 0.f;
-        }
-    }
     if (use_tab) {
 #pragma unroll
-        for (int j = 0; j < kTabMax / kBlock; ++j) {
-            const int e = threadIdx.x + kBlock * j;
-            dsc[j] = e < E ? *(const u32x4 *)(a.experts + e) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < kTabMax / kBlock; ++j)
+            dsc[j] = *(const GLOBAL_AS u32x4 *)(a.experts + min((int)threadIdx.x + kBlock * j, E - 1));
     }
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
     const int nch = H / 16;
-    float v[2][16];
+    Chunk16 xc[2], nc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int m = min(threadIdx.x + kBlock * j, nch - 1);      // clamped; extra chunks unused
-        load_chunk16(x, a.x_dtype, m, v[j]);
+        const int m = min((int)threadIdx.x + kBlock * j, nch - 1);   // clamped; extra chunks unused
+        issue_chunk16(x, a.x_dtype, m, xc[j]);
+        if (a.norm_w) issue_chunk16(a.norm_w, MOE_BF16, m, nc[j]);
     }
-    if (!a.idx_in) {
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_EXPERTS / kBlock; ++j) {
-            const int e = threadIdx.x + kBlock * j;
-            if (e < E) s_lg[e] = lgv[j];
-        }
+
+    // 2. routing in registers (each wave, identical results)
+    int my_idx = 0;
+    float my_w = 0.f;
+    if (a.idx_in) {
+        if (lane < K) my_idx = a.idx_in[(size_t)t * K + lane];
+    } else {
+        uint32_t key[NP];
+        logit_keys<NP>(lg, E, key);
+        wave_topk<NP>(key, K, my_idx, my_w);
     }
+
+    // 3. descriptor table and RMSNorm statistics; one barrier publishes the table
     if (use_tab) {
 #pragma unroll
         for (int j = 0; j < kTabMax / kBlock; ++j) {
@@ -590,29 +654,25 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
             if (e < E) s_tab[e] = pack_sel(((uint64_t)dsc[j].y << 32) | dsc[j].x, dsc[j].z);
         }
     }
-    float ss = 0.f;
+    float v[2][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        if ((int)threadIdx.x + kBlock * j < nch) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
-        }
+    for (int j = 0; j < 2; ++j) chunk16_f32(xc[j], a.x_dtype, v[j]);
     float inv = 1.f;
     if (a.norm_w) {
-        ss = block_sum(ss, red);   // also makes s_lg / s_tab visible
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if ((int)threadIdx.x + kBlock * j < nch) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
+            }
+        ss = block_sum(ss, red);   // also makes s_tab visible
         inv = 1.0f / sqrtf(ss / (float)H + a.eps);
     } else {
         __syncthreads();
     }
 
-    // 2. routing (each wave, identical results) and the first unit's weight loads
-    int my_idx = 0;
-    float my_w = 0.f;
-    if (a.idx_in) {
-        if (lane < K) my_idx = a.idx_in[(size_t)t * K + lane];
-    } else {
-        wave_topk<NP>(s_lg, E, K, my_idx, my_w);
-    }
+    // 4. routing outputs and the first unit's weight loads
     if (blockIdx.x == 0 && wave == 0 && lane < K) {
         const size_t o = (size_t)t * K + lane;
         if (a.idx_out) a.idx_out[o] = my_idx;
@@ -630,7 +690,7 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     Planes pl[3];
     if (u < units) {
         const int k = u / nblk;
-        sel = lookup_sel(__shfl(my_idx, k), E, use_tab, s_tab, a.experts);
+        sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
         if (sel) {
             expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
             if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
@@ -638,7 +698,7 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
         }
     }
 
-    // 3. activation layouts for both code widths, straight from registers
+    // 5. activation layouts for both code widths, straight from registers
     uint32_t *h4 = lds, *l4 = lds + H / 2, *h2 = lds + H, *l2 = lds + 3 * H / 2;
     float *xs = (float *)(lds + 2 * H);
 #pragma unroll
@@ -648,27 +708,27 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
         if (m < nch) {
             if (a.norm_w) {
                 float w[16];
-                load_chunk16(a.norm_w, MOE_BF16, m, w);
+                chunk16_f32(nc[j], MOE_BF16, w);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
             }
             sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
             write_chunk<2, SPLIT>(m, v[j], h2, l2);
         }
-        sum += __shfl_xor(sum, 1);                   // chunks 2s and 2s+1 sit in lanes l and l^1
+        sum += dppf<0xB1>(sum);                      // chunks 2s and 2s+1 sit in lanes l and l^1
         if (m < nch && !(m & 1)) xs[m >> 1] = sum;
     }
     __syncthreads();
     const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
 
-    // 4. work units
+    // 6. work units
     bool first = true;
     for (; u < units; u += gridDim.x * kWaves) {
         const int k = u / nblk;
         const int r0 = (u - k * nblk) * RB;
         float *hout = a.h + ((size_t)t * K + k) * I;
         if (!first) {
-            sel = lookup_sel(__shfl(my_idx, k), E, use_tab, s_tab, a.experts);
+            sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
             if (sel) {
                 expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
                 if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
@@ -736,24 +796,30 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     constexpr int RG = dn_rg<NJ>();
     const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // 1. selected experts (wave-uniform), routing weights, first unit's weight loads
-    uint64_t sel[KM];
-    float wk[KM];
-    uint32_t two_mask = 0;   // bit k: expert k has 2-bit codes
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        sel[k] = k < K ? a.sel[(size_t)t * K + k] : 0;
-        wk[k] = (COMBINE && k < K) ? a.w[(size_t)t * K + k] : 0.f;
-        if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
-    }
-    // h chunks of this thread (first pass), loaded alongside
+    // 1. h chunks of this thread (first pass) and the selected experts + routing weights, all in
+    //    flight together (branch-free clamped loads); then the first unit's weight loads
     const int per = down_lds_per_expert(I);
     const int cpe = I / 16;                         // chunks per expert
     const int nch = K * cpe;
     const float *hrow = a.h + (size_t)t * K * I;
-    float v[2][16];
+    Chunk16 hc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_chunk16(hrow, MOE_F32, min(threadIdx.x + kBlock * j, nch - 1), v[j]);
+    for (int j = 0; j < 2; ++j) issue_chunk16(hrow, MOE_F32, min((int)threadIdx.x + kBlock * j, nch - 1), hc[j]);
+    uint64_t sel[KM];
+    float wk[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        const size_t o = (size_t)t * K + min(k, K - 1);
+        sel[k] = ((const GLOBAL_AS uint64_t *)a.sel)[o];
+        wk[k] = COMBINE ? ((const GLOBAL_AS float *)a.w)[o] : 0.f;
+    }
+    uint32_t two_mask = 0;   // bit k: expert k has 2-bit codes
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        sel[k] = k < K ? sel[k] : 0;
+        wk[k] = k < K ? wk[k] : 0.f;
+        if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
+    }
     const Geo g = make_geo(I);
     const int RB = RG * g.rpi;
     const int nblk = (H + RB - 1) / RB;
@@ -772,17 +838,25 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
             uint32_t *hi = lds + kk * per, *lo = hi + I / 2;
             sum = ((two_mask >> kk) & 1u) ? write_chunk<2, true>(mm, vv, hi, lo) : write_chunk<4, true>(mm, vv, hi, lo);
         }
-        sum += __shfl_xor(sum, 1);
+        sum += dppf<0xB1>(sum);
         if (m < nch && !(mm & 1)) ((float *)(lds + kk * per + I))[mm >> 1] = sum;
     };
+    float v[2][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) stage(threadIdx.x + kBlock * j, v[j]);
+    for (int j = 0; j < 2; ++j) {
+        chunk16_f32(hc[j], MOE_F32, v[j]);
+        stage(threadIdx.x + kBlock * j, v[j]);
+    }
     for (int base = 2 * kBlock; base < nch; base += 2 * kBlock) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int m = base + threadIdx.x + kBlock * j;
-            if (m < nch) load_chunk16(hrow, MOE_F32, m, v[j]);
-            stage(m, v[j]);
+            issue_chunk16(hrow, MOE_F32, min(m, nch - 1), hc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            chunk16_f32(hc[j], MOE_F32, v[j]);
+            stage(base + threadIdx.x + kBlock * j, v[j]);
         }
     }
     __syncthreads();
