@@ -47,6 +47,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run device-to-device copies of 1 GiB (reference for the HBM byte counters)")
+    p.add_argument("--traffic-from", metavar="DIR",
+                   help="read rocprofv3 --pmc output under DIR/{fetch,write,copy_fetch,copy_write} and write "
+                        "profiles/traffic.json for this workload")
     return p.parse_args()
 
 
@@ -75,11 +80,77 @@ def load_traffic(kernel: str, workload_key: str):
     return None
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """Plain device-to-device copies of known size: each reads and writes COPY_BYTES."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_BYTES} bytes 4 times")
+
+
+def read_counter_csv(d: str, counter: str):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv under d."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_from(d: str, workload_key: str):
+    """HBM bytes per launch of each decode kernel: FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each
+    scaled so that the copy kernel reads and writes exactly COPY_BYTES."""
+    scale = {}
+    for c, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        vals = [v for k, vs in read_counter_csv(os.path.join(d, sub), c).items() for v in vs
+                if "copy" in k.lower() or "elementwise" in k.lower()]
+        big = [v for v in vals if v * 1024 > COPY_BYTES / 2]
+        if not big:
+            raise SystemExit(f"no copy dispatch found for {c}")
+        scale[c] = COPY_BYTES / (float(np.median(big)) * 1024)
+    fetch = read_counter_csv(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = read_counter_csv(os.path.join(d, "write"), "WRITE_SIZE")
+    res = {}
+    for short in ("k_router", "k_gateup", "k_down", "k_gu_mfma", "k_dn_mfma", "k_group"):
+        fk = [k for k in fetch if f"{short}<" in k or f"{short}(" in k]
+        wk = [k for k in write if f"{short}<" in k or f"{short}(" in k]
+        if not fk or not wk:
+            continue
+        f = float(np.mean([v for k in fk for v in fetch[k]])) * 1024 * scale["FETCH_SIZE"]
+        w = float(np.mean([v for k in wk for v in write[k]])) * 1024 * scale["WRITE_SIZE"]
+        res[short] = {"bytes_per_launch": f + w, "fetch_bytes": f, "write_bytes": w,
+                      "dispatches": sum(len(fetch[k]) for k in fk), "source_hash": source_hash(),
+                      "scale_fetch": scale["FETCH_SIZE"], "scale_write": scale["WRITE_SIZE"]}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    allp = json.load(open(p)) if os.path.exists(p) else {}
+    allp[workload_key] = res
+    json.dump(allp, open(p, "w"), indent=1, sort_keys=True)
+    log(f"[bench] wrote {p}: {json.dumps(res)}")
+
+
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration()
+        return
+    if a.traffic_from:
+        traffic_from(a.traffic_from, f"config{a.config}")
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the decode path runs on a single MI355X here "
-              "(see the sharding notes in DESIGN.md); run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU (the expert path of one device); multi-GPU runs are not "
+              "part of this benchmark: run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -203,7 +274,8 @@ def main():
     gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] {tok_s:,.0f} tok/s, {gbps:,.1f} GB/s of weights ({gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)")
 
-    # per-kernel durations (events on the library's stream, eager issue)
+    # per-kernel durations: HIP events recorded by the library on its own stream between the
+    # kernels of each step
     roof = None
     kernel_us = {}
     if not batched:
@@ -213,8 +285,12 @@ def main():
             for e in row:
                 e.record(stream)
         torch.cuda.synchronize()
-        for t in range(n_t):
-            M.moe_layer_decode_timed(d, L, bank[t], outs[t % G], evs[t], idxs[t], wts[t], residual=wl.norm, ws=ws)
+
+        def timed_steps():
+            for t in range(n_t):
+                M.moe_layer_decode_timed(d, L, bank[t], outs[t % G], evs[t], idxs[t], wts[t], residual=wl.norm,
+                                         ws=ws)
+        timed_steps()            # ROCm records no event nodes inside captured graphs: eager issue
         torch.cuda.synchronize()
         names = ["router", "gateup", "down"]
         dur = {n: [] for n in names}
@@ -231,7 +307,8 @@ def main():
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": load_traffic("k_gateup", f"config{a.config}"),
-                "bytes_per_launch": float(np.mean(gu_b)), "us_per_launch": round(gu_us, 3)}
+                "bytes_per_launch": float(np.mean(gu_b)), "us_per_launch": round(gu_us, 3),
+                "timing": "HIP events between the kernels of each step, eager issue"}
         log(f"[bench] kernel us: {kernel_us}; gate/up {achieved:,.1f} GB/s")
 
     # CPU baseline: the oracle on a bounded sample of the same workload
@@ -248,7 +325,7 @@ def main():
         oracle.stack_token(x0, ols, H, I, K, residual=wl.norm) if wl.n_layers > 1 else \
             oracle.layer_token(x0, ols[0], H, I, K)
         per = time.perf_counter() - t1
-        n_s = max(1, min(256, int(a.cpu_seconds / max(per, 1e-3))))
+        n_s = max(1, min(4096, int(a.cpu_seconds / max(per, 1e-3))))
         if batched:
             n_s = min(n_s, wl.tokens)
         # pre-generate the expert blobs the sample needs, so that only the oracle is timed
