@@ -22,6 +22,7 @@ MOE_OK = 0
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OP_ROUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE = 1, 2, 3
 MOE_FLAG_RESIDUAL = 1
+MOE_FLAG_SEPARATE_KERNELS = 2
 GROUP = 64
 MAX_TOPK = 8
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_BITS",
@@ -227,7 +228,7 @@ def moe_workspace_bytes(op: int, dims: moe_dims, T: int = 1, n_layers: int = 1) 
 def workspace(op: int, dims: moe_dims, T: int = 1, n_layers: int = 1, device="cuda"):
     import torch
     n = moe_workspace_bytes(op, dims, T, n_layers)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 # ----------------------------------------------------------------------------- compute
@@ -249,9 +250,12 @@ def moe_combine(y, w, out, residual=None, stream=None) -> None:
 
 
 def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, w=None, residual: bool = False,
-                     ws=None, stream=None) -> None:
+                     ws=None, stream=None, separate_kernels: bool = False) -> None:
+    """One decode token through the layers.  ``ws`` must come from :func:`workspace` (zero-filled)
+    and be reused only by stream-ordered calls; ``separate_kernels`` selects the three-kernel
+    schedule instead of one launch per layer."""
     arr = (moe_layer * len(layers))(*[L.c for L in layers])
-    flags = MOE_FLAG_RESIDUAL if residual else 0
+    flags = (MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                   _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))

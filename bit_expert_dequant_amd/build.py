@@ -1,9 +1,13 @@
-"""Build the gfx950 library in-tree: bit_expert_dequant_amd/libmoe_dequant.so."""
+"""Build the gfx950 library in-tree: bit_expert_dequant_amd/libmoe_dequant.so.
+
+Each source is compiled to an object on its own (in parallel), then the objects are linked."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -11,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_dequant.so")
 
-SOURCES = ["moe_api.cpp", "moe_decode.hip", "moe_grouped.hip"]
+SOURCES = ["moe_api.cpp", "moe_decode.hip", "moe_grouped.hip", "moe_layer.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -25,18 +29,37 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", *HIP_FLAGS, "-shared", f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd))
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = [l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l]
-    if r.returncode != 0:
-        sys.stderr.write("\n".join(errs) + "\n")
-        raise RuntimeError(f"hipcc failed with code {r.returncode}")
-    if verbose and errs:
-        sys.stderr.write("\n".join(errs) + "\n")
+    return r.returncode, errs
+
+
+def build(verbose: bool = False) -> str:
+    srcs = sources()
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpd:
+        objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [["hipcc", *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, cmds))
+        for (rc, errs), s in zip(results, srcs):
+            if rc != 0:
+                sys.stderr.write("\n".join(errs) + "\n")
+                raise RuntimeError(f"hipcc failed on {os.path.basename(s)} with code {rc}")
+            if verbose and errs:
+                sys.stderr.write("\n".join(errs) + "\n")
+        tmp = LIB + ".tmp"
+        link = ["hipcc", "--offload-arch=gfx950", "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link))
+        rc, errs = _run(link)
+        if rc != 0:
+            sys.stderr.write("\n".join(errs) + "\n")
+            raise RuntimeError(f"link failed with code {rc}")
     os.replace(tmp, LIB)
     return LIB
 

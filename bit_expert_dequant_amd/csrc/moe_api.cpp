@@ -122,15 +122,36 @@ size_t ffn_ws(const moe_dims *d, int T) {
     c.take<uint64_t>((size_t)T * d->top_k);
     return c.off;
 }
-size_t decode_ws(const moe_dims *d) {
-    Carve c{nullptr};
-    c.take<float>(d->n_experts);
-    c.take<uint64_t>(d->top_k);
-    c.take<float>(d->top_k);
-    c.take<float>((size_t)d->top_k * d->inter);
-    c.take<float>(2 * (size_t)d->hidden);
-    return c.off;
+// Layer-decode workspace: the one-launch schedule's hand-over words first (they must start
+// zeroed), then the buffers both schedules use.
+struct DecodeWs {
+    uint32_t *sync;      // [0] launch counter, [1] error word
+    uint64_t *slots;     // [copies][E] tagged logits
+    float *logits;
+    uint64_t *sel;
+    float *w;
+    float *h;
+    float *xbuf;
+    size_t bytes;
+};
+DecodeWs decode_layout(const moe_dims *d, void *ws) {
+    Carve c{(char *)ws};
+    DecodeWs r;
+    r.sync = c.take<uint32_t>(2);
+    r.slots = c.take<uint64_t>((size_t)moe::layer_logit_copies() * d->n_experts);
+    r.logits = c.take<float>(d->n_experts);
+    r.sel = c.take<uint64_t>(d->top_k);
+    r.w = c.take<float>(d->top_k);
+    r.h = c.take<float>((size_t)d->top_k * d->inter);
+    r.xbuf = c.take<float>(2 * (size_t)d->hidden);
+    r.bytes = c.off;
+    return r;
 }
+
+size_t decode_ws(const moe_dims *d) {
+    return decode_layout(d, nullptr).bytes;
+}
+
 
 }  // namespace
 
@@ -344,7 +365,7 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     moe::GateUpLaunch ga{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, nullptr, idx, nullptr, nullptr,
                          sel, nullptr, layer->experts, h, dims->hidden, dims->inter, dims->n_experts, dims->top_k, T};
     if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
-    moe::DownLaunch da{h, sel, nullptr, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter, dims->top_k, T};
+    moe::DownLaunch da{h, nullptr, nullptr, sel, nullptr, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter, dims->top_k, T};
     if (int s = launched(moe::launch_down(da, st), "down")) return s;
     return ok();
 }
@@ -382,36 +403,53 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
     if (int s = check_dtype(x_dtype, "x")) return s;
     if (!x || !out) return fail(MOE_ERR_NULL, "x and out are required");
     if ((idx == nullptr) != (w == nullptr)) return fail(MOE_ERR_NULL, "idx and w must both be given or both NULL");
-    if (flags & ~MOE_FLAG_RESIDUAL) return fail(MOE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if (flags & ~(MOE_FLAG_RESIDUAL | MOE_FLAG_SEPARATE_KERNELS))
+        return fail(MOE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_ALIGN, "x and out must be 16-byte aligned");
     if ((idx && !aligned(idx, 4)) || (w && !aligned(w, 4))) return fail(MOE_ERR_ALIGN, "idx/w not 4-byte aligned");
     if (out == x) return fail(MOE_ERR_SHAPE, "out must not alias x");
     if (int s = check_ws(ws, ws_bytes, decode_ws(dims))) return s;
 
     const int H = dims->hidden, I = dims->inter, E = dims->n_experts, K = dims->top_k;
-    Carve c{(char *)ws};
-    float *logits = c.take<float>(E);
-    uint64_t *sel_ws = c.take<uint64_t>(K);
-    float *w_ws = c.take<float>(K);
-    float *h = c.take<float>((size_t)K * I);
-    float *xbuf = c.take<float>(2 * (size_t)H);
+    const DecodeWs W = decode_layout(dims, ws);
     hipStream_t st = (hipStream_t)stream;
     const bool residual = flags & MOE_FLAG_RESIDUAL;
+    const bool separate = events != nullptr || (flags & MOE_FLAG_SEPARATE_KERNELS);
     if (int s = record(events, 0, st)) return s;
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer &L = layers[l];
-        const void *xl = l == 0 ? x : (const void *)(xbuf + (size_t)((l - 1) & 1) * H);
+        const void *xl = l == 0 ? x : (const void *)(W.xbuf + (size_t)((l - 1) & 1) * H);
         const int xdt = l == 0 ? x_dtype : MOE_F32;
-        float *ol = l == n_layers - 1 ? out : xbuf + (size_t)(l & 1) * H;
-        moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, logits, H, E, 1};
+        float *ol = l == n_layers - 1 ? out : W.xbuf + (size_t)(l & 1) * H;
+        int32_t *idx_l = idx ? idx + (size_t)l * K : nullptr;
+        float *w_l = w ? w + (size_t)l * K : nullptr;
+        moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, W.logits, H, E, 1};
+        if (!separate) {
+            moe::LayerLaunch la{};
+            la.r = ra;
+            la.experts = L.experts;
+            la.idx_out = idx_l;
+            la.w_out = w_l;
+            la.sel_ws = W.sel;
+            la.w_ws = W.w;
+            la.h = W.h;
+            la.H = H; la.I = I; la.E = E; la.K = K;
+            la.split = !(xdt == MOE_BF16 && L.norm_w == nullptr);
+            la.seq = W.sync;
+            la.err = W.sync + 1;
+            la.slots = W.slots;
+            if (int s = launched(moe::launch_layer(la, st), "router + gate/up")) return s;
+            moe::DownLaunch da{W.h, W.sync, W.sync + 1, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
+            if (int s = launched(moe::launch_down(da, st), "down")) return s;
+            continue;
+        }
         if (int s = launched(moe::launch_router(ra, st), "router")) return s;
         if (int s = record(events, 3 * l + 1, st)) return s;
-        moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, logits, nullptr,
-                             idx ? idx + (size_t)l * K : nullptr, w ? w + (size_t)l * K : nullptr, sel_ws, w_ws,
-                             L.experts, h, H, I, E, K, 1};
+        moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, W.logits, nullptr, idx_l, w_l, W.sel, W.w,
+                             L.experts, W.h, H, I, E, K, 1};
         if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
         if (int s = record(events, 3 * l + 2, st)) return s;
-        moe::DownLaunch da{h, sel_ws, w_ws, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
+        moe::DownLaunch da{W.h, nullptr, nullptr, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
         if (int s = launched(moe::launch_down(da, st), "down")) return s;
         if (int s = record(events, 3 * l + 3, st)) return s;
     }

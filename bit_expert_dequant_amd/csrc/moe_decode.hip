@@ -34,487 +34,18 @@
 // about two memory latencies: all independent loads (logits, descriptor table, activation,
 // norm weight) are issued together; the first work unit's weight loads are issued before the
 // activation layouts are written to LDS, so they are in flight while the workgroup stages.
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
-#include <type_traits>
-
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace moe {
 namespace {
 
-#define GLOBAL_AS __attribute__((address_space(1)))
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both 16-bit halves
-constexpr int kBlock = 256;               // threads per workgroup (4 wavefronts)
-constexpr int kWaves = kBlock / 64;
-constexpr int kDPS = 16;                  // activation dwords per slot (32 columns, bf16 pairs)
-constexpr int kTabMax = 512;              // experts whose descriptors are prefetched into LDS
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ float load_act(const void *x, int dtype, size_t i) {
-    return dtype == MOE_BF16 ? bf16_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
-}
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// Sum over aligned groups of gs lanes (gs a power of two <= 64); every lane gets its group's sum.
-// Butterfly in registers: quad permutes and row mirrors (DPP) inside 16-lane rows, then the gfx950
-// row swaps (v_permlane16/32_swap) across rows.  After the steps below gs, every lane holds the sum
-// of its aligned group of gs lanes, and both partners of a step add the same two values, so all
-// lanes of a group hold identical bits.  Branch-free so that several sums interleave.
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float group_sum(float v, int gs) {
-    v += gs > 1 ? dppf<0xB1>(v) : 0.f;      // quad_perm [1,0,3,2]
-    v += gs > 2 ? dppf<0x4E>(v) : 0.f;      // quad_perm [2,3,0,1]
-    v += gs > 4 ? dppf<0x141>(v) : 0.f;     // row_half_mirror
-    v += gs > 8 ? dppf<0x140>(v) : 0.f;     // row_mirror
-    if (gs > 16) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    }
-    if (gs > 32) {
-        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-    }
-    return v;
-}
-
-__device__ float block_sum(float v, float *red) {
-    v = group_sum(v, 64);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float t = 0.f;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
-    __syncthreads();
-    return t;
-}
-
-__host__ __device__ __forceinline__ int next_pow2(int v) {
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
-}
-__host__ __device__ __forceinline__ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-// Selected expert, packed for the down kernel: blob address (256-byte aligned) | code width.
-__device__ __forceinline__ uint64_t pack_sel(uint64_t blob, uint32_t bits) { return blob ? (blob | (bits == 2 ? 2u : 4u)) : 0; }
-__device__ __forceinline__ uint64_t sel_blob(uint64_t s) { return s & ~(uint64_t)255; }
-__device__ __forceinline__ int sel_bits(uint64_t s) { return (int)(s & 255u) == 2 ? 2 : 4; }
-
-// Packed selection of expert e (0 for an index outside [0, E)).
-__device__ __forceinline__ uint64_t lookup_sel(int e, int E, bool use_tab, const uint64_t *tab,
-                                               const moe_expert_desc *experts) {
-    if (e < 0 || e >= E) return 0;
-    if (use_tab) return tab[e];
-    const moe_expert_desc d = experts[e];
-    return pack_sel(d.blob, d.bits);
-}
-
-// --------------------------------------------------------------------------- activation staging
-// A thread stages "chunks" of 16 consecutive columns (two chunks per 32-column slot).
-// Slot s: 4-bit dword s*16 + 4k + i packs columns (8k+i, 8k+i+4), k < 4, i < 4; 2-bit dword
-// s*16 + 8k + i packs (16k+i, 16k+i+8), k < 2, i < 8.  Chunk m = 2s + half therefore owns the 8
-// contiguous dwords s*16 + 8*half .. +8 of both layouts.
-// A chunk of 16 consecutive activations (32 bytes of bf16 or 64 of fp32) is loaded in two steps:
-// issue_chunk16 starts four 16-byte loads with no data-dependent branch (bf16 repeats its second
-// load), chunk16_f32 converts once the data is needed.  Keeping the conversion out of the issue
-// step lets every chunk a thread needs be in flight at once instead of one memory latency each.
-struct Chunk16 {
-    u32x4 q[4];
-};
-__device__ __forceinline__ void issue_chunk16(const void *x, int dtype, int m, Chunk16 &c) {
-    const int cb = dtype == MOE_BF16 ? 32 : 64;
-    const GLOBAL_AS uint8_t *p = (const GLOBAL_AS uint8_t *)x + (size_t)m * cb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c.q[i] = *(const GLOBAL_AS u32x4 *)(p + min(16 * i, cb - 16));
-}
-__device__ __forceinline__ void chunk16_f32(const Chunk16 &c, int dtype, float v[16]) {
-    if (dtype == MOE_BF16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = bf16_f32(c.q[0][j] & 0xFFFFu); v[2 * j + 1] = bf16_f32(c.q[0][j] >> 16);
-            v[8 + 2 * j] = bf16_f32(c.q[1][j] & 0xFFFFu); v[8 + 2 * j + 1] = bf16_f32(c.q[1][j] >> 16);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(c.q[q][j]);
-    }
-}
-
-// Writes chunk m's dwords of one layout (BITS) and returns the chunk's sum of hi + lo.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ float write_chunk(int m, const float v[16], uint32_t *hi, uint32_t *lo) {
-    uint32_t hv[16], lv[16];
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        hv[i] = bf16_rne(v[i]);
-        lv[i] = SPLIT ? bf16_rne(v[i] - bf16_f32(hv[i])) : 0u;
-        sum += bf16_f32(hv[i]) + (SPLIT ? bf16_f32(lv[i]) : 0.f);
-    }
-    uint32_t H[8], L[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int a = BITS == 4 ? (j >> 2) * 8 + (j & 3) : j;
-        const int b = a + (BITS == 4 ? 4 : 8);
-        H[j] = hv[a] | (hv[b] << 16);
-        L[j] = lv[a] | (lv[b] << 16);
-    }
-    const int d0 = (m >> 1) * kDPS + 8 * (m & 1);
-    *(u32x4 *)(hi + d0) = u32x4{H[0], H[1], H[2], H[3]};
-    *(u32x4 *)(hi + d0 + 4) = u32x4{H[4], H[5], H[6], H[7]};
-    if (SPLIT) {
-        *(u32x4 *)(lo + d0) = u32x4{L[0], L[1], L[2], L[3]};
-        *(u32x4 *)(lo + d0 + 4) = u32x4{L[4], L[5], L[6], L[7]};
-    }
-    return sum;
-}
-
-struct ActView {
-    const uint32_t *hi, *lo;  // [cols/2] packed bf16 pairs (lo: bf16 of the remainder)
-    const float *xs;          // [cols/32] sum over the slot of hi + lo
-};
-
-// --------------------------------------------------------------------------- slot dot products
-// s * sum(q x) + b * sum(x) over one slot, given its codes and (scale, bias) dword.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t *X, const uint32_t *XL, uint32_t sb,
-                                          float xs) {
-    float a0 = 0.f, a1 = 0.f, l0 = 0.f, l1 = 0.f;
-    constexpr int NW = BITS == 4 ? 4 : 2;     // code dwords per slot
-    constexpr int PW = BITS == 4 ? 4 : 8;     // pairs per dword
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const uint32_t v = q[k];
-#pragma unroll
-        for (int i = 0; i < PW; ++i) {
-            const uint32_t p = BITS == 4 ? (((v >> (4 * i)) & 0x000F000Fu) | kMagic)
-                                         : (((v >> (2 * i)) & 0x00030003u) | kMagic);
-            const int d = k * PW + i;
-            if (d & 1) a1 = dot2(p, X[d], a1); else a0 = dot2(p, X[d], a0);
-            if (SPLIT) { if (d & 1) l1 = dot2(p, XL[d], l1); else l0 = dot2(p, XL[d], l0); }
-        }
-    }
-    const float acc = SPLIT ? (a0 + a1) + (l0 + l1) : a0 + a1;
-    const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
-    return s * acc + (b - 128.f * s) * xs;
-}
-
-typedef const GLOBAL_AS uint8_t *gbytes;
-typedef const GLOBAL_AS uint32_t *gwords;
-
-template <int BITS>
-__device__ __forceinline__ u32x4 load_slot(gbytes row, int slot) {
-    if (BITS == 4) return *(const GLOBAL_AS u32x4 *)(row + (size_t)slot * 16);
-    const u32x2 v = *(const GLOBAL_AS u32x2 *)(row + (size_t)slot * 8);
-    return u32x4{v.x, v.y, 0u, 0u};
-}
-
-// Lane geometry for rows of `cols` inputs.
-struct Geo {
-    int spr;    // slots per row
-    int gsz;    // lanes per row group
-    int rpi;    // rows per wave instruction
-    int lrow;   // this lane's row within the instruction
-    int lsl;    // this lane's first slot
-};
-__device__ __forceinline__ Geo make_geo(int cols) {
-    Geo g;
-    const int lane = threadIdx.x & 63;
-    g.spr = cols / 32;
-    if (g.spr >= 64) {
-        g.gsz = 64; g.rpi = 1; g.lrow = 0; g.lsl = lane;
-    } else {
-        g.gsz = next_pow2(g.spr); g.rpi = 64 / g.gsz; g.lrow = lane / g.gsz; g.lsl = lane % g.gsz;
-    }
-    return g;
-}
-
-// Weight planes are read through global (address space 1) pointers: the blob addresses come from
-// the descriptor table as integers, and generic pointers would turn every load into a flat load.
-struct Planes {
-    gbytes q; gwords sb;
-};
-__device__ __forceinline__ void expert_planes(uint64_t blob_addr, int H, int I, int bits, Planes p[3]) {
-    gbytes blob = (gbytes)blob_addr;
-    const size_t cin = (size_t)I * H * bits / 8, sbin = (size_t)I * (H / 64) * 4;
-    const size_t cout = (size_t)H * I * bits / 8;
-    size_t off = 0;
-    p[0].q = blob + off; off = round256(off + cin);
-    p[0].sb = (gwords)(blob + off); off = round256(off + sbin);
-    p[1].q = blob + off; off = round256(off + cin);
-    p[1].sb = (gwords)(blob + off); off = round256(off + sbin);
-    p[2].q = blob + off; off = round256(off + cout);
-    p[2].sb = (gwords)(blob + off);
-}
-
-// --------------------------------------------------------------------------- top-K (one wave)
-// Largest K logits, descending, equal values -> lower index; NaN counts as -inf.  The weights are
-// the softmax over the selected logits, which equals the softmax over all E renormalised.
-//
-// A logit is compared through an order-preserving 32-bit key (its fp32 bits with the sign folded;
-// -0 is first canonicalised to +0 so that equal floats give equal keys); key 0 marks an absent
-// expert and is below every real key.  The experts are laid out lane-major: lane l holds experts
-// NP*l .. NP*l+NP-1 in registers, so among lanes whose best keys tie the lowest lane holds the lowest
-// index, and inside a lane the lowest slot does.  Each lane keeps its best two untaken keys.  A
-// round takes the wave maximum of the lane heads with DPP inside 16-lane rows and the gfx950 row
-// swaps across rows (every lane gets it, no scalar round trip), finds the lowest lane holding it
-// with one ballot, and promotes that lane's second key.  A lane that wins twice recomputes its
-// two best untaken keys.  The winner records its slot in a per-round bit field; lane k reads the
-// field of round k's winner once, after the last round.  Everything stays in registers: a round
-// is a short dependent chain, which is what bounds a single wave here.
-__device__ __forceinline__ uint32_t logit_key(float v) {
-    v = (v != v) ? -INFINITY : v + 0.0f;
-    const uint32_t u = __float_as_uint(v);
-    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-__device__ __forceinline__ float key_logit(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp0(uint32_t v) {   // DPP move; lanes without a source read 0
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
-}
-// Wave-wide maximum, returned in every lane.
-__device__ __forceinline__ uint32_t wave_max_all(uint32_t v) {
-    v = max(v, dpp0<0xB1>(v));      // quad_perm [1,0,3,2]
-    v = max(v, dpp0<0x4E>(v));      // quad_perm [2,3,0,1]
-    v = max(v, dpp0<0x141>(v));     // row_half_mirror
-    v = max(v, dpp0<0x140>(v));     // row_mirror: the 16-lane row maximum
-    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);    // rows 0<->1, 2<->3
-    v = max(a[0], a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);    // halves
-    return max(b[0], b[1]);
-}
-// The two best keys of this lane that are not in `taken` (ties: lower slot first).  Pairwise
-// tree: list A always comes from lower slots than list B.
-struct Top2 {
-    uint32_t h1, h2;
-    int s1, s2;
-};
-__device__ __forceinline__ Top2 top2_merge(const Top2 &A, const Top2 &B) {
-    const bool bw = B.h1 > A.h1;
-    Top2 r;
-    r.h1 = bw ? B.h1 : A.h1;
-    r.s1 = bw ? B.s1 : A.s1;
-    const bool a2 = bw ? (A.h1 >= B.h2) : (A.h2 >= B.h1);   // second: A's candidate wins ties
-    r.h2 = bw ? (a2 ? A.h1 : B.h2) : (a2 ? A.h2 : B.h1);
-    r.s2 = bw ? (a2 ? A.s1 : B.s2) : (a2 ? A.s2 : B.s1);
-    return r;
-}
-template <int N>
-__device__ __forceinline__ Top2 top2_range(const uint32_t *key, uint32_t taken, int t0) {
-    if constexpr (N == 1) {
-        return Top2{((taken >> t0) & 1u) ? 0u : key[t0], 0u, t0, t0};
-    } else {
-        return top2_merge(top2_range<N / 2>(key, taken, t0), top2_range<N / 2>(key, taken, t0 + N / 2));
-    }
-}
-
-// `key`: this lane's NP keys (experts NP*lane + t).  Lane k < K returns selection k.
-template <int NP>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[NP], int K, int &my_idx, float &my_w) {
-    constexpr int FW = NP <= 8 ? 3 : 5;                            // bits per recorded slot
-    typedef typename std::conditional<NP <= 8, uint32_t, uint64_t>::type rec_t;
-    const int lane = threadIdx.x & 63;
-    Top2 c = top2_range<NP>(key, 0u, 0);
-    uint32_t taken = 0, my_key = 0, top = 0;
-    rec_t rec = 0;
-    int my_wl = 0;
-    uint64_t second_stale = 0;     // lanes whose second key was promoted and not yet recomputed
-    for (int k = 0; k < K; ++k) {
-        const uint32_t m = wave_max_all(c.h1);
-        top = k == 0 ? m : top;
-        const int wl = __ffsll((unsigned long long)__ballot(c.h1 == m)) - 1;
-        const bool me = lane == wl;
-        rec |= me ? (rec_t)c.s1 << (FW * k) : (rec_t)0;
-        taken |= me ? 1u << c.s1 : 0u;
-        my_key = lane == k ? m : my_key;
-        my_wl = lane == k ? wl : my_wl;
-        if ((second_stale >> wl) & 1ull) {
-            const Top2 r = top2_range<NP>(key, taken, 0);
-            c.h1 = me ? r.h1 : c.h1; c.s1 = me ? r.s1 : c.s1;
-            c.h2 = me ? r.h2 : c.h2; c.s2 = me ? r.s2 : c.s2;
-            second_stale &= ~(1ull << wl);
-        } else {
-            c.h1 = me ? c.h2 : c.h1;
-            c.s1 = me ? c.s2 : c.s1;
-            second_stale |= 1ull << wl;
-        }
-    }
-    rec_t r;
-    if constexpr (NP <= 8) {
-        r = (rec_t)__shfl((int)rec, my_wl);
-    } else {
-        r = (rec_t)(uint32_t)__shfl((int)(uint32_t)rec, my_wl) | ((rec_t)(uint32_t)__shfl((int)(uint32_t)(rec >> 32), my_wl) << 32);
-    }
-    const int slot = lane < K ? (int)((r >> (FW * lane)) & ((1u << FW) - 1)) : 0;
-    my_idx = my_wl * NP + slot;
-    // weights: softmax over the K selected logits, max-subtracted; the sum runs over lanes 0..7
-    const float val = key_logit(my_key), top0 = key_logit(top);
-    const float ex = lane < K ? (top0 > -INFINITY ? expf(val - top0) : 1.f) : 0.f;
-    float z = ex;
-    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0xB1, 0xF, 0xF, true));
-    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x4E, 0xF, 0xF, true));
-    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x141, 0xF, 0xF, true));
-    my_w = ex / z;
-}
-
-// Keys of this lane's experts NP*lane .. NP*lane+NP-1 from a logit row (absent experts: 0).  The
-// loads are branch-free (clamped address) so they are all in flight together.
-template <int NP>
-__device__ __forceinline__ void issue_logits(const float *row, int E, float (&lg)[NP]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int t = 0; t < NP; ++t) lg[t] = ((const GLOBAL_AS float *)row)[min(NP * lane + t, E - 1)];
-}
-template <int NP>
-__device__ __forceinline__ void logit_keys(const float (&lg)[NP], int E, uint32_t (&key)[NP]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int t = 0; t < NP; ++t) key[t] = NP * lane + t < E ? logit_key(lg[t]) : 0u;
-}
-
-// --------------------------------------------------------------------------- router
-// Row loads per batch and lane (16 bytes each).
-constexpr int kRouterBatch = 8;
-
-// bf16 router: the activation is staged as bf16 pairs (columns 2i, 2i+1) plus the bf16 remainder
-// when it is not exactly bf16, so a 16-byte chunk of 8 weights meets one 16-byte LDS read per part
-// and four v_dot2_f32_bf16.  fp32 router: fp32 activation, float4 LDS reads, fp32 FMAs.
 template <int RDT, bool SPLIT>
 __global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
-    extern __shared__ __align__(16) uint32_t s_r[];   // bf16: hi [H/2] + lo [H/2]; fp32: x [H]
+    extern __shared__ __align__(16) uint32_t s_r[];
     __shared__ float red[kWaves];
-    const int t = blockIdx.y;
-    const int H = a.H;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * kWaves + wave;
-    constexpr int EB = RDT == MOE_BF16 ? 2 : 4;           // bytes per weight
-    constexpr int EPL = 16 / EB;                          // weights per 16-byte load
-    const int nld = (H / EPL + 63) / 64;
-    const uint8_t *row = (const uint8_t *)a.router + (size_t)(e < a.E ? e : 0) * H * EB;
-    // 1. first batch of this wave's row, issued before the activation arrives
-    u32x4 wv[kRouterBatch];
-#pragma unroll
-    for (int j = 0; j < kRouterBatch; ++j) {
-        const int c = min((lane + 64 * j) * EPL, H - EPL);       // clamped; unused lanes ignore it
-        wv[j] = *(const u32x4 *)(row + (size_t)c * EB);
-    }
-    // 2. activation (+ RMSNorm) into LDS
-    const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
-    const int nch = H / 16;
-    Chunk16 xc[2], nc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = min((int)threadIdx.x + kBlock * j, nch - 1);   // clamped; extra chunks unused
-        issue_chunk16(x, a.x_dtype, m, xc[j]);
-        if (a.norm_w) issue_chunk16(a.norm_w, MOE_BF16, m, nc[j]);
-    }
-    float v[2][16];
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        chunk16_f32(xc[j], a.x_dtype, v[j]);
-        if ((int)threadIdx.x + kBlock * j < nch) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
-        }
-    }
-    float inv = 1.f;
-    if (a.norm_w) {
-        ss = block_sum(ss, red);
-        inv = 1.0f / sqrtf(ss / (float)H + a.eps);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = threadIdx.x + kBlock * j;
-        if (m < nch) {
-            if (a.norm_w) {
-                float w[16];
-                chunk16_f32(nc[j], MOE_BF16, w);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
-            }
-            if (RDT == MOE_BF16) {
-                uint32_t hv[16], lv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    hv[i] = bf16_rne(v[j][i]);
-                    lv[i] = SPLIT ? bf16_rne(v[j][i] - bf16_f32(hv[i])) : 0u;
-                }
-                uint32_t *hi = s_r + 8 * m, *lo = s_r + H / 2 + 8 * m;
-#pragma unroll
-                for (int q = 0; q < 8; q += 4) {
-                    *(u32x4 *)(hi + q) = u32x4{hv[2 * q] | (hv[2 * q + 1] << 16), hv[2 * q + 2] | (hv[2 * q + 3] << 16),
-                                               hv[2 * q + 4] | (hv[2 * q + 5] << 16), hv[2 * q + 6] | (hv[2 * q + 7] << 16)};
-                    if (SPLIT)
-                        *(u32x4 *)(lo + q) = u32x4{lv[2 * q] | (lv[2 * q + 1] << 16), lv[2 * q + 2] | (lv[2 * q + 3] << 16),
-                                                   lv[2 * q + 4] | (lv[2 * q + 5] << 16), lv[2 * q + 6] | (lv[2 * q + 7] << 16)};
-                }
-            } else {
-                float *xs = (float *)s_r + 16 * m;
-#pragma unroll
-                for (int q = 0; q < 16; q += 4)
-                    *(u32x4 *)(xs + q) = u32x4{__float_as_uint(v[j][q]), __float_as_uint(v[j][q + 1]),
-                                               __float_as_uint(v[j][q + 2]), __float_as_uint(v[j][q + 3])};
-            }
-        }
-    }
-    __syncthreads();
-    if (e >= a.E) return;
-    // 3. dot product, further batches for long rows
-    float acc = 0.f, acc2 = 0.f;
-    for (int base = 0; base < nld; base += kRouterBatch) {
-        if (base > 0) {
-#pragma unroll
-            for (int j = 0; j < kRouterBatch; ++j) {
-                const int c = min((lane + 64 * (base + j)) * EPL, H - EPL);
-                wv[j] = *(const u32x4 *)(row + (size_t)c * EB);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kRouterBatch; ++j) {
-            const int c = (lane + 64 * (base + j)) * EPL;
-            if (base + j < nld && c < H) {
-                if (RDT == MOE_BF16) {
-                    const u32x4 xh = *(const u32x4 *)(s_r + c / 2);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = dot2(wv[j][q], xh[q], acc);
-                    if (SPLIT) {
-                        const u32x4 xl = *(const u32x4 *)(s_r + H / 2 + c / 2);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc2 = dot2(wv[j][q], xl[q], acc2);
-                    }
-                } else {
-                    const u32x4 xf = *(const u32x4 *)((const float *)s_r + c);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(wv[j][q]), __uint_as_float(xf[q]), acc);
-                }
-            }
-        }
-    }
-    acc = group_sum(acc + acc2, 64);
-    if (lane == 0) a.logits[(size_t)t * a.E + e] = acc + (a.logit_bias ? a.logit_bias[e] : 0.f);
+    float lg;
+    if (router_row<RDT, SPLIT>(a, blockIdx.x, blockIdx.y, s_r, red, lg) && (threadIdx.x & 63) == 0)
+        a.logits[(size_t)blockIdx.y * a.E + blockIdx.x * kWaves + (threadIdx.x >> 6)] = lg;
 }
 
 template <int NP>
@@ -530,77 +61,6 @@ __global__ void __launch_bounds__(64) k_topk(TopkLaunch a) {
     if ((int)threadIdx.x < a.K) {
         a.idx[(size_t)t * a.K + threadIdx.x] = my_idx;
         a.w[(size_t)t * a.K + threadIdx.x] = my_w;
-    }
-}
-
-// --------------------------------------------------------------------------- gate/up + SwiGLU
-// Instruction groups per work unit: enough loads in flight per lane (about 16 slots of gate+up).
-template <int NJ>
-__host__ __device__ constexpr int gu_rg() { return NJ >= 4 ? 1 : 4 / NJ; }
-
-template <int NJ, int RG>
-struct GULoads {
-    u32x4 qg[RG][NJ], qu[RG][NJ];
-    uint32_t sg[RG][NJ], su[RG][NJ];
-};
-
-// Issue the loads of one work unit: RB consecutive rows of gate and up of one expert.
-template <int BITS, int NJ, int RG>
-__device__ __forceinline__ void gu_issue(const Planes *pl, const Geo &g, int H, int I, int r0, int RB,
-                                         GULoads<NJ, RG> &L) {
-    // Branch-free: rows past the matrix and idle slots read a clamped, in-bounds address.  Their
-    // contribution vanishes (idle slots have zero activation operands and sum; rows past the
-    // block are never written), so nothing needs masking here.
-    const int G = H / 64;
-    const size_t rowb = (size_t)H * BITS / 8;
-#pragma unroll
-    for (int gi = 0; gi < RG; ++gi) {
-        const int r = min(r0 + gi * g.rpi + g.lrow, I - 1);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int slot = min(g.lsl + 64 * j, g.spr - 1);
-            L.qg[gi][j] = load_slot<BITS>(pl[0].q + (size_t)r * rowb, slot);
-            L.qu[gi][j] = load_slot<BITS>(pl[1].q + (size_t)r * rowb, slot);
-            const size_t sbi = (size_t)r * G + (slot >> 1);
-            L.sg[gi][j] = pl[0].sb[sbi];
-            L.su[gi][j] = pl[1].sb[sbi];
-        }
-    }
-}
-
-template <int BITS, int NJ, int RG, bool SPLIT>
-__device__ __forceinline__ void gu_finish(const Geo &g, int I, int r0, int RB, const ActView &av,
-                                          const GULoads<NJ, RG> &L, float *hout) {
-    uint32_t X[NJ][kDPS], XL[NJ][SPLIT ? kDPS : 1];
-    float XS[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int slot = g.lsl + 64 * j;
-        const bool ok = slot < g.spr;
-        const int ss = ok ? slot : 0;
-#pragma unroll
-        for (int i = 0; i < kDPS; i += 4) {
-            const u32x4 h = *(const u32x4 *)(av.hi + ss * kDPS + i);
-            X[j][i] = ok ? h.x : 0u; X[j][i + 1] = ok ? h.y : 0u; X[j][i + 2] = ok ? h.z : 0u; X[j][i + 3] = ok ? h.w : 0u;
-            if (SPLIT) {
-                const u32x4 l = *(const u32x4 *)(av.lo + ss * kDPS + i);
-                XL[j][i] = ok ? l.x : 0u; XL[j][i + 1] = ok ? l.y : 0u; XL[j][i + 2] = ok ? l.z : 0u; XL[j][i + 3] = ok ? l.w : 0u;
-            }
-        }
-        XS[j] = ok ? av.xs[ss] : 0.f;
-    }
-#pragma unroll
-    for (int gi = 0; gi < RG; ++gi) {
-        float pg = 0.f, pu = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            pg += slot_dot<BITS, SPLIT>(L.qg[gi][j], X[j], XL[j], L.sg[gi][j], XS[j]);
-            pu += slot_dot<BITS, SPLIT>(L.qu[gi][j], X[j], XL[j], L.su[gi][j], XS[j]);
-        }
-        pg = group_sum(pg, g.gsz);
-        pu = group_sum(pu, g.gsz);
-        const int rr = gi * g.rpi + g.lrow;
-        if (g.lsl == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu(pg) * pu;
     }
 }
 
@@ -745,57 +205,19 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     }
 }
 
-// --------------------------------------------------------------------------- down + combine
-template <int NJ>
-__host__ __device__ constexpr int dn_rg() { return NJ >= 2 ? 1 : 2; }
-
-template <int NJ, int RG, int KM>
-struct DLoads {
-    u32x4 q[KM][RG][NJ];
-    uint32_t sb[KM][RG][NJ];
-};
-
-template <int BITS, int NJ, int RG, int KM>
-__device__ __forceinline__ void dn_issue(const Planes &pl, const Geo &g, int H, int I, int r0, int RB, int k,
-                                         DLoads<NJ, RG, KM> &L) {
-    const int G = I / 64;
-    const size_t rowb = (size_t)I * BITS / 8;
-#pragma unroll
-    for (int gi = 0; gi < RG; ++gi) {
-        const int r = min(r0 + gi * g.rpi + g.lrow, H - 1);     // clamped; see gu_issue
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int slot = min(g.lsl + 64 * j, g.spr - 1);
-            L.q[k][gi][j] = load_slot<BITS>(pl.q + (size_t)r * rowb, slot);
-            L.sb[k][gi][j] = pl.sb[(size_t)r * G + (slot >> 1)];
-        }
-    }
-}
-
-// Issue every selected expert's loads for one unit (output rows r0..r0+RB-1).
-template <int NJ, int RG, int KM>
-__device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, const Geo &g, int H, int I, int r0,
-                                             int RB, DLoads<NJ, RG, KM> &L) {
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        if (k < K && sel[k]) {
-            Planes pl[3];
-            expert_planes(sel_blob(sel[k]), H, I, sel_bits(sel[k]), pl);
-            if (sel_bits(sel[k]) == 2) dn_issue<2, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
-            else dn_issue<4, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
-        }
-    }
-}
-
-// LDS per expert: hi [I/2], lo [I/2], xs [I/32].
-__host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I + ((I / 32 + 3) & ~3); }
-
 template <int NJ, bool COMBINE, int KM>
 __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     constexpr int RG = dn_rg<NJ>();
     const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // 0. one-launch schedule: advance the launch counter (every workgroup of the router + gate/up
+    //    launch read it before this kernel started) and pick up its error word
+    if (a.seq && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        const uint32_t nt = a.seq[0] + 1u;
+        __hip_atomic_store(a.seq, nt ? nt : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const bool bad = a.err && *a.err != 0;
     // 1. h chunks of this thread (first pass) and the selected experts + routing weights, all in
     //    flight together (branch-free clamped loads); then the first unit's weight loads
     const int per = down_lds_per_expert(I);
@@ -921,7 +343,8 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
                 const int rr = gi * g.rpi + g.lrow;
                 const int r = r0 + rr;
                 if (g.lsl == 0 && rr < RB && r < H)
-                    a.out[(size_t)t * H + r] = s + (res ? load_act(res, a.residual_dtype, r) : 0.f);
+                    a.out[(size_t)t * H + r] = bad ? __uint_as_float(0x7FC00000u)
+                                                   : s + (res ? load_act(res, a.residual_dtype, r) : 0.f);
             }
         }
     }
@@ -935,16 +358,6 @@ __global__ void __launch_bounds__(kBlock) k_combine(CombineLaunch a) {
         for (int k = 0; k < a.K; ++k) acc += a.w[t * a.K + k] * a.y[(t * a.K + k) * a.H + c];
         a.out[i] = acc + (a.residual ? a.residual[i] : 0.f);
     }
-}
-
-int nj_for(int cols) {
-    const int spr = cols / 32;
-    const int nj = spr >= 64 ? (spr + 63) / 64 : 1;
-    return nj <= 1 ? 1 : nj <= 2 ? 2 : 4;
-}
-int rpi_for(int cols) {
-    const int spr = cols / 32;
-    return spr >= 64 ? 1 : 64 / next_pow2(spr);
 }
 
 }  // namespace

@@ -51,6 +51,8 @@ hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s);
 
 struct DownLaunch {
     const float *h;                                // [T][K][I]
+    uint32_t *seq;                                 // one-launch schedule: advance this launch counter, or NULL
+    const uint32_t *err;                           // one-launch schedule: nonzero -> NaN outputs, or NULL
     const uint64_t *sel;                           // [T][K] blob address | code width (0: no expert)
     const float *w;                                // [T][K] (combine) or NULL (per-expert output)
     const void *residual; int residual_dtype; int residual_stride;   // [T][stride] or NULL
@@ -83,6 +85,26 @@ struct GroupedLaunch {
     float *y;                                      // [T*K][H]
 };
 hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, hipStream_t s);
+
+// Router + gate/up of one decode token in one launch (two groups of workgroups; the logits pass
+// through tagged workspace words, see moe_layer.hip).  The down kernel follows on the stream.
+struct LayerLaunch {
+    RouterLaunch r;                                // x, norm, router, logit bias (logits unused), T = 1
+    const moe_expert_desc *experts;
+    int32_t *idx_out; float *w_out;                // [K] routing results, or NULL
+    uint64_t *sel_ws; float *w_ws;                 // [K] selections and weights for the down kernel
+    float *h;                                      // [K][I] SwiGLU outputs
+    int H, I, E, K;
+    int split;                                     // activation not exactly bf16: hi/lo split
+    const uint32_t *seq;                           // launch counter (advanced by the down kernel)
+    uint64_t *slots;                               // [layer_logit_copies()][E] tag << 32 | logit bits
+    uint32_t *err;                                 // timed-out waits (nonzero: the down kernel writes NaN)
+    int nr, ng;                                    // workgroups per phase (set by launch_layer)
+};
+void layer_grid(int H, int I, int E, int K, int *nr, int *ng);
+int layer_logit_copies();
+size_t layer_lds_bytes(int H, int E);
+hipError_t launch_layer(const LayerLaunch &a, hipStream_t s);
 
 struct CombineLaunch {
     const float *y; const float *w; const float *residual; float *out;

@@ -1,0 +1,331 @@
+// moe_layer.hip -- router and gate/up of one decode token in ONE launch.
+//
+// The router and gate/up phases of a layer run as two groups of workgroups of a single grid, in
+// that blockIdx order, and the logits pass between them through words in the workspace instead
+// of a kernel boundary (a boundary costs about 1.5 us on this part plus the memory latency of the
+// next kernel's first loads):
+//
+//   router workgroups   publish each logit as one 64-bit word, launch tag << 32 | fp32 bits,
+//                       into kLogitCopies copies of the logit row;
+//   gate/up workgroups  issue their descriptor-table and activation loads, then wave 0 polls one
+//                       copy until all E words carry this launch's tag; routing (top-K in
+//                       registers, every wave), the gate/up stream and h follow as in the
+//                       separate gate/up kernel.
+//
+// The down projection stays a kernel of its own: every down workgroup needs all of h, and the
+// kernel boundary publishes h to all L2 slices at once, where in-kernel hand-over would need a
+// release fence per producer and uncached reads per consumer (both measured far slower here).
+//
+// Copies.  Hundreds of workgroups polling one 4 KB row with cache-bypassing loads all land on
+// the few memory channels that hold it; each workgroup polls copy (index % kLogitCopies), which
+// spreads the polls over the channels.
+//
+// Progress.  A gate/up workgroup only waits for router workgroups, which have lower indices and
+// are started first, so the wait cannot deadlock whether or not the whole grid is resident.  The
+// wait is also bounded: if it runs out, the workspace error word counts it, and the down kernel
+// writes NaN outputs while that word is nonzero, so a failure shows in the output instead of
+// hanging the device.
+//
+// Launch tags.  The tag is seq + 1 (never 0), where seq is a workspace word every workgroup reads
+// when it starts; the down kernel that follows on the stream stores the tag into seq, so the
+// next launch uses a new tag and no word left by an earlier launch can pass for a fresh one.  The
+// workspace must therefore be zero-filled before its first use.
+#include "moe_device.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSpinLimit = 1 << 18;       // polls per wait (each at least one memory round trip)
+constexpr int kLogitCopies = 16;          // copies of the tagged logit row (<= 64)
+
+__device__ __forceinline__ uint32_t ld_word(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_word64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_word(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Published with an agent-scope atomic exchange rather than a store: the atomic is performed
+// where every L2 slice sees it, while a plain store can sit in the writer's L2 slice for
+// microseconds before the polling workgroups of other slices observe it.
+__device__ __forceinline__ void publish_word64(uint64_t *p, uint64_t v) {
+    (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t launch_tag(uint32_t seq) {
+    const uint32_t t = seq + 1u;
+    return t ? t : 1u;
+}
+
+// One wave waits until the E logit words carry `tag` and copies the logits to LDS.  It polls a
+// single word (the last expert's: the router workgroups finish within a fraction of a
+// microsecond of each other) and only then reads the whole row, which it re-reads until every
+// tag matches: polling the full row from hundreds of workgroups would swamp the memory system.
+// Returns false if the wait ran out (the logits are then NaN, which ranks last, and the error
+// word counts it).
+template <int NP>
+__device__ bool wait_logits(const uint64_t *slots, int E, uint32_t tag, float *s_lg, uint32_t *err) {
+    const int lane = threadIdx.x & 63;
+    int it = 0;
+    for (; it < kSpinLimit; ++it) {
+        if ((uint32_t)(ld_word64(slots + E - 1) >> 32) == tag) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    for (; it < kSpinLimit; ++it) {
+        uint64_t v[NP];
+#pragma unroll
+        for (int t = 0; t < NP; ++t) v[t] = ld_word64(slots + min(NP * lane + t, E - 1));
+        bool ok = true;
+#pragma unroll
+        for (int t = 0; t < NP; ++t) ok = ok && (NP * lane + t >= E || (uint32_t)(v[t] >> 32) == tag);
+        if (__all(ok)) {
+#pragma unroll
+            for (int t = 0; t < NP; ++t)
+                if (NP * lane + t < E) s_lg[NP * lane + t] = __uint_as_float((uint32_t)v[t]);
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int t = 0; t < NP; ++t)
+        if (NP * lane + t < E) s_lg[NP * lane + t] = __uint_as_float(0x7FC00000u);
+    if (lane == 0) atomicAdd(err, 1u);
+    return false;
+}
+
+// Keys of this lane's experts NP*lane .. +NP from the logits in LDS.
+template <int NP>
+__device__ __forceinline__ void lds_keys(const float *s_lg, int E, uint32_t (&key)[NP]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+        const int e = NP * lane + t;
+        key[t] = e < E ? logit_key(s_lg[min(e, E - 1)]) : 0u;
+    }
+}
+
+// ----------------------------------------------------------------------------------- router
+__device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_t *lds, float *red, uint32_t seq) {
+    float lg = 0.f;
+    bool ok;
+    if (a.r.router_dtype == MOE_BF16)
+        ok = a.split ? router_row<MOE_BF16, true>(a.r, b, 0, lds, red, lg)
+                     : router_row<MOE_BF16, false>(a.r, b, 0, lds, red, lg);
+    else
+        ok = router_row<MOE_F32, false>(a.r, b, 0, lds, red, lg);
+    const int lane = threadIdx.x & 63;
+    if (ok && lane < kLogitCopies)
+        publish_word64(a.slots + (size_t)lane * a.E + b * kWaves + (threadIdx.x >> 6),
+                       ((uint64_t)launch_tag(seq) << 32) | __float_as_uint(lg));
+}
+
+// ----------------------------------------------------------------------------------- gate/up
+template <int NJ, bool SPLIT, int NP>
+__device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32_t *lds, uint64_t *s_tab, float *red,
+                                             uint32_t seq) {
+    constexpr int RG = gu_rg<NJ>();
+    const int H = a.H, I = a.I, E = a.E, K = a.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool use_tab = E <= kTabMax;
+    float *s_lg = (float *)lds;
+    uint32_t *act = lds + ((E + 3) & ~3);
+
+    // 1. independent loads: descriptor table, activation, norm weight
+    u32x4 dsc[kTabMax / kBlock];
+    if (use_tab) {
+#pragma unroll
+        for (int j = 0; j < kTabMax / kBlock; ++j)
+            dsc[j] = *(const GLOBAL_AS u32x4 *)(a.experts + min((int)threadIdx.x + kBlock * j, E - 1));
+    }
+    const void *x = a.r.x;
+    const int xdt = a.r.x_dtype;
+    const int nch = H / 16;
+    Chunk16 xc[2], nc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = min((int)threadIdx.x + kBlock * j, nch - 1);
+        issue_chunk16(x, xdt, m, xc[j]);
+        if (a.r.norm_w) issue_chunk16(a.r.norm_w, MOE_BF16, m, nc[j]);
+    }
+
+    // 2. wave 0 waits for this launch's logits and copies them to LDS
+    if (wave == 0) {
+        wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, launch_tag(seq), s_lg, a.err);
+    }
+
+    // 3. descriptor table and RMSNorm statistics; the barrier publishes logits and table
+    if (use_tab) {
+#pragma unroll
+        for (int j = 0; j < kTabMax / kBlock; ++j) {
+            const int e = threadIdx.x + kBlock * j;
+            if (e < E) s_tab[e] = pack_sel(((uint64_t)dsc[j].y << 32) | dsc[j].x, dsc[j].z);
+        }
+    }
+    // x (and, with a norm, x * w_norm: the 1/rms factor follows once the block sum is known) in
+    // registers now, so that no later step waits on these loads behind the weight loads
+    float v[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) chunk16_f32(xc[j], xdt, v[j]);
+    float inv = 1.f;
+    if (a.r.norm_w) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float w[16];
+            chunk16_f32(nc[j], MOE_BF16, w);
+            if ((int)threadIdx.x + kBlock * j < nch) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ss += v[j][i] * v[j][i];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[j][i] *= w[i];
+        }
+        ss = block_sum(ss, red);
+        inv = 1.0f / sqrtf(ss / (float)H + a.r.eps);
+    } else {
+        __syncthreads();
+    }
+
+    // 4. routing in registers (each wave, identical results)
+    int my_idx = 0;
+    float my_w = 0.f;
+    {
+        uint32_t key[NP];
+        lds_keys<NP>(s_lg, E, key);
+        wave_topk<NP>(key, K, my_idx, my_w);
+    }
+    if (gb == 0 && wave == 0 && lane < K) {
+        if (a.idx_out) a.idx_out[lane] = my_idx;
+        if (a.w_out) a.w_out[lane] = my_w;
+        a.w_ws[lane] = my_w;
+        a.sel_ws[lane] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
+    }
+
+    // 5. the first unit's weight loads, then the activation layouts
+    const Geo g = make_geo(H);
+    const int RB = RG * g.rpi;
+    const int nblk = (I + RB - 1) / RB;
+    const int units = K * nblk;
+    const int stride = a.ng * kWaves;
+    int u = gb * kWaves + wave;
+    GULoads<NJ, RG> L;
+    uint64_t sel = 0;
+    Planes pl[3];
+    if (u < units) {
+        const int k = u / nblk;
+        sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+        if (sel) {
+            expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+            if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
+            else gu_issue<4, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
+        }
+    }
+    uint32_t *h4 = act, *l4 = act + H / 2, *h2 = act + H, *l2 = act + 3 * H / 2;
+    float *xs = (float *)(act + 2 * H);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = threadIdx.x + kBlock * j;
+        float sum = 0.f;
+        if (m < nch) {
+            if (a.r.norm_w) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[j][i] *= inv;
+            }
+            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
+            write_chunk<2, SPLIT>(m, v[j], h2, l2);
+        }
+        sum += dppf<0xB1>(sum);
+        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
+    }
+    __syncthreads();
+    const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
+
+    // 6. work units -> h
+    bool first = true;
+    for (; u < units; u += stride) {
+        const int k = u / nblk;
+        const int r0 = (u - k * nblk) * RB;
+        float *hout = a.h + (size_t)k * I;
+        if (!first) {
+            sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+            if (sel) {
+                expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+                if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
+                else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
+            }
+        }
+        first = false;
+        if (!sel) {
+            for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
+            continue;
+        }
+        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG, SPLIT>(g, I, r0, RB, v2, L, hout);
+        else gu_finish<4, NJ, RG, SPLIT>(g, I, r0, RB, v4, L, hout);
+    }
+}
+
+// ----------------------------------------------------------------------------------- kernel
+template <int NP, int NJ>
+__global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    __shared__ uint64_t s_tab[kTabMax];
+    __shared__ float red[kWaves];
+    // The launch counter is loaded through an offset the compiler cannot prove uniform, so it stays
+    // in a vector register and is waited for where the tag is first used, not here.
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const uint32_t seq = ld_word(a.seq + zero);
+    const int b = blockIdx.x;
+    if (b < a.nr) {
+        router_phase(a, b, lds, red, seq);
+    } else {
+        if (a.split) gateup_phase<NJ, true, NP>(a, b - a.nr, lds, s_tab, red, seq);
+        else gateup_phase<NJ, false, NP>(a, b - a.nr, lds, s_tab, red, seq);
+    }
+}
+
+template <int NP, int NJ>
+hipError_t layer_impl(const LayerLaunch &a, size_t lds, hipStream_t s) {
+    auto fn = k_route_gateup<NP, NJ>;
+    if (lds > 64 * 1024)
+        if (hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
+            return e;
+    hipLaunchKernelGGL(fn, dim3(a.nr + a.ng), dim3(kBlock), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int NP>
+hipError_t layer_nj(const LayerLaunch &a, size_t lds, hipStream_t s) {
+    switch (nj_for(a.H)) {
+        case 1: return layer_impl<NP, 1>(a, lds, s);
+        case 2: return layer_impl<NP, 2>(a, lds, s);
+        default: return layer_impl<NP, 4>(a, lds, s);
+    }
+}
+
+}  // namespace
+
+void layer_grid(int H, int I, int E, int K, int *nr, int *ng) {
+    const int rbg = gateup_rows_per_unit(H);
+    *nr = (E + kWaves - 1) / kWaves;
+    *ng = (K * ((I + rbg - 1) / rbg) + kWaves - 1) / kWaves;
+}
+
+int layer_logit_copies() { return kLogitCopies; }
+
+size_t layer_lds_bytes(int H, int E) {
+    const size_t e4 = (size_t)((E + 3) & ~3) * 4;
+    const size_t r = (size_t)H * 4;                             // router: x layouts
+    const size_t g = e4 + gateup_lds_bytes(H);                  // gate/up: logits + x layouts
+    return r > g ? r : g;
+}
+
+hipError_t launch_layer(const LayerLaunch &a_in, hipStream_t s) {
+    LayerLaunch a = a_in;
+    layer_grid(a.H, a.I, a.E, a.K, &a.nr, &a.ng);
+    const size_t lds = layer_lds_bytes(a.H, a.E);
+    return a.E <= 512 ? layer_nj<8>(a, lds, s) : layer_nj<32>(a, lds, s);
+}
+
+}  // namespace moe

@@ -173,9 +173,14 @@ int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts);
 #define MOE_OP_LAYER_DECODE 3
 
 /* Device workspace bytes needed by one call of `op` with these dims and T tokens
- * (n_layers for MOE_OP_LAYER_DECODE).  0 for unsupported arguments.  The workspace is
- * scratch: its contents need no initialisation and are undefined after the call.  Two
- * calls that may run concurrently need separate workspaces. */
+ * (n_layers for MOE_OP_LAYER_DECODE).  0 for unsupported arguments.  For MOE_OP_ROUTE and
+ * MOE_OP_EXPERT_FFN the workspace is scratch: its contents need no initialisation and are
+ * undefined after the call.  A MOE_OP_LAYER_DECODE workspace carries state from one
+ * moe_layer_decode call to the next (a launch counter and hand-over words of the one-launch
+ * layer schedule): zero-fill it once before its first moe_layer_decode call, and again
+ * before going back to moe_layer_decode after using the same memory for anything else.
+ * Calls sharing a workspace must be ordered (same stream, or synchronised); two calls that
+ * may run concurrently need separate workspaces. */
 size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers);
 
 /* --------------------------------------------------------------------------- compute */
@@ -208,29 +213,39 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
 int moe_combine(const float *y, const float *w, int T, int K, int H, const float *residual,
                 float *out, void *stream);
 
-#define MOE_FLAG_RESIDUAL 1u   /* out = x + MoE(x) (pre-norm residual block) */
+#define MOE_FLAG_RESIDUAL 1u          /* out = x + MoE(x) (pre-norm residual block) */
+#define MOE_FLAG_SEPARATE_KERNELS 2u  /* run each layer as three kernels (router, gate/up, down) */
 
 /* One decode token through n_layers layers (1 <= n_layers <= 4096); layer l's output is
  * layer l+1's input.  Per layer: [RMSNorm] -> router -> top-K -> gate/up/SwiGLU for all K
- * experts in one launch -> down projection + weighted combine (+ residual) in one launch.
+ * experts -> down projection + weighted combine (+ residual).
+ * By default a layer is two kernel launches: router and gate/up run as two groups of
+ * workgroups of one grid, the logits passing between them through the workspace (see
+ * moe_workspace_bytes for its zero-fill rule), then the down + combine kernel.  The gate/up
+ * workgroups only wait for router workgroups started before them, and the wait is bounded: if it
+ * ever runs out, the workspace's error word becomes nonzero and this and every later call with
+ * that workspace write NaN outputs until it is zero-filled again.  MOE_FLAG_SEPARATE_KERNELS
+ * selects three launches per layer (router, gate/up, down) with the same arithmetic.
  *   layers host [n_layers]
  *   x      device [H] x_dtype (input of the first layer), 16-byte aligned
  *   out    device [H] fp32 output of the last layer
  *   idx    device [n_layers][K] int32, or NULL
  *   w      device [n_layers][K] fp32, or NULL
- * Errors as moe_route. */
+ * Errors as moe_route (MOE_ERR_UNSUPPORTED for unknown flags). */
 int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
                      int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                      void *ws, size_t ws_bytes, void *stream);
 
-/* moe_layer_decode with per-kernel timing, the library's counterpart of the pages' per-layer
- * timing breakdown (lilting.ch page, "遅延GPU実行" section, per-layer time table).
+/* moe_layer_decode on the three-kernel schedule with per-kernel timing, the library's
+ * counterpart of the pages' per-layer timing breakdown (lilting.ch page, "遅延GPU実行"
+ * section, per-layer time table).
  *   events  host array of 3*n_layers + 1 hipEvent_t (created by the caller on the current
  *           device).  events[0] is recorded on `stream` before the first kernel and
  *           events[3l+1], events[3l+2], events[3l+3] after layer l's router, gate/up and down
  *           kernels, so hipEventElapsedTime(events[i], events[i+1]) spans one kernel (including
- *           its dispatch).  When the stream is being captured the records become external event
- *           nodes of the graph.
+ *           its dispatch).  When the stream is being captured the records are attempted as
+ *           external event nodes of the graph (a runtime that refuses them makes the call
+ *           fail with MOE_ERR_LAUNCH).
  * Other arguments and errors as moe_layer_decode (MOE_ERR_NULL when events is NULL). */
 int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
                            int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,

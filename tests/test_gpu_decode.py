@@ -23,15 +23,21 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_decode(dl, x, residual=False):
+def ws_error_word(ws) -> int:
+    """The layer-decode workspace's error word (count of timed-out waits of the one-launch schedule)."""
+    return int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+
+
+def run_decode(dl, x, residual=False, separate=False, ws=None):
     wl = dl.wl
     d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
-    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1) if ws is None else ws
     out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
     idx = torch.empty(wl.K, dtype=torch.int32, device="cuda")
     w = torch.empty(wl.K, dtype=torch.float32, device="cuda")
-    M.moe_layer_decode(d, [dl.L], x, out, idx, w, residual=residual, ws=ws)
+    M.moe_layer_decode(d, [dl.L], x, out, idx, w, residual=residual, ws=ws, separate_kernels=separate)
     torch.cuda.synchronize()
+    assert ws_error_word(ws) == 0
     return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
 
 
@@ -63,19 +69,44 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("separate", [False, True], ids=["one_launch", "three_kernels"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_layer_decode_small_shapes(case):
+def test_layer_decode_small_shapes(case, separate):
     name, H, I, E, K, bits, extra = case
-    say(f"[decode small] {name}")
+    say(f"[decode small] {name} separate={separate}")
     wl = small_workload(name, 0xC0DE + H + I + E, H, I, E, K, bits, **extra)
     dl = build_layer(wl)
     ol = oracle_layer(wl)
     bank = wl.tokens_bank(3)
+    d = M.make_dims(H, I, E, K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)      # one workspace for the three calls
     for t in range(3):
         residual = t == 2
         x = act_tensor(wl, bank[t])
-        out, idx, w = run_decode(dl, x, residual=residual)
+        out, idx, w = run_decode(dl, x, residual=residual, separate=separate, ws=ws)
         check_token(wl, ol, x, act_f64(wl, bank[t]), out, idx, w, residual, f"{name} token {t}")
+
+
+def test_one_launch_many_calls_one_workspace():
+    """Back-to-back calls on one workspace (each launch must see only its own hand-over words):
+    every call matches the three-kernel schedule on the same token, and repeats are bit-identical."""
+    wl = small_workload("seq", 4711, 1024, 512, 64, 4, 4, norm=True)
+    dl = build_layer(wl)
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    ws2 = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    bank = wl.tokens_bank(8)
+    first = {}
+    for i in range(48):
+        t = (i * 5) % 8
+        x = act_tensor(wl, bank[t])
+        out, idx, w = run_decode(dl, x, residual=True, ws=ws)
+        ref, ridx, rw = run_decode(dl, x, residual=True, separate=True, ws=ws2)
+        assert list(idx) == list(ridx), f"call {i} token {t}"
+        assert_close(out, ref, f"call {i} token {t} one launch vs three kernels", rel=2e-5)
+        if t in first:
+            assert np.array_equal(first[t], out), f"call {i} token {t} not reproducible"
+        first.setdefault(t, out)
 
 
 @pytest.mark.parametrize("case", SMALL[:8], ids=[c[0] for c in SMALL[:8]])
