@@ -140,19 +140,19 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
         if (a.w_ws) a.w_ws[o] = my_w;
         a.sel_ws[o] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
     }
-    const Geo g = make_geo(H);
-    const int RB = RG * g.rpi;
-    const int nblk = (I + RB - 1) / RB;
+    const Geo g = make_geo(a.geo);
+    const int RB = a.geo.rb;
+    const int nblk = a.geo.nblk;
     const int units = K * nblk;
     int u = blockIdx.x * kWaves + wave;
     GULoads<NJ, RG> L;
     uint64_t sel = 0;
     Planes pl[3];
     if (u < units) {
-        const int k = u / nblk;
+        const int k = blk_of(u, a.geo);
         sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
         if (sel) {
-            expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+            expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
             if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
             else gu_issue<4, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
         }
@@ -184,13 +184,13 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     // 6. work units
     bool first = true;
     for (; u < units; u += gridDim.x * kWaves) {
-        const int k = u / nblk;
+        const int k = blk_of(u, a.geo);
         const int r0 = (u - k * nblk) * RB;
         float *hout = a.h + ((size_t)t * K + k) * I;
         if (!first) {
             sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
             if (sel) {
-                expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
+                expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
                 if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
                 else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
             }
@@ -242,12 +242,12 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
         wk[k] = k < K ? wk[k] : 0.f;
         if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
     }
-    const Geo g = make_geo(I);
-    const int RB = RG * g.rpi;
-    const int nblk = (H + RB - 1) / RB;
+    const Geo g = make_geo(a.geo);
+    const int RB = a.geo.rb;
+    const int nblk = a.geo.nblk;
     int u = blockIdx.x * kWaves + wave;
     DLoads<NJ, RG, KM> L;
-    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, RB, L);
+    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, RB, a.pt, L);
 
     // 2. stage h of every expert in its code width's layout.  The first pass is straight-line code
     //    (the chunks loaded above), so the weight loads just issued stay in flight meanwhile.
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     bool first = true;
     for (; u < nblk; u += gridDim.x * kWaves) {
         const int r0 = u * RB;
-        if (!first) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, r0, RB, L);
+        if (!first) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, r0, RB, a.pt, L);
         first = false;
         float acc[RG];
 #pragma unroll
@@ -371,6 +371,41 @@ int down_rows_per_unit(int cols) {
     const int nj = nj_for(cols);
     return (nj == 1 ? dn_rg<1>() : nj == 2 ? dn_rg<2>() : dn_rg<4>()) * rpi_for(cols);
 }
+static RowGeo row_geo(int cols, int rows, int rg) {
+    RowGeo r;
+    r.spr = cols / 32;
+    const int gsz = r.spr >= 64 ? 64 : next_pow2(r.spr);
+    r.gsh = 0;
+    while ((1 << r.gsh) < gsz) ++r.gsh;
+    r.rpi = 64 / gsz;
+    r.rb = rg * r.rpi;
+    r.nblk = (rows + r.rb - 1) / r.rb;
+    r.blk_mul = ((uint64_t)1 << 32) / (uint64_t)r.nblk + (((uint64_t)1 << 32) % (uint64_t)r.nblk ? 1 : 0);
+    return r;
+}
+RowGeo gateup_geo(int H, int I) {
+    const int nj = nj_for(H);
+    return row_geo(H, I, nj == 1 ? gu_rg<1>() : nj == 2 ? gu_rg<2>() : gu_rg<4>());
+}
+RowGeo down_geo(int H, int I) {
+    const int nj = nj_for(I);
+    return row_geo(I, H, nj == 1 ? dn_rg<1>() : nj == 2 ? dn_rg<2>() : dn_rg<4>());
+}
+PlaneTable plane_table(int H, int I) {
+    PlaneTable t;
+    for (int b = 0; b < 2; ++b) {
+        const size_t bits = b == 0 ? 2 : 4;
+        const size_t cin = (size_t)I * H * bits / 8, sbin = (size_t)I * (H / 64) * 4, cout = (size_t)H * I * bits / 8;
+        const size_t sbout = (size_t)H * (I / 64) * 4;
+        const size_t sizes[6] = {cin, sbin, cin, sbin, cout, sbout};
+        size_t off = 0;
+        for (int p = 0; p < 6; ++p) {
+            t.off[b][p] = off;
+            off = round256(off + sizes[p]);
+        }
+    }
+    return t;
+}
 size_t gateup_lds_bytes(int H) { return ((size_t)2 * H + H / 32) * 4; }
 size_t down_lds_bytes(int I, int K) { return (size_t)K * down_lds_per_expert(I) * 4; }
 
@@ -403,8 +438,7 @@ hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
 
 template <int NJ, bool SPLIT, int NP>
 static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s) {
-    const int RB = gateup_rows_per_unit(a.H);
-    const int units = a.K * ((a.I + RB - 1) / RB);
+    const int units = a.K * a.geo.nblk;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = gateup_lds_bytes(a.H);
     auto fn = k_gateup<NJ, SPLIT, NP>;
@@ -418,7 +452,10 @@ static hipError_t gateup_impl(const GateUpLaunch &a, hipStream_t s) {
     return a.E <= 512 ? gateup_impl_np<NJ, SPLIT, 8>(a, s) : gateup_impl_np<NJ, SPLIT, 32>(a, s);
 }
 
-hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s) {
+hipError_t launch_gateup(const GateUpLaunch &a_in, hipStream_t s) {
+    GateUpLaunch a = a_in;
+    a.geo = gateup_geo(a.H, a.I);
+    a.pt = plane_table(a.H, a.I);
     const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
     switch (nj_for(a.H)) {
         case 1: return split ? gateup_impl<1, true>(a, s) : gateup_impl<1, false>(a, s);
@@ -429,8 +466,7 @@ hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s) {
 
 template <int NJ, bool COMBINE, int KM>
 static hipError_t down_impl_k(const DownLaunch &a, hipStream_t s) {
-    const int RB = down_rows_per_unit(a.I);
-    const int units = (a.H + RB - 1) / RB;
+    const int units = a.geo.nblk;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = down_lds_bytes(a.I, a.K);
     auto fn = k_down<NJ, COMBINE, KM>;
@@ -446,7 +482,10 @@ static hipError_t down_impl(const DownLaunch &a, hipStream_t s) {
     return down_impl_k<NJ, COMBINE, 8>(a, s);
 }
 
-hipError_t launch_down(const DownLaunch &a, hipStream_t s) {
+hipError_t launch_down(const DownLaunch &a_in, hipStream_t s) {
+    DownLaunch a = a_in;
+    a.geo = down_geo(a.H, a.I);
+    a.pt = plane_table(a.H, a.I);
     const bool comb = a.w != nullptr;
     switch (nj_for(a.I)) {
         case 1: return comb ? down_impl<1, true>(a, s) : down_impl<1, false>(a, s);

@@ -207,16 +207,19 @@ struct Geo {
     int lrow;   // this lane's row within the instruction
     int lsl;    // this lane's first slot
 };
-__device__ __forceinline__ Geo make_geo(int cols) {
+__device__ __forceinline__ Geo make_geo(const RowGeo &r) {
     Geo g;
     const int lane = threadIdx.x & 63;
-    g.spr = cols / 32;
-    if (g.spr >= 64) {
-        g.gsz = 64; g.rpi = 1; g.lrow = 0; g.lsl = lane;
-    } else {
-        g.gsz = next_pow2(g.spr); g.rpi = 64 / g.gsz; g.lrow = lane / g.gsz; g.lsl = lane % g.gsz;
-    }
+    g.spr = r.spr;
+    g.gsz = 1 << r.gsh;
+    g.rpi = r.rpi;
+    g.lrow = lane >> r.gsh;
+    g.lsl = lane & (g.gsz - 1);
     return g;
+}
+// u / nblk for a unit index u < 2^16 (see RowGeo).
+__device__ __forceinline__ int blk_of(int u, const RowGeo &r) {
+    return (int)(((uint64_t)(uint32_t)u * r.blk_mul) >> 32);
 }
 
 // Weight planes are read through global (address space 1) pointers: the blob addresses come from
@@ -224,17 +227,14 @@ __device__ __forceinline__ Geo make_geo(int cols) {
 struct Planes {
     gbytes q; gwords sb;
 };
-__device__ __forceinline__ void expert_planes(uint64_t blob_addr, int H, int I, int bits, Planes p[3]) {
+__device__ __forceinline__ void expert_planes(uint64_t blob_addr, int bits, const PlaneTable &t, Planes p[3]) {
     gbytes blob = (gbytes)blob_addr;
-    const size_t cin = (size_t)I * H * bits / 8, sbin = (size_t)I * (H / 64) * 4;
-    const size_t cout = (size_t)H * I * bits / 8;
-    size_t off = 0;
-    p[0].q = blob + off; off = round256(off + cin);
-    p[0].sb = (gwords)(blob + off); off = round256(off + sbin);
-    p[1].q = blob + off; off = round256(off + cin);
-    p[1].sb = (gwords)(blob + off); off = round256(off + sbin);
-    p[2].q = blob + off; off = round256(off + cout);
-    p[2].sb = (gwords)(blob + off);
+    const uint64_t *o = t.off[bits == 2 ? 0 : 1];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        p[m].q = blob + o[2 * m];
+        p[m].sb = (gwords)(blob + o[2 * m + 1]);
+    }
 }
 
 // --------------------------------------------------------------------------- top-K (one wave)
@@ -589,12 +589,12 @@ __device__ __forceinline__ void dn_issue(const Planes &pl, const Geo &g, int H, 
 // Issue every selected expert's loads for one unit (output rows r0..r0+RB-1).
 template <int NJ, int RG, int KM>
 __device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, const Geo &g, int H, int I, int r0,
-                                             int RB, DLoads<NJ, RG, KM> &L) {
+                                             int RB, const PlaneTable &pt, DLoads<NJ, RG, KM> &L) {
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
         if (k < K && sel[k]) {
             Planes pl[3];
-            expert_planes(sel_blob(sel[k]), H, I, sel_bits(sel[k]), pl);
+            expert_planes(sel_blob(sel[k]), sel_bits(sel[k]), pt, pl);
             if (sel_bits(sel[k]) == 2) dn_issue<2, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
             else dn_issue<4, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
         }

@@ -11,6 +11,22 @@ namespace moe {
 
 constexpr int kGroup = 64;
 
+// Lane geometry of one matrix family (rows of `cols` inputs), computed on the host so that the
+// kernels do no integer division: 32-column slots per row, lanes per row group (2^gsh), rows per
+// wave instruction, rows per work unit, row blocks per matrix, and the multiplier with which
+// (u * blk_mul) >> 32 == u / nblk for every unit index u < 2^16.
+struct RowGeo {
+    int spr, gsh, rpi, rb, nblk;
+    uint64_t blk_mul;
+};
+// Byte offsets of the six planes of an expert blob, for 2-bit ([0]) and 4-bit ([1]) experts.
+struct PlaneTable {
+    uint64_t off[2][6];
+};
+RowGeo gateup_geo(int H, int I);   // gate/up rows: I rows of H inputs
+RowGeo down_geo(int H, int I);     // down rows: H rows of I inputs
+PlaneTable plane_table(int H, int I);
+
 // Rows of the gate/up matrices one wavefront handles per work unit, for a given
 // input width (cols) at 4-bit; the 2-bit path covers the same rows.
 int gateup_rows_per_unit(int cols);
@@ -46,6 +62,7 @@ struct GateUpLaunch {
     const moe_expert_desc *experts;
     float *h;                                      // [T][K][I]
     int H, I, E, K, T;
+    RowGeo geo; PlaneTable pt;                     // set by launch_gateup
 };
 hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s);
 
@@ -58,6 +75,7 @@ struct DownLaunch {
     const void *residual; int residual_dtype; int residual_stride;   // [T][stride] or NULL
     float *out;                                    // combine: [T][H]; else y [T][K][H]
     int H, I, K, T;
+    RowGeo geo; PlaneTable pt;                     // set by launch_down
 };
 hipError_t launch_down(const DownLaunch &a, hipStream_t s);
 
@@ -99,7 +117,8 @@ struct LayerLaunch {
     const uint32_t *seq;                           // launch counter (advanced by the down kernel)
     uint64_t *slots;                               // [layer_logit_copies()][E] tag << 32 | logit bits
     uint32_t *err;                                 // timed-out waits (nonzero: the down kernel writes NaN)
-    int nr, ng;                                    // workgroups per phase (set by launch_layer)
+    int nr, ng;                                    // workgroups per group (set by launch_layer)
+    RowGeo geo; PlaneTable pt;                     // gate/up geometry (set by launch_layer)
 };
 void layer_grid(int H, int I, int E, int K, int *nr, int *ng);
 int layer_logit_copies();

@@ -149,12 +149,8 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         if (a.r.norm_w) issue_chunk16(a.r.norm_w, MOE_BF16, m, nc[j]);
     }
 
-    // 2. wave 0 waits for this launch's logits and copies them to LDS
-    if (wave == 0) {
-        wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, launch_tag(seq), s_lg, a.err);
-    }
-
-    // 3. descriptor table and RMSNorm statistics; the barrier publishes logits and table
+    // 2. while the router workgroups run: descriptor table and activation layouts (both code
+    //    widths; with a norm, x * w_norm scaled by 1/rms once the block sum is known)
     if (use_tab) {
 #pragma unroll
         for (int j = 0; j < kTabMax / kBlock; ++j) {
@@ -162,12 +158,9 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
             if (e < E) s_tab[e] = pack_sel(((uint64_t)dsc[j].y << 32) | dsc[j].x, dsc[j].z);
         }
     }
-    // x (and, with a norm, x * w_norm: the 1/rms factor follows once the block sum is known) in
-    // registers now, so that no later step waits on these loads behind the weight loads
     float v[2][16];
 #pragma unroll
     for (int j = 0; j < 2; ++j) chunk16_f32(xc[j], xdt, v[j]);
-    float inv = 1.f;
     if (a.r.norm_w) {
         float ss = 0.f;
 #pragma unroll
@@ -182,10 +175,31 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
             for (int i = 0; i < 16; ++i) v[j][i] *= w[i];
         }
         ss = block_sum(ss, red);
-        inv = 1.0f / sqrtf(ss / (float)H + a.r.eps);
-    } else {
-        __syncthreads();
+        const float inv = 1.0f / sqrtf(ss / (float)H + a.r.eps);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[j][i] *= inv;
     }
+    uint32_t *h4 = act, *l4 = act + H / 2, *h2 = act + H, *l2 = act + 3 * H / 2;
+    float *xs = (float *)(act + 2 * H);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = threadIdx.x + kBlock * j;
+        float sum = 0.f;
+        if (m < nch) {
+            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
+            write_chunk<2, SPLIT>(m, v[j], h2, l2);
+        }
+        sum += dppf<0xB1>(sum);
+        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
+    }
+    const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
+
+    // 3. wave 0 waits for this launch's logits and copies them to LDS; the barrier publishes the
+    //    logits, the table and the layouts
+    if (wave == 0) wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, launch_tag(seq), s_lg, a.err);
+    __syncthreads();
 
     // 4. routing in registers (each wave, identical results)
     int my_idx = 0;
@@ -202,60 +216,28 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         a.sel_ws[lane] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
     }
 
-    // 5. the first unit's weight loads, then the activation layouts
-    const Geo g = make_geo(H);
-    const int RB = RG * g.rpi;
-    const int nblk = (I + RB - 1) / RB;
+    // 5. geometry of the work units
+    const Geo g = make_geo(a.geo);
+    const int RB = a.geo.rb;
+    const int nblk = a.geo.nblk;
     const int units = K * nblk;
     const int stride = a.ng * kWaves;
     int u = gb * kWaves + wave;
     GULoads<NJ, RG> L;
     uint64_t sel = 0;
     Planes pl[3];
-    if (u < units) {
-        const int k = u / nblk;
-        sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
-        if (sel) {
-            expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
-            if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
-            else gu_issue<4, NJ, RG>(pl, g, H, I, (u - k * nblk) * RB, RB, L);
-        }
-    }
-    uint32_t *h4 = act, *l4 = act + H / 2, *h2 = act + H, *l2 = act + 3 * H / 2;
-    float *xs = (float *)(act + 2 * H);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = threadIdx.x + kBlock * j;
-        float sum = 0.f;
-        if (m < nch) {
-            if (a.r.norm_w) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[j][i] *= inv;
-            }
-            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
-            write_chunk<2, SPLIT>(m, v[j], h2, l2);
-        }
-        sum += dppf<0xB1>(sum);
-        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
-    }
-    __syncthreads();
-    const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
 
     // 6. work units -> h
-    bool first = true;
     for (; u < units; u += stride) {
-        const int k = u / nblk;
+        const int k = blk_of(u, a.geo);
         const int r0 = (u - k * nblk) * RB;
         float *hout = a.h + (size_t)k * I;
-        if (!first) {
-            sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
-            if (sel) {
-                expert_planes(sel_blob(sel), H, I, sel_bits(sel), pl);
-                if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
-                else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
-            }
+        sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+        if (sel) {
+            expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
+            if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
+            else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
         }
-        first = false;
         if (!sel) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
@@ -307,9 +289,9 @@ hipError_t layer_nj(const LayerLaunch &a, size_t lds, hipStream_t s) {
 }  // namespace
 
 void layer_grid(int H, int I, int E, int K, int *nr, int *ng) {
-    const int rbg = gateup_rows_per_unit(H);
+    const RowGeo gg = gateup_geo(H, I);
     *nr = (E + kWaves - 1) / kWaves;
-    *ng = (K * ((I + rbg - 1) / rbg) + kWaves - 1) / kWaves;
+    *ng = (K * gg.nblk + kWaves - 1) / kWaves;
 }
 
 int layer_logit_copies() { return kLogitCopies; }
@@ -324,6 +306,8 @@ size_t layer_lds_bytes(int H, int E) {
 hipError_t launch_layer(const LayerLaunch &a_in, hipStream_t s) {
     LayerLaunch a = a_in;
     layer_grid(a.H, a.I, a.E, a.K, &a.nr, &a.ng);
+    a.geo = gateup_geo(a.H, a.I);
+    a.pt = plane_table(a.H, a.I);
     const size_t lds = layer_lds_bytes(a.H, a.E);
     return a.E <= 512 ? layer_nj<8>(a, lds, s) : layer_nj<32>(a, lds, s);
 }
