@@ -253,7 +253,7 @@ def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, 
                      ws=None, stream=None, separate_kernels: bool = False) -> None:
     """One decode token through the layers.  ``ws`` must come from :func:`workspace` (zero-filled)
     and be reused only by stream-ordered calls; ``separate_kernels`` selects the three-kernel
-    schedule instead of one launch per layer."""
+    schedule instead of the default two launches per layer."""
     arr = (moe_layer * len(layers))(*[L.c for L in layers])
     flags = (MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
@@ -262,15 +262,20 @@ def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, 
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,
-                           residual: bool = False, ws=None, stream=None) -> None:
-    """As moe_layer_decode, recording ``events`` (3*len(layers)+1 torch.cuda.Event objects with
-    timing enabled) before the first kernel and after every kernel, on the library's stream."""
+                           residual: bool = False, ws=None, stream=None, separate_kernels: bool = False) -> None:
+    """As moe_layer_decode, with a start/stop pair of ``events`` (torch.cuda.Event objects with
+    timing enabled) per kernel: events[2j].elapsed_time(events[2j+1]) is kernel j's execution time.
+    Two kernels per layer on the default schedule (router + gate/up, down), three with
+    ``separate_kernels`` (router, gate/up, down)."""
     arr = (moe_layer * len(layers))(*[L.c for L in layers])
+    need = 2 * (3 if separate_kernels else 2) * len(layers)
+    if len(events) < need:
+        raise ValueError(f"{need} events needed, {len(events)} given")
     handles = [e.cuda_event for e in events]
     if not all(handles):
         raise ValueError("events must have been recorded once (torch creates HIP events lazily)")
     ev = (ctypes.c_void_p * len(events))(*handles)
-    flags = MOE_FLAG_RESIDUAL if residual else 0
+    flags = (MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
     _check(lib().moe_layer_decode_timed(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                         _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                         _stream(stream), ev))

@@ -381,15 +381,14 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
     return ok();
 }
 
-static int record(void *const *events, int i, hipStream_t st) {
-    if (!events) return MOE_OK;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(st, &cs);
-    if (e == hipSuccess)
-        e = cs == hipStreamCaptureStatusActive ? hipEventRecordWithFlags((hipEvent_t)events[i], st, hipEventRecordExternal)
-                                               : hipEventRecord((hipEvent_t)events[i], st);
-    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "event %d: %s", i, hipGetErrorString(e));
-    return MOE_OK;
+// Start/stop events of kernel j of a timed call: events[2j], events[2j+1].
+static moe::KernelEvents kernel_events(void *const *events, int j) {
+    moe::KernelEvents ev;
+    if (events) {
+        ev.start = (hipEvent_t)events[2 * j];
+        ev.stop = (hipEvent_t)events[2 * j + 1];
+    }
+    return ev;
 }
 
 static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
@@ -414,8 +413,7 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
     const DecodeWs W = decode_layout(dims, ws);
     hipStream_t st = (hipStream_t)stream;
     const bool residual = flags & MOE_FLAG_RESIDUAL;
-    const bool separate = events != nullptr || (flags & MOE_FLAG_SEPARATE_KERNELS);
-    if (int s = record(events, 0, st)) return s;
+    const bool separate = flags & MOE_FLAG_SEPARATE_KERNELS;
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer &L = layers[l];
         const void *xl = l == 0 ? x : (const void *)(W.xbuf + (size_t)((l - 1) & 1) * H);
@@ -438,20 +436,17 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
             la.seq = W.sync;
             la.err = W.sync + 1;
             la.slots = W.slots;
-            if (int s = launched(moe::launch_layer(la, st), "router + gate/up")) return s;
+            if (int s = launched(moe::launch_layer(la, st, kernel_events(events, 2 * l)), "router + gate/up")) return s;
             moe::DownLaunch da{W.h, W.sync, W.sync + 1, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
-            if (int s = launched(moe::launch_down(da, st), "down")) return s;
+            if (int s = launched(moe::launch_down(da, st, kernel_events(events, 2 * l + 1)), "down")) return s;
             continue;
         }
-        if (int s = launched(moe::launch_router(ra, st), "router")) return s;
-        if (int s = record(events, 3 * l + 1, st)) return s;
+        if (int s = launched(moe::launch_router(ra, st, kernel_events(events, 3 * l)), "router")) return s;
         moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, W.logits, nullptr, idx_l, w_l, W.sel, W.w,
                              L.experts, W.h, H, I, E, K, 1};
-        if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
-        if (int s = record(events, 3 * l + 2, st)) return s;
+        if (int s = launched(moe::launch_gateup(ga, st, kernel_events(events, 3 * l + 1)), "gate/up")) return s;
         moe::DownLaunch da{W.h, nullptr, nullptr, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
-        if (int s = launched(moe::launch_down(da, st), "down")) return s;
-        if (int s = record(events, 3 * l + 3, st)) return s;
+        if (int s = launched(moe::launch_down(da, st, kernel_events(events, 3 * l + 2)), "down")) return s;
     }
     return ok();
 }
@@ -465,8 +460,13 @@ int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_
                            unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes,
                            void *stream, void *const *events) {
     if (!events) return fail(MOE_ERR_NULL, "events is NULL");
-    for (int i = 0; i < 3 * (n_layers > 0 ? n_layers : 0) + 1 && n_layers <= 4096; ++i)
+    if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_SHAPE, "n_layers=%d outside [1, 4096]", n_layers);
+    const int per_layer = (flags & MOE_FLAG_SEPARATE_KERNELS) ? 3 : 2;
+    for (int i = 0; i < 2 * per_layer * n_layers; ++i)
         if (!events[i]) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode_timed cannot be captured into a graph");
     return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, events);
 }
 

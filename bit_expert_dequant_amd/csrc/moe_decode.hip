@@ -415,19 +415,18 @@ static hipError_t set_lds(const void *fn, size_t lds) {
 }
 
 template <int RDT, bool SPLIT>
-static hipError_t router_impl(const RouterLaunch &a, hipStream_t s) {
+static hipError_t router_impl(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev) {
     dim3 grid((a.E + kWaves - 1) / kWaves, a.T);
     const size_t lds = (size_t)a.H * 4;
     auto fn = k_router<RDT, SPLIT>;
     if (hipError_t e = set_lds((const void *)fn, lds)) return e;
-    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-    return hipGetLastError();
+    return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
-hipError_t launch_router(const RouterLaunch &a, hipStream_t s) {
-    if (a.router_dtype != MOE_BF16) return router_impl<MOE_F32, false>(a, s);
+hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev) {
+    if (a.router_dtype != MOE_BF16) return router_impl<MOE_F32, false>(a, s, ev);
     const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
-    return split ? router_impl<MOE_BF16, true>(a, s) : router_impl<MOE_BF16, false>(a, s);
+    return split ? router_impl<MOE_BF16, true>(a, s, ev) : router_impl<MOE_BF16, false>(a, s, ev);
 }
 
 hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
@@ -437,60 +436,58 @@ hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
 }
 
 template <int NJ, bool SPLIT, int NP>
-static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s) {
+static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s, const KernelEvents &ev) {
     const int units = a.K * a.geo.nblk;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = gateup_lds_bytes(a.H);
     auto fn = k_gateup<NJ, SPLIT, NP>;
     if (hipError_t e = set_lds((const void *)fn, lds)) return e;
-    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-    return hipGetLastError();
+    return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
 template <int NJ, bool SPLIT>
-static hipError_t gateup_impl(const GateUpLaunch &a, hipStream_t s) {
-    return a.E <= 512 ? gateup_impl_np<NJ, SPLIT, 8>(a, s) : gateup_impl_np<NJ, SPLIT, 32>(a, s);
+static hipError_t gateup_impl(const GateUpLaunch &a, hipStream_t s, const KernelEvents &ev) {
+    return a.E <= 512 ? gateup_impl_np<NJ, SPLIT, 8>(a, s, ev) : gateup_impl_np<NJ, SPLIT, 32>(a, s, ev);
 }
 
-hipError_t launch_gateup(const GateUpLaunch &a_in, hipStream_t s) {
+hipError_t launch_gateup(const GateUpLaunch &a_in, hipStream_t s, const KernelEvents &ev) {
     GateUpLaunch a = a_in;
     a.geo = gateup_geo(a.H, a.I);
     a.pt = plane_table(a.H, a.I);
     const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
     switch (nj_for(a.H)) {
-        case 1: return split ? gateup_impl<1, true>(a, s) : gateup_impl<1, false>(a, s);
-        case 2: return split ? gateup_impl<2, true>(a, s) : gateup_impl<2, false>(a, s);
-        default: return split ? gateup_impl<4, true>(a, s) : gateup_impl<4, false>(a, s);
+        case 1: return split ? gateup_impl<1, true>(a, s, ev) : gateup_impl<1, false>(a, s, ev);
+        case 2: return split ? gateup_impl<2, true>(a, s, ev) : gateup_impl<2, false>(a, s, ev);
+        default: return split ? gateup_impl<4, true>(a, s, ev) : gateup_impl<4, false>(a, s, ev);
     }
 }
 
 template <int NJ, bool COMBINE, int KM>
-static hipError_t down_impl_k(const DownLaunch &a, hipStream_t s) {
+static hipError_t down_impl_k(const DownLaunch &a, hipStream_t s, const KernelEvents &ev) {
     const int units = a.geo.nblk;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = down_lds_bytes(a.I, a.K);
     auto fn = k_down<NJ, COMBINE, KM>;
     if (hipError_t e = set_lds((const void *)fn, lds)) return e;
-    hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-    return hipGetLastError();
+    return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
 template <int NJ, bool COMBINE>
-static hipError_t down_impl(const DownLaunch &a, hipStream_t s) {
-    if (a.K <= 2) return down_impl_k<NJ, COMBINE, 2>(a, s);
-    if (a.K <= 4) return down_impl_k<NJ, COMBINE, 4>(a, s);
-    return down_impl_k<NJ, COMBINE, 8>(a, s);
+static hipError_t down_impl(const DownLaunch &a, hipStream_t s, const KernelEvents &ev) {
+    if (a.K <= 2) return down_impl_k<NJ, COMBINE, 2>(a, s, ev);
+    if (a.K <= 4) return down_impl_k<NJ, COMBINE, 4>(a, s, ev);
+    return down_impl_k<NJ, COMBINE, 8>(a, s, ev);
 }
 
-hipError_t launch_down(const DownLaunch &a_in, hipStream_t s) {
+hipError_t launch_down(const DownLaunch &a_in, hipStream_t s, const KernelEvents &ev) {
     DownLaunch a = a_in;
     a.geo = down_geo(a.H, a.I);
     a.pt = plane_table(a.H, a.I);
     const bool comb = a.w != nullptr;
     switch (nj_for(a.I)) {
-        case 1: return comb ? down_impl<1, true>(a, s) : down_impl<1, false>(a, s);
-        case 2: return comb ? down_impl<2, true>(a, s) : down_impl<2, false>(a, s);
-        default: return comb ? down_impl<4, true>(a, s) : down_impl<4, false>(a, s);
+        case 1: return comb ? down_impl<1, true>(a, s, ev) : down_impl<1, false>(a, s, ev);
+        case 2: return comb ? down_impl<2, true>(a, s, ev) : down_impl<2, false>(a, s, ev);
+        default: return comb ? down_impl<4, true>(a, s, ev) : down_impl<4, false>(a, s, ev);
     }
 }
 

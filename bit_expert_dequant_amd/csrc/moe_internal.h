@@ -1,6 +1,7 @@
 // moe_internal.h -- launchers shared between the C-ABI layer and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,6 +11,21 @@
 namespace moe {
 
 constexpr int kGroup = 64;
+
+// Optional start/stop events of one launch.  When either is set the kernel goes out through
+// hipExtLaunchKernel, which stamps the events with the dispatch's own start and end times, so
+// hipEventElapsedTime(start, stop) is the kernel's execution time alone.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename A>
+inline hipError_t dispatch(F fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, const KernelEvents &ev,
+                           const A &a) {
+    if (ev.start || ev.stop) hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, a);
+    else hipLaunchKernelGGL(fn, grid, block, lds, s, a);
+    return hipGetLastError();
+}
 
 // Lane geometry of one matrix family (rows of `cols` inputs), computed on the host so that the
 // kernels do no integer division: 32-column slots per row, lanes per row group (2^gsh), rows per
@@ -43,7 +59,7 @@ struct RouterLaunch {
     float *logits;                                 // [T][E]
     int H, E, T;
 };
-hipError_t launch_router(const RouterLaunch &a, hipStream_t s);
+hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 
 struct TopkLaunch {
     const float *logits; int E, K, T;
@@ -64,12 +80,12 @@ struct GateUpLaunch {
     int H, I, E, K, T;
     RowGeo geo; PlaneTable pt;                     // set by launch_gateup
 };
-hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s);
+hipError_t launch_gateup(const GateUpLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 
 struct DownLaunch {
     const float *h;                                // [T][K][I]
-    uint32_t *seq;                                 // one-launch schedule: advance this launch counter, or NULL
-    const uint32_t *err;                           // one-launch schedule: nonzero -> NaN outputs, or NULL
+    uint32_t *seq;                                 // two-launch schedule: advance this launch counter, or NULL
+    const uint32_t *err;                           // two-launch schedule: nonzero -> NaN outputs, or NULL
     const uint64_t *sel;                           // [T][K] blob address | code width (0: no expert)
     const float *w;                                // [T][K] (combine) or NULL (per-expert output)
     const void *residual; int residual_dtype; int residual_stride;   // [T][stride] or NULL
@@ -77,7 +93,7 @@ struct DownLaunch {
     int H, I, K, T;
     RowGeo geo; PlaneTable pt;                     // set by launch_down
 };
-hipError_t launch_down(const DownLaunch &a, hipStream_t s);
+hipError_t launch_down(const DownLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 
 // Batched path (T > 1): grouping of the T*K (token, slot) pairs by expert, then grouped GEMMs.
 struct GroupLaunch {
@@ -123,7 +139,7 @@ struct LayerLaunch {
 void layer_grid(int H, int I, int E, int K, int *nr, int *ng);
 int layer_logit_copies();
 size_t layer_lds_bytes(int H, int E);
-hipError_t launch_layer(const LayerLaunch &a, hipStream_t s);
+hipError_t launch_layer(const LayerLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 
 struct CombineLaunch {
     const float *y; const float *w; const float *residual; float *out;

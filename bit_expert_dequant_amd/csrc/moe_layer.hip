@@ -268,21 +268,20 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
 }
 
 template <int NP, int NJ>
-hipError_t layer_impl(const LayerLaunch &a, size_t lds, hipStream_t s) {
+hipError_t layer_impl(const LayerLaunch &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
     auto fn = k_route_gateup<NP, NJ>;
     if (lds > 64 * 1024)
         if (hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
             return e;
-    hipLaunchKernelGGL(fn, dim3(a.nr + a.ng), dim3(kBlock), lds, s, a);
-    return hipGetLastError();
+    return dispatch(fn, dim3(a.nr + a.ng), dim3(kBlock), lds, s, ev, a);
 }
 
 template <int NP>
-hipError_t layer_nj(const LayerLaunch &a, size_t lds, hipStream_t s) {
+hipError_t layer_nj(const LayerLaunch &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
     switch (nj_for(a.H)) {
-        case 1: return layer_impl<NP, 1>(a, lds, s);
-        case 2: return layer_impl<NP, 2>(a, lds, s);
-        default: return layer_impl<NP, 4>(a, lds, s);
+        case 1: return layer_impl<NP, 1>(a, lds, s, ev);
+        case 2: return layer_impl<NP, 2>(a, lds, s, ev);
+        default: return layer_impl<NP, 4>(a, lds, s, ev);
     }
 }
 
@@ -303,13 +302,13 @@ size_t layer_lds_bytes(int H, int E) {
     return r > g ? r : g;
 }
 
-hipError_t launch_layer(const LayerLaunch &a_in, hipStream_t s) {
+hipError_t launch_layer(const LayerLaunch &a_in, hipStream_t s, const KernelEvents &ev) {
     LayerLaunch a = a_in;
     layer_grid(a.H, a.I, a.E, a.K, &a.nr, &a.ng);
     a.geo = gateup_geo(a.H, a.I);
     a.pt = plane_table(a.H, a.I);
     const size_t lds = layer_lds_bytes(a.H, a.E);
-    return a.E <= 512 ? layer_nj<8>(a, lds, s) : layer_nj<32>(a, lds, s);
+    return a.E <= 512 ? layer_nj<8>(a, lds, s, ev) : layer_nj<32>(a, lds, s, ev);
 }
 
 }  // namespace moe

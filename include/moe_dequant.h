@@ -176,7 +176,7 @@ int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts);
  * (n_layers for MOE_OP_LAYER_DECODE).  0 for unsupported arguments.  For MOE_OP_ROUTE and
  * MOE_OP_EXPERT_FFN the workspace is scratch: its contents need no initialisation and are
  * undefined after the call.  A MOE_OP_LAYER_DECODE workspace carries state from one
- * moe_layer_decode call to the next (a launch counter and hand-over words of the one-launch
+ * moe_layer_decode call to the next (a launch counter and hand-over words of the two-launch
  * layer schedule): zero-fill it once before its first moe_layer_decode call, and again
  * before going back to moe_layer_decode after using the same memory for anything else.
  * Calls sharing a workspace must be ordered (same stream, or synchronised); two calls that
@@ -236,17 +236,21 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
                      int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                      void *ws, size_t ws_bytes, void *stream);
 
-/* moe_layer_decode on the three-kernel schedule with per-kernel timing, the library's
- * counterpart of the pages' per-layer timing breakdown (lilting.ch page, "遅延GPU実行"
- * section, per-layer time table).
- *   events  host array of 3*n_layers + 1 hipEvent_t (created by the caller on the current
- *           device).  events[0] is recorded on `stream` before the first kernel and
- *           events[3l+1], events[3l+2], events[3l+3] after layer l's router, gate/up and down
- *           kernels, so hipEventElapsedTime(events[i], events[i+1]) spans one kernel (including
- *           its dispatch).  When the stream is being captured the records are attempted as
- *           external event nodes of the graph (a runtime that refuses them makes the call
- *           fail with MOE_ERR_LAUNCH).
- * Other arguments and errors as moe_layer_decode (MOE_ERR_NULL when events is NULL). */
+/* moe_layer_decode with per-kernel timing, the library's counterpart of the pages' per-layer
+ * timing breakdown (lilting.ch page, "遅延GPU実行" section, per-layer time table).  It runs the
+ * schedule `flags` selects, kernel j of the call (in issue order) getting the start/stop pair
+ * events[2j], events[2j+1]:
+ *   default (two launches per layer): 4*n_layers events; layer l's router + gate/up launch is
+ *           kernel 2l and its down kernel 2l+1;
+ *   MOE_FLAG_SEPARATE_KERNELS: 6*n_layers events; layer l's router, gate/up and down kernels are
+ *           kernels 3l, 3l+1, 3l+2.
+ * Each kernel is launched through hipExtLaunchKernel with its pair, which the runtime stamps with
+ * the dispatch's own start and end, so hipEventElapsedTime(events[2j], events[2j+1]) is kernel
+ * j's execution time without the gaps between kernels.  The events are hipEvent_t created by the
+ * caller on the current device.  The call cannot be captured into a graph (MOE_ERR_UNSUPPORTED
+ * while `stream` is capturing).
+ * Other arguments and errors as moe_layer_decode (MOE_ERR_NULL when events or one of its
+ * entries is NULL). */
 int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
                            int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                            void *ws, size_t ws_bytes, void *stream, void *const *events);

@@ -24,7 +24,7 @@ def say(msg):
 
 
 def ws_error_word(ws) -> int:
-    """The layer-decode workspace's error word (count of timed-out waits of the one-launch schedule)."""
+    """The layer-decode workspace's error word (count of timed-out waits of the two-launch schedule)."""
     return int(ws[4:8].cpu().numpy().view(np.uint32)[0])
 
 
@@ -69,7 +69,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("separate", [False, True], ids=["one_launch", "three_kernels"])
+@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_layer_decode_small_shapes(case, separate):
     name, H, I, E, K, bits, extra = case
@@ -87,7 +87,7 @@ def test_layer_decode_small_shapes(case, separate):
         check_token(wl, ol, x, act_f64(wl, bank[t]), out, idx, w, residual, f"{name} token {t}")
 
 
-def test_one_launch_many_calls_one_workspace():
+def test_two_launch_many_calls_one_workspace():
     """Back-to-back calls on one workspace (each launch must see only its own hand-over words):
     every call matches the three-kernel schedule on the same token, and repeats are bit-identical."""
     wl = small_workload("seq", 4711, 1024, 512, 64, 4, 4, norm=True)
@@ -103,7 +103,7 @@ def test_one_launch_many_calls_one_workspace():
         out, idx, w = run_decode(dl, x, residual=True, ws=ws)
         ref, ridx, rw = run_decode(dl, x, residual=True, separate=True, ws=ws2)
         assert list(idx) == list(ridx), f"call {i} token {t}"
-        assert_close(out, ref, f"call {i} token {t} one launch vs three kernels", rel=2e-5)
+        assert_close(out, ref, f"call {i} token {t} two launches vs three kernels", rel=2e-5)
         if t in first:
             assert np.array_equal(first[t], out), f"call {i} token {t} not reproducible"
         first.setdefault(t, out)
@@ -209,6 +209,44 @@ def test_two_layer_stack_small():
             assert list(idx.cpu().numpy()[l]) == list(r.idx), f"layer {l}"
             assert_close(w.cpu().numpy()[l], r.w, f"layer {l} w")
         assert_close(out.cpu().numpy(), ref_out, "stack out")
+
+
+@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+def test_timed_decode_matches_untimed(separate):
+    """moe_layer_decode_timed runs the same schedule as moe_layer_decode (bit-identical outputs and
+    routing on a 2-layer stack) and stamps a start/stop event pair per kernel, in stream order."""
+    wl = small_workload("timed", 777, 1024, 512, 16, 4, 4, norm=True, n_layers=2)
+    dls = [build_layer(wl, l) for l in range(2)]
+    L = [dl.L for dl in dls]
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 2)
+    x = act_tensor(wl, wl.tokens_bank(1)[0])
+    res = []
+    for timed in (False, True):
+        out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(2, wl.K, dtype=torch.int32, device="cuda")
+        w = torch.empty(2, wl.K, dtype=torch.float32, device="cuda")
+        if timed:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (3 if separate else 2) * 2)]
+            for e in evs:
+                e.record()
+            torch.cuda.synchronize()
+            with pytest.raises(ValueError):
+                M.moe_layer_decode_timed(d, L, x, out, evs[:-1], idx, w, residual=True, ws=ws,
+                                         separate_kernels=separate)
+            M.moe_layer_decode_timed(d, L, x, out, evs, idx, w, residual=True, ws=ws, separate_kernels=separate)
+        else:
+            M.moe_layer_decode(d, L, x, out, idx, w, residual=True, ws=ws, separate_kernels=separate)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()))
+        if timed:
+            kernels = [evs[2 * j].elapsed_time(evs[2 * j + 1]) for j in range(len(evs) // 2)]
+            assert all(0 < k < 1e3 for k in kernels), kernels
+            starts = [evs[0].elapsed_time(evs[2 * j]) for j in range(len(evs) // 2)]
+            assert all(b >= a for a, b in zip(starts, starts[1:])), starts
+    for u, v in zip(*res):
+        assert np.array_equal(u, v)
+    assert ws_error_word(ws) == 0
 
 
 @pytest.mark.parametrize("E", [40, 700])
