@@ -122,7 +122,7 @@ size_t ffn_ws(const moe_dims *d, int T) {
     c.take<uint64_t>((size_t)T * d->top_k);
     return c.off;
 }
-// Layer-decode workspace: the one-launch schedule's hand-over words first (they must start
+// Layer-decode workspace: the two-launch schedule's hand-over words first (they must start
 // zeroed), then the buffers both schedules use.
 struct DecodeWs {
     uint32_t *sync;      // [0] launch counter, [1] error word

@@ -4,7 +4,7 @@
 //   k_router : [RMSNorm] + router matvec -> logits[T][E]
 //   k_topk   : softmax / top-K / renormalise (for moe_route)
 //   k_gateup : every wavefront recomputes top-K from the logits (no host round trip, no grid
-//              barrier), stages the activation once in LDS in the order the unpack consumes it,
+//              barrier), stages the activation once in LDS as digit planes in the code order,
 //              and streams the gate and up rows of all K selected experts in one launch,
 //              writing h = silu(g) * u
 //   k_down   : down projection of all K experts for a block of output rows, combined with the
@@ -14,14 +14,14 @@
 // Dequantisation.  The affine form w = q*s + b and its FMA rewrite fma(q, s*x, b*x) come from
 // the lilting.ch page "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE", section "Metal
 // Compute Shaders".  Summed over the 32 inputs one lane handles (half a group of 64) it becomes
-// s * sum(q x) + b * sum(x), and sum(x) is computed once per slot.  Codes become bf16 operands
-// without a table (the nzkcom page lists a lookup-table dequant among its rejected experiments)
-// by OR-ing them into the mantissa of 128.0: (q | 0x4300) is the bf16 value 128 + q, so two codes
-// at the same bit position of the two 16-bit halves of a dword become one packed operand with a
-// single AND-OR, and v_dot2_f32_bf16 accumulates (128+q_a) x_a + (128+q_b) x_b in fp32 with exact
-// products.  The 128 * sum(x) offset folds into the bias term: s * acc + (b - 128 s) * sum(x).
-// Activations that are not exactly bf16 (fp32 inputs, RMSNorm outputs, the SwiGLU output h) are
-// split into bf16 hi + lo parts with one more dot2 for the lo part (about 16 significant bits).
+// s * sum(q x) + b * sum(x), and sum(x) is computed once per slot.  Codes are never converted to
+// floats (the nzkcom page lists a lookup-table dequant among its rejected experiments): the
+// activation is staged once per workgroup as 16-bit fixed point per slot, in four planes of signed
+// 4-bit digits, so sum(q x) is an exact integer dot product that v_dot8_i32_i4 takes eight codes
+// at a time, straight from the code dwords (4-bit codes XOR 8; 2-bit codes spread to nibbles with
+// one AND per parity).  The slot's scale turns it back into fp32.  Per weight this costs about a
+// quarter of the vector instructions of a bf16 dot2 on unpacked codes, which matters because a
+// decode step has the whole GPU's vector units for only a few microseconds.
 //
 // Lane geometry.  A lane "slot" is 32 consecutive input columns: 16 bytes of 4-bit codes or 8
 // bytes of 2-bit codes, always inside one group of 64.  For rows of >= 64 slots, lane l takes
@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(64) k_topk(TopkLaunch a) {
     }
 }
 
-template <int NJ, bool SPLIT, int NP>
+template <int NJ, int NP>
 __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ uint64_t s_tab[kTabMax];
@@ -158,28 +158,22 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
         }
     }
 
-    // 5. activation layouts for both code widths, straight from registers
-    uint32_t *h4 = lds, *l4 = lds + H / 2, *h2 = lds + H, *l2 = lds + 3 * H / 2;
-    float *xs = (float *)(lds + 2 * H);
+    // 5. activation digit planes for both code widths, straight from registers
+    uint32_t *d4 = lds, *d2 = lds + H / 2;
+    float2 *xs = (float2 *)(lds + H);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int m = threadIdx.x + kBlock * j;
-        float sum = 0.f;
-        if (m < nch) {
-            if (a.norm_w) {
-                float w[16];
-                chunk16_f32(nc[j], MOE_BF16, w);
+        if (a.norm_w && m < nch) {
+            float w[16];
+            chunk16_f32(nc[j], MOE_BF16, w);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
-            }
-            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
-            write_chunk<2, SPLIT>(m, v[j], h2, l2);
+            for (int i = 0; i < 16; ++i) v[j][i] = v[j][i] * inv * w[i];
         }
-        sum += dppf<0xB1>(sum);                      // chunks 2s and 2s+1 sit in lanes l and l^1
-        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
+        stage_chunk(m, m < nch, v[j], d4, d2, xs);
     }
     __syncthreads();
-    const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
+    const ActView v4{d4, xs}, v2{d2, xs};
 
     // 6. work units
     bool first = true;
@@ -200,8 +194,8 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
         }
-        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG, SPLIT>(g, I, r0, RB, v2, L, hout);
-        else gu_finish<4, NJ, RG, SPLIT>(g, I, r0, RB, v4, L, hout);
+        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
+        else gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
     }
 }
 
@@ -211,15 +205,18 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     constexpr int RG = dn_rg<NJ>();
     const int H = a.H, I = a.I, K = a.K, t = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // 0. one-launch schedule: advance the launch counter (every workgroup of the router + gate/up
+    // 0. two-launch schedule: advance the launch counter (every workgroup of the router + gate/up
     //    launch read it before this kernel started) and pick up its error word
     if (a.seq && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         const uint32_t nt = a.seq[0] + 1u;
         __hip_atomic_store(a.seq, nt ? nt : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const bool bad = a.err && *a.err != 0;
+    // The error word is loaded without a branch (a harmless in-bounds word stands in when there is
+    // none) so that its wait falls at the output stores, not here.
+    const uint32_t err_word = *(const GLOBAL_AS uint32_t *)(a.err ? a.err : (const uint32_t *)a.sel);
     // 1. h chunks of this thread (first pass) and the selected experts + routing weights, all in
-    //    flight together (branch-free clamped loads); then the first unit's weight loads
+    //    flight together (branch-free clamped loads); the chunks are converted before the first
+    //    unit's weight loads go out, so no wait for them can fall behind those loads
     const int per = down_lds_per_expert(I);
     const int cpe = I / 16;                         // chunks per expert
     const int nch = K * cpe;
@@ -242,6 +239,13 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
         wk[k] = k < K ? wk[k] : 0.f;
         if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
     }
+    float v[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        chunk16_f32(hc[j], MOE_F32, v[j]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[j][i]));   // materialised here
+    }
     const Geo g = make_geo(a.geo);
     const int RB = a.geo.rb;
     const int nblk = a.geo.nblk;
@@ -249,26 +253,18 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     DLoads<NJ, RG, KM> L;
     if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, RB, a.pt, L);
 
-    // 2. stage h of every expert in its code width's layout.  The first pass is straight-line code
-    //    (the chunks loaded above), so the weight loads just issued stay in flight meanwhile.
+    // 2. stage h of every expert in its code width's digit-plane order.  The first pass works on
+    //    registers only, so the weight loads just issued stay in flight meanwhile.
     auto stage = [&](int m, const float (&vv)[16]) {
-        float sum = 0.f;
-        int kk = 0, mm = 0;
-        if (m < nch) {
-            kk = m / cpe;
-            mm = m - kk * cpe;
-            uint32_t *hi = lds + kk * per, *lo = hi + I / 2;
-            sum = ((two_mask >> kk) & 1u) ? write_chunk<2, true>(mm, vv, hi, lo) : write_chunk<4, true>(mm, vv, hi, lo);
-        }
-        sum += dppf<0xB1>(sum);
-        if (m < nch && !(mm & 1)) ((float *)(lds + kk * per + I))[mm >> 1] = sum;
+        const bool valid = m < nch;
+        const int kk = valid ? m / cpe : 0;
+        const int mm = m - kk * cpe;
+        uint32_t *d = lds + kk * per;
+        const bool two = (two_mask >> kk) & 1u;
+        stage_chunk(mm, valid, vv, two ? nullptr : d, two ? d : nullptr, (float2 *)(d + I / 2));
     };
-    float v[2][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        chunk16_f32(hc[j], MOE_F32, v[j]);
-        stage(threadIdx.x + kBlock * j, v[j]);
-    }
+    for (int j = 0; j < 2; ++j) stage(threadIdx.x + kBlock * j, v[j]);
     for (int base = 2 * kBlock; base < nch; base += 2 * kBlock) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -285,6 +281,7 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
 
     // 3. units: all experts of a block of output rows
     const char *res = a.residual ? (const char *)a.residual + (size_t)t * a.residual_stride * (a.residual_dtype == MOE_BF16 ? 2 : 4) : nullptr;
+    const bool bad = a.err && err_word != 0;
     bool first = true;
     for (; u < nblk; u += gridDim.x * kWaves) {
         const int r0 = u * RB;
@@ -300,28 +297,20 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
 #pragma unroll
             for (int gi = 0; gi < RG; ++gi) part[gi] = 0.f;
             if (sel[k]) {
-                const uint32_t *hi = lds + k * per;
-                const ActView av{hi, hi + I / 2, (const float *)(hi + I)};
+                const uint32_t *d = lds + k * per;
+                const ActView av{d, (const float2 *)(d + I / 2)};
                 const bool two = sel_bits(sel[k]) == 2;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
+                    // idle lanes (slot past the row) read clamped codes against zero operands
                     const int slot = g.lsl + 64 * j;
-                    const bool ok = slot < g.spr;
-                    const int ss = ok ? slot : 0;
-                    uint32_t X[kDPS], XL[kDPS];
-#pragma unroll
-                    for (int i = 0; i < kDPS; i += 4) {
-                        const u32x4 h = *(const u32x4 *)(av.hi + ss * kDPS + i);
-                        const u32x4 l = *(const u32x4 *)(av.lo + ss * kDPS + i);
-                        // idle lanes (slot past the row) read clamped codes: zero operands
-                        X[i] = ok ? h.x : 0u; X[i + 1] = ok ? h.y : 0u; X[i + 2] = ok ? h.z : 0u; X[i + 3] = ok ? h.w : 0u;
-                        XL[i] = ok ? l.x : 0u; XL[i + 1] = ok ? l.y : 0u; XL[i + 2] = ok ? l.z : 0u; XL[i + 3] = ok ? l.w : 0u;
-                    }
-                    const float xsv = ok ? av.xs[ss] : 0.f;
+                    uint32_t D[kSlotDw];
+                    float2 xsv;
+                    load_act_slot(av, slot, slot < g.spr, D, xsv);
 #pragma unroll
                     for (int gi = 0; gi < RG; ++gi)
-                        part[gi] += two ? slot_dot<2, true>(L.q[k][gi][j], X, XL, L.sb[k][gi][j], xsv)
-                                        : slot_dot<4, true>(L.q[k][gi][j], X, XL, L.sb[k][gi][j], xsv);
+                        part[gi] += two ? slot_dot<2>(L.q[k][gi][j], D, L.sb[k][gi][j], xsv)
+                                        : slot_dot<4>(L.q[k][gi][j], D, L.sb[k][gi][j], xsv);
                 }
             }
             if (COMBINE) {
@@ -406,7 +395,7 @@ PlaneTable plane_table(int H, int I) {
     }
     return t;
 }
-size_t gateup_lds_bytes(int H) { return ((size_t)2 * H + H / 32) * 4; }
+size_t gateup_lds_bytes(int H) { return ((size_t)H + H / 16) * 4; }   // both orders + xs
 size_t down_lds_bytes(int I, int K) { return (size_t)K * down_lds_per_expert(I) * 4; }
 
 static hipError_t set_lds(const void *fn, size_t lds) {
@@ -435,30 +424,29 @@ hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int NJ, bool SPLIT, int NP>
+template <int NJ, int NP>
 static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s, const KernelEvents &ev) {
     const int units = a.K * a.geo.nblk;
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = gateup_lds_bytes(a.H);
-    auto fn = k_gateup<NJ, SPLIT, NP>;
+    auto fn = k_gateup<NJ, NP>;
     if (hipError_t e = set_lds((const void *)fn, lds)) return e;
     return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
-template <int NJ, bool SPLIT>
+template <int NJ>
 static hipError_t gateup_impl(const GateUpLaunch &a, hipStream_t s, const KernelEvents &ev) {
-    return a.E <= 512 ? gateup_impl_np<NJ, SPLIT, 8>(a, s, ev) : gateup_impl_np<NJ, SPLIT, 32>(a, s, ev);
+    return a.E <= 512 ? gateup_impl_np<NJ, 8>(a, s, ev) : gateup_impl_np<NJ, 32>(a, s, ev);
 }
 
 hipError_t launch_gateup(const GateUpLaunch &a_in, hipStream_t s, const KernelEvents &ev) {
     GateUpLaunch a = a_in;
     a.geo = gateup_geo(a.H, a.I);
     a.pt = plane_table(a.H, a.I);
-    const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
     switch (nj_for(a.H)) {
-        case 1: return split ? gateup_impl<1, true>(a, s, ev) : gateup_impl<1, false>(a, s, ev);
-        case 2: return split ? gateup_impl<2, true>(a, s, ev) : gateup_impl<2, false>(a, s, ev);
-        default: return split ? gateup_impl<4, true>(a, s, ev) : gateup_impl<4, false>(a, s, ev);
+        case 1: return gateup_impl<1>(a, s, ev);
+        case 2: return gateup_impl<2>(a, s, ev);
+        default: return gateup_impl<4>(a, s, ev);
     }
 }
 

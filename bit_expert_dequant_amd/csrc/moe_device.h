@@ -1,5 +1,5 @@
 // moe_device.h -- device-side building blocks shared by the decode kernels (moe_decode.hip) and the
-// fused one-launch layer kernel (moe_layer.hip): activation staging, in-register dequant dot
+// router + gate/up layer kernel (moe_layer.hip): activation staging, in-register dequant dot
 // products, the wave top-K, and the per-unit load/compute steps of the gate/up and down phases.
 // Everything lives in an unnamed namespace, so each translation unit gets its own copy.
 #pragma once
@@ -20,10 +20,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both 16-bit halves
 constexpr int kBlock = 256;               // threads per workgroup (4 wavefronts)
 constexpr int kWaves = kBlock / 64;
-constexpr int kDPS = 16;                  // activation dwords per slot (32 columns, bf16 pairs)
 constexpr int kTabMax = 512;              // experts whose descriptors are prefetched into LDS
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -98,10 +96,24 @@ __device__ __forceinline__ uint64_t lookup_sel(int e, int E, bool use_tab, const
 }
 
 // --------------------------------------------------------------------------- activation staging
-// A thread stages "chunks" of 16 consecutive columns (two chunks per 32-column slot).
-// Slot s: 4-bit dword s*16 + 4k + i packs columns (8k+i, 8k+i+4), k < 4, i < 4; 2-bit dword
-// s*16 + 8k + i packs (16k+i, 16k+i+8), k < 2, i < 8.  Chunk m = 2s + half therefore owns the 8
-// contiguous dwords s*16 + 8*half .. +8 of both layouts.
+// An activation vector is held in LDS as 16-bit fixed point per 32-column slot: column c of slot s
+// is X_c * sx_s, with X_c an integer in [-kXMax, kXMax] and sx_s = (largest |x| of the slot) / kXMax,
+// plus the slot's exact fp32 sum of x for the bias term.  X is kept as four balanced base-16 digits,
+// X = d0 + 16 d1 + 256 d2 + 4096 d3 with every d_p in [-8, 7] (kXMax is the largest X four such
+// digits reach), and digit p of eight columns is one dword of 4-bit two's-complement nibbles.  A
+// dword of eight weight codes then meets one such "plane" dword per v_dot8_i32_i4, which does eight
+// multiply-adds in the time a bf16 dot2 does two.
+//
+// Slot layout (kSlotDw dwords): plane p occupies dwords 4p .. 4p+3.  4-bit order: dword 4p + j holds
+// columns 8j .. 8j+7 (nibble n = column 8j+n), matching code dword j of the slot.  2-bit order: dword
+// 4p + 2j + e holds columns 16j + 2n + e (n < 8), matching the even (e = 0) and odd (e = 1) codes of
+// code dword j once they are spread to nibbles.  A thread stages one 16-column chunk m = 2s + h;
+// in both orders it owns dwords 4p + 2h and 4p + 2h + 1 of every plane.
+//
+// Precision: a column's rounding error is at most sx/2, 2^-16 of the slot's largest |x|.
+constexpr int kSlotDw = 16;
+constexpr float kXMax = 30583.f;
+
 // A chunk of 16 consecutive activations (32 bytes of bf16 or 64 of fp32) is loaded in two steps:
 // issue_chunk16 starts four 16-byte loads with no data-dependent branch (bf16 repeats its second
 // load), chunk16_f32 converts once the data is needed.  Keeping the conversion out of the issue
@@ -130,72 +142,135 @@ __device__ __forceinline__ void chunk16_f32(const Chunk16 &c, int dtype, float v
     }
 }
 
-// Writes chunk m's dwords of one layout (BITS) and returns the chunk's sum of hi + lo.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ float write_chunk(int m, const float v[16], uint32_t *hi, uint32_t *lo) {
-    uint32_t hv[16], lv[16];
-    float sum = 0.f;
+// Plane dwords of eight columns.  y[n] = X_n + 0x8888, whose hex digits are the balanced digits
+// plus 8; out[p] nibble n = digit p of column n in two's complement (hex digit XOR 8).
+__device__ __forceinline__ void planes8(const uint32_t (&y)[8], uint32_t (&out)[4]) {
+    uint32_t P[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        hv[i] = bf16_rne(v[i]);
-        lv[i] = SPLIT ? bf16_rne(v[i] - bf16_f32(hv[i])) : 0u;
-        sum += bf16_f32(hv[i]) + (SPLIT ? bf16_f32(lv[i]) : 0.f);
-    }
-    uint32_t H[8], L[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int a = BITS == 4 ? (j >> 2) * 8 + (j & 3) : j;
-        const int b = a + (BITS == 4 ? 4 : 8);
-        H[j] = hv[a] | (hv[b] << 16);
-        L[j] = lv[a] | (lv[b] << 16);
-    }
-    const int d0 = (m >> 1) * kDPS + 8 * (m & 1);
-    *(u32x4 *)(hi + d0) = u32x4{H[0], H[1], H[2], H[3]};
-    *(u32x4 *)(hi + d0 + 4) = u32x4{H[4], H[5], H[6], H[7]};
-    if (SPLIT) {
-        *(u32x4 *)(lo + d0) = u32x4{L[0], L[1], L[2], L[3]};
-        *(u32x4 *)(lo + d0 + 4) = u32x4{L[4], L[5], L[6], L[7]};
-    }
-    return sum;
+    for (int a = 0; a < 4; ++a) P[a] = y[a] | (y[a + 4] << 16);   // columns a and a+4
+    // digits 0/1 (low byte of each column) and 2/3 (high byte) of the even and odd columns:
+    // byte i of e01 = low byte of column 2i, etc.
+    const uint32_t e01 = __builtin_amdgcn_perm(P[2], P[0], 0x06020400u);
+    const uint32_t o01 = __builtin_amdgcn_perm(P[3], P[1], 0x06020400u);
+    const uint32_t e23 = __builtin_amdgcn_perm(P[2], P[0], 0x07030501u);
+    const uint32_t o23 = __builtin_amdgcn_perm(P[3], P[1], 0x07030501u);
+    constexpr uint32_t lo = 0x0F0F0F0Fu;
+    out[0] = ((e01 & lo) | ((o01 << 4) & ~lo)) ^ 0x88888888u;
+    out[1] = (((e01 >> 4) & lo) | (o01 & ~lo)) ^ 0x88888888u;
+    out[2] = ((e23 & lo) | ((o23 << 4) & ~lo)) ^ 0x88888888u;
+    out[3] = (((e23 >> 4) & lo) | (o23 & ~lo)) ^ 0x88888888u;
 }
 
-struct ActView {
-    const uint32_t *hi, *lo;  // [cols/2] packed bf16 pairs (lo: bf16 of the remainder)
-    const float *xs;          // [cols/32] sum over the slot of hi + lo
-};
-
-// --------------------------------------------------------------------------- slot dot products
-// s * sum(q x) + b * sum(x) over one slot, given its codes and (scale, bias) dword.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t *X, const uint32_t *XL, uint32_t sb,
-                                          float xs) {
-    float a0 = 0.f, a1 = 0.f, l0 = 0.f, l1 = 0.f;
-    constexpr int NW = BITS == 4 ? 4 : 2;     // code dwords per slot
-    constexpr int PW = BITS == 4 ? 4 : 8;     // pairs per dword
+// Stages chunk m (columns v[0..15]) into the 4-bit order at d4 and/or the 2-bit order at d2 (a
+// null pointer skips that order) and, from the slot's even chunk, writes xs[s] = {sx, sum of x}.
+// Every lane of the wave calls it together: the slot's two chunks sit in lanes l and l^1 and meet
+// through DPP.  A lane with !valid takes part in the exchange only.
+__device__ __forceinline__ void stage_chunk(int m, bool valid, const float (&v)[16], uint32_t *d4, uint32_t *d2,
+                                            float2 *xs) {
+    float mx = 0.f, sum = 0.f;
+    if (valid) {
 #pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const uint32_t v = q[k];
-#pragma unroll
-        for (int i = 0; i < PW; ++i) {
-            const uint32_t p = BITS == 4 ? (((v >> (4 * i)) & 0x000F000Fu) | kMagic)
-                                         : (((v >> (2 * i)) & 0x00030003u) | kMagic);
-            const int d = k * PW + i;
-            if (d & 1) a1 = dot2(p, X[d], a1); else a0 = dot2(p, X[d], a0);
-            if (SPLIT) { if (d & 1) l1 = dot2(p, XL[d], l1); else l0 = dot2(p, XL[d], l0); }
+        for (int i = 0; i < 16; ++i) {
+            mx = fmaxf(mx, fabsf(v[i]));
+            sum += v[i];
         }
     }
-    const float acc = SPLIT ? (a0 + a1) + (l0 + l1) : a0 + a1;
+    mx = fmaxf(mx, dppf<0xB1>(mx));
+    sum += dppf<0xB1>(sum);
+    if (!valid) return;
+    int ex = 0;
+    const float mant = frexpf(mx, &ex);                    // mx = mant * 2^ex, mant in [0.5, 1)
+    const float f = mx > 0.f ? kXMax / mant : 0.f;         // X = round(x * 2^-ex * f)
+    uint32_t y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        // 1.5 * 2^23 + X rounds to the nearest integer in one fma; its bits are 0x4B400000 + X
+        const float t = fmaf(ldexpf(v[i], -ex), f, 12582912.f);
+        y[i] = __float_as_uint(t) - (0x4B400000u - 0x8888u);
+    }
+    const int h = m & 1;
+    uint32_t *base4 = d4 ? d4 + (m >> 1) * kSlotDw + 2 * h : nullptr;
+    uint32_t *base2 = d2 ? d2 + (m >> 1) * kSlotDw + 2 * h : nullptr;
+    if (base4) {
+        uint32_t a[8], b[8], pa[4], pb[4];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) { a[n] = y[n]; b[n] = y[8 + n]; }
+        planes8(a, pa);
+        planes8(b, pb);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) *(u32x2 *)(base4 + 4 * p) = u32x2{pa[p], pb[p]};
+    }
+    if (base2) {
+        uint32_t a[8], b[8], pa[4], pb[4];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) { a[n] = y[2 * n]; b[n] = y[2 * n + 1]; }
+        planes8(a, pa);
+        planes8(b, pb);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) *(u32x2 *)(base2 + 4 * p) = u32x2{pa[p], pb[p]};
+    }
+    if (!h) xs[m >> 1] = float2{mant > 0.f ? ldexpf(mant / kXMax, ex) : 0.f, sum};
+}
+
+// One code width's view of a staged activation vector.
+struct ActView {
+    const uint32_t *d;   // [cols/32][kSlotDw] digit planes in that width's order
+    const float2 *xs;    // [cols/32] {sx, sum of x}
+};
+
+// Loads slot ss of a view into registers (zeros when !ok: an idle lane's slot adds nothing).
+__device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok, uint32_t (&D)[kSlotDw], float2 &xs) {
+    const int s = ok ? ss : 0;
+#pragma unroll
+    for (int i = 0; i < kSlotDw; i += 4) {
+        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + i);
+        D[i] = ok ? d.x : 0u; D[i + 1] = ok ? d.y : 0u; D[i + 2] = ok ? d.z : 0u; D[i + 3] = ok ? d.w : 0u;
+    }
+    const float2 t = av.xs[s];
+    xs = ok ? t : float2{0.f, 0.f};
+}
+
+// --------------------------------------------------------------------------- slot dot products
+// s * sum(q x) + b * sum(x) over one slot, given its codes, (scale, bias) dword and staged
+// activation.  4-bit codes enter v_dot8_i32_i4 as q - 8 (the code XOR 8 read as a signed nibble),
+// so the bias becomes b + 8 s; 2-bit codes spread to nibbles are already in [0, 3].  Per plane
+// the integer sums are at most 32 * 8 * 8, so the combined sum is exact in int32 and in fp32.
+template <int BITS>
+__device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
+    int A[4] = {0, 0, 0, 0};
+    if (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = (int)(q[j] ^ 0x88888888u);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) A[p] = __builtin_amdgcn_sdot8(c, (int)D[4 * p + j], A[p], false);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e0 = (int)(q[j] & 0x33333333u), e1 = (int)((q[j] >> 2) & 0x33333333u);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                A[p] = __builtin_amdgcn_sdot8(e0, (int)D[4 * p + 2 * j], A[p], false);
+                A[p] = __builtin_amdgcn_sdot8(e1, (int)D[4 * p + 2 * j + 1], A[p], false);
+            }
+        }
+    }
+    const int acc = A[0] + A[1] * 16 + A[2] * 256 + A[3] * 4096;
     const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
-    return s * acc + (b - 128.f * s) * xs;
+    const float bb = BITS == 4 ? fmaf(8.f, s, b) : b;
+    return fmaf(s * xs.x, (float)acc, bb * xs.y);
 }
 
 typedef const GLOBAL_AS uint8_t *gbytes;
 typedef const GLOBAL_AS uint32_t *gwords;
 
+// Weight bytes are read once per step, so they are loaded non-temporally: streaming them must not
+// push the kernels' code, the activations and the descriptor tables out of the L2.
 template <int BITS>
 __device__ __forceinline__ u32x4 load_slot(gbytes row, int slot) {
-    if (BITS == 4) return *(const GLOBAL_AS u32x4 *)(row + (size_t)slot * 16);
-    const u32x2 v = *(const GLOBAL_AS u32x2 *)(row + (size_t)slot * 8);
+    if (BITS == 4) return __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)slot * 16));
+    const u32x2 v = __builtin_nontemporal_load((const GLOBAL_AS u32x2 *)(row + (size_t)slot * 8));
     return u32x4{v.x, v.y, 0u, 0u};
 }
 
@@ -388,7 +463,7 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
 #pragma unroll
     for (int j = 0; j < kRouterBatch; ++j) {
         const int c = min((lane + 64 * j) * EPL, H - EPL);       // clamped; unused lanes ignore it
-        wv[j] = *(const GLOBAL_AS u32x4 *)(row + (size_t)c * EB);
+        wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
     }
     // 2. activation (+ RMSNorm) into LDS
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
@@ -459,7 +534,7 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
 #pragma unroll
             for (int j = 0; j < kRouterBatch; ++j) {
                 const int c = min((lane + 64 * (base + j)) * EPL, H - EPL);
-                wv[j] = *(const GLOBAL_AS u32x4 *)(row + (size_t)c * EB);
+                wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
             }
         }
 #pragma unroll
@@ -517,40 +592,29 @@ __device__ __forceinline__ void gu_issue(const Planes *pl, const Geo &g, int H, 
             L.qg[gi][j] = load_slot<BITS>(pl[0].q + (size_t)r * rowb, slot);
             L.qu[gi][j] = load_slot<BITS>(pl[1].q + (size_t)r * rowb, slot);
             const size_t sbi = (size_t)r * G + (slot >> 1);
-            L.sg[gi][j] = pl[0].sb[sbi];
-            L.su[gi][j] = pl[1].sb[sbi];
+            L.sg[gi][j] = __builtin_nontemporal_load(pl[0].sb + sbi);
+            L.su[gi][j] = __builtin_nontemporal_load(pl[1].sb + sbi);
         }
     }
 }
 
-template <int BITS, int NJ, int RG, bool SPLIT>
+template <int BITS, int NJ, int RG>
 __device__ __forceinline__ void gu_finish(const Geo &g, int I, int r0, int RB, const ActView &av,
                                           const GULoads<NJ, RG> &L, float *hout) {
-    uint32_t X[NJ][kDPS], XL[NJ][SPLIT ? kDPS : 1];
-    float XS[NJ];
+    uint32_t D[NJ][kSlotDw];
+    float2 XS[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int slot = g.lsl + 64 * j;
-        const bool ok = slot < g.spr;
-        const int ss = ok ? slot : 0;
-#pragma unroll
-        for (int i = 0; i < kDPS; i += 4) {
-            const u32x4 h = *(const u32x4 *)(av.hi + ss * kDPS + i);
-            X[j][i] = ok ? h.x : 0u; X[j][i + 1] = ok ? h.y : 0u; X[j][i + 2] = ok ? h.z : 0u; X[j][i + 3] = ok ? h.w : 0u;
-            if (SPLIT) {
-                const u32x4 l = *(const u32x4 *)(av.lo + ss * kDPS + i);
-                XL[j][i] = ok ? l.x : 0u; XL[j][i + 1] = ok ? l.y : 0u; XL[j][i + 2] = ok ? l.z : 0u; XL[j][i + 3] = ok ? l.w : 0u;
-            }
-        }
-        XS[j] = ok ? av.xs[ss] : 0.f;
+        load_act_slot(av, slot, slot < g.spr, D[j], XS[j]);
     }
 #pragma unroll
     for (int gi = 0; gi < RG; ++gi) {
         float pg = 0.f, pu = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            pg += slot_dot<BITS, SPLIT>(L.qg[gi][j], X[j], XL[j], L.sg[gi][j], XS[j]);
-            pu += slot_dot<BITS, SPLIT>(L.qu[gi][j], X[j], XL[j], L.su[gi][j], XS[j]);
+            pg += slot_dot<BITS>(L.qg[gi][j], D[j], L.sg[gi][j], XS[j]);
+            pu += slot_dot<BITS>(L.qu[gi][j], D[j], L.su[gi][j], XS[j]);
         }
         pg = group_sum(pg, g.gsz);
         pu = group_sum(pu, g.gsz);
@@ -581,7 +645,7 @@ __device__ __forceinline__ void dn_issue(const Planes &pl, const Geo &g, int H, 
         for (int j = 0; j < NJ; ++j) {
             const int slot = min(g.lsl + 64 * j, g.spr - 1);
             L.q[k][gi][j] = load_slot<BITS>(pl.q + (size_t)r * rowb, slot);
-            L.sb[k][gi][j] = pl.sb[(size_t)r * G + (slot >> 1)];
+            L.sb[k][gi][j] = __builtin_nontemporal_load(pl.sb + ((size_t)r * G + (slot >> 1)));
         }
     }
 }
@@ -601,8 +665,9 @@ __device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, c
     }
 }
 
-// LDS per expert: hi [I/2], lo [I/2], xs [I/32].
-__host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I + ((I / 32 + 3) & ~3); }
+// LDS dwords per expert: digit planes [I/32][kSlotDw] in the expert's code width's order, then
+// xs [I/32] float2 (I is a multiple of 64, so every part stays 16-byte aligned).
+__host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I / 2 + I / 16; }
 
 int nj_for(int cols) {
     const int spr = cols / 32;

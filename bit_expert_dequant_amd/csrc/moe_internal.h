@@ -129,7 +129,7 @@ struct LayerLaunch {
     uint64_t *sel_ws; float *w_ws;                 // [K] selections and weights for the down kernel
     float *h;                                      // [K][I] SwiGLU outputs
     int H, I, E, K;
-    int split;                                     // activation not exactly bf16: hi/lo split
+    int split;                                     // router activation not exactly bf16: hi/lo split
     const uint32_t *seq;                           // launch counter (advanced by the down kernel)
     uint64_t *slots;                               // [layer_logit_copies()][E] tag << 32 | logit bits
     uint32_t *err;                                 // timed-out waits (nonzero: the down kernel writes NaN)

@@ -121,7 +121,7 @@ __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_
 }
 
 // ----------------------------------------------------------------------------------- gate/up
-template <int NJ, bool SPLIT, int NP>
+template <int NJ, int NP>
 __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32_t *lds, uint64_t *s_tab, float *red,
                                              uint32_t seq) {
     constexpr int RG = gu_rg<NJ>();
@@ -181,20 +181,14 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[j][i] *= inv;
     }
-    uint32_t *h4 = act, *l4 = act + H / 2, *h2 = act + H, *l2 = act + 3 * H / 2;
-    float *xs = (float *)(act + 2 * H);
+    uint32_t *d4 = act, *d2 = act + H / 2;
+    float2 *xs = (float2 *)(act + H);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int m = threadIdx.x + kBlock * j;
-        float sum = 0.f;
-        if (m < nch) {
-            sum = write_chunk<4, SPLIT>(m, v[j], h4, l4);
-            write_chunk<2, SPLIT>(m, v[j], h2, l2);
-        }
-        sum += dppf<0xB1>(sum);
-        if (m < nch && !(m & 1)) xs[m >> 1] = sum;
+        stage_chunk(m, m < nch, v[j], d4, d2, xs);
     }
-    const ActView v4{h4, l4, xs}, v2{h2, l2, xs};
+    const ActView v4{d4, xs}, v2{d2, xs};
 
     // 3. wave 0 waits for this launch's logits and copies them to LDS; the barrier publishes the
     //    logits, the table and the layouts
@@ -242,8 +236,8 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
         }
-        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG, SPLIT>(g, I, r0, RB, v2, L, hout);
-        else gu_finish<4, NJ, RG, SPLIT>(g, I, r0, RB, v4, L, hout);
+        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
+        else gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
     }
 }
 
@@ -262,8 +256,7 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
     if (b < a.nr) {
         router_phase(a, b, lds, red, seq);
     } else {
-        if (a.split) gateup_phase<NJ, true, NP>(a, b - a.nr, lds, s_tab, red, seq);
-        else gateup_phase<NJ, false, NP>(a, b - a.nr, lds, s_tab, red, seq);
+        gateup_phase<NJ, NP>(a, b - a.nr, lds, s_tab, red, seq);
     }
 }
 
