@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     const int nblk = a.geo.nblk;
     int u = blockIdx.x * kWaves + wave;
     DLoads<NJ, RG, KM> L;
-    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, RB, a.pt, L);
+    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, a.pt, L);
 
     // 2. stage h of every expert in its code width's digit-plane order.  The first pass works on
     //    registers only, so the weight loads just issued stay in flight meanwhile.
@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     bool first = true;
     for (; u < nblk; u += gridDim.x * kWaves) {
         const int r0 = u * RB;
-        if (!first) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, r0, RB, a.pt, L);
+        if (!first) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, r0, a.pt, L);
         first = false;
         float acc[RG];
 #pragma unroll

@@ -633,35 +633,46 @@ struct DLoads {
     uint32_t sb[KM][RG][NJ];
 };
 
-template <int BITS, int NJ, int RG, int KM>
-__device__ __forceinline__ void dn_issue(const Planes &pl, const Geo &g, int H, int I, int r0, int RB, int k,
+// Loads of one expert's down rows for one unit.  The code width is a run-time value and every slot
+// is read as 16 bytes (a 2-bit slot uses the first 8; the extra 8 stay inside the blob, since a
+// scale/bias plane follows every code plane), so the loads of all experts issue without a branch
+// and the arithmetic on the first expert waits for its own loads only.
+template <int NJ, int RG, int KM>
+__device__ __forceinline__ void dn_issue(const Planes &pl, int bits, const Geo &g, int H, int I, int r0, int k,
                                          DLoads<NJ, RG, KM> &L) {
     const int G = I / 64;
-    const size_t rowb = (size_t)I * BITS / 8;
+    const size_t rowb = (size_t)I * bits / 8;
+    const int ssh = bits == 4 ? 4 : 3;
 #pragma unroll
     for (int gi = 0; gi < RG; ++gi) {
         const int r = min(r0 + gi * g.rpi + g.lrow, H - 1);     // clamped; see gu_issue
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int slot = min(g.lsl + 64 * j, g.spr - 1);
-            L.q[k][gi][j] = load_slot<BITS>(pl.q + (size_t)r * rowb, slot);
+            L.q[k][gi][j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(pl.q + (size_t)r * rowb + ((size_t)slot << ssh)));
             L.sb[k][gi][j] = __builtin_nontemporal_load(pl.sb + ((size_t)r * G + (slot >> 1)));
         }
     }
 }
 
-// Issue every selected expert's loads for one unit (output rows r0..r0+RB-1).
+// Issue every selected expert's loads for one unit (output rows r0..r0+RB-1) as straight-line
+// code.  Slots past K and absent experts (sel 0) read a present expert's rows instead (their
+// results are never used), so no branch separates the loads from the arithmetic; with no expert
+// present at all nothing is loaded.
 template <int NJ, int RG, int KM>
 __device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, const Geo &g, int H, int I, int r0,
-                                             int RB, const PlaneTable &pt, DLoads<NJ, RG, KM> &L) {
+                                             const PlaneTable &pt, DLoads<NJ, RG, KM> &L) {
+    uint64_t any = 0;
+#pragma unroll
+    for (int k = KM - 1; k >= 0; --k)
+        if (k < K && sel[k]) any = sel[k];
+    if (!any) return;
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-        if (k < K && sel[k]) {
-            Planes pl[3];
-            expert_planes(sel_blob(sel[k]), sel_bits(sel[k]), pt, pl);
-            if (sel_bits(sel[k]) == 2) dn_issue<2, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
-            else dn_issue<4, NJ, RG, KM>(pl[2], g, H, I, r0, RB, k, L);
-        }
+        const uint64_t sk = (k < K && sel[k]) ? sel[k] : any;
+        Planes pl[3];
+        expert_planes(sel_blob(sk), sel_bits(sk), pt, pl);
+        dn_issue<NJ, RG, KM>(pl[2], sel_bits(sk), g, H, I, r0, k, L);
     }
 }
 

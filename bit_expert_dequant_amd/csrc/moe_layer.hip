@@ -227,17 +227,20 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         const int r0 = (u - k * nblk) * RB;
         float *hout = a.h + (size_t)k * I;
         sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
-        if (sel) {
-            expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
-            if (sel_bits(sel) == 2) gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
-            else gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
-        }
         if (!sel) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
         }
-        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
-        else gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
+        // Loads and arithmetic of one code width sit in one branch, so the arithmetic on the first
+        // slots waits only for their own loads while the later ones are still arriving.
+        expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
+        if (sel_bits(sel) == 2) {
+            gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
+            gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
+        } else {
+            gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
+            gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
+        }
     }
 }
 
