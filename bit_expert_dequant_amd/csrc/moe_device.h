@@ -375,53 +375,108 @@ __device__ __forceinline__ Top2 top2_range(const uint32_t *key, uint32_t taken, 
     }
 }
 
-// `key`: this lane's NP keys (experts NP*lane + t).  Lane k < K returns selection k.
+// The K rounds.  `key`: this lane's NP keys (positions NP*lane + t of the wave).  Lane k < K
+// returns the k-th largest key and its position (equal keys: lower position first).
 template <int NP>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[NP], int K, int &my_idx, float &my_w) {
+__device__ __forceinline__ void wave_topk_core(const uint32_t (&key)[NP], int K, uint32_t &my_key, int &my_pos) {
     constexpr int FW = NP <= 8 ? 3 : 5;                            // bits per recorded slot
     typedef typename std::conditional<NP <= 8, uint32_t, uint64_t>::type rec_t;
     const int lane = threadIdx.x & 63;
     Top2 c = top2_range<NP>(key, 0u, 0);
-    uint32_t taken = 0, my_key = 0, top = 0;
+    uint32_t taken = 0;
+    my_key = 0;
     rec_t rec = 0;
     int my_wl = 0;
     uint64_t second_stale = 0;     // lanes whose second key was promoted and not yet recomputed
     for (int k = 0; k < K; ++k) {
         const uint32_t m = wave_max_all(c.h1);
-        top = k == 0 ? m : top;
         const int wl = __ffsll((unsigned long long)__ballot(c.h1 == m)) - 1;
         const bool me = lane == wl;
         rec |= me ? (rec_t)c.s1 << (FW * k) : (rec_t)0;
         taken |= me ? 1u << c.s1 : 0u;
         my_key = lane == k ? m : my_key;
         my_wl = lane == k ? wl : my_wl;
-        if ((second_stale >> wl) & 1ull) {
+        if (NP > 2 && ((second_stale >> wl) & 1ull)) {
             const Top2 r = top2_range<NP>(key, taken, 0);
             c.h1 = me ? r.h1 : c.h1; c.s1 = me ? r.s1 : c.s1;
             c.h2 = me ? r.h2 : c.h2; c.s2 = me ? r.s2 : c.s2;
             second_stale &= ~(1ull << wl);
         } else {
+            // with two keys a lane holds no third: after its second win it offers key 0
             c.h1 = me ? c.h2 : c.h1;
             c.s1 = me ? c.s2 : c.s1;
+            if (NP <= 2) c.h2 = me ? 0u : c.h2;
             second_stale |= 1ull << wl;
         }
     }
     rec_t r;
-    if constexpr (NP <= 8) {
+    if constexpr (NP == 1) {
+        r = 0;
+    } else if constexpr (NP <= 8) {
         r = (rec_t)__shfl((int)rec, my_wl);
     } else {
         r = (rec_t)(uint32_t)__shfl((int)(uint32_t)rec, my_wl) | ((rec_t)(uint32_t)__shfl((int)(uint32_t)(rec >> 32), my_wl) << 32);
     }
     const int slot = lane < K ? (int)((r >> (FW * lane)) & ((1u << FW) - 1)) : 0;
-    my_idx = my_wl * NP + slot;
-    // weights: softmax over the K selected logits, max-subtracted; the sum runs over lanes 0..7
-    const float val = key_logit(my_key), top0 = key_logit(top);
+    my_pos = my_wl * NP + slot;
+}
+
+// Routing weight of lane k < K (0 elsewhere): the softmax over the K selected logits,
+// max-subtracted (the largest is lane 0's), summed over lanes 0..7.
+__device__ __forceinline__ float topk_weight(uint32_t my_key, int K) {
+    const int lane = threadIdx.x & 63;
+    const float val = key_logit(my_key), top0 = key_logit(__builtin_amdgcn_readfirstlane(my_key));
     const float ex = lane < K ? (top0 > -INFINITY ? expf(val - top0) : 1.f) : 0.f;
     float z = ex;
     z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0xB1, 0xF, 0xF, true));
     z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x4E, 0xF, 0xF, true));
     z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x141, 0xF, 0xF, true));
-    my_w = ex / z;
+    return ex / z;
+}
+
+// One wave: lane k < K returns selection k (expert NP*lane + t layout) and its weight.
+template <int NP>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[NP], int K, int &my_idx, float &my_w) {
+    uint32_t mk;
+    wave_topk_core<NP>(key, K, mk, my_idx);
+    my_w = topk_weight(mk, K);
+}
+
+// A whole workgroup (kWaves waves, every wave gets the result): wave w takes experts
+// [w * 64 * NP/kWaves, (w+1) * 64 * NP/kWaves) from the logits in LDS and finds its own top K;
+// the kWaves * K candidates meet in LDS (wave-major, each wave's in rank order, so among equal
+// keys a lower candidate is a lower expert) and K rounds over one candidate per lane finish the
+// selection.  A quarter of the keys per wave and no recomputation make this several times
+// cheaper than one wave walking all E keys.  s_cand: 2 * kWaves * K dwords of LDS.  Contains a
+// barrier: the whole workgroup calls it.
+template <int NP>
+__device__ __forceinline__ void block_topk(const float *s_lg, int E, int K, uint32_t *s_cand, int &my_idx,
+                                           float &my_w) {
+    constexpr int NPW = NP / kWaves;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = wave * 64 * NPW;
+    uint32_t key[NPW];
+#pragma unroll
+    for (int t = 0; t < NPW; ++t) {
+        const int e = base + NPW * lane + t;
+        key[t] = e < E ? logit_key(s_lg[min(e, E - 1)]) : 0u;
+    }
+    uint32_t ck;
+    int cp;
+    wave_topk_core<NPW>(key, K, ck, cp);
+    const int nc = kWaves * K;
+    if (lane < K) {
+        s_cand[wave * K + lane] = ck;
+        s_cand[nc + wave * K + lane] = (uint32_t)(base + cp);
+    }
+    __syncthreads();
+    const uint32_t fk[1] = {lane < nc ? s_cand[lane] : 0u};
+    const int fi = lane < nc ? (int)s_cand[nc + lane] : 0;
+    uint32_t mk;
+    int pos;
+    wave_topk_core<1>(fk, K, mk, pos);
+    my_idx = __shfl(fi, pos);
+    my_w = topk_weight(mk, K);
 }
 
 // Keys of this lane's experts NP*lane .. NP*lane+NP-1 from a logit row (absent experts: 0).  The

@@ -94,17 +94,6 @@ __device__ bool wait_logits(const uint64_t *slots, int E, uint32_t tag, float *s
     return false;
 }
 
-// Keys of this lane's experts NP*lane .. +NP from the logits in LDS.
-template <int NP>
-__device__ __forceinline__ void lds_keys(const float *s_lg, int E, uint32_t (&key)[NP]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int t = 0; t < NP; ++t) {
-        const int e = NP * lane + t;
-        key[t] = e < E ? logit_key(s_lg[min(e, E - 1)]) : 0u;
-    }
-}
-
 // ----------------------------------------------------------------------------------- router
 __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_t *lds, float *red, uint32_t seq) {
     float lg = 0.f;
@@ -122,8 +111,8 @@ __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_
 
 // ----------------------------------------------------------------------------------- gate/up
 template <int NJ, int NP>
-__device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32_t *lds, uint64_t *s_tab, float *red,
-                                             uint32_t seq) {
+__device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32_t *lds, uint64_t *s_tab,
+                                             uint32_t *s_cand, float *red, uint32_t seq) {
     constexpr int RG = gu_rg<NJ>();
     const int H = a.H, I = a.I, E = a.E, K = a.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -195,14 +184,11 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
     if (wave == 0) wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, launch_tag(seq), s_lg, a.err);
     __syncthreads();
 
-    // 4. routing in registers (each wave, identical results)
+    // 4. routing: each wave takes a quarter of the logits, then the candidates meet in LDS (every
+    //    wave ends with the same selection in lanes 0..K-1)
     int my_idx = 0;
     float my_w = 0.f;
-    {
-        uint32_t key[NP];
-        lds_keys<NP>(s_lg, E, key);
-        wave_topk<NP>(key, K, my_idx, my_w);
-    }
+    block_topk<NP>(s_lg, E, K, s_cand, my_idx, my_w);
     if (gb == 0 && wave == 0 && lane < K) {
         if (a.idx_out) a.idx_out[lane] = my_idx;
         if (a.w_out) a.w_out[lane] = my_w;
@@ -250,6 +236,7 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ uint64_t s_tab[kTabMax];
     __shared__ float red[kWaves];
+    __shared__ uint32_t s_cand[2 * kWaves * MOE_MAX_TOPK];
     // The launch counter is loaded through an offset the compiler cannot prove uniform, so it stays
     // in a vector register and is waited for where the tag is first used, not here.
     int zero;
@@ -259,7 +246,7 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
     if (b < a.nr) {
         router_phase(a, b, lds, red, seq);
     } else {
-        gateup_phase<NJ, NP>(a, b - a.nr, lds, s_tab, red, seq);
+        gateup_phase<NJ, NP>(a, b - a.nr, lds, s_tab, s_cand, red, seq);
     }
 }
 

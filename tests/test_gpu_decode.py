@@ -249,6 +249,40 @@ def test_timed_decode_matches_untimed(separate):
     assert ws_error_word(ws) == 0
 
 
+@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+@pytest.mark.parametrize("E,K", [(40, 8), (512, 4), (700, 8), (2048, 3)])
+def test_layer_decode_routing_ties(E, K, separate):
+    """Routing inside moe_layer_decode on logits with exact ties, +0/-0, -inf and NaN: an fp32
+    router and a one-hot fp32 token make each logit equal to one router entry, so the selection
+    (equal logits -> lower index; NaN ranks as -inf) and the weights are fixed exactly."""
+    H, I = 64, 64
+    rng = np.random.default_rng(E + K)
+    col = rng.choice([-1.5, -0.0, 0.0, 0.25, 2.0, 3.0], size=E).astype(np.float32)
+    col[E // 3] = -np.inf
+    col[1] = np.nan
+    wl = small_workload("ties", 31 + E, H, I, E, K, 4, router_bf16=False, x_bf16=False)
+    dl = build_layer(wl)
+    router = np.zeros((E, H), dtype=np.float32)
+    router[:, 0] = col
+    L = M.Layer(torch.from_numpy(router).cuda(), dl.table)
+    x = torch.zeros(H, dtype=torch.float32, device="cuda")
+    x[0] = 1.0
+    d = M.make_dims(H, I, E, K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    out = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    for _ in range(2):                     # the second call reuses the workspace
+        M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, separate_kernels=separate)
+        torch.cuda.synchronize()
+        lg = col.astype(np.float64)
+        lg[np.isnan(lg)] = -np.inf
+        ri, rw, _ = oracle.route(lg, K)
+        assert list(idx.cpu().numpy()) == list(ri)
+        assert_close(w.cpu().numpy(), rw, "tie weights")
+    assert ws_error_word(ws) == 0
+
+
 @pytest.mark.parametrize("E", [40, 700])
 def test_route_ties_zeros_and_infinities(E):
     """Top-K on logits with exact ties, +0/-0 and -inf: an fp32 router and a one-hot fp32 token
