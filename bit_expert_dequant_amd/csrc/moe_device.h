@@ -501,26 +501,24 @@ constexpr int kRouterBatch = 8;
 // bf16 router: the activation is staged as bf16 pairs (columns 2i, 2i+1) plus the bf16 remainder
 // when it is not exactly bf16, so a 16-byte chunk of 8 weights meets one 16-byte LDS read per part
 // and four v_dot2_f32_bf16.  fp32 router: fp32 activation, float4 LDS reads, fp32 FMAs.
-// Logit of expert bx*4 + wave for token t (every lane of the wave returns it); false for a wave past
-// the last expert.  s_r: H*4 bytes of LDS (bf16: hi [H/2] + lo [H/2]; fp32: x [H]); red: kWaves floats.
-template <int RDT, bool SPLIT>
+// WPR waves share a row (each takes H/WPR consecutive columns; their sums meet in LDS in a fixed
+// order), so a workgroup covers kWaves/WPR experts: bx*(kWaves/WPR) + wave/WPR.  `logit` is that
+// expert's logit in every lane of every wave of the row; the return value is true for the row's
+// first wave when the expert exists.  s_r: H*4 bytes of LDS (bf16: hi [H/2] + lo [H/2]; fp32:
+// x [H]); red: kWaves floats.  Contains barriers: the whole workgroup calls it.
+template <int RDT, bool SPLIT, int WPR = 1>
 __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t, uint32_t *s_r, float *red,
                                            float &logit) {
     const int H = a.H;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = bx * kWaves + wave;
+    const int e = bx * (kWaves / WPR) + wave / WPR;
+    const int part = wave % WPR;
     constexpr int EB = RDT == MOE_BF16 ? 2 : 4;           // bytes per weight
     constexpr int EPL = 16 / EB;                          // weights per 16-byte load
-    const int nld = (H / EPL + 63) / 64;
+    const int cols = H / WPR, c0 = part * cols;           // this wave's columns
+    const int nld = (cols / EPL + 63) / 64;
     const GLOBAL_AS uint8_t *row = (const GLOBAL_AS uint8_t *)a.router + (size_t)(e < a.E ? e : 0) * H * EB;
-    // 1. first batch of this wave's row, issued before the activation arrives
-    u32x4 wv[kRouterBatch];
-#pragma unroll
-    for (int j = 0; j < kRouterBatch; ++j) {
-        const int c = min((lane + 64 * j) * EPL, H - EPL);       // clamped; unused lanes ignore it
-        wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
-    }
-    // 2. activation (+ RMSNorm) into LDS
+    // 1. activation (+ norm weight) first: its wait then does not include the row loads issued after
     const void *x = (const char *)a.x + (size_t)t * a.x_stride * (a.x_dtype == MOE_BF16 ? 2 : 4);
     const int nch = H / 16;
     Chunk16 xc[2], nc[2];
@@ -530,6 +528,14 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
         issue_chunk16(x, a.x_dtype, m, xc[j]);
         if (a.norm_w) issue_chunk16(a.norm_w, MOE_BF16, m, nc[j]);
     }
+    // 2. first batch of this wave's part of the row
+    u32x4 wv[kRouterBatch];
+#pragma unroll
+    for (int j = 0; j < kRouterBatch; ++j) {
+        const int c = c0 + min((lane + 64 * j) * EPL, cols - EPL);   // clamped; unused lanes ignore it
+        wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
+    }
+    // 3. activation (+ RMSNorm) into LDS
     float v[2][16];
     float ss = 0.f;
 #pragma unroll
@@ -581,41 +587,51 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
         }
     }
     __syncthreads();
-    if (e >= a.E) return false;
-    // 3. dot product, further batches for long rows
+    // 4. dot product over this wave's columns, further batches for long rows
     float acc = 0.f, acc2 = 0.f;
-    for (int base = 0; base < nld; base += kRouterBatch) {
-        if (base > 0) {
+    if (e < a.E) {
+        for (int base = 0; base < nld; base += kRouterBatch) {
+            if (base > 0) {
+#pragma unroll
+                for (int j = 0; j < kRouterBatch; ++j) {
+                    const int c = c0 + min((lane + 64 * (base + j)) * EPL, cols - EPL);
+                    wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
+                }
+            }
 #pragma unroll
             for (int j = 0; j < kRouterBatch; ++j) {
-                const int c = min((lane + 64 * (base + j)) * EPL, H - EPL);
-                wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
-            }
-        }
+                const int cl = (lane + 64 * (base + j)) * EPL;
+                const int c = c0 + cl;
+                if (base + j < nld && cl < cols) {
+                    if (RDT == MOE_BF16) {
+                        const u32x4 xh = *(const u32x4 *)(s_r + c / 2);
 #pragma unroll
-        for (int j = 0; j < kRouterBatch; ++j) {
-            const int c = (lane + 64 * (base + j)) * EPL;
-            if (base + j < nld && c < H) {
-                if (RDT == MOE_BF16) {
-                    const u32x4 xh = *(const u32x4 *)(s_r + c / 2);
+                        for (int q = 0; q < 4; ++q) acc = dot2(wv[j][q], xh[q], acc);
+                        if (SPLIT) {
+                            const u32x4 xl = *(const u32x4 *)(s_r + H / 2 + c / 2);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = dot2(wv[j][q], xh[q], acc);
-                    if (SPLIT) {
-                        const u32x4 xl = *(const u32x4 *)(s_r + H / 2 + c / 2);
+                            for (int q = 0; q < 4; ++q) acc2 = dot2(wv[j][q], xl[q], acc2);
+                        }
+                    } else {
+                        const u32x4 xf = *(const u32x4 *)((const float *)s_r + c);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc2 = dot2(wv[j][q], xl[q], acc2);
+                        for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(wv[j][q]), __uint_as_float(xf[q]), acc);
                     }
-                } else {
-                    const u32x4 xf = *(const u32x4 *)((const float *)s_r + c);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(wv[j][q]), __uint_as_float(xf[q]), acc);
                 }
             }
         }
     }
     acc = group_sum(acc + acc2, 64);
-    logit = acc + (a.logit_bias ? a.logit_bias[e] : 0.f);
-    return true;
+    if (WPR > 1) {
+        if (lane == 0) red[wave] = acc;
+        __syncthreads();
+        const int w0 = wave - part;
+        acc = red[w0];
+#pragma unroll
+        for (int q = 1; q < WPR; ++q) acc += red[w0 + q];
+    }
+    logit = acc + (e < a.E && a.logit_bias ? a.logit_bias[e] : 0.f);
+    return e < a.E && part == 0;
 }
 
 // --------------------------------------------------------------------------- gate/up + SwiGLU

@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kSpinLimit = 1 << 18;       // polls per wait (each at least one memory round trip)
 constexpr int kLogitCopies = 16;          // copies of the tagged logit row (<= 64)
+constexpr int kRouterWPR = 1;             // waves per router row (2 measured equal, 4 slower)
 
 __device__ __forceinline__ uint32_t ld_word(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -99,14 +100,14 @@ __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_
     float lg = 0.f;
     bool ok;
     if (a.r.router_dtype == MOE_BF16)
-        ok = a.split ? router_row<MOE_BF16, true>(a.r, b, 0, lds, red, lg)
-                     : router_row<MOE_BF16, false>(a.r, b, 0, lds, red, lg);
+        ok = a.split ? router_row<MOE_BF16, true, kRouterWPR>(a.r, b, 0, lds, red, lg)
+                     : router_row<MOE_BF16, false, kRouterWPR>(a.r, b, 0, lds, red, lg);
     else
-        ok = router_row<MOE_F32, false>(a.r, b, 0, lds, red, lg);
+        ok = router_row<MOE_F32, false, kRouterWPR>(a.r, b, 0, lds, red, lg);
     const int lane = threadIdx.x & 63;
+    const int e = b * (kWaves / kRouterWPR) + (threadIdx.x >> 6) / kRouterWPR;
     if (ok && lane < kLogitCopies)
-        publish_word64(a.slots + (size_t)lane * a.E + b * kWaves + (threadIdx.x >> 6),
-                       ((uint64_t)launch_tag(seq) << 32) | __float_as_uint(lg));
+        publish_word64(a.slots + (size_t)lane * a.E + e, ((uint64_t)launch_tag(seq) << 32) | __float_as_uint(lg));
 }
 
 // ----------------------------------------------------------------------------------- gate/up
@@ -272,7 +273,7 @@ hipError_t layer_nj(const LayerLaunch &a, size_t lds, hipStream_t s, const Kerne
 
 void layer_grid(int H, int I, int E, int K, int *nr, int *ng) {
     const RowGeo gg = gateup_geo(H, I);
-    *nr = (E + kWaves - 1) / kWaves;
+    *nr = (E * kRouterWPR + kWaves - 1) / kWaves;
     *ng = (K * gg.nblk + kWaves - 1) / kWaves;
 }
 
