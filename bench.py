@@ -82,6 +82,7 @@ def load_traffic(kernel: str, workload_key: str):
 
 
 COPY_BYTES = 1 << 30
+STREAM_BYTES = 4 << 30
 
 
 def copy_calibration():
@@ -318,6 +319,28 @@ def main():
         log(f"[bench] kernel us: {kernel_us}; three-kernel schedule: {kernel_us_3k}; "
             f"router + gate/up {achieved:,.1f} GB/s")
 
+    # measured read-stream reference: moe_stream_read over 4 GiB (best of 5 after 2 warm-ups)
+    sbuf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev)
+    sbuf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        M.moe_stream_read(sbuf, sink)
+    s_ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        M.moe_stream_read(sbuf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s_ms.append(e0.elapsed_time(e1))
+    del sbuf
+    stream_gbps = STREAM_BYTES / (min(s_ms) * 1e-3) / 1e9
+    stream = {"GBps": round(stream_gbps, 1), "bytes": STREAM_BYTES, "kernel": "moe_stream_read (16-byte non-temporal "
+              "loads from every CU)", "runs_ms": [round(x, 4) for x in s_ms]}
+    if roof is not None:
+        roof["frac_of_measured_stream"] = round(roof["achieved"] / stream_gbps, 4)
+    log(f"[bench] read stream {stream_gbps:,.1f} GB/s over {STREAM_BYTES >> 30} GiB")
+
     # CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     parity = None
@@ -379,6 +402,7 @@ def main():
         "config": cfg,
         "weight_bytes_per_step": bytes_per_step, "weight_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "stream_frac": round(gbps / stream_gbps, 4), "stream": stream,
         "kernel_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "kernel_us_three_kernel_schedule": {k: round(v, 3) for k, v in kernel_us_3k.items()},
         "roofline": roof, "cpu_baseline": cpu, "parity": parity,

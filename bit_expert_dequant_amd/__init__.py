@@ -80,6 +80,7 @@ def lib():
             "moe_combine": (I32, [P, P, I32, I32, I32, P, P, P]),
             "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
             "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
+            "moe_stream_read": (I32, [P, SZ, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -93,7 +94,7 @@ def exported_symbols() -> List[str]:
     return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
-            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed"]
+            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read"]
 
 
 def _check(status: int):
@@ -259,6 +260,12 @@ def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, 
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                   _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
+
+
+def moe_stream_read(buf, sink, stream=None) -> None:
+    """Read-stream reference (see moe_stream_read in the header): XOR of every dword of `buf`
+    (a contiguous device tensor, 16-byte aligned, size a multiple of 16 bytes) into sink[0]."""
+    _check(lib().moe_stream_read(_tptr(buf), buf.numel() * buf.element_size(), _tptr(sink), _stream(stream)))
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,

@@ -291,6 +291,14 @@ int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts) {
     return ok();
 }
 
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return fail(MOE_ERR_NULL, "buf and sink are required");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(MOE_ERR_ALIGN, "buf must be 16-byte, sink 4-byte aligned");
+    if (bytes == 0 || bytes % 16) return fail(MOE_ERR_SHAPE, "bytes=%zu is not a positive multiple of 16", bytes);
+    if (int s = launched(moe::launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream read")) return s;
+    return ok();
+}
+
 // ------------------------------------------------------------------------------- workspace
 size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers) {
     if (!dims || check_dims(dims) != MOE_OK || T < 1) return 0;

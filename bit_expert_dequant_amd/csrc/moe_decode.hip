@@ -339,6 +339,28 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     }
 }
 
+// Read-stream reference: every thread walks 16-byte chunks with a grid stride, four loads in
+// flight, and the XOR of all dwords lands in sink[0] (one atomic per wave).
+__global__ void __launch_bounds__(kBlock) k_stream_read(const u32x4 *p, size_t n16, uint32_t *sink) {
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(p + i));
+        const u32x4 b = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(p + i + stride));
+        const u32x4 c = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(p + i + 2 * stride));
+        const u32x4 d = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(p + i + 3 * stride));
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(p + i));
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+}
+
 __global__ void __launch_bounds__(kBlock) k_combine(CombineLaunch a) {
     const size_t n = (size_t)a.T * a.H;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
@@ -477,6 +499,15 @@ hipError_t launch_down(const DownLaunch &a_in, hipStream_t s, const KernelEvents
         case 2: return comb ? down_impl<2, true>(a, s, ev) : down_impl<2, false>(a, s, ev);
         default: return comb ? down_impl<4, true>(a, s, ev) : down_impl<4, false>(a, s, ev);
     }
+}
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s) {
+    int dev = 0, cus = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return e;
+    if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return e;
+    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)(cus * 8)), dim3(kBlock), 0, s, (const u32x4 *)buf, bytes / 16,
+                       sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {

@@ -147,4 +147,7 @@ struct CombineLaunch {
 };
 hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
 
+// Read-stream reference kernel (XOR of every dword of buf into *sink).
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
+
 }  // namespace moe

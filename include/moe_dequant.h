@@ -255,6 +255,19 @@ int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_
                            int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                            void *ws, size_t ws_bytes, void *stream, void *const *events);
 
+/* --------------------------------------------------------------------------- measurement */
+
+/* Read-stream reference for the HBM roofline, not part of the expert path: reads the `bytes`
+ * bytes at `buf` once with 16-byte non-temporal loads from every compute unit (the access
+ * pattern of the expert weight stream) and XORs every dword into *sink, one atomic per
+ * wavefront.  The benchmark times it over a buffer far larger than the caches to report the
+ * measured read bandwidth beside the nominal peak.
+ *   buf   device, 16-byte aligned, caller-owned
+ *   bytes a positive multiple of 16
+ *   sink  device uint32, 4-byte aligned; zero it first to get the XOR of the data
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_LAUNCH. */
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

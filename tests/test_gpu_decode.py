@@ -321,3 +321,17 @@ def test_route_ties_zeros_and_infinities(E):
     ri2, rw2, _ = oracle.route(lg2, K)
     assert list(idx.cpu().numpy()[0]) == list(ri2)
     assert np.all(np.isfinite(w.cpu().numpy()))
+
+
+def test_stream_read_xor():
+    """The read-stream reference reads every byte: its XOR of all dwords matches numpy's."""
+    rng = np.random.default_rng(5)
+    for n in (16, 4096, 1 << 20, (1 << 22) + 48):
+        host = rng.integers(0, 2**32, size=n // 4, dtype=np.uint32)
+        buf = torch.from_numpy(host.view(np.int32)).cuda()
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        M.moe_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host)), n
+    with pytest.raises(M.MoeError):        # 12 bytes: not a multiple of 16
+        M.moe_stream_read(torch.zeros(3, dtype=torch.int32, device="cuda"), sink)
