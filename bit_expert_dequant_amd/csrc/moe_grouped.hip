@@ -185,23 +185,42 @@ __global__ void __launch_bounds__(256) k_norm_rows(const void *x, int x_dtype, c
 }
 
 // --------------------------------------------------------------------------- shared GEMM pieces
-// Stage K columns [kc, kc+kKC) of the tile's tokens: each of the 256 threads converts 32 columns
-// of one token (hi, and lo when SPLIT) into the pair order of BITS and the token's group sums.
-// src(row, c) returns the fp32 activation of tile row `row` (< kTM) at column c.
-template <int BITS, bool SPLIT, typename F>
-__device__ __forceinline__ void stage_chunk(F src, int kc, int K, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
-    const int row = threadIdx.x >> 3, slot = threadIdx.x & 7;     // 32 rows x 8 slots of 32 columns
-    const int c0 = kc + 32 * slot;
-    float v[32];
+// Staging of K columns [kc, kc+kKC) of the tile's tokens: each of the 256 threads owns 32 columns
+// (one slot) of one token row.  The loads (16 bytes each: 4 for bf16, 8 for fp32, none for a row
+// that is absent or a slot past K) are issued by xload before the next chunk's weight loads, and
+// converted by xstage into the pair order of BITS (hi, and lo when SPLIT) plus the group sums.
+struct XChunk {
+    u32x4 q[8];
+};
+__device__ __forceinline__ void xload(const void *rowp, int dtype, int kc, int K, XChunk &xc) {
+    const int c0 = kc + 32 * (threadIdx.x & 7);
+    const bool ok = rowp != nullptr && c0 < K;                 // K is a multiple of 64: all or none
+    const int nb = dtype == MOE_BF16 ? 4 : 8;
+    const GLOBAL_AS u32x4 *p = (const GLOBAL_AS u32x4 *)((const char *)rowp + (size_t)c0 * (dtype == MOE_BF16 ? 2 : 4));
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = src(row, min(c0 + i, K - 1));
+    for (int i = 0; i < 8; ++i) xc.q[i] = (ok && i < nb) ? p[i] : u32x4{0u, 0u, 0u, 0u};
+}
+template <int BITS, bool SPLIT>
+__device__ __forceinline__ void xstage(const XChunk &xc, int dtype, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    const int row = threadIdx.x >> 3, slot = threadIdx.x & 7;     // 32 rows x 8 slots of 32 columns
+    float v[32];
+    if (dtype == MOE_BF16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t w = xc.q[i >> 2][i & 3];
+            v[2 * i] = bf16_f32(w & 0xFFFFu);
+            v[2 * i + 1] = bf16_f32(w >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(xc.q[i >> 2][i & 3]);
+    }
     uint32_t hv[32], lv[32];
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float x = (c0 + i < K) ? v[i] : 0.f;
-        hv[i] = bf16_rne(x);
-        lv[i] = SPLIT ? bf16_rne(x - bf16_f32(hv[i])) : 0u;
+        hv[i] = bf16_rne(v[i]);
+        lv[i] = SPLIT ? bf16_rne(v[i] - bf16_f32(hv[i])) : 0u;
         sum += bf16_f32(hv[i]) + (SPLIT ? bf16_f32(lv[i]) : 0.f);
     }
     uint32_t *hi = s_hi + row * kRowDw + slot * 16, *lo = s_lo + row * kRowDw + slot * 16;
@@ -268,21 +287,23 @@ __device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, g
     const int r = blockIdx.x * kTN + wave * 32 + (lane & 31);
     const int rc = min(r, I - 1);
     f32x16 accG = {}, accU = {};
-    const float *xf = (const float *)a.x;
-    const uint16_t *xb = (const uint16_t *)a.x;
     const int xdt = a.x_dtype;
-    auto src = [&](int row, int c) -> float {
-        const int t = s_tok[row];
-        if (t < 0) return 0.f;
-        return xdt == MOE_BF16 ? bf16_f32(xb[(size_t)t * H + c]) : xf[(size_t)t * H + c];
-    };
-    for (int kc = 0; kc < H; kc += kKC) {
-        u32x4 q_g[4], q_u[4];
-        uint32_t s_g[4], s_u[4];
-        load_chunk_w<BITS>(qg, sg, rc, H, kc, h, q_g, s_g);
-        load_chunk_w<BITS>(qu, su, rc, H, kc, h, q_u, s_u);
+    const int trow = s_tok[threadIdx.x >> 3];
+    const void *xrow = trow < 0 ? nullptr : (const char *)a.x + (size_t)trow * H * (xdt == MOE_BF16 ? 2 : 4);
+    // weights of chunk kc + kKC are requested before chunk kc is staged and multiplied
+    u32x4 q_g[2][4], q_u[2][4];
+    uint32_t s_g[2][4], s_u[2][4];
+    load_chunk_w<BITS>(qg, sg, rc, H, 0, h, q_g[0], s_g[0]);
+    load_chunk_w<BITS>(qu, su, rc, H, 0, h, q_u[0], s_u[0]);
+    auto chunk = [&](int kc, int cur) {
+        XChunk xc;
+        xload(xrow, xdt, kc, H, xc);
+        if (kc + kKC < H) {
+            load_chunk_w<BITS>(qg, sg, rc, H, kc + kKC, h, q_g[cur ^ 1], s_g[cur ^ 1]);
+            load_chunk_w<BITS>(qu, su, rc, H, kc + kKC, h, q_u[cur ^ 1], s_u[cur ^ 1]);
+        }
         __syncthreads();                        // previous chunk fully consumed
-        stage_chunk<BITS, SPLIT>(src, kc, H, s_hi, s_lo, s_sum);
+        xstage<BITS, SPLIT>(xc, xdt, s_hi, s_lo, s_sum);
         __syncthreads();
         const int m = lane & 31;
 #pragma unroll
@@ -293,7 +314,7 @@ __device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, g
             for (int st = 0; st < 4; ++st) {
                 const int off = m * kRowDw + a_offset<BITS>(gl, st, h);
                 const u32x4 A = *(const u32x4 *)(s_hi + off);
-                const u32x4 Bg = unpack_b<BITS>(q_g[gl], st, h), Bu = unpack_b<BITS>(q_u[gl], st, h);
+                const u32x4 Bg = unpack_b<BITS>(q_g[cur][gl], st, h), Bu = unpack_b<BITS>(q_u[cur][gl], st, h);
                 Pg = mfma(A, Bg, Pg);
                 Pu = mfma(A, Bu, Pu);
                 if (SPLIT) {
@@ -302,9 +323,13 @@ __device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, g
                     Pu = mfma(Al, Bu, Pu);
                 }
             }
-            apply_group(accG, Pg, s_g[gl], s_sum, gl, h);
-            apply_group(accU, Pu, s_u[gl], s_sum, gl, h);
+            apply_group(accG, Pg, s_g[cur][gl], s_sum, gl, h);
+            apply_group(accU, Pu, s_u[cur][gl], s_sum, gl, h);
         }
+    };
+    for (int kc = 0; kc < H; kc += 2 * kKC) {
+        chunk(kc, 0);
+        if (kc + kKC < H) chunk(kc + kKC, 1);
     }
     if (r < I) {
 #pragma unroll
@@ -342,15 +367,18 @@ __device__ void dn_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, g
     const int r = blockIdx.x * kTN + wave * 32 + (lane & 31);
     const int rc = min(r, H - 1);
     f32x16 acc = {};
-    const float *hb = a.hbuf + (size_t)(ti.base + ti.m0) * I;
     const int n = ti.n;
-    auto src = [&](int row, int c) -> float { return row < n ? hb[(size_t)row * I + c] : 0.f; };
-    for (int kc = 0; kc < I; kc += kKC) {
-        u32x4 qv[4];
-        uint32_t sv[4];
-        load_chunk_w<BITS>(qd, sd, rc, I, kc, h, qv, sv);
+    const int hr = threadIdx.x >> 3;
+    const void *hrow = hr < n ? (const void *)(a.hbuf + (size_t)(ti.base + ti.m0 + hr) * I) : nullptr;
+    u32x4 qv[2][4];
+    uint32_t sv[2][4];
+    load_chunk_w<BITS>(qd, sd, rc, I, 0, h, qv[0], sv[0]);
+    auto chunk = [&](int kc, int cur) {
+        XChunk xc;
+        xload(hrow, MOE_F32, kc, I, xc);
+        if (kc + kKC < I) load_chunk_w<BITS>(qd, sd, rc, I, kc + kKC, h, qv[cur ^ 1], sv[cur ^ 1]);
         __syncthreads();
-        stage_chunk<BITS, true>(src, kc, I, s_hi, s_lo, s_sum);
+        xstage<BITS, true>(xc, MOE_F32, s_hi, s_lo, s_sum);
         __syncthreads();
         const int m = lane & 31;
 #pragma unroll
@@ -360,12 +388,16 @@ __device__ void dn_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, g
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int off = m * kRowDw + a_offset<BITS>(gl, st, h);
-                const u32x4 B = unpack_b<BITS>(qv[gl], st, h);
+                const u32x4 B = unpack_b<BITS>(qv[cur][gl], st, h);
                 P = mfma(*(const u32x4 *)(s_hi + off), B, P);
                 P = mfma(*(const u32x4 *)(s_lo + off), B, P);
             }
-            apply_group(acc, P, sv[gl], s_sum, gl, h);
+            apply_group(acc, P, sv[cur][gl], s_sum, gl, h);
         }
+    };
+    for (int kc = 0; kc < I; kc += 2 * kKC) {
+        chunk(kc, 0);
+        if (kc + kKC < I) chunk(kc + kKC, 1);
     }
     if (r < H) {
 #pragma unroll
