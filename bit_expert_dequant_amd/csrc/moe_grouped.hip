@@ -106,56 +106,94 @@ __device__ __forceinline__ void planes_of(uint64_t blob_addr, int R0, int C0, in
 }
 
 // --------------------------------------------------------------------------- grouping
+__host__ __device__ __forceinline__ int pow2_at_least(int v) {
+    int p = 2;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Exclusive block scan (1024 threads) of two values per thread; returns each thread's prefixes and
+// writes the totals to *tot0, *tot1 (visible to all threads after the call).
+__device__ __forceinline__ void block_scan2(int v0, int v1, int &p0, int &p1, int *s_w, int *tot0, int *tot1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int i0 = v0, i1 = v1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u0 = __shfl_up(i0, o), u1 = __shfl_up(i1, o);
+        if (lane >= o) { i0 += u0; i1 += u1; }
+    }
+    if (lane == 63) { s_w[wave] = i0; s_w[16 + wave] = i1; }
+    __syncthreads();
+    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) { b0 += s_w[w]; b1 += s_w[16 + w]; }
+        t0 += s_w[w];
+        t1 += s_w[16 + w];
+    }
+    p0 = b0 + i0 - v0;
+    p1 = b1 + i1 - v1;
+    if (threadIdx.x == 0) { *tot0 = t0; *tot1 = t1; }
+    __syncthreads();
+}
+
+// Counting sort of the T*K (token, slot) pairs by expert, stable in the pair index, in one
+// 1024-thread workgroup: an LDS histogram, a block scan of the counts and of the 32-token tiles
+// per expert, and a bitonic sort of the keys expert * P + pair (their ascending order is exactly
+// the stable order by expert), then the work list of (expert, tile) in parallel over experts.
 __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
     extern __shared__ int s_all[];
-    const int P = a.T * a.K, E = a.E;
-    int *s_idx = s_all;                // [P]
-    int *s_cnt = s_idx + P;            // [E]
-    int *s_off = s_cnt + E;            // [E + 1]
-    int *s_toff = s_off + E + 1;       // [E + 1]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-    for (int p = tid; p < P; p += blockDim.x) {
-        const int e = a.idx[p];
-        s_idx[p] = (e >= 0 && e < E) ? e : -1;
-    }
+    __shared__ int s_w[32];
+    __shared__ int s_tot[2];
+    const int P = a.T * a.K, E = a.E, NP2 = pow2_at_least(P);
+    uint32_t *s_key = (uint32_t *)s_all;     // [NP2]
+    int *s_cnt = s_all + NP2;                // [E]
+    int *s_off = s_cnt + E;                  // [E + 1]
+    int *s_toff = s_off + E + 1;             // [E + 1]
+    const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += blockDim.x)
-        if (s_idx[p] >= 0) atomicAdd(&s_cnt[s_idx[p]], 1);
-    // pairs naming no valid expert get a zero output row (as in the decode path); such pairs are
-    // a caller error, so one thread per pair is enough
-    for (int p = tid; p < P; p += blockDim.x)
-        if (s_idx[p] < 0)
-            for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
-    __syncthreads();
-    if (tid == 0) {      // E <= 2048: a serial scan is a few microseconds at most
-        int acc = 0, tacc = 0;
-        for (int e = 0; e < E; ++e) {
-            s_off[e] = acc;
-            s_toff[e] = tacc;
-            acc += s_cnt[e];
-            tacc += (s_cnt[e] + kTM - 1) / kTM;
+    for (int p = tid; p < NP2; p += blockDim.x) {
+        uint32_t key = 0xFFFFFFFFu;          // padding and pairs naming no expert sort last
+        if (p < P) {
+            const int e = a.idx[p];
+            if (e >= 0 && e < E) {
+                key = (uint32_t)e * (uint32_t)P + (uint32_t)p;
+                atomicAdd(&s_cnt[e], 1);
+            } else {
+                // such pairs are a caller error and get a zero output row, as in the decode path
+                for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
+            }
         }
-        s_off[E] = acc;
-        s_toff[E] = tacc;
-        *a.ntiles = tacc;
+        s_key[p] = key;
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += blockDim.x) a.off[e] = s_off[e];
-    // stable scatter, one wave per expert
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int e = wave; e < E; e += nw) {
-        const int n = s_cnt[e];
-        if (n == 0) continue;
-        int base = 0;
-        for (int c = 0; c < P && base < n; c += 64) {
-            const int p = c + lane;
-            const bool m = p < P && s_idx[p] == e;
-            const uint64_t mask = __ballot(m);
-            if (m) a.perm[s_off[e] + base + __popcll(mask & lt)] = p;
-            base += __popcll(mask);
+    // offsets and tile offsets: thread t owns experts 2t and 2t+1 (E <= 2048)
+    const int e0 = 2 * tid, e1 = 2 * tid + 1;
+    const int c0 = e0 < E ? s_cnt[e0] : 0, c1 = e1 < E ? s_cnt[e1] : 0;
+    int p0, pt;
+    block_scan2(c0 + c1, (c0 + kTM - 1) / kTM + (c1 + kTM - 1) / kTM, p0, pt, s_w, &s_tot[0], &s_tot[1]);
+    if (e0 < E) { s_off[e0] = p0; s_toff[e0] = pt; }
+    if (e1 < E) { s_off[e1] = p0 + c0; s_toff[e1] = pt + (c0 + kTM - 1) / kTM; }
+    if (tid == 0) { s_off[E] = s_tot[0]; s_toff[E] = s_tot[1]; *a.ntiles = s_tot[1]; }
+    // bitonic sort, ascending
+    for (int k = 2; k <= NP2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < NP2; i += blockDim.x) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint32_t x = s_key[i], y = s_key[ixj];
+                    if ((x > y) == ((i & k) == 0)) { s_key[i] = y; s_key[ixj] = x; }
+                }
+            }
+            __syncthreads();
         }
-        for (int j = lane; j < (n + kTM - 1) / kTM; j += 64) {
+    }
+    const int nv = s_off[E];
+    for (int i = tid; i < nv; i += blockDim.x) a.perm[i] = (int)(s_key[i] % (uint32_t)P);
+    for (int e = tid; e <= E; e += blockDim.x) a.off[e] = s_off[e];
+    for (int e = tid; e < E; e += blockDim.x) {
+        const int nt = (s_cnt[e] + kTM - 1) / kTM;
+        for (int j = 0; j < nt; ++j) {
             a.tiles[2 * (s_toff[e] + j)] = e;
             a.tiles[2 * (s_toff[e] + j) + 1] = j * kTM;
         }
@@ -434,7 +472,7 @@ int grouped_max_tiles(int T, int K, int E) {
     return (P + kTM - 1) / kTM + (E < P ? E : P);
 }
 
-size_t group_lds_bytes(int T, int K, int E) { return ((size_t)T * K + 3 * (size_t)E + 2) * 4; }
+size_t group_lds_bytes(int T, int K, int E) { return ((size_t)pow2_at_least(T * K) + 3 * (size_t)E + 2) * 4; }
 
 hipError_t launch_group(const GroupLaunch &a, hipStream_t s) {
     const size_t lds = group_lds_bytes(a.T, a.K, a.E);
