@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -96,10 +97,12 @@ struct Carve {
 size_t route_ws(const moe_dims *d, int T) { return r256((size_t)T * d->n_experts * 4); }
 // Batched path workspace: grouping tables, SwiGLU outputs in expert order, normalised rows.
 struct GroupedWs {
-    int32_t *off, *ntiles, *perm, *tiles;
+    int32_t *off, *ntiles, *perm, *tiles, *nsmall;
+    moe::SmallRec *small;
     float *hbuf, *xn;
     size_t bytes;
 };
+int grouped_max_small(const moe_dims *d, int T) { return std::min(d->n_experts, T * d->top_k); }
 GroupedWs grouped_ws(const moe_dims *d, int T, void *base) {
     const int P = T * d->top_k;
     Carve c{(char *)base};
@@ -108,6 +111,8 @@ GroupedWs grouped_ws(const moe_dims *d, int T, void *base) {
     g.ntiles = c.take<int32_t>(1);
     g.perm = c.take<int32_t>(P);
     g.tiles = c.take<int32_t>(2 * (size_t)moe::grouped_max_tiles(T, d->top_k, d->n_experts));
+    g.small = c.take<moe::SmallRec>((size_t)grouped_max_small(d, T));
+    g.nsmall = c.take<int32_t>(1);
     g.hbuf = c.take<float>((size_t)P * d->inter);
     g.xn = c.take<float>((size_t)T * d->hidden);
     g.bytes = c.off;
@@ -358,11 +363,14 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
             xa = g.xn;
             xdt = MOE_F32;
         }
-        moe::GroupLaunch gl{idx, T, dims->top_k, dims->n_experts, g.off, g.perm, g.tiles, g.ntiles, y, dims->hidden};
+        const bool small = moe::small_path_fits(dims->hidden, dims->inter);
+        moe::GroupLaunch gl{idx, T, dims->top_k, dims->n_experts, layer->experts, g.off, g.perm, g.tiles, g.ntiles,
+                            g.small, g.nsmall, small ? moe::kSmallTokens : 0, y, dims->hidden};
         if (int s = launched(moe::launch_group(gl, st), "group")) return s;
         moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, g.off, g.perm,
-                              g.tiles, g.ntiles, g.hbuf, y};
-        if (int s = launched(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts), st),
+                              g.tiles, g.ntiles, g.small, g.nsmall, g.hbuf, y, {}, {}};
+        if (int s = launched(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts),
+                                                     small ? grouped_max_small(dims, T) : 0, st),
                              "grouped ffn"))
             return s;
         return ok();

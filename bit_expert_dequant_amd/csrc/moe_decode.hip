@@ -382,7 +382,7 @@ int down_rows_per_unit(int cols) {
     const int nj = nj_for(cols);
     return (nj == 1 ? dn_rg<1>() : nj == 2 ? dn_rg<2>() : dn_rg<4>()) * rpi_for(cols);
 }
-static RowGeo row_geo(int cols, int rows, int rg) {
+RowGeo row_geo(int cols, int rows, int rg) {
     RowGeo r;
     r.spr = cols / 32;
     const int gsz = r.spr >= 64 ? 64 : next_pow2(r.spr);

@@ -38,29 +38,57 @@ __device__ __forceinline__ float load_act(const void *x, int dtype, size_t i) {
 }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Sum over aligned groups of gs lanes (gs a power of two <= 64); every lane gets its group's sum.
+// Sum over aligned groups of GS lanes (GS a power of two <= 64); every lane gets its group's sum.
 // Butterfly in registers: quad permutes and row mirrors (DPP) inside 16-lane rows, then the gfx950
-// row swaps (v_permlane16/32_swap) across rows.  After the steps below gs, every lane holds the sum
-// of its aligned group of gs lanes, and both partners of a step add the same two values, so all
-// lanes of a group hold identical bits.  Branch-free so that several sums interleave.
+// row swaps (v_permlane16/32_swap) across rows.  After the steps below GS, every lane holds the sum
+// of its aligned group of GS lanes, and both partners of a step add the same two values, so all
+// lanes of a group hold identical bits.  The group size is a compile-time constant so that each
+// step is one DPP-fused add; group_sum dispatches a uniform run-time size to it.
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float group_sum(float v, int gs) {
-    v += gs > 1 ? dppf<0xB1>(v) : 0.f;      // quad_perm [1,0,3,2]
-    v += gs > 2 ? dppf<0x4E>(v) : 0.f;      // quad_perm [2,3,0,1]
-    v += gs > 4 ? dppf<0x141>(v) : 0.f;     // row_half_mirror
-    v += gs > 8 ? dppf<0x140>(v) : 0.f;     // row_mirror
-    if (gs > 16) {
+template <int GS>
+__device__ __forceinline__ float group_sum_c(float v) {
+    if constexpr (GS > 1) v += dppf<0xB1>(v);      // quad_perm [1,0,3,2]
+    if constexpr (GS > 2) v += dppf<0x4E>(v);      // quad_perm [2,3,0,1]
+    if constexpr (GS > 4) v += dppf<0x141>(v);     // row_half_mirror
+    if constexpr (GS > 8) v += dppf<0x140>(v);     // row_mirror
+    if constexpr (GS > 16) {
         const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
         v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     }
-    if (gs > 32) {
+    if constexpr (GS > 32) {
         const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
         v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
     }
     return v;
+}
+__device__ __forceinline__ float group_sum(float v, int gs) {
+    switch (gs) {
+        case 1: return v;
+        case 2: return group_sum_c<2>(v);
+        case 4: return group_sum_c<4>(v);
+        case 8: return group_sum_c<8>(v);
+        case 16: return group_sum_c<16>(v);
+        case 32: return group_sum_c<32>(v);
+        default: return group_sum_c<64>(v);
+    }
+}
+// Group sums of two values at once (GS = 32 or 64): the first butterfly step exchanges a's upper
+// half-group for b's lower one, so afterwards the lower half of every group carries a and the
+// upper half b, and the remaining steps reduce both together.  Lane l receives the sum of a over
+// its group when l % GS < GS / 2, else that of b.
+template <int GS>
+__device__ __forceinline__ float pair_sum(float a, float b) {
+    static_assert(GS == 32 || GS == 64, "pair_sum: groups of 32 or 64 lanes");
+    if constexpr (GS == 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return group_sum_c<32>(__uint_as_float(p[0]) + __uint_as_float(p[1]));
+    } else {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return group_sum_c<16>(__uint_as_float(p[0]) + __uint_as_float(p[1]));
+    }
 }
 
 __device__ __forceinline__ float block_sum(float v, float *red) {
@@ -218,6 +246,15 @@ struct ActView {
     const float2 *xs;    // [cols/32] {sx, sum of x}
 };
 
+// Loads slot s of a view into registers, for a lane whose slot exists.
+__device__ __forceinline__ void load_act_slot_full(const ActView &av, int s, uint32_t (&D)[kSlotDw], float2 &xs) {
+#pragma unroll
+    for (int i = 0; i < kSlotDw; i += 4) {
+        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + i);
+        D[i] = d.x; D[i + 1] = d.y; D[i + 2] = d.z; D[i + 3] = d.w;
+    }
+    xs = av.xs[s];
+}
 // Loads slot ss of a view into registers (zeros when !ok: an idle lane's slot adds nothing).
 __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok, uint32_t (&D)[kSlotDw], float2 &xs) {
     const int s = ok ? ss : 0;
@@ -235,28 +272,38 @@ __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok
 // activation.  4-bit codes enter v_dot8_i32_i4 as q - 8 (the code XOR 8 read as a signed nibble),
 // so the bias becomes b + 8 s; 2-bit codes spread to nibbles are already in [0, 3].  Per plane
 // the integer sums are at most 32 * 8 * 8, so the combined sum is exact in int32 and in fp32.
+// The four digit planes are combined in Horner form, acc = ((A3 * 16 + A2) * 16 + A1) * 16 + A0,
+// with every plane's dot products accumulated straight into acc.
 template <int BITS>
 __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
-    int A[4] = {0, 0, 0, 0};
+    int acc = 0;
     if (BITS == 4) {
+        int c[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = (int)(q[j] ^ 0x88888888u);
+        for (int j = 0; j < 4; ++j) c[j] = (int)(q[j] ^ 0x88888888u);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) A[p] = __builtin_amdgcn_sdot8(c, (int)D[4 * p + j], A[p], false);
+        for (int p = 3; p >= 0; --p) {
+            acc *= 16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], acc, false);
         }
     } else {
+        int e[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int e0 = (int)(q[j] & 0x33333333u), e1 = (int)((q[j] >> 2) & 0x33333333u);
+            e[j][0] = (int)(q[j] & 0x33333333u);
+            e[j][1] = (int)((q[j] >> 2) & 0x33333333u);
+        }
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                A[p] = __builtin_amdgcn_sdot8(e0, (int)D[4 * p + 2 * j], A[p], false);
-                A[p] = __builtin_amdgcn_sdot8(e1, (int)D[4 * p + 2 * j + 1], A[p], false);
+        for (int p = 3; p >= 0; --p) {
+            acc *= 16;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                acc = __builtin_amdgcn_sdot8(e[j][0], (int)D[4 * p + 2 * j], acc, false);
+                acc = __builtin_amdgcn_sdot8(e[j][1], (int)D[4 * p + 2 * j + 1], acc, false);
             }
         }
     }
-    const int acc = A[0] + A[1] * 16 + A[2] * 256 + A[3] * 4096;
     const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
     const float bb = BITS == 4 ? fmaf(8.f, s, b) : b;
     return fmaf(s * xs.x, (float)acc, bb * xs.y);

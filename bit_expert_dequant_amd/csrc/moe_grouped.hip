@@ -112,38 +112,56 @@ __host__ __device__ __forceinline__ int pow2_at_least(int v) {
     return p;
 }
 
-// Exclusive block scan (1024 threads) of two values per thread; returns each thread's prefixes and
-// writes the totals to *tot0, *tot1 (visible to all threads after the call).
-__device__ __forceinline__ void block_scan2(int v0, int v1, int &p0, int &p1, int *s_w, int *tot0, int *tot1) {
+// Exclusive block scan (1024 threads) of N values per thread: p receives this thread's prefixes and
+// tot the totals (the same in every thread).  s_w: 16 * N words of LDS.
+template <int N>
+__device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&p)[N], uint32_t (&tot)[N], uint32_t *s_w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int i0 = v0, i1 = v1;
+    uint32_t inc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) inc[i] = v[i];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int u0 = __shfl_up(i0, o), u1 = __shfl_up(i1, o);
-        if (lane >= o) { i0 += u0; i1 += u1; }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t u = (uint32_t)__shfl_up((int)inc[i], o);
+            if (lane >= o) inc[i] += u;
+        }
     }
-    if (lane == 63) { s_w[wave] = i0; s_w[16 + wave] = i1; }
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_w[16 * i + wave] = inc[i];
+    }
     __syncthreads();
-    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
-    for (int w = 0; w < 16; ++w) {
-        if (w < wave) { b0 += s_w[w]; b1 += s_w[16 + w]; }
-        t0 += s_w[w];
-        t1 += s_w[16 + w];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t before = 0, t = 0;
+        for (int w = 0; w < 16; ++w) {
+            const uint32_t x = s_w[16 * i + w];
+            before += w < wave ? x : 0u;
+            t += x;
+        }
+        p[i] = before + inc[i] - v[i];
+        tot[i] = t;
     }
-    p0 = b0 + i0 - v0;
-    p1 = b1 + i1 - v1;
-    if (threadIdx.x == 0) { *tot0 = t0; *tot1 = t1; }
     __syncthreads();
 }
 
+// Count of bin n (1..8) in a word array holding two 16-bit bins per word (bin n in word (n-1)/2).
+__device__ __forceinline__ int bin_of(const uint32_t (&w)[4], int n) {
+    return (int)((w[(n - 1) >> 1] >> (16 * ((n - 1) & 1))) & 0xFFFFu);
+}
+static_assert(kSmallTokens <= 8, "the small-list ranking packs eight token-count bins");
+
 // Counting sort of the T*K (token, slot) pairs by expert, stable in the pair index, in one
-// 1024-thread workgroup: an LDS histogram, a block scan of the counts and of the 32-token tiles
-// per expert, and a bitonic sort of the keys expert * P + pair (their ascending order is exactly
-// the stable order by expert), then the work list of (expert, tile) in parallel over experts.
+// 1024-thread workgroup: an LDS histogram, block scans of the counts, of the 32-token MFMA tiles
+// of busy experts and of the small experts binned by token count, and a bitonic sort of the keys
+// expert * P + pair (their ascending order is exactly the stable order by expert); then the MFMA
+// work list of (expert, tile) and the small-expert records, most tokens first, so that the longest
+// workgroups of the small-expert kernels start first.
 __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
     extern __shared__ int s_all[];
-    __shared__ int s_w[32];
-    __shared__ int s_tot[2];
+    __shared__ uint32_t s_w[64];
     const int P = a.T * a.K, E = a.E, NP2 = pow2_at_least(P);
     uint32_t *s_key = (uint32_t *)s_all;     // [NP2]
     int *s_cnt = s_all + NP2;                // [E]
@@ -167,14 +185,38 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
         s_key[p] = key;
     }
     __syncthreads();
-    // offsets and tile offsets: thread t owns experts 2t and 2t+1 (E <= 2048)
+    // thread t owns experts 2t and 2t+1 (E <= 2048)
     const int e0 = 2 * tid, e1 = 2 * tid + 1;
     const int c0 = e0 < E ? s_cnt[e0] : 0, c1 = e1 < E ? s_cnt[e1] : 0;
-    int p0, pt;
-    block_scan2(c0 + c1, (c0 + kTM - 1) / kTM + (c1 + kTM - 1) / kTM, p0, pt, s_w, &s_tot[0], &s_tot[1]);
-    if (e0 < E) { s_off[e0] = p0; s_toff[e0] = pt; }
-    if (e1 < E) { s_off[e1] = p0 + c0; s_toff[e1] = pt + (c0 + kTM - 1) / kTM; }
-    if (tid == 0) { s_off[E] = s_tot[0]; s_toff[E] = s_tot[1]; *a.ntiles = s_tot[1]; }
+    const int cap = a.small_cap;
+    const bool sm0 = c0 >= 1 && c0 <= cap, sm1 = c1 >= 1 && c1 <= cap;
+    const int t0 = sm0 ? 0 : (c0 + kTM - 1) / kTM, t1 = sm1 ? 0 : (c1 + kTM - 1) / kTM;
+    // offsets and MFMA tile offsets
+    {
+        const uint32_t v[2] = {(uint32_t)(c0 + c1), (uint32_t)(t0 + t1)};
+        uint32_t p[2], tot[2];
+        block_scan<2>(v, p, tot, s_w);
+        if (e0 < E) { s_off[e0] = (int)p[0]; s_toff[e0] = (int)p[1]; }
+        if (e1 < E) { s_off[e1] = (int)p[0] + c0; s_toff[e1] = (int)p[1] + t0; }
+        if (tid == 0) { s_off[E] = (int)tot[0]; s_toff[E] = (int)tot[1]; *a.ntiles = (int)tot[1]; }
+    }
+    // small-expert list positions: bins by token count (two 16-bit bins per word), bin n starting
+    // after every bin with more tokens, experts in index order inside a bin
+    int pos0 = -1, pos1 = -1;
+    {
+        uint32_t v[4] = {0u, 0u, 0u, 0u}, p[4], tot[4];
+        if (sm0) v[(c0 - 1) >> 1] += 1u << (16 * ((c0 - 1) & 1));
+        if (sm1) v[(c1 - 1) >> 1] += 1u << (16 * ((c1 - 1) & 1));
+        block_scan<4>(v, p, tot, s_w);
+        int start[9], nsm = 0;
+        for (int n = kSmallTokens; n >= 1; --n) {
+            start[n] = nsm;
+            nsm += n <= cap ? bin_of(tot, n) : 0;
+        }
+        if (sm0) pos0 = start[c0] + bin_of(p, c0);
+        if (sm1) pos1 = start[c1] + bin_of(p, c1) + (sm0 && c0 == c1 ? 1 : 0);
+        if (tid == 0) *a.nsmall = nsm;
+    }
     // bitonic sort, ascending
     for (int k = 2; k <= NP2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
@@ -192,12 +234,27 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
     for (int i = tid; i < nv; i += blockDim.x) a.perm[i] = (int)(s_key[i] % (uint32_t)P);
     for (int e = tid; e <= E; e += blockDim.x) a.off[e] = s_off[e];
     for (int e = tid; e < E; e += blockDim.x) {
-        const int nt = (s_cnt[e] + kTM - 1) / kTM;
+        const int nt = s_toff[e + 1] - s_toff[e];
         for (int j = 0; j < nt; ++j) {
             a.tiles[2 * (s_toff[e] + j)] = e;
             a.tiles[2 * (s_toff[e] + j) + 1] = j * kTM;
         }
     }
+    auto small_rec = [&](int e, int n, int pos) {
+        const moe_expert_desc d = a.experts[e];
+        SmallRec r;
+        r.blob = d.blob;
+        r.e = e;
+        r.n = n;
+        r.base = s_off[e];
+        r.bits = d.bits == 2 ? 2 : 4;
+        r.pad[0] = r.pad[1] = 0;
+#pragma unroll
+        for (int t = 0; t < kSmallTokens; ++t) r.pair[t] = (int)(s_key[r.base + min(t, n - 1)] % (uint32_t)P);
+        a.small[pos] = r;
+    };
+    if (sm0) small_rec(e0, c0, pos0);
+    if (sm1) small_rec(e1, c1, pos1);
 }
 
 __global__ void __launch_bounds__(256) k_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, float eps,
@@ -464,6 +521,137 @@ __global__ void __launch_bounds__(256) k_dn_mfma(GroupedLaunch a) {
     else dn_tile<4>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
 }
 
+// --------------------------------------------------------------------------- down, h resident
+// When a tile's whole h fits in LDS (I <= kDnResI), a workgroup stages it once -- bf16 hi/lo in the
+// pair order of the expert's code width, plus the group sums -- and then covers kDnRB blocks of
+// 128 output rows with no further barrier, the next row block's weights (all its chunks) loading
+// while the current one is multiplied.  Against the chunked kernel this stages h once per 1024
+// output rows instead of once per 128 and keeps two row blocks of weights in flight per wave.
+constexpr int kDnResI = 1024;              // largest I staged whole (LDS ~132 KiB)
+constexpr int kDnRB = 8;                   // 128-row blocks per workgroup
+constexpr int kDnCh = kDnResI / kKC;       // chunks of kKC columns per row
+
+__host__ __device__ __forceinline__ int dn_res_rowdw(int I) { return ((I + kKC - 1) / kKC) * (kKC / 2) + 4; }
+size_t dn_res_lds_bytes(int I) {
+    return ((size_t)2 * kTM * dn_res_rowdw(I) + (size_t)kTM * ((I + 63) / 64)) * 4;
+}
+
+template <int BITS>
+__device__ void dn_res_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, gwords sd, const int *s_pair,
+                            uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+    const int rs = dn_res_rowdw(I), G = (I + 63) / 64, nch = (I + kKC - 1) / kKC;
+    const int n = ti.n, m = lane & 31;
+    // 1. stage the tile's h: thread (row, slot) converts slot `slot` of every chunk of its token row
+    {
+        const int hr = threadIdx.x >> 3, slot = threadIdx.x & 7;
+        const void *hrow = hr < n ? (const void *)(a.hbuf + (size_t)(ti.base + ti.m0 + hr) * I) : nullptr;
+        for (int c = 0; c < nch; ++c) {
+            XChunk xc;
+            xload(hrow, MOE_F32, c * kKC, I, xc);
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(xc.q[i >> 2][i & 3]);
+            uint32_t hv[32], lv[32];
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                hv[i] = bf16_rne(v[i]);
+                lv[i] = bf16_rne(v[i] - bf16_f32(hv[i]));
+                sum += bf16_f32(hv[i]) + bf16_f32(lv[i]);
+            }
+            uint32_t *hi = s_hi + hr * rs + c * (kKC / 2) + slot * 16, *lo = s_lo + hr * rs + c * (kKC / 2) + slot * 16;
+#pragma unroll
+            for (int d = 0; d < 16; d += 4) {
+                u32x4 H4, L4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    H4[j] = hv[pair_col<BITS>(d + j, 0)] | (hv[pair_col<BITS>(d + j, 1)] << 16);
+                    L4[j] = lv[pair_col<BITS>(d + j, 0)] | (lv[pair_col<BITS>(d + j, 1)] << 16);
+                }
+                *(u32x4 *)(hi + d) = H4;
+                *(u32x4 *)(lo + d) = L4;
+            }
+            sum += __shfl_xor(sum, 1);
+            const int g = c * (kKC / 64) + (slot >> 1);
+            if (!(slot & 1) && g < G) s_sum[hr * G + g] = sum;
+        }
+    }
+    __syncthreads();
+    // 2. row blocks: weights of block rb+1 in flight while block rb is multiplied
+    u32x4 qA[kDnCh][4], qB[kDnCh][4];
+    uint32_t sA[kDnCh][4], sB[kDnCh][4];
+    const int rb0 = blockIdx.x * kDnRB;
+    auto rowof = [&](int rb) { return rb * kTN + wave * 32 + m; };
+    auto load_rb = [&](int rb, u32x4 (&q)[kDnCh][4], uint32_t (&sv)[kDnCh][4]) {
+        const int rc = min(rowof(rb), H - 1);
+#pragma unroll
+        for (int c = 0; c < kDnCh; ++c)
+            if (c < nch) load_chunk_w<BITS>(qd, sd, rc, I, c * kKC, h, q[c], sv[c]);
+    };
+    auto compute_rb = [&](int rb, const u32x4 (&q)[kDnCh][4], const uint32_t (&sv)[kDnCh][4]) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int c = 0; c < kDnCh; ++c) {
+            if (c >= nch) break;
+#pragma unroll
+            for (int gl = 0; gl < 4; ++gl) {
+                const int g = c * (kKC / 64) + gl;
+                if (g >= G) break;
+                f32x16 P = {};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int off = m * rs + c * (kKC / 2) + a_offset<BITS>(gl, st, h);
+                    const u32x4 B = unpack_b<BITS>(q[c][gl], st, h);
+                    P = mfma(*(const u32x4 *)(s_hi + off), B, P);
+                    P = mfma(*(const u32x4 *)(s_lo + off), B, P);
+                }
+                const float sc = bf16_f32(sv[c][gl] & 0xFFFFu), bc = bf16_f32(sv[c][gl] >> 16) - 128.f * sc;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int mm = 8 * (v >> 2) + 4 * h + (v & 3);
+                    acc[v] += sc * P[v] + bc * s_sum[mm * G + g];
+                }
+            }
+        }
+        const int r = rowof(rb);
+        if (r < H) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int mm = 8 * (v >> 2) + 4 * h + (v & 3);
+                if (mm < n) a.y[(size_t)s_pair[mm] * H + r] = acc[v];
+            }
+        }
+    };
+    const int nrb = min(kDnRB, (H + kTN - 1) / kTN - rb0);
+    load_rb(rb0, qA, sA);
+    for (int i = 0; i < nrb; i += 2) {
+        if (i + 1 < nrb) load_rb(rb0 + i + 1, qB, sB);
+        compute_rb(rb0 + i, qA, sA);
+        if (i + 2 < nrb) load_rb(rb0 + i + 2, qA, sA);
+        if (i + 1 < nrb) compute_rb(rb0 + i + 1, qB, sB);
+    }
+}
+
+__global__ void __launch_bounds__(256) k_dn_res(GroupedLaunch a) {
+    extern __shared__ __align__(16) uint32_t s_dyn[];
+    __shared__ int s_pair[kTM];
+    TileInfo ti;
+    if (!tile_info(a, ti)) return;
+    const int rs = dn_res_rowdw(a.I);
+    uint32_t *s_hi = s_dyn, *s_lo = s_dyn + kTM * rs;
+    float *s_sum = (float *)(s_lo + kTM * rs);
+    if (threadIdx.x < kTM) s_pair[threadIdx.x] = (int)threadIdx.x < ti.n ? a.perm[ti.base + ti.m0 + threadIdx.x] : 0;
+    const moe_expert_desc d = a.experts[ti.e];
+    gbytes q[3];
+    gwords sb[3];
+    const int bits = d.bits == 2 ? 2 : 4;
+    planes_of(d.blob, a.I, a.H, a.H, a.I, bits, q, sb);
+    __syncthreads();
+    if (bits == 2) dn_res_tile<2>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
+    else dn_res_tile<4>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
@@ -475,6 +663,7 @@ int grouped_max_tiles(int T, int K, int E) {
 size_t group_lds_bytes(int T, int K, int E) { return ((size_t)pow2_at_least(T * K) + 3 * (size_t)E + 2) * 4; }
 
 hipError_t launch_group(const GroupLaunch &a, hipStream_t s) {
+    if (grouped_max_tiles(a.T, a.K, a.E) >= (1 << 16)) return hipErrorInvalidValue;   // packed scan word
     const size_t lds = group_lds_bytes(a.T, a.K, a.E);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)k_group, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -490,12 +679,32 @@ hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, 
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, hipStream_t s) {
+static hipError_t grouped_down_mfma(const GroupedLaunch &a, int max_tiles, hipStream_t s);
+
+// Order: MFMA gate/up (busy experts), small-expert gate/up, MFMA down, small-expert down.
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s) {
     const bool split = a.x_dtype != MOE_BF16;
     dim3 g1((a.I + kTN - 1) / kTN, max_tiles);
     if (split) hipLaunchKernelGGL(k_gu_mfma<true>, g1, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_gu_mfma<false>, g1, dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError()) return e;
+    if (max_small > 0)
+        if (hipError_t e = launch_small_gateup(a, max_small, s)) return e;
+    if (hipError_t e = grouped_down_mfma(a, max_tiles, s)) return e;
+    return max_small > 0 ? launch_small_down(a, max_small, s) : hipSuccess;
+}
+
+static hipError_t grouped_down_mfma(const GroupedLaunch &a, int max_tiles, hipStream_t s) {
+    if (a.I <= kDnResI) {
+        const size_t lds = dn_res_lds_bytes(a.I);
+        if (lds > 64 * 1024)
+            if (hipError_t e = hipFuncSetAttribute((const void *)k_dn_res, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds))
+                return e;
+        dim3 g2(((a.H + kTN - 1) / kTN + kDnRB - 1) / kDnRB, max_tiles);
+        hipLaunchKernelGGL(k_dn_res, g2, dim3(256), lds, s, a);
+        return hipGetLastError();
+    }
     dim3 g2((a.H + kTN - 1) / kTN, max_tiles);
     hipLaunchKernelGGL(k_dn_mfma, g2, dim3(256), 0, s, a);
     return hipGetLastError();

@@ -39,6 +39,7 @@ struct RowGeo {
 struct PlaneTable {
     uint64_t off[2][6];
 };
+RowGeo row_geo(int cols, int rows, int rg);   // rg: wave instructions (row groups) per unit
 RowGeo gateup_geo(int H, int I);   // gate/up rows: I rows of H inputs
 RowGeo down_geo(int H, int I);     // down rows: H rows of I inputs
 PlaneTable plane_table(int H, int I);
@@ -96,12 +97,30 @@ struct DownLaunch {
 hipError_t launch_down(const DownLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 
 // Batched path (T > 1): grouping of the T*K (token, slot) pairs by expert, then grouped GEMMs.
+// Experts with at most kSmallTokens tokens in a batch take the integer dot-product kernels (work
+// proportional to their tokens); busier experts take the MFMA tiles of 32 tokens.
+constexpr int kSmallTokens = 8;
+
+// One entry of the small-expert list: everything a workgroup needs to start, in one 64-byte load.
+struct SmallRec {
+    uint64_t blob;                                 // the expert's blob address
+    int32_t e, n, base, bits;                      // expert, tokens (1..kSmallTokens), first sorted position, code width
+    int32_t pad[2];
+    int32_t pair[kSmallTokens];                    // pair index (t*K + k) of its tokens, in expert order
+};
+static_assert(sizeof(SmallRec) == 64, "SmallRec is one 64-byte record");
+
 struct GroupLaunch {
     const int32_t *idx; int T, K, E;
+    const moe_expert_desc *experts;
     int32_t *off;                                  // [E+1] first sorted position of each expert
     int32_t *perm;                                 // [T*K] pair index (t*K+k) in expert order
-    int32_t *tiles;                                // [2*max_tiles] (expert, first token) per tile
+    int32_t *tiles;                                // [2*max_tiles] (expert, first token) per MFMA tile
     int32_t *ntiles;                               // [1]
+    SmallRec *small;                               // [min(E, T*K)] experts with 1..small_cap tokens,
+                                                   // most tokens first (ties: lower expert first)
+    int32_t *nsmall;                               // [1]
+    int small_cap;                                 // kSmallTokens, or 0: every expert takes MFMA tiles
     float *y; int H;                               // rows of out-of-range pairs are zeroed
 };
 int grouped_max_tiles(int T, int K, int E);
@@ -115,10 +134,17 @@ struct GroupedLaunch {
     int H, I, K;
     const moe_expert_desc *experts;
     const int32_t *off, *perm, *tiles, *ntiles;
+    const SmallRec *small; const int32_t *nsmall;
     float *hbuf;                                   // [T*K][I] SwiGLU outputs in expert order
     float *y;                                      // [T*K][H]
+    RowGeo geo; PlaneTable pt;                     // set by the small-expert launchers
 };
-hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, hipStream_t s);
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s);
+// Integer dot-product kernels for the small experts (moe_batched8.hip); false when the shapes do
+// not fit them (everything then takes the MFMA tiles).
+bool small_path_fits(int H, int I);
+hipError_t launch_small_gateup(const GroupedLaunch &a, int max_small, hipStream_t s);
+hipError_t launch_small_down(const GroupedLaunch &a, int max_small, hipStream_t s);
 
 // Router + gate/up of one decode token in one launch (two groups of workgroups; the logits pass
 // through tagged workspace words, see moe_layer.hip).  The down kernel follows on the stream.
