@@ -42,64 +42,66 @@ __device__ __forceinline__ bool small_entry(const GroupedLaunch &a, SmallRec &r)
     return j < ns;
 }
 
-// Stages rows 0..n-1 (cols activations each, row t at rows[t]) into LDS: row t occupies
-// row_dw(cols) dwords at lds + t * row_dw(cols), digit planes in the order of code width BITS,
-// then its slots' {sx, sum of x}.  The loads of chunk batch 0 are issued by stage_issue (before
-// the caller's first weight loads, so that waiting for them does not wait for the weights) and
-// converted by stage_convert; further batches (more than 4 chunks per thread) load and convert in
-// turn.  Every thread of the workgroup calls them; the caller puts a barrier after stage_rest.
-struct StageBatch {
-    Chunk16 c[4];
-};
-__device__ __forceinline__ const void *row_of(const uint64_t (&rows)[kSmallTokens], int t) {
-    uint64_t r = rows[0];
-#pragma unroll
-    for (int i = 1; i < kSmallTokens; ++i) r = t == i ? rows[i] : r;
-    return (const void *)r;
-}
-__device__ __forceinline__ void stage_issue(const uint64_t (&rows)[kSmallTokens], int n, int cols, int dtype, int c0,
-                                            StageBatch &sb) {
-    const int nch = cols / 16, total = n * nch;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = min(c0 + j * kBlock + (int)threadIdx.x, total - 1);   // clamped; extra chunks unused
-        const int t = c / nch;
-        issue_chunk16(row_of(rows, t), dtype, c - t * nch, sb.c[j]);
-    }
-}
-template <int BITS>
-__device__ __forceinline__ void stage_convert(int n, int cols, int dtype, int c0, const StageBatch &sb, uint32_t *lds) {
-    const int nch = cols / 16, total = n * nch, rd = row_dw(cols);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (c0 + j * kBlock >= total) break;                                 // uniform
-        const int c = c0 + j * kBlock + (int)threadIdx.x;
-        const bool valid = c < total;
-        const int cc = valid ? c : 0;
-        const int t = cc / nch, m = cc - t * nch;
-        float v[16];
-        chunk16_f32(sb.c[j], dtype, v);
-        uint32_t *d = lds + t * rd;
-        stage_chunk(m, valid, v, BITS == 4 ? d : nullptr, BITS == 2 ? d : nullptr, (float2 *)(d + cols / 2));
-    }
-}
-template <int BITS>
-__device__ __forceinline__ void stage_rest(const uint64_t (&rows)[kSmallTokens], int n, int cols, int dtype,
-                                           uint32_t *lds) {
-    const int total = n * (cols / 16);
-    for (int c0 = 4 * kBlock; c0 < total; c0 += 4 * kBlock) {
-        StageBatch sb;
-        stage_issue(rows, n, cols, dtype, c0, sb);
-        stage_convert<BITS>(n, cols, dtype, c0, sb, lds);
-    }
-}
-
 // Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     if constexpr (I < N) {
         f(std::integral_constant<int, I>{});
         static_for<I + 1, N>(f);
+    }
+}
+
+// Staging of the expert's token rows into LDS: row t occupies row_dw(cols) dwords at
+// lds + t * row_dw(cols), digit planes in the order of code width BITS, then its slots' {sx, sum
+// of x}.  Thread `tid` takes chunk tid (+ kBlock, ... for rows of more than kBlock chunks) of every
+// row, so a token's index is a compile-time constant everywhere and its row address a uniform
+// value: row_addr(t) for t < kSmallTokens (t >= n gives a duplicate of a present row).  Tokens go
+// in two batches of four; the loads of the first pass's first batch are issued by stage_issue,
+// before the caller's first weight loads, and everything else happens in stage_finish.  Every
+// thread of the workgroup calls both; the caller puts a barrier after stage_finish.
+struct StageBatch {
+    Chunk16 c[4];
+};
+template <int B, typename RowAddr>
+__device__ __forceinline__ void stage_batch_issue(RowAddr &&row_addr, int dtype, int mc, StageBatch &sb) {
+    static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        issue_chunk16(row_addr(4 * B + j), dtype, mc, sb.c[j]);
+    });
+}
+template <int BITS, int B>
+__device__ __forceinline__ void stage_batch_convert(int n, int cols, int dtype, int m, const StageBatch &sb,
+                                                    uint32_t *lds) {
+    const int nch = cols / 16, rd = row_dw(cols);
+    const bool valid = m < nch;
+    const int mc = min(m, nch - 1);
+    static_for<0, 4>([&](auto jc) {
+        constexpr int t = 4 * B + decltype(jc)::value;
+        if (t < n) {                                                         // uniform
+            float v[16];
+            chunk16_f32(sb.c[t - 4 * B], dtype, v);
+            uint32_t *d = lds + t * rd;
+            stage_chunk(mc, valid, v, BITS == 4 ? d : nullptr, BITS == 2 ? d : nullptr, (float2 *)(d + cols / 2));
+        }
+    });
+}
+template <typename RowAddr>
+__device__ __forceinline__ void stage_issue(RowAddr &&row_addr, int cols, int dtype, StageBatch &sb) {
+    stage_batch_issue<0>(row_addr, dtype, min((int)threadIdx.x, cols / 16 - 1), sb);
+}
+template <int BITS, typename RowAddr>
+__device__ __forceinline__ void stage_finish(RowAddr &&row_addr, int n, int cols, int dtype, StageBatch &sb,
+                                             uint32_t *lds) {
+    static_assert(kSmallTokens == 8, "two batches of four tokens");
+    const int nch = cols / 16;
+    for (int m0 = 0; m0 < nch; m0 += kBlock) {                               // uniform; usually one pass
+        const int m = m0 + (int)threadIdx.x, mc = min(m, nch - 1);
+        if (m0 > 0) stage_batch_issue<0>(row_addr, dtype, mc, sb);
+        stage_batch_convert<BITS, 0>(n, cols, dtype, m, sb, lds);
+        if (n > 4) {
+            stage_batch_issue<1>(row_addr, dtype, mc, sb);
+            stage_batch_convert<BITS, 1>(n, cols, dtype, m, sb, lds);
+        }
     }
 }
 
@@ -146,19 +148,16 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const SmallRec 
     auto r0_of = [&](int i) { return min(ub + min(i, last) * kWaves, nblk - 1) * RB; };
 
     // 1. activation chunks of the expert's tokens, then the first units' weights
-    uint64_t rows[kSmallTokens];
     const size_t rowb = (size_t)H * (a.x_dtype == MOE_BF16 ? 2 : 4);
-#pragma unroll
-    for (int t = 0; t < kSmallTokens; ++t) rows[t] = (uint64_t)((const char *)a.x + (size_t)(se.pair[t] / a.K) * rowb);
+    auto row_addr = [&](int t) { return (const void *)((const char *)a.x + (size_t)(se.pair[t] / a.K) * rowb); };
     StageBatch sb;
-    stage_issue(rows, se.n, H, a.x_dtype, 0, sb);
+    stage_issue(row_addr, H, a.x_dtype, sb);
     GULoads<NJ, RG> L[kGuNB];
     auto issue = [&](int i, GULoads<NJ, RG> &B) { gu_issue<BITS, NJ, RG>(pl, g, H, I, r0_of(i), RB, B); };
     static_for<0, kGuNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging (registers first, so the weight loads stay in flight)
-    stage_convert<BITS>(se.n, H, a.x_dtype, 0, sb, lds);
-    stage_rest<BITS>(rows, se.n, H, a.x_dtype, lds);
+    stage_finish<BITS>(row_addr, se.n, H, a.x_dtype, sb, lds);
     __syncthreads();
 
     // 3. units: each loaded unit meets every token
@@ -254,18 +253,15 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const SmallRec 
     auto r0_of = [&](int i) { return min(ub + min(i, last) * kWaves, nblk - 1) * RB; };
 
     // 1. h rows (consecutive in the expert-ordered buffer), then the first units' weights
-    uint64_t rows[kSmallTokens];
-#pragma unroll
-    for (int t = 0; t < kSmallTokens; ++t) rows[t] = (uint64_t)(a.hbuf + (size_t)(se.base + min(t, se.n - 1)) * I);
+    auto row_addr = [&](int t) { return (const void *)(a.hbuf + (size_t)(se.base + min(t, se.n - 1)) * I); };
     StageBatch sb;
-    stage_issue(rows, se.n, I, MOE_F32, 0, sb);
+    stage_issue(row_addr, I, MOE_F32, sb);
     D8Loads<NJ, RG> L[kDnNB];
     auto issue = [&](int i, D8Loads<NJ, RG> &B) { dn8_issue<BITS, NJ, RG>(pl[2], g, H, I, r0_of(i), B); };
     static_for<0, kDnNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging
-    stage_convert<BITS>(se.n, I, MOE_F32, 0, sb, lds);
-    stage_rest<BITS>(rows, se.n, I, MOE_F32, lds);
+    stage_finish<BITS>(row_addr, se.n, I, MOE_F32, sb, lds);
     __syncthreads();
 
     // 3. units
