@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -94,7 +95,33 @@ struct Carve {
     }
 };
 
-size_t route_ws(const moe_dims *d, int T) { return r256((size_t)T * d->n_experts * 4); }
+// Per-device side stream of the batched path (created on first use, kept until the process ends;
+// default priority, non-blocking with respect to the null stream).
+std::mutex g_side_mu;
+std::vector<moe::SideStream> g_side;
+int side_stream(const moe::SideStream **out) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return fail(MOE_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if ((int)g_side.size() <= dev) g_side.resize(dev + 1, moe::SideStream{nullptr, nullptr, nullptr});
+    moe::SideStream &ss = g_side[dev];
+    if (!ss.stream) {
+        moe::SideStream n{nullptr, nullptr, nullptr};
+        hipError_t e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "side stream: %s", hipGetErrorString(e));
+        ss = n;
+    }
+    *out = &ss;
+    return MOE_OK;
+}
+
+// Router workspace: logits (when the caller passes none), then for T > 1 the normalised rows that
+// the MFMA router reads (optional: without room for them the matvec router normalises in place).
+size_t route_ws(const moe_dims *d, int T) {
+    return r256((size_t)T * d->n_experts * 4) + (T > 1 ? r256((size_t)T * d->hidden * 4) : 0);
+}
 // Batched path workspace: grouping tables, SwiGLU outputs in expert order, normalised rows.
 struct GroupedWs {
     int32_t *off, *ntiles, *perm, *tiles, *nsmall;
@@ -326,12 +353,17 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
     if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
     if (!aligned(idx, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)))
         return fail(MOE_ERR_ALIGN, "idx/w/logits not 4-byte aligned");
-    const size_t need = logits ? 0 : route_ws(dims, T);
-    if (int s = check_ws(ws, ws_bytes, need)) return s;
-    float *lg = logits ? logits : (float *)ws;
+    Carve c{(char *)ws};
+    float *lg = logits ? logits : c.take<float>((size_t)T * dims->n_experts);
+    if (int s = check_ws(ws, ws_bytes, c.off)) return s;
+    float *xn = nullptr;
+    if (T > 1 && ws) {
+        float *p = c.take<float>((size_t)T * dims->hidden);
+        if (ws_bytes >= c.off) xn = p;
+    }
     hipStream_t st = (hipStream_t)stream;
     moe::RouterLaunch ra{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, layer->router,
-                         layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T};
+                         layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T, xn};
     if (int s = launched(moe::launch_router(ra, st), "router")) return s;
     moe::TopkLaunch ta{lg, dims->n_experts, dims->top_k, T, idx, w};
     if (int s = launched(moe::launch_topk(ta, st), "top-k")) return s;
@@ -369,8 +401,13 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
         if (int s = launched(moe::launch_group(gl, st), "group")) return s;
         moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, g.off, g.perm,
                               g.tiles, g.ntiles, g.small, g.nsmall, g.hbuf, y, {}, {}};
+        const moe::SideStream *side = nullptr;
+        if (small)
+            if (int s = side_stream(&side)) return s;
+        // the fork/join events are shared per device: enqueue the forked section under the lock
+        std::lock_guard<std::mutex> lock(g_side_mu);
         if (int s = launched(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts),
-                                                     small ? grouped_max_small(dims, T) : 0, st),
+                                                     small ? grouped_max_small(dims, T) : 0, st, side),
                              "grouped ffn"))
             return s;
         return ok();
@@ -437,7 +474,8 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
         float *ol = l == n_layers - 1 ? out : W.xbuf + (size_t)(l & 1) * H;
         int32_t *idx_l = idx ? idx + (size_t)l * K : nullptr;
         float *w_l = w ? w + (size_t)l * K : nullptr;
-        moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, W.logits, H, E, 1};
+        moe::RouterLaunch ra{xl, xdt, H, L.norm_w, L.norm_eps, L.router, L.router_dtype, L.logit_bias, W.logits, H, E, 1,
+                             nullptr};
         if (!separate) {
             moe::LayerLaunch la{};
             la.r = ra;

@@ -435,6 +435,7 @@ static hipError_t router_impl(const RouterLaunch &a, hipStream_t s, const Kernel
 }
 
 hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev) {
+    if (router_mfma_fits(a) && !ev.start && !ev.stop) return launch_router_mfma(a, s);
     if (a.router_dtype != MOE_BF16) return router_impl<MOE_F32, false>(a, s, ev);
     const bool split = !(a.x_dtype == MOE_BF16 && a.norm_w == nullptr);
     return split ? router_impl<MOE_BF16, true>(a, s, ev) : router_impl<MOE_BF16, false>(a, s, ev);

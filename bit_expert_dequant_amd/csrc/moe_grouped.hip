@@ -282,24 +282,27 @@ __global__ void __launch_bounds__(256) k_norm_rows(const void *x, int x_dtype, c
 // --------------------------------------------------------------------------- shared GEMM pieces
 // Staging of K columns [kc, kc+kKC) of the tile's tokens: each of the 256 threads owns 32 columns
 // (one slot) of one token row.  The loads (16 bytes each: 4 for bf16, 8 for fp32, none for a row
-// that is absent or a slot past K) are issued by xload before the next chunk's weight loads, and
-// converted by xstage into the pair order of BITS (hi, and lo when SPLIT) plus the group sums.
+// that is absent or a slot past K) are issued by xload one chunk ahead, together with that chunk's
+// weight loads, and converted by xstage into the pair order of BITS (hi, and lo when SPLIT) plus
+// the group sums.
+template <int DT>
 struct XChunk {
-    u32x4 q[8];
+    u32x4 q[DT == MOE_BF16 ? 4 : 8];
 };
-__device__ __forceinline__ void xload(const void *rowp, int dtype, int kc, int K, XChunk &xc) {
+template <int DT>
+__device__ __forceinline__ void xload(const void *rowp, int kc, int K, XChunk<DT> &xc) {
+    constexpr int NB = DT == MOE_BF16 ? 4 : 8;
     const int c0 = kc + 32 * (threadIdx.x & 7);
     const bool ok = rowp != nullptr && c0 < K;                 // K is a multiple of 64: all or none
-    const int nb = dtype == MOE_BF16 ? 4 : 8;
-    const GLOBAL_AS u32x4 *p = (const GLOBAL_AS u32x4 *)((const char *)rowp + (size_t)c0 * (dtype == MOE_BF16 ? 2 : 4));
+    const GLOBAL_AS u32x4 *p = (const GLOBAL_AS u32x4 *)((const char *)rowp + (size_t)c0 * (DT == MOE_BF16 ? 2 : 4));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xc.q[i] = (ok && i < nb) ? p[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NB; ++i) xc.q[i] = ok ? p[i] : u32x4{0u, 0u, 0u, 0u};
 }
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ void xstage(const XChunk &xc, int dtype, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+template <int BITS, bool SPLIT, int DT>
+__device__ __forceinline__ void xstage(const XChunk<DT> &xc, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
     const int row = threadIdx.x >> 3, slot = threadIdx.x & 7;     // 32 rows x 8 slots of 32 columns
     float v[32];
-    if (dtype == MOE_BF16) {
+    if constexpr (DT == MOE_BF16) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t w = xc.q[i >> 2][i & 3];
@@ -375,30 +378,31 @@ __device__ __forceinline__ bool tile_info(const GroupedLaunch &a, TileInfo &ti) 
 }
 
 // --------------------------------------------------------------------------- gate/up
+// Activations and weights of chunk kc + kKC are requested before chunk kc is staged and multiplied
+// (branch-free: past the last chunk the activation loads are off and the weight loads re-read the
+// last group), so one chunk of both is always in flight behind the MFMA work.
 template <int BITS, bool SPLIT>
 __device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, gwords sg, gbytes qu, gwords su,
                         const int *s_tok, uint32_t *s_hi, uint32_t *s_lo, float *s_sum) {
+    constexpr int DT = SPLIT ? MOE_F32 : MOE_BF16;     // the launcher picks SPLIT from the dtype
     const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
     const int r = blockIdx.x * kTN + wave * 32 + (lane & 31);
     const int rc = min(r, I - 1);
     f32x16 accG = {}, accU = {};
-    const int xdt = a.x_dtype;
     const int trow = s_tok[threadIdx.x >> 3];
-    const void *xrow = trow < 0 ? nullptr : (const char *)a.x + (size_t)trow * H * (xdt == MOE_BF16 ? 2 : 4);
-    // weights of chunk kc + kKC are requested before chunk kc is staged and multiplied
+    const void *xrow = trow < 0 ? nullptr : (const char *)a.x + (size_t)trow * H * (DT == MOE_BF16 ? 2 : 4);
+    XChunk<DT> xc[2];
     u32x4 q_g[2][4], q_u[2][4];
     uint32_t s_g[2][4], s_u[2][4];
+    xload<DT>(xrow, 0, H, xc[0]);
     load_chunk_w<BITS>(qg, sg, rc, H, 0, h, q_g[0], s_g[0]);
     load_chunk_w<BITS>(qu, su, rc, H, 0, h, q_u[0], s_u[0]);
     auto chunk = [&](int kc, int cur) {
-        XChunk xc;
-        xload(xrow, xdt, kc, H, xc);
-        if (kc + kKC < H) {
-            load_chunk_w<BITS>(qg, sg, rc, H, kc + kKC, h, q_g[cur ^ 1], s_g[cur ^ 1]);
-            load_chunk_w<BITS>(qu, su, rc, H, kc + kKC, h, q_u[cur ^ 1], s_u[cur ^ 1]);
-        }
+        xload<DT>(xrow, kc + kKC, H, xc[cur ^ 1]);
+        load_chunk_w<BITS>(qg, sg, rc, H, kc + kKC, h, q_g[cur ^ 1], s_g[cur ^ 1]);
+        load_chunk_w<BITS>(qu, su, rc, H, kc + kKC, h, q_u[cur ^ 1], s_u[cur ^ 1]);
         __syncthreads();                        // previous chunk fully consumed
-        xstage<BITS, SPLIT>(xc, xdt, s_hi, s_lo, s_sum);
+        xstage<BITS, SPLIT, DT>(xc[cur], s_hi, s_lo, s_sum);
         __syncthreads();
         const int m = lane & 31;
 #pragma unroll
@@ -424,7 +428,7 @@ __device__ void gu_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qg, g
     };
     for (int kc = 0; kc < H; kc += 2 * kKC) {
         chunk(kc, 0);
-        if (kc + kKC < H) chunk(kc + kKC, 1);
+        chunk(kc + kKC, 1);                     // past H: nothing to multiply, loads clamped or off
     }
     if (r < I) {
 #pragma unroll
@@ -465,15 +469,16 @@ __device__ void dn_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, g
     const int n = ti.n;
     const int hr = threadIdx.x >> 3;
     const void *hrow = hr < n ? (const void *)(a.hbuf + (size_t)(ti.base + ti.m0 + hr) * I) : nullptr;
+    XChunk<MOE_F32> xc[2];
     u32x4 qv[2][4];
     uint32_t sv[2][4];
+    xload<MOE_F32>(hrow, 0, I, xc[0]);
     load_chunk_w<BITS>(qd, sd, rc, I, 0, h, qv[0], sv[0]);
     auto chunk = [&](int kc, int cur) {
-        XChunk xc;
-        xload(hrow, MOE_F32, kc, I, xc);
-        if (kc + kKC < I) load_chunk_w<BITS>(qd, sd, rc, I, kc + kKC, h, qv[cur ^ 1], sv[cur ^ 1]);
+        xload<MOE_F32>(hrow, kc + kKC, I, xc[cur ^ 1]);
+        load_chunk_w<BITS>(qd, sd, rc, I, kc + kKC, h, qv[cur ^ 1], sv[cur ^ 1]);
         __syncthreads();
-        xstage<BITS, true>(xc, MOE_F32, s_hi, s_lo, s_sum);
+        xstage<BITS, true, MOE_F32>(xc[cur], s_hi, s_lo, s_sum);
         __syncthreads();
         const int m = lane & 31;
 #pragma unroll
@@ -492,7 +497,7 @@ __device__ void dn_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes qd, g
     };
     for (int kc = 0; kc < I; kc += 2 * kKC) {
         chunk(kc, 0);
-        if (kc + kKC < I) chunk(kc + kKC, 1);
+        chunk(kc + kKC, 1);
     }
     if (r < H) {
 #pragma unroll
@@ -528,7 +533,7 @@ __global__ void __launch_bounds__(256) k_dn_mfma(GroupedLaunch a) {
 // while the current one is multiplied.  Against the chunked kernel this stages h once per 1024
 // output rows instead of once per 128 and keeps two row blocks of weights in flight per wave.
 constexpr int kDnResI = 1024;              // largest I staged whole (LDS ~132 KiB)
-constexpr int kDnRB = 8;                   // 128-row blocks per workgroup
+constexpr int kDnRB = 4;                   // 128-row blocks per workgroup
 constexpr int kDnCh = kDnResI / kKC;       // chunks of kKC columns per row
 
 __host__ __device__ __forceinline__ int dn_res_rowdw(int I) { return ((I + kKC - 1) / kKC) * (kKC / 2) + 4; }
@@ -547,8 +552,8 @@ __device__ void dn_res_tile(const GroupedLaunch &a, const TileInfo &ti, gbytes q
         const int hr = threadIdx.x >> 3, slot = threadIdx.x & 7;
         const void *hrow = hr < n ? (const void *)(a.hbuf + (size_t)(ti.base + ti.m0 + hr) * I) : nullptr;
         for (int c = 0; c < nch; ++c) {
-            XChunk xc;
-            xload(hrow, MOE_F32, c * kKC, I, xc);
+            XChunk<MOE_F32> xc;
+            xload<MOE_F32>(hrow, c * kKC, I, xc);
             float v[32];
 #pragma unroll
             for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(xc.q[i >> 2][i & 3]);
@@ -652,6 +657,84 @@ __global__ void __launch_bounds__(256) k_dn_res(GroupedLaunch a) {
     else dn_res_tile<4>(a, ti, q[2], sb[2], s_pair, s_hi, s_lo, s_sum);
 }
 
+// --------------------------------------------------------------------------- batched router
+// logits[t][e] = sum_c x[t][c] R[e][c] (+ bias[e]) for a bf16 router R, as v_mfma_f32_32x32x16_bf16
+// tiles of 32 tokens (A rows) by 32 experts (B columns).  The four waves of a workgroup take the
+// four quarters of the K range and meet in LDS in a fixed order.  Both operands come straight from
+// memory (the router rows and the token rows are re-read from L2 by the other tiles): inside each
+// block of 64 columns lane half h takes columns 32h .. 32h+31, 8 per MFMA step, for A and B alike
+// (the order of the K-values inside a step only has to agree between the operands), so each lane
+// reads 64 contiguous bytes of its router row per block.  Activations that are not exactly bf16
+// are split into hi + lo bf16 parts, two MFMAs per step, as in the matvec router.
+constexpr int kRtTile = 32;
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) k_router_mfma(RouterLaunch a) {
+    __shared__ float s_red[3][16][64];
+    constexpr int XB = SPLIT ? 4 : 2;                  // activation bytes
+    constexpr int XQ = SPLIT ? 8 : 4;                  // 16-byte loads of activations per block and lane
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, m = lane & 31;
+    const int H = a.H, E = a.E, T = a.T;
+    const int t0 = blockIdx.y * kRtTile, e0 = blockIdx.x * kRtTile;
+    const int tok = min(t0 + m, T - 1), ex = min(e0 + m, E - 1);      // clamped rows are not written
+    const int kq = H / 4, k0 = wave * kq, nblk = kq / 64;
+    const GLOBAL_AS uint8_t *rrow = (const GLOBAL_AS uint8_t *)a.router + ((size_t)ex * H + k0 + 32 * h) * 2;
+    const GLOBAL_AS uint8_t *xrow = (const GLOBAL_AS uint8_t *)a.x + ((size_t)tok * a.x_stride + k0 + 32 * h) * XB;
+    constexpr int NB = 4;                              // blocks in flight per wave
+    u32x4 bq[NB][4], xq[NB][XQ];
+    auto load = [&](int blk, int buf) {
+        blk = min(blk, nblk - 1);                      // past the end: a harmless re-read
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bq[buf][i] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(rrow + (size_t)blk * 128 + 16 * i));
+#pragma unroll
+        for (int i = 0; i < XQ; ++i) xq[buf][i] = *(const GLOBAL_AS u32x4 *)(xrow + (size_t)blk * 64 * XB + 16 * i);
+    };
+    f32x16 acc = {};
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if constexpr (SPLIT) {
+                u32x4 hi, lo;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w0 = xq[buf][2 * st + (j >> 1)][2 * (j & 1)], w1 = xq[buf][2 * st + (j >> 1)][2 * (j & 1) + 1];
+                    const float f0 = __uint_as_float(w0), f1 = __uint_as_float(w1);
+                    const uint32_t h0 = bf16_rne(f0), h1 = bf16_rne(f1);
+                    hi[j] = h0 | (h1 << 16);
+                    lo[j] = bf16_rne(f0 - bf16_f32(h0)) | (bf16_rne(f1 - bf16_f32(h1)) << 16);
+                }
+                acc = mfma(hi, bq[buf][st], acc);
+                acc = mfma(lo, bq[buf][st], acc);
+            } else {
+                acc = mfma(xq[buf][st], bq[buf][st], acc);
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load(i, i);
+    for (int b = 0; b < nblk; b += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (b + i < nblk) compute(i);
+            load(b + NB + i, i);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s_red[wave - 1][v][lane] = acc[v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int e = e0 + m;
+        const float bias = (a.logit_bias && e < E) ? a.logit_bias[e] : 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float sum = ((acc[v] + s_red[0][v][lane]) + s_red[1][v][lane]) + s_red[2][v][lane];
+            const int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (t < T && e < E) a.logits[(size_t)t * E + e] = sum + bias;
+        }
+    }
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
@@ -679,19 +762,55 @@ hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, 
     return hipGetLastError();
 }
 
+bool router_mfma_fits(const RouterLaunch &a) {
+    return a.router_dtype == MOE_BF16 && a.T > 1 && a.H % 256 == 0 && (a.norm_w == nullptr || a.xn_ws != nullptr);
+}
+
+hipError_t launch_router_mfma(const RouterLaunch &a_in, hipStream_t s) {
+    RouterLaunch a = a_in;
+    if (a.norm_w) {
+        // RMSNorm of every row into the workspace, then the fp32 rows feed the MFMA tiles
+        if (hipError_t e = launch_norm_rows(a.x, a.x_dtype, a.norm_w, a.eps, a.H, a.T, a.xn_ws, s)) return e;
+        a.x = a.xn_ws;
+        a.x_dtype = MOE_F32;
+        a.x_stride = a.H;
+        a.norm_w = nullptr;
+    }
+    const dim3 grid((a.E + kRtTile - 1) / kRtTile, (a.T + kRtTile - 1) / kRtTile);
+    if (a.x_dtype == MOE_BF16) hipLaunchKernelGGL(k_router_mfma<false>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_router_mfma<true>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 static hipError_t grouped_down_mfma(const GroupedLaunch &a, int max_tiles, hipStream_t s);
 
-// Order: MFMA gate/up (busy experts), small-expert gate/up, MFMA down, small-expert down.
-hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s) {
+// The MFMA chain (busy experts) and the small-expert chain touch disjoint rows of h and y, so with a
+// side stream they run concurrently: the MFMA kernels have few, long, latency-bound workgroups and
+// the small-expert kernels fill the rest of the machine.  Without one they run in sequence.
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s,
+                              const SideStream *side) {
+    const bool fork = side != nullptr && max_small > 0;
+    hipStream_t sm = s;
+    if (fork) {
+        if (hipError_t e = hipEventRecord(side->fork, s)) return e;
+        if (hipError_t e = hipStreamWaitEvent(side->stream, side->fork, 0)) return e;
+        sm = side->stream;
+    }
     const bool split = a.x_dtype != MOE_BF16;
     dim3 g1((a.I + kTN - 1) / kTN, max_tiles);
-    if (split) hipLaunchKernelGGL(k_gu_mfma<true>, g1, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_gu_mfma<false>, g1, dim3(256), 0, s, a);
+    if (split) hipLaunchKernelGGL(k_gu_mfma<true>, g1, dim3(256), 0, sm, a);
+    else hipLaunchKernelGGL(k_gu_mfma<false>, g1, dim3(256), 0, sm, a);
     if (hipError_t e = hipGetLastError()) return e;
-    if (max_small > 0)
+    if (hipError_t e = grouped_down_mfma(a, max_tiles, sm)) return e;
+    if (max_small > 0) {
         if (hipError_t e = launch_small_gateup(a, max_small, s)) return e;
-    if (hipError_t e = grouped_down_mfma(a, max_tiles, s)) return e;
-    return max_small > 0 ? launch_small_down(a, max_small, s) : hipSuccess;
+        if (hipError_t e = launch_small_down(a, max_small, s)) return e;
+    }
+    if (fork) {
+        if (hipError_t e = hipEventRecord(side->join, side->stream)) return e;
+        if (hipError_t e = hipStreamWaitEvent(s, side->join, 0)) return e;
+    }
+    return hipSuccess;
 }
 
 static hipError_t grouped_down_mfma(const GroupedLaunch &a, int max_tiles, hipStream_t s) {

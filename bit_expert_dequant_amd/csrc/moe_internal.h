@@ -59,8 +59,12 @@ struct RouterLaunch {
     const float *logit_bias;
     float *logits;                                 // [T][E]
     int H, E, T;
+    float *xn_ws;                                  // [T][H] workspace for normalised rows, or NULL
 };
 hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev = {});
+// Batched bf16 router as MFMA tiles (moe_grouped.hip); false when the shape does not fit it.
+bool router_mfma_fits(const RouterLaunch &a);
+hipError_t launch_router_mfma(const RouterLaunch &a, hipStream_t s);
 
 struct TopkLaunch {
     const float *logits; int E, K, T;
@@ -139,7 +143,13 @@ struct GroupedLaunch {
     float *y;                                      // [T*K][H]
     RowGeo geo; PlaneTable pt;                     // set by the small-expert launchers
 };
-hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s);
+// A second stream of the device with its fork and join events (see launch_grouped_ffn).
+struct SideStream {
+    hipStream_t stream;
+    hipEvent_t fork, join;
+};
+hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_small, hipStream_t s,
+                              const SideStream *side);
 // Integer dot-product kernels for the small experts (moe_batched8.hip); false when the shapes do
 // not fit them (everything then takes the MFMA tiles).
 bool small_path_fits(int H, int I);
