@@ -17,8 +17,6 @@
 // The dequantisation is the decode path's: w = q*s + b summed per slot as s * sum(q x) +
 // b * sum(x) (the FMA rewrite on the lilting.ch page "397Bパラメータモデルを48GB MacBookで動かす
 // Flash-MoE", section "Metal Compute Shaders"), with sum(q x) an exact integer dot product.
-#include <type_traits>
-
 #include "moe_device.h"
 
 namespace moe {
@@ -32,103 +30,18 @@ constexpr int kDnUPW = 8, kDnNB = 3;
 template <int NJ>
 __host__ __device__ constexpr int dn8_rg() { return NJ >= 4 ? 2 : NJ == 2 ? 4 : 8; }
 
-__host__ __device__ __forceinline__ int row_dw(int cols) { return cols / 2 + cols / 16; }   // planes + xs
-
-// The workgroup's list entry (one scalar load; entries past the list end exit at once).
-__device__ __forceinline__ bool small_entry(const GroupedLaunch &a, SmallRec &r) {
-    const int j = blockIdx.y;
-    const int ns = *a.nsmall;
-    r = a.small[j];
-    return j < ns;
-}
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
+// Digit-plane staging of one chunk of token row t (see stage_finish): row t occupies row_dw(cols)
+// dwords at lds + t * row_dw(cols), digit planes in the order of code width BITS, then its slots'
+// {sx, sum of x}.
+template <int BITS>
+struct DigitStage {
+    uint32_t *lds;
+    int cols;
+    __device__ __forceinline__ void operator()(int t, int mc, bool valid, const float (&v)[16]) const {
+        uint32_t *d = lds + t * row_dw(cols);
+        stage_chunk(mc, valid, v, BITS == 4 ? d : nullptr, BITS == 2 ? d : nullptr, (float2 *)(d + cols / 2));
     }
-}
-
-// Staging of the expert's token rows into LDS: row t occupies row_dw(cols) dwords at
-// lds + t * row_dw(cols), digit planes in the order of code width BITS, then its slots' {sx, sum
-// of x}.  Thread `tid` takes chunk tid (+ kBlock, ... for rows of more than kBlock chunks) of every
-// row, so a token's index is a compile-time constant everywhere and its row address a uniform
-// value: row_addr(t) for t < kSmallTokens (t >= n gives a duplicate of a present row).  Tokens go
-// in two batches of four; the loads of the first pass's first batch are issued by stage_issue,
-// before the caller's first weight loads, and everything else happens in stage_finish.  Every
-// thread of the workgroup calls both; the caller puts a barrier after stage_finish.
-struct StageBatch {
-    Chunk16 c[4];
 };
-template <int B, typename RowAddr>
-__device__ __forceinline__ void stage_batch_issue(RowAddr &&row_addr, int dtype, int mc, StageBatch &sb) {
-    static_for<0, 4>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        issue_chunk16(row_addr(4 * B + j), dtype, mc, sb.c[j]);
-    });
-}
-template <int BITS, int B>
-__device__ __forceinline__ void stage_batch_convert(int n, int cols, int dtype, int m, const StageBatch &sb,
-                                                    uint32_t *lds) {
-    const int nch = cols / 16, rd = row_dw(cols);
-    const bool valid = m < nch;
-    const int mc = min(m, nch - 1);
-    static_for<0, 4>([&](auto jc) {
-        constexpr int t = 4 * B + decltype(jc)::value;
-        if (t < n) {                                                         // uniform
-            float v[16];
-            chunk16_f32(sb.c[t - 4 * B], dtype, v);
-            uint32_t *d = lds + t * rd;
-            stage_chunk(mc, valid, v, BITS == 4 ? d : nullptr, BITS == 2 ? d : nullptr, (float2 *)(d + cols / 2));
-        }
-    });
-}
-template <typename RowAddr>
-__device__ __forceinline__ void stage_issue(RowAddr &&row_addr, int cols, int dtype, StageBatch &sb) {
-    stage_batch_issue<0>(row_addr, dtype, min((int)threadIdx.x, cols / 16 - 1), sb);
-}
-template <int BITS, typename RowAddr>
-__device__ __forceinline__ void stage_finish(RowAddr &&row_addr, int n, int cols, int dtype, StageBatch &sb,
-                                             uint32_t *lds) {
-    static_assert(kSmallTokens == 8, "two batches of four tokens");
-    const int nch = cols / 16;
-    for (int m0 = 0; m0 < nch; m0 += kBlock) {                               // uniform; usually one pass
-        const int m = m0 + (int)threadIdx.x, mc = min(m, nch - 1);
-        if (m0 > 0) stage_batch_issue<0>(row_addr, dtype, mc, sb);
-        stage_batch_convert<BITS, 0>(n, cols, dtype, m, sb, lds);
-        if (n > 4) {
-            stage_batch_issue<1>(row_addr, dtype, mc, sb);
-            stage_batch_convert<BITS, 1>(n, cols, dtype, m, sb, lds);
-        }
-    }
-}
-
-// The unit pipeline of one wave: UPW units, NB register buffers, the loads of unit i + NB - 1 issued
-// before unit i is finished, so NB - 1 units are in flight while one is computed.  Fully unrolled
-// (buffer indices are compile-time) and branch-free around the loads: a wave with fewer than UPW
-// units (the ragged end of a matrix) re-reads its last unit's rows instead, and only the finishing
-// step is skipped.  issue(i, buf) must clamp i itself.
-template <int UPW, int NB, typename Buf, typename Issue, typename Finish>
-__device__ __forceinline__ void unit_pipeline(int nu, Buf (&B)[NB], Issue &&issue, Finish &&finish) {
-    static_for<0, UPW>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + NB - 1 < UPW) issue(i + NB - 1, B[(i + NB - 1) % NB]);
-        if (i < nu) finish(i, B[i % NB]);
-    });
-}
-
-// Slot operands of this lane for one staged row: FULL (GS != 0) when every lane's slots exist.
-template <int NJ, int GS>
-__device__ __forceinline__ void row_slots(const ActView &av, const Geo &g, uint32_t (&D)[NJ][kSlotDw], float2 (&XS)[NJ]) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int slot = g.lsl + 64 * j;
-        if constexpr (GS != 0) load_act_slot_full(av, slot, D[j], XS[j]);
-        else load_act_slot(av, slot, slot < g.spr, D[j], XS[j]);
-    }
-}
 
 // --------------------------------------------------------------------------- gate/up
 // GS: lanes per row group when it is a compile-time 32 or 64 and every lane's slots exist, else 0
@@ -157,7 +70,7 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const SmallRec 
     static_for<0, kGuNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging (registers first, so the weight loads stay in flight)
-    stage_finish<BITS>(row_addr, se.n, H, a.x_dtype, sb, lds);
+    stage_finish(row_addr, se.n, H, a.x_dtype, sb, DigitStage<BITS>{lds, H});
     __syncthreads();
 
     // 3. units: each loaded unit meets every token
@@ -261,7 +174,7 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const SmallRec 
     static_for<0, kDnNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging
-    stage_finish<BITS>(row_addr, se.n, I, MOE_F32, sb, lds);
+    stage_finish(row_addr, se.n, I, MOE_F32, sb, DigitStage<BITS>{lds, I});
     __syncthreads();
 
     // 3. units

@@ -506,7 +506,8 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hip
     int dev = 0, cus = 0;
     if (hipError_t e = hipGetDevice(&dev)) return e;
     if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return e;
-    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)(cus * 8)), dim3(kBlock), 0, s, (const u32x4 *)buf, bytes / 16,
+    // two workgroups per CU measured fastest (7.06 TB/s against 6.33 with eight, 4 GiB)
+    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)(cus * 2)), dim3(kBlock), 0, s, (const u32x4 *)buf, bytes / 16,
                        sink);
     return hipGetLastError();
 }

@@ -798,6 +798,102 @@ __device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, c
 // xs [I/32] float2 (I is a multiple of 64, so every part stays 16-byte aligned).
 __host__ __device__ __forceinline__ int down_lds_per_expert(int I) { return I / 2 + I / 16; }
 
+// --------------------------------------------------------------------------- small-expert helpers
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The unit pipeline of one wave: UPW units, NB register buffers, the loads of unit i + NB - 1 issued
+// before unit i is finished, so NB - 1 units are in flight while one is computed.  Fully unrolled
+// (buffer indices are compile-time) and branch-free around the loads: a wave with fewer than UPW
+// units (the ragged end of a matrix) re-reads its last unit's rows instead, and only the finishing
+// step is skipped.  issue(i, buf) must clamp i itself.
+template <int UPW, int NB, typename Buf, typename Issue, typename Finish>
+__device__ __forceinline__ void unit_pipeline(int nu, Buf (&B)[NB], Issue &&issue, Finish &&finish) {
+    static_for<0, UPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + NB - 1 < UPW) issue(i + NB - 1, B[(i + NB - 1) % NB]);
+        if (i < nu) finish(i, B[i % NB]);
+    });
+}
+
+// Slot operands of this lane for one staged row: FULL (GS != 0) when every lane's slots exist.
+template <int NJ, int GS>
+__device__ __forceinline__ void row_slots(const ActView &av, const Geo &g, uint32_t (&D)[NJ][kSlotDw], float2 (&XS)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int slot = g.lsl + 64 * j;
+        if constexpr (GS != 0) load_act_slot_full(av, slot, D[j], XS[j]);
+        else load_act_slot(av, slot, slot < g.spr, D[j], XS[j]);
+    }
+}
+
+// The workgroup's list entry (one scalar load; entries past the list end exit at once).
+__device__ __forceinline__ bool small_entry(const GroupedLaunch &a, SmallRec &r) {
+    const int j = blockIdx.y;
+    const int ns = *a.nsmall;
+    r = a.small[j];
+    return j < ns;
+}
+
+// Staging of an expert's token rows into LDS.  Thread `tid` takes chunk tid (+ kBlock, ... for rows
+// of more than kBlock chunks) of 16 activations of every row, so a token's index is a compile-time
+// constant everywhere and its row address a uniform value: row_addr(t) for t < kSmallTokens (t >= n
+// gives a duplicate of a present row).  Tokens go in two batches of four; the loads of the first
+// pass's first batch are issued by stage_issue, before the caller's first weight loads, and
+// everything else happens in stage_finish, which hands every chunk to conv(t, chunk, valid, v).
+// Every thread of the workgroup calls both (conv may exchange data between the lanes of a wave);
+// the caller puts a barrier after stage_finish.
+struct StageBatch {
+    Chunk16 c[4];
+};
+template <int B, typename RowAddr>
+__device__ __forceinline__ void stage_batch_issue(RowAddr &&row_addr, int dtype, int mc, StageBatch &sb) {
+    static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        issue_chunk16(row_addr(4 * B + j), dtype, mc, sb.c[j]);
+    });
+}
+template <int B, typename Conv>
+__device__ __forceinline__ void stage_batch_convert(int n, int nch, int dtype, int m, const StageBatch &sb, Conv &&conv) {
+    const bool valid = m < nch;
+    const int mc = min(m, nch - 1);
+    static_for<0, 4>([&](auto jc) {
+        constexpr int t = 4 * B + decltype(jc)::value;
+        if (t < n) {                                                         // uniform
+            float v[16];
+            chunk16_f32(sb.c[t - 4 * B], dtype, v);
+            conv(t, mc, valid, v);
+        }
+    });
+}
+template <typename RowAddr>
+__device__ __forceinline__ void stage_issue(RowAddr &&row_addr, int cols, int dtype, StageBatch &sb) {
+    stage_batch_issue<0>(row_addr, dtype, min((int)threadIdx.x, cols / 16 - 1), sb);
+}
+template <typename RowAddr, typename Conv>
+__device__ __forceinline__ void stage_finish(RowAddr &&row_addr, int n, int cols, int dtype, StageBatch &sb,
+                                             Conv &&conv) {
+    static_assert(kSmallTokens == 8, "two batches of four tokens");
+    const int nch = cols / 16;
+    for (int m0 = 0; m0 < nch; m0 += kBlock) {                               // uniform; usually one pass
+        const int m = m0 + (int)threadIdx.x, mc = min(m, nch - 1);
+        if (m0 > 0) stage_batch_issue<0>(row_addr, dtype, mc, sb);
+        stage_batch_convert<0>(n, nch, dtype, m, sb, conv);
+        if (n > 4) {
+            stage_batch_issue<1>(row_addr, dtype, mc, sb);
+            stage_batch_convert<1>(n, nch, dtype, m, sb, conv);
+        }
+    }
+}
+
+__host__ __device__ __forceinline__ int row_dw(int cols) { return cols / 2 + cols / 16; }   // planes + xs
+
 int nj_for(int cols) {
     const int spr = cols / 32;
     const int nj = spr >= 64 ? (spr + 63) / 64 : 1;

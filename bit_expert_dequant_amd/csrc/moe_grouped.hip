@@ -217,9 +217,11 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
         if (sm1) pos1 = start[c1] + bin_of(p, c1) + (sm0 && c0 == c1 ? 1 : 0);
         if (tid == 0) *a.nsmall = nsm;
     }
-    // bitonic sort, ascending
+    // bitonic sort, ascending: exchange distances of 64 and more through LDS (one barrier each),
+    // the rest of each merge inside the wave with shuffles (one barrier for all of them)
     for (int k = 2; k <= NP2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
+        int j = k >> 1;
+        for (; j >= 64; j >>= 1) {
             for (int i = tid; i < NP2; i += blockDim.x) {
                 const int ixj = i ^ j;
                 if (ixj > i) {
@@ -229,6 +231,15 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
             }
             __syncthreads();
         }
+        for (int i = tid; i < NP2; i += blockDim.x) {       // whole waves, or all of NP2 < 64
+            uint32_t v = s_key[i];
+            for (int jj = j; jj > 0; jj >>= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)v, jj);
+                v = (((i & jj) == 0) == ((i & k) == 0)) ? min(v, o) : max(v, o);
+            }
+            s_key[i] = v;
+        }
+        __syncthreads();
     }
     const int nv = s_off[E];
     for (int i = tid; i < nv; i += blockDim.x) a.perm[i] = (int)(s_key[i] % (uint32_t)P);
