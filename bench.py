@@ -125,7 +125,8 @@ def traffic_from(d: str, workload_key: str):
     fetch = read_counter_csv(os.path.join(d, "fetch"), "FETCH_SIZE")
     write = read_counter_csv(os.path.join(d, "write"), "WRITE_SIZE")
     res = {}
-    for short in ("k_route_gateup", "k_router", "k_gateup", "k_down", "k_gu_mfma", "k_dn_mfma", "k_group"):
+    for short in ("k_route_gateup", "k_router", "k_gateup", "k_down", "k_router_mfma", "k_group", "k_gu_mfma",
+                  "k_dn_mfma", "k_dn_res", "k_gu8", "k_dn8"):
         fk = [k for k in fetch if f"{short}<" in k or f"{short}(" in k]
         wk = [k for k in write if f"{short}<" in k or f"{short}(" in k]
         if not fk or not wk:
