@@ -16,6 +16,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -42,6 +43,9 @@ def parse():
     p.add_argument("--steps", type=int, default=4096)
     p.add_argument("--warmup", type=int, default=512)
     p.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    p.add_argument("--tokens", type=int, default=0,
+                   help="tokens per call through the batched path (2..4096) instead of the config's own; "
+                        "for single-layer configs (small-T multi-token decode)")
     p.add_argument("--graph-steps", type=int, default=0, help="steps per captured graph (0: auto)")
     p.add_argument("--no-graph", action="store_true", help="issue steps eagerly instead of via HIP graphs")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -165,6 +169,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[a.config]
+    if a.tokens:
+        if wl.n_layers != 1 or not 2 <= a.tokens <= 4096:
+            print("--tokens takes 2..4096 and a single-layer config (0, 1, 2 or 4)", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, tokens=a.tokens,
+                                 name=f"{wl.name.split(',')[0]}, {a.tokens} tokens per call (batched path)")
     H, I, E, K = wl.H, wl.I, wl.E, wl.K
     d = M.make_dims(H, I, E, K)
     batched = wl.tokens > 1

@@ -117,10 +117,11 @@ int side_stream(const moe::SideStream **out) {
     return MOE_OK;
 }
 
-// Router workspace: logits (when the caller passes none), then for T > 1 the normalised rows that
-// the MFMA router reads (optional: without room for them the matvec router normalises in place).
+// Router workspace: logits (when the caller passes none), then for T >= kRouterMfmaMinT the
+// normalised rows that the MFMA router reads (optional: without room for them the matvec router
+// normalises in place).
 size_t route_ws(const moe_dims *d, int T) {
-    return r256((size_t)T * d->n_experts * 4) + (T > 1 ? r256((size_t)T * d->hidden * 4) : 0);
+    return r256((size_t)T * d->n_experts * 4) + (T >= moe::kRouterMfmaMinT ? r256((size_t)T * d->hidden * 4) : 0);
 }
 // Batched path workspace: grouping tables, SwiGLU outputs in expert order, normalised rows.
 struct GroupedWs {
@@ -146,9 +147,15 @@ GroupedWs grouped_ws(const moe_dims *d, int T, void *base) {
     return g;
 }
 constexpr int kMaxGroupedPairs = 32768;   // the grouping kernel keeps every pair in LDS
+// Up to this many tokens per call the expert FFN runs the decode kernels with one grid row per
+// token: with few tokens almost every selected expert is distinct, so sharing weight reads saves
+// little, while grouping costs a fixed ~40 us (grouping, two kernel chains).  Measured on the
+// config-1 layer: 29 against 78 us at 2 tokens, 114 against 133 at 16, 206 against 195 at 32.
+constexpr int kPerTokenMaxT = 24;
+bool grouped_ffn(int T) { return T > kPerTokenMaxT; }
 
 size_t ffn_ws(const moe_dims *d, int T) {
-    if (T >= 2) return grouped_ws(d, T, nullptr).bytes;
+    if (grouped_ffn(T)) return grouped_ws(d, T, nullptr).bytes;
     Carve c{nullptr};
     c.take<float>((size_t)T * d->top_k * d->inter);
     c.take<uint64_t>((size_t)T * d->top_k);
@@ -357,7 +364,7 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
     float *lg = logits ? logits : c.take<float>((size_t)T * dims->n_experts);
     if (int s = check_ws(ws, ws_bytes, c.off)) return s;
     float *xn = nullptr;
-    if (T > 1 && ws) {
+    if (T >= moe::kRouterMfmaMinT && ws) {
         float *p = c.take<float>((size_t)T * dims->hidden);
         if (ws_bytes >= c.off) xn = p;
     }
@@ -379,12 +386,12 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     if (T < 1 || T > 65535) return fail(MOE_ERR_SHAPE, "T=%d outside [1, 65535]", T);
     if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
     if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MOE_ERR_ALIGN, "idx/y not 4-byte aligned");
-    if (T >= 2 && T * dims->top_k > kMaxGroupedPairs)
+    if (grouped_ffn(T) && T * dims->top_k > kMaxGroupedPairs)
         return fail(MOE_ERR_UNSUPPORTED, "T*top_k=%d exceeds %d for the grouped path", T * dims->top_k, kMaxGroupedPairs);
     if (int s = check_ws(ws, ws_bytes, ffn_ws(dims, T))) return s;
     hipStream_t st = (hipStream_t)stream;
-    if (T >= 2) {
-        // batched: group the (token, slot) pairs by expert, then the MFMA grouped dequant-GEMMs
+    if (grouped_ffn(T)) {
+        // batched: group the (token, slot) pairs by expert, then the grouped kernels
         GroupedWs g = grouped_ws(dims, T, ws);
         const void *xa = x;
         int xdt = x_dtype;

@@ -774,7 +774,8 @@ hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, 
 }
 
 bool router_mfma_fits(const RouterLaunch &a) {
-    return a.router_dtype == MOE_BF16 && a.T > 1 && a.H % 256 == 0 && (a.norm_w == nullptr || a.xn_ws != nullptr);
+    return a.router_dtype == MOE_BF16 && a.T >= kRouterMfmaMinT && a.H % 256 == 0 &&
+           (a.norm_w == nullptr || a.xn_ws != nullptr);
 }
 
 hipError_t launch_router_mfma(const RouterLaunch &a_in, hipStream_t s) {

@@ -62,7 +62,11 @@ struct RouterLaunch {
     float *xn_ws;                                  // [T][H] workspace for normalised rows, or NULL
 };
 hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev = {});
-// Batched bf16 router as MFMA tiles (moe_grouped.hip); false when the shape does not fit it.
+// Batched bf16 router as MFMA tiles (moe_grouped.hip); false when the shape does not fit it.  From
+// kRouterMfmaMinT tokens on: below that the tiles are too few to fill the GPU (16 workgroups up to
+// 32 tokens at E = 512) and the matvec router, whose workgroups each take 4 experts of one token,
+// is faster.
+constexpr int kRouterMfmaMinT = 64;
 bool router_mfma_fits(const RouterLaunch &a);
 hipError_t launch_router_mfma(const RouterLaunch &a, hipStream_t s);
 

@@ -190,7 +190,7 @@ size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers);
  *   idx    device [T][K] int32, descending weight (ties: lower expert index first)
  *   w      device [T][K] fp32 renormalised weights (each row sums to 1)
  *   logits device [T][E] fp32 pre-softmax logits (bias included), or NULL
- * For T > 1 with a bf16 router (H a multiple of 256) the logits come from MFMA tiles; with a norm
+ * For T >= 64 with a bf16 router (H a multiple of 256) the logits come from MFMA tiles; with a norm
  * weight the normalised rows are first written to the workspace after the logits (the size from
  * moe_workspace_bytes includes them; a smaller workspace that still holds the logits makes the
  * matvec router normalise in registers instead).
@@ -204,8 +204,9 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
  *   x   device [T][H] x_dtype (normalised inside when the layer has a norm weight)
  *   idx device [T][K] int32; an entry outside [0, E) gives a zero row of y
  *   y   device [T][K][H] fp32
- * T == 1 runs the decode matvec kernels (all K experts in one launch per phase); T > 1
- * groups the T*K (token, slot) pairs by expert: experts with more than 8 tokens run the grouped
+ * T <= 24 runs the decode matvec kernels (all K experts in one launch per phase, one grid row
+ * per token); T > 24 groups the T*K (token, slot) pairs by expert (T*K <= 32768): experts with
+ * more than 8 tokens run the grouped
  * dequant-GEMM (MFMA) kernels, the others integer dot-product kernels over their staged tokens.
  * The MFMA kernels run on a second stream of the device, forked from `stream` with an event and
  * joined back to it before the call returns (graph capture follows the fork); the library

@@ -36,12 +36,18 @@ BATCH = [
     ("t64_h2048_i768_e8_k8_2b", 64, 2048, 768, 8, 8, 2, {}),
     ("t40_h4096_i1024_e20_k4_tiered_fp32", 40, 4096, 1024, 20, 4, 4, {"tiered": True, "n_hot": 7, "x_bf16": False}),
     ("t100_h640_i1344_e3_k3_multitile", 100, 640, 1344, 3, 3, 4, {}),
-    # experts with few tokens take the integer dot-product kernels: 2-bit only, a wide row
-    # (four slots per lane), and a mix around the eight-token boundary with fp32 activations
-    ("t12_h1024_i512_e32_k3_2b_few", 12, 1024, 512, 32, 3, 2, {}),
-    ("t10_h8192_i256_e6_k2_wide", 10, 8192, 256, 6, 2, 4, {}),
-    ("t24_h2048_i576_e9_k3_fp32_boundary", 24, 2048, 576, 9, 3, 4, {"x_bf16": False}),
-    ("t16_h3072_i2048_e12_k3_partial_slots", 16, 3072, 2048, 12, 3, 4, {}),
+    # above 24 tokens, experts with few tokens take the integer dot-product kernels: 2-bit only, a
+    # wide row (four slots per lane), a mix around the eight-token boundary with fp32 activations,
+    # and partial slots
+    ("t48_h1024_i512_e64_k2_2b_few", 48, 1024, 512, 64, 2, 2, {}),
+    ("t30_h8192_i256_e24_k2_wide", 30, 8192, 256, 24, 2, 4, {}),
+    ("t32_h2048_i576_e12_k3_fp32_boundary", 32, 2048, 576, 12, 3, 4, {"x_bf16": False}),
+    ("t32_h3072_i2048_e24_k3_partial_slots", 32, 3072, 2048, 24, 3, 4, {}),
+    # up to 24 tokens the decode kernels run one grid row per token
+    ("t24_h4096_i1024_e40_k4_per_token", 24, 4096, 1024, 40, 4, 4, {"tiered": True, "n_hot": 12}),
+    ("t5_h1024_i512_e16_k4_norm_per_token", 5, 1024, 512, 16, 4, 4, {"norm": True, "x_bf16": False}),
+    # from 64 tokens the router runs as MFMA tiles; with a norm weight on normalised fp32 rows
+    ("t80_h1024_i256_e32_k4_norm_mfma_router", 80, 1024, 256, 32, 4, 4, {"norm": True}),
 ]
 
 
