@@ -111,3 +111,41 @@ def test_batched_deterministic_and_given_routing():
             e = int(idx[t, k])
             if 0 <= e < wl.E:
                 assert_close(y[t, k], cache.y(e, x64[t]), f"token {t} slot {k} expert {e}")
+
+
+ROUTER_CASES = [
+    # name, T, H, E, extra: MFMA tiles from 64 tokens (bf16 rows; normalised fp32 rows split into
+    # hi + lo; ragged token and expert tiles), the matvec router below
+    ("t64_h4096_e512_bf16_tiles", 64, 4096, 512, {}),
+    ("t96_h1024_e40_norm_split_ragged", 96, 1024, 40, {"norm": True}),
+    ("t70_h512_e8_fp32_split", 70, 512, 8, {"x_bf16": False}),
+    ("t8_h4096_e512_matvec", 8, 4096, 512, {"zipf": True}),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES, ids=[c[0] for c in ROUTER_CASES])
+def test_batched_router_logits(case):
+    """moe_route's logits for T tokens against the oracle's, element by element (tolerance 1e-4 of
+    the logits' rms: the fp32 sums over H and the hi + lo split of non-bf16 rows stay far below)."""
+    name, T, H, E, extra = case
+    print(f"[router] {name}", flush=True)
+    wl = small_workload(name, 0x70C0 + T + H + E, H, 256, E, 4, 4, **extra)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    bank = wl.tokens_bank(T)
+    x = act_tensor(wl, bank)
+    d = M.make_dims(H, 256, E, 4)
+    idx = torch.empty(T, 4, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, 4, dtype=torch.float32, device="cuda")
+    lg = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_route(d, dl.L, x, idx, w, logits=lg, ws=M.workspace(M.MOE_OP_ROUTE, d, T))
+    torch.cuda.synchronize()
+    lg_h, idx_h = lg.cpu().numpy(), idx.cpu().numpy()
+    x64 = act_f64(wl, bank)
+    for t in range(T):
+        n = oracle.rmsnorm(x64[t], ol.norm_w, ol.norm_eps) if ol.norm_w is not None else x64[t]
+        ref = oracle.router_logits(ol.router, n, ol.logit_bias, wl.router_bf16)
+        assert_close(lg_h[t], ref, f"{name} token {t} logits", rel=1e-4)
+        ri, _, margin = oracle.route(ref, 4)
+        if margin > MIN_MARGIN:
+            assert list(idx_h[t]) == list(ri), f"{name} token {t}"
