@@ -77,6 +77,8 @@ def lib():
         L.orc_combine.argtypes = [P, P, c_int, c_int, P, P]
         L.orc_silu_export.restype = c_dbl
         L.orc_silu_export.argtypes = [c_dbl]
+        L.orc_quantize.argtypes = [P, c_int, c_int, c_int, P, P, P]
+        L.orc_quantize.restype = None
         _lib = L
     return _lib
 
@@ -199,6 +201,18 @@ def combine(y: np.ndarray, w: np.ndarray, residual: Optional[np.ndarray] = None)
     out = np.empty(H)
     lib().orc_combine(_p(y), _p(w), K, H, _p(r), _p(out))
     return out
+
+
+def quantize(W: np.ndarray, bits: int):
+    """Quantise-from-float of an fp32 [rows][cols] matrix (see orc_quantize): (codes uint8
+    [rows][cols], scale bf16 bits [rows][cols/64], bias bf16 bits [rows][cols/64])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    rows, cols = W.shape
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scale = np.empty((rows, cols // GROUP), dtype=np.uint16)
+    bias = np.empty((rows, cols // GROUP), dtype=np.uint16)
+    lib().orc_quantize(_p(W), rows, cols, bits, _p(codes), _p(scale), _p(bias))
+    return codes, scale, bias
 
 
 def silu(z: float) -> float:

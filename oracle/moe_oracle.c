@@ -224,5 +224,54 @@ void orc_combine(const double *y, const double *w, int K, int H, const double *r
     }
 }
 
+/* float -> bf16 bits, round to nearest even (finite inputs). */
+static uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Quantise-from-float (the step before packing), group by group along each row.  The pages
+ * name an MLX 4-bit affine base (tomo3141592653.github.io, "iPhone 17 Proで400Bパラメータ LLM
+ * を動かす「flash-moe」", section "ハイブリッド量子化") and the affine form w = q * scale + bias
+ * (lilting.ch page, section "Metal Compute Shaders") but not the rounding; the plain reading:
+ *   lo, hi = min and max of the group's 64 weights;
+ *   scale  = bf16((hi - lo) / (2^b - 1)),  bias = bf16(lo);
+ *   code   = nearest integer, ties to even, to (w - bias) / scale, clamped to [0, 2^b - 1],
+ *            and 0 when the bf16 scale is 0 (a constant group),
+ * every step in fp32 with the bf16 scale and bias already rounded, so that the stored pair
+ * dequantises the codes.  W [rows][cols] finite fp32; codes [rows][cols] one per byte,
+ * scale and bias [rows][cols/64] bf16 bits. */
+void orc_quantize(const float *W, int rows, int cols, int bits, uint8_t *codes, uint16_t *scale,
+                  uint16_t *bias) {
+    const int G = cols / ORC_GROUP;
+    const float qmax = (float)((1 << bits) - 1);
+    for (int r = 0; r < rows; ++r) {
+        for (int g = 0; g < G; ++g) {
+            const float *w = W + (size_t)r * cols + (size_t)g * ORC_GROUP;
+            float lo = w[0], hi = w[0];
+            for (int i = 1; i < ORC_GROUP; ++i) {
+                if (w[i] < lo) lo = w[i];
+                if (w[i] > hi) hi = w[i];
+            }
+            const uint16_t sb = orc_f32_to_bf16((hi - lo) / qmax);
+            const uint16_t bb = orc_f32_to_bf16(lo);
+            const float s = orc_bf16_to_f32(sb), b = orc_bf16_to_f32(bb);
+            scale[(size_t)r * G + g] = sb;
+            bias[(size_t)r * G + g] = bb;
+            for (int i = 0; i < ORC_GROUP; ++i) {
+                int q = 0;
+                if (s > 0.0f) {
+                    const float t = w[i] - b;
+                    const float u = nearbyintf(t / s);
+                    q = u < 0.0f ? 0 : (u > qmax ? (int)qmax : (int)u);
+                }
+                codes[(size_t)r * cols + (size_t)g * ORC_GROUP + i] = (uint8_t)q;
+            }
+        }
+    }
+}
+
 /* silu exported for its own pins. */
 double orc_silu_export(double z) { return orc_silu(z); }

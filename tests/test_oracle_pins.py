@@ -378,3 +378,89 @@ def test_random_expert_matches_independent_numpy(orc, bits):
     assert np.allclose(g, gr, rtol=1e-12, atol=1e-12) and np.allclose(u, ur, rtol=1e-12, atol=1e-12)
     assert np.allclose(h, hr, rtol=1e-12, atol=1e-12)
     assert np.allclose(y, Wd @ hr, rtol=1e-11, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------- quantise-from-float
+def _bf16_value(bits16: np.ndarray) -> np.ndarray:
+    return (bits16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _rne_bf16(x: float) -> float:
+    """bf16 round-to-nearest-even of an fp32 value, by exhaustive neighbour search in float64
+    (independent of bit tricks): the nearest of the two bf16 neighbours, ties to even mantissa."""
+    f = float(np.float32(x))
+    u = int(np.array([f], dtype=np.float32).view(np.uint32)[0])
+    lo_u = u & 0xFFFF0000
+    cand = [lo_u, lo_u + 0x10000]
+    vals = [float(np.array([c], dtype=np.uint32).view(np.float32)[0]) for c in cand]
+    d = [abs(v - f) for v in vals]
+    if d[0] != d[1]:
+        return vals[0] if d[0] < d[1] else vals[1]
+    return vals[0] if ((cand[0] >> 16) & 1) == 0 else vals[1]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_quantize_exact_grid(bits):
+    """Pins orc_quantize on groups that lie exactly on a bf16 grid: w = lo + k * s with lo, s and
+    the extremes exactly representable, both k = 0 and k = 2^b - 1 present.  Then the scale, the
+    bias and every code are known exactly (a wrong qmax, swapped scale/bias, an offset code or a
+    floor instead of round fails)."""
+    import oracle
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(7 + bits)
+    rows, G = 3, 4
+    W = np.empty((rows, 64 * G), dtype=np.float32)
+    ks = rng.integers(0, qmax + 1, size=(rows, 64 * G))
+    ks[:, ::64] = 0
+    ks[:, 1::64] = qmax
+    los = np.array([-0.75, 0.125, -3.0, 2.5], dtype=np.float64)
+    ss = np.array([2.0 ** -5, 2.0 ** -3, 0.375, 2.0 ** -9], dtype=np.float64)
+    for g in range(G):
+        W[:, 64 * g:64 * (g + 1)] = (los[g] + ks[:, 64 * g:64 * (g + 1)] * ss[g]).astype(np.float32)
+    codes, scale, bias = oracle.quantize(W, bits)
+    assert np.array_equal(codes, ks)
+    for g in range(G):
+        assert np.all(_bf16_value(scale[:, g]) == ss[g]) and np.all(_bf16_value(bias[:, g]) == los[g])
+
+
+def test_quantize_constant_group():
+    """A constant group has scale 0, codes 0, and the bf16-rounded value as its bias (so it
+    dequantises to bf16(v)); neighbouring groups are unaffected."""
+    import oracle
+    W = np.zeros((2, 128), dtype=np.float32)
+    W[0, :64] = 0.1
+    W[1, :64] = -7.3
+    W[:, 64:] = np.linspace(-1, 1, 64, dtype=np.float32)
+    codes, scale, bias = oracle.quantize(W, 4)
+    assert np.all(codes[:, :64] == 0) and np.all(scale[:, 0] == 0)
+    assert _bf16_value(bias[0, 0]) == _rne_bf16(0.1) and _bf16_value(bias[1, 0]) == _rne_bf16(-7.3)
+    assert codes[0, 64] == 0 and codes[0, 127] == 15
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_quantize_nearest_code_brute_force(bits):
+    """Pins the codes of random groups (normal, uniform, negative-only, wide and narrow ranges,
+    values far from zero) against brute force in float64: with the stored bf16 scale s and bias b,
+    every code is the nearest of all 2^b codes to w (up to fp32 rounding of the ratio), and s and
+    b are the round-to-nearest-even bf16 of (max - min) / (2^b - 1) and of min (checked against an
+    independent neighbour search)."""
+    import oracle
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(11 + bits)
+    groups = [rng.normal(0, 1, 64), rng.uniform(-0.02, 0.02, 64), -rng.uniform(1, 2, 64),
+              rng.normal(0, 30, 64), 100.3 + rng.uniform(0, 1e-3, 64), rng.normal(0, 1e-4, 64),
+              np.concatenate([rng.normal(0, 1, 63), [40.0]])]
+    W = np.concatenate(groups).astype(np.float32).reshape(1, -1)
+    codes, scale, bias = oracle.quantize(W, bits)
+    for g in range(len(groups)):
+        w = W[0, 64 * g:64 * (g + 1)].astype(np.float64)
+        s, b = _bf16_value(scale[0, g]), _bf16_value(bias[0, g])
+        lo, hi = float(np.float32(w.min())), float(np.float32(w.max()))
+        assert s == _rne_bf16(float(np.float32(np.float32(hi - lo) / np.float32(qmax))))
+        assert b == _rne_bf16(lo)
+        grid = b + s * np.arange(qmax + 1)
+        for i in range(64):
+            err = np.abs(w[i] - grid)
+            best = err.min()
+            c = int(codes[0, 64 * g + i])
+            assert err[c] <= best + 1e-5 * max(s, 1e-30) * 2, (g, i, c, int(err.argmin()))
