@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")
+    p.add_argument("--quantize", action="store_true",
+                   help="measure quantise-from-float (moe_quantize_matrix) instead of the expert path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run device-to-device copies of 1 GiB (reference for the HBM byte counters)")
     p.add_argument("--traffic-from", metavar="DIR",
@@ -147,8 +149,66 @@ def traffic_from(d: str, workload_key: str):
     log(f"[bench] wrote {p}: {json.dumps(res)}")
 
 
+def quantize_bench(a):
+    """Quantise-from-float: 64 fp32 matrices of 1024 x 4096 (the shape of a 4-bit expert's gate and
+    up) into 4-bit packed planes, 16 matrices stacked row-wise per launch (a bulk conversion; a
+    single 19 MB matrix per launch is dominated by the launch's ramp), timed with events on the
+    launch stream.
+    Algorithmic bytes per launch: the weights read once plus the code and (scale, bias) planes
+    written once.  Parity: every code and pair of the first matrix against the oracle."""
+    import torch
+    import bit_expert_dequant_amd as M
+    import oracle
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rows, cols, bits, n, per = 1024, 4096, 4, 64, 16
+    cb, sbb = M.lib().moe_packed_codes_bytes(rows, cols, bits), M.lib().moe_packed_sb_bytes(rows, cols)
+    gen = torch.Generator(device="cuda").manual_seed(0x9A47)
+    W = torch.randn(n, rows, cols, device="cuda", dtype=torch.float32, generator=gen) * 0.05
+    codes = torch.empty(n, cb, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(n, sbb // 2, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    nl = n // per
+
+    def run():
+        for i in range(nl):
+            M.moe_quantize_matrix(W[i * per:(i + 1) * per].view(per * rows, cols), bits, codes[i * per:(i + 1) * per],
+                                  sb[i * per:(i + 1) * per])
+    run()
+    torch.cuda.synchronize()
+    reps = 8
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nl)
+    per_launch = per * (rows * cols * 4 + cb + sbb)
+    gbps = per_launch / (us * 1e-6) / 1e9
+    oc, os_, ob = oracle.quantize(W[0].cpu().numpy(), bits)
+    plane = codes[0].cpu().numpy().reshape(rows, cols // 2)
+    gc = np.empty((rows, cols), dtype=np.uint8)
+    gc[:, 0::2], gc[:, 1::2] = plane & 15, plane >> 4
+    gsb = sb[0].cpu().numpy().view(np.uint16).reshape(rows, cols // 64, 2)
+    parity_ok = bool(np.array_equal(gc, oc) and np.array_equal(gsb[:, :, 0], os_) and np.array_equal(gsb[:, :, 1], ob))
+    line = {"metric": "quantise-from-float GB/s (fp32 weights -> 4-bit packed planes)", "value": round(gbps, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": reps * nl, "warmup": nl, "ms_per_step": round(us * 1e-3, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"{n} fp32 matrices of {rows} x {cols}, 4-bit, group 64, {per} per launch",
+                       "rows": per * rows, "cols": cols, "bits": bits},
+            "roofline": {"bound": "hbm", "kernel": "k_quantize", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "bytes_per_launch": per_launch, "us_per_launch": round(us, 3),
+                         "timing": "HIP events around back-to-back launches on the launch stream"},
+            "parity": {"matrices": 1, "bit_exact": parity_ok}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.quantize:
+        quantize_bench(a)
+        return
     if a.copy_calibration:
         copy_calibration()
         return

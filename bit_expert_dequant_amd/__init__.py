@@ -81,6 +81,7 @@ def lib():
             "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
             "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
             "moe_stream_read": (I32, [P, SZ, P, P]),
+            "moe_quantize_matrix": (I32, [P, I32, I32, I32, I32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -94,7 +95,8 @@ def exported_symbols() -> List[str]:
     return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
-            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read"]
+            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read",
+            "moe_quantize_matrix"]
 
 
 def _check(status: int):
@@ -266,6 +268,15 @@ def moe_stream_read(buf, sink, stream=None) -> None:
     """Read-stream reference (see moe_stream_read in the header): XOR of every dword of `buf`
     (a contiguous device tensor, 16-byte aligned, size a multiple of 16 bytes) into sink[0]."""
     _check(lib().moe_stream_read(_tptr(buf), buf.numel() * buf.element_size(), _tptr(sink), _stream(stream)))
+
+
+def moe_quantize_matrix(w, bits: int, codes, sb, stream=None) -> None:
+    """Quantise a device [rows][cols] fp32 or bf16 tensor `w` into the packed code plane `codes`
+    (uint8 tensor, moe_packed_codes_bytes bytes) and (scale, bias) plane `sb` (int16 tensor of
+    2 * rows * cols / 64 entries); see moe_quantize_matrix in the header."""
+    rows, cols = w.shape
+    _check(lib().moe_quantize_matrix(_tptr(w), _dtype_code(w), rows, cols, bits, _tptr(codes), _tptr(sb),
+                                     _stream(stream)))
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,

@@ -441,6 +441,20 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
     return ok();
 }
 
+int moe_quantize_matrix(const void *w, int w_dtype, int rows, int cols, int bits, uint8_t *codes, uint16_t *sb,
+                        void *stream) {
+    if (!w || !codes || !sb) return fail(MOE_ERR_NULL, "w, codes and sb are required");
+    if (int s = check_dtype(w_dtype, "w")) return s;
+    if (rows < 1 || cols < 64 || cols % 64 != 0 || (uint64_t)rows * (uint64_t)cols > ((uint64_t)1 << 40))
+        return fail(MOE_ERR_SHAPE, "rows=%d cols=%d (cols a positive multiple of 64)", rows, cols);
+    if (bits != 2 && bits != 4) return fail(MOE_ERR_BITS, "bits=%d (2 or 4)", bits);
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(sb, 4))
+        return fail(MOE_ERR_ALIGN, "w and codes must be 16-byte aligned, sb 4-byte aligned");
+    moe::QuantLaunch qa{w, w_dtype, rows, cols, bits, codes, sb};
+    if (int s = launched(moe::launch_quantize(qa, (hipStream_t)stream), "quantize")) return s;
+    return ok();
+}
+
 // Start/stop events of kernel j of a timed call: events[2j], events[2j+1].
 static moe::KernelEvents kernel_events(void *const *events, int j) {
     moe::KernelEvents ev;

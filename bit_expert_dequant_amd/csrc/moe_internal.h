@@ -187,6 +187,15 @@ struct CombineLaunch {
 };
 hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
 
+// Quantise-from-float of an R x C matrix into the packed code and (scale, bias) planes.
+struct QuantLaunch {
+    const void *w; int w_dtype;                    // [rows][cols] fp32 or bf16
+    int rows, cols, bits;
+    uint8_t *codes;                                // packed code plane
+    uint16_t *sb;                                  // (scale, bias) plane
+};
+hipError_t launch_quantize(const QuantLaunch &a, hipStream_t s);
+
 // Read-stream reference kernel (XOR of every dword of buf into *sink).
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 

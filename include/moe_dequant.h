@@ -161,6 +161,26 @@ int moe_pack_expert(const uint8_t *const codes[3], const uint16_t *const scale[3
                     const uint16_t *const bias[3], int hidden, int inter, int bits,
                     void *blob_out, size_t blob_out_bytes);
 
+/* Quantise real weights into the packed format (device in, device out; the step before the
+ * packer): per row r and group g of 64 columns, lo and hi = min and max of the 64 weights,
+ *   scale = bf16((hi - lo) / (2^bits - 1)),  bias = bf16(lo),
+ *   code  = nearest integer (ties to even) to (w - bias) / scale, clamped to [0, 2^bits - 1],
+ *           and 0 where the bf16 scale is 0,
+ * every step in fp32 with the stored bf16 pair.  The pages name an MLX 4-bit affine base
+ * (tomo3141592653.github.io, "iPhone 17 Proで400Bパラメータ LLM を動かす「flash-moe」",
+ * section "ハイブリッド量子化") and the form w = q * scale + bias (lilting.ch, "397Bパラメータ
+ * モデルを48GB MacBookで動かすFlash-MoE", section "Metal Compute Shaders"), not the rounding;
+ * this is the plain reading.
+ *   w      device [rows][cols], w_dtype (MOE_F32 or MOE_BF16), finite values, 16-byte aligned
+ *   codes  device code plane, moe_packed_codes_bytes(rows, cols, bits) bytes, 16-byte aligned
+ *   sb     device (scale, bias) plane, moe_packed_sb_bytes(rows, cols) bytes, 4-byte aligned
+ * The planes are the layout above: gate, up and down of an expert quantised into the offsets of
+ * moe_expert_plane_offsets make a blob.  Asynchronous on `stream`.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (rows < 1, cols not a positive multiple of 64),
+ * MOE_ERR_DTYPE, MOE_ERR_BITS, MOE_ERR_ALIGN, MOE_ERR_LAUNCH. */
+int moe_quantize_matrix(const void *w, int w_dtype, int rows, int cols, int bits, uint8_t *codes,
+                        uint16_t *sb, void *stream);
+
 /* Copy a device descriptor table to the host (synchronously, on the null stream) and
  * check it: non-NULL, 256-byte aligned blobs, bits in {2,4}, reserved == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_BITS, MOE_ERR_SHAPE, MOE_ERR_DEVICE. */

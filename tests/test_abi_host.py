@@ -170,3 +170,22 @@ def test_expert_ffn_and_decode_validation(L):
     assert L.moe_combine(None, FAKE, 1, 2, 64, None, FAKE, None) == 1
     assert L.moe_combine(FAKE, FAKE, 1, 9, 64, None, FAKE, None) == 2
     assert L.moe_check_experts(None, 4) == 1
+
+
+def test_quantize_matrix_validates_before_launch(L):
+    """moe_quantize_matrix refuses bad arguments with a status and enqueues nothing (no device
+    pointer is ever dereferenced: every call below fails validation)."""
+    P = ctypes.c_void_p
+    w, codes, sb = P(0x100000), P(0x200000), P(0x300000)
+    q = L.moe_quantize_matrix
+    assert q(None, M.MOE_F32, 4, 64, 4, codes, sb, None) == 1                 # MOE_ERR_NULL
+    assert q(w, M.MOE_F32, 4, 64, 4, None, sb, None) == 1
+    assert q(w, 7, 4, 64, 4, codes, sb, None) == 3                           # MOE_ERR_DTYPE
+    assert q(w, M.MOE_F32, 0, 64, 4, codes, sb, None) == 2                   # MOE_ERR_SHAPE
+    assert q(w, M.MOE_F32, 4, 96, 4, codes, sb, None) == 2
+    assert q(w, M.MOE_BF16, 4, 0, 4, codes, sb, None) == 2
+    assert q(w, M.MOE_F32, 4, 64, 3, codes, sb, None) == 4                   # MOE_ERR_BITS
+    assert q(P(0x100004), M.MOE_F32, 4, 64, 4, codes, sb, None) == 5          # MOE_ERR_ALIGN
+    assert q(w, M.MOE_F32, 4, 64, 2, P(0x200008), sb, None) == 5
+    assert q(w, M.MOE_F32, 4, 64, 2, codes, P(0x300002), None) == 5
+    assert b"bits" in L.moe_last_error() or b"align" in L.moe_last_error()
