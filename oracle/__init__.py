@@ -13,7 +13,8 @@ Where the Flash-MoE pages define a step (affine dequantisation and its FMA form,
 4-/2-bit matvec kernels, two-pass RMSNorm, the weighted-sum combine: lilting.ch,
 "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE", section "Metal Compute Shaders")
 this follows them; where they are silent it takes the plain reading written in the
-header of ``moe_oracle.c``.
+header of ``moe_oracle.c``.  Beside the per-token path: quantise-from-float (``quantize``) and the
+policy side of the tiered store (``expert_usage``, ``hot_order``, ``requantize_expert``).
 """
 from __future__ import annotations
 
@@ -213,6 +214,52 @@ def quantize(W: np.ndarray, bits: int):
     bias = np.empty((rows, cols // GROUP), dtype=np.uint16)
     lib().orc_quantize(_p(W), rows, cols, bits, _p(codes), _p(scale), _p(bias))
     return codes, scale, bias
+
+
+# ----------------------------------------------------------------------------- hot set, re-tiering
+# The pages keep the frequently used experts at 4 bits and store the others at 2 bits (nzkcom.pages.dev,
+# "flash-moe-romance-vs-utility", adopted-optimisation table; tomo3141592653.github.io, section
+# "ハイブリッド量子化": the base is MLX 4-bit).  They do not say how "frequently used" is measured or
+# how a 2-bit expert is made.  Plain reading: count the selections of each expert over a stream of
+# routed tokens; the n most selected are hot (equal counts: the lower expert index first); a cold
+# expert is dequantised from its base blob and quantised again at the cold width with quantize().
+
+def expert_usage(idx: np.ndarray, E: int) -> np.ndarray:
+    """counts[e] = number of entries of idx (any shape, e.g. [T][K] routing indices) equal to e;
+    entries outside [0, E) are not counted.  int64 [E]."""
+    idx = np.asarray(idx, dtype=np.int64).ravel()
+    counts = np.zeros(E, dtype=np.int64)
+    np.add.at(counts, idx[(idx >= 0) & (idx < E)], 1)
+    return counts
+
+
+def hot_order(counts: np.ndarray) -> np.ndarray:
+    """Experts ranked by usage, most used first; equal counts rank the lower expert index first.
+    int32 [E]; the first n entries are the hot set of size n."""
+    counts = np.asarray(counts, dtype=np.int64)
+    return np.lexsort((np.arange(counts.size), -counts)).astype(np.int32)
+
+
+def requantize_matrix(codes_plane: np.ndarray, sb_plane: np.ndarray, rows: int, cols: int, bits_in: int,
+                      bits_out: int):
+    """A packed matrix at bits_in re-quantised at bits_out: quantize(dequant(...)).  Returns
+    (codes uint8 [rows][cols], scale bf16 bits [rows][cols/64], bias bf16 bits [rows][cols/64])."""
+    return quantize(dequant(codes_plane, sb_plane, rows, cols, bits_in), bits_out)
+
+
+def requantize_expert(blob: np.ndarray, H: int, I: int, bits_in: int, bits_out: int):
+    """The three matrices (gate I x H, up I x H, down H x I) of one packed expert, each re-quantised
+    at bits_out: a list of three (codes, scale, bias) as requantize_matrix returns."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    off, _ = blob_layout(H, I, bits_in)
+    shapes = [(I, H), (I, H), (H, I)]
+    out = []
+    for m, (rows, cols) in enumerate(shapes):
+        c0, s0 = off[2 * m], off[2 * m + 1]
+        codes = blob[c0:c0 + codes_bytes(rows, cols, bits_in)]
+        sb = blob[s0:s0 + sb_bytes(rows, cols)].view(np.uint16)
+        out.append(requantize_matrix(codes, sb, rows, cols, bits_in, bits_out))
+    return out
 
 
 def silu(z: float) -> float:

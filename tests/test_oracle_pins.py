@@ -464,3 +464,111 @@ def test_quantize_nearest_code_brute_force(bits):
             best = err.min()
             c = int(codes[0, 64 * g + i])
             assert err[c] <= best + 1e-5 * max(s, 1e-30) * 2, (g, i, c, int(err.argmin()))
+
+
+# --------------------------------------------------------------------------- hot set and re-tiering
+def test_expert_usage_brute_force():
+    """Pins oracle.expert_usage against a plain dictionary count on routing indices with
+    out-of-range entries (which are not counted), and the total against the valid entry count."""
+    import oracle
+    rng = np.random.default_rng(21)
+    E = 37
+    idx = rng.integers(-3, E + 3, size=(200, 4)).astype(np.int32)
+    counts = oracle.expert_usage(idx, E)
+    ref = {}
+    for v in idx.ravel().tolist():
+        if 0 <= v < E:
+            ref[v] = ref.get(v, 0) + 1
+    assert [int(c) for c in counts] == [ref.get(e, 0) for e in range(E)]
+    assert int(counts.sum()) == int(((idx >= 0) & (idx < E)).sum())
+
+
+def test_hot_order_hand_case_and_invariants():
+    """Pins oracle.hot_order on a hand case with ties, and on random counts with many ties by the
+    properties that fix the order uniquely: a permutation, counts non-increasing along it, and the
+    expert index increasing inside each run of equal counts."""
+    import oracle
+    assert oracle.hot_order(np.array([3, 5, 5, 0, 3, 7])).tolist() == [5, 1, 2, 0, 4, 3]
+    rng = np.random.default_rng(22)
+    counts = rng.integers(0, 6, size=300)
+    order = oracle.hot_order(counts)
+    assert sorted(order.tolist()) == list(range(300))
+    c = counts[order]
+    assert np.all(c[:-1] >= c[1:])
+    same = c[:-1] == c[1:]
+    assert np.all(order[:-1][same] < order[1:][same])
+
+
+def _exact_matrix(rng, rows, cols, bits, k_set, s_vals, b_vals):
+    """Codes drawn from k_set with every member present in every group, dyadic scales and
+    biases: (codes, scale, bias) as make_expert_blob takes them."""
+    G = cols // 64
+    k_set = np.asarray(k_set)
+    codes = k_set[rng.integers(0, k_set.size, size=(rows, cols))]
+    for g in range(G):
+        codes[:, 64 * g:64 * g + k_set.size] = k_set
+    scale = np.array([[s_vals[(r + g) % len(s_vals)] for g in range(G)] for r in range(rows)])
+    bias = np.array([[b_vals[(2 * r + g) % len(b_vals)] for g in range(G)] for r in range(rows)])
+    return codes.astype(np.uint8), scale, bias
+
+
+def _check_requant(result, expected):
+    for (codes, scale, bias), (ec, es, eb) in zip(result, expected):
+        assert np.array_equal(codes, ec)
+        assert np.array_equal(_bf16_value(scale), es) and np.array_equal(_bf16_value(bias), eb)
+
+
+def test_requantize_expert_exact_cases(orc):
+    """Pins oracle.requantize_expert where the answer is exact, with different patterns in gate,
+    up and down (a swapped or mis-offset matrix fails):
+      4 -> 4 with codes 0 and 15 in every group returns the same codes and pairs;
+      4 -> 2 with codes {0, 5, 10, 15} gives code / 5, scale 5s and the same bias;
+      2 -> 4 with codes {0..3} and s = 5 * 2^-7 gives 5 * code, scale s / 5 and the same bias."""
+    import oracle
+    H, I = 192, 128
+    rng = np.random.default_rng(23)
+    s4 = [2.0 ** -6, 2.0 ** -4, 0.375 * 2.0 ** -5]
+    b4 = [-0.5, 0.25, -2.0 ** -3, 1.5]
+    for bits_in, bits_out, k_set, s_vals, mult in [
+            (4, 4, list(range(16)), s4, None),
+            (4, 2, [0, 5, 10, 15], s4, 5),
+            (2, 4, [0, 1, 2, 3], [5 * 2.0 ** -7, 5 * 2.0 ** -9], 0.2)]:
+        mats = [_exact_matrix(rng, I, H, bits_in, k_set, s_vals, b4),
+                _exact_matrix(rng, I, H, bits_in, k_set[::-1], s_vals[::-1], b4[1:]),
+                _exact_matrix(rng, H, I, bits_in, k_set, s_vals[1:] + s_vals[:1], b4[::-1])]
+        blob = make_expert_blob(orc, H, I, bits_in, *mats)
+        got = oracle.requantize_expert(blob, H, I, bits_in, bits_out)
+        if mult is None:
+            exp = [(c, s, b) for c, s, b in mats]
+        elif mult == 5:
+            exp = [(c // 5, s * 5, b) for c, s, b in mats]
+        else:
+            exp = [(c * 5, s / 5, b) for c, s, b in mats]
+        _check_requant(got, exp)
+
+
+@pytest.mark.parametrize("bits_in,bits_out", [(4, 2), (2, 4), (4, 4)])
+def test_requantize_error_bound(orc, bits_in, bits_out):
+    """Pins oracle.requantize_matrix by the quantiser's error bound on random packed matrices: with
+    the new pair (s', b') of a group whose dequantised weights span [lo, hi], every weight w is
+    within s'/2 + |lo - b'| + qmax |s' - (hi - lo)/qmax| (+ fp32 rounding) of q' s' + b'."""
+    import oracle
+    rng = np.random.default_rng(24 + bits_in + 3 * bits_out)
+    rows, cols = 16, 512
+    G = cols // 64
+    codes = rng.integers(0, 1 << bits_in, size=(rows, cols)).astype(np.uint8)
+    scale = np.array([[_rne_bf16(float(v)) for v in row] for row in rng.uniform(1e-3, 0.05, (rows, G))])
+    bias = np.array([[_rne_bf16(float(v)) for v in row] for row in rng.uniform(-0.5, 0.5, (rows, G))])
+    plane = pack_codes_by_hand(codes, bits_in)
+    sb = sb_plane(scale, bias)
+    W = np.repeat(scale, 64, axis=1) * codes + np.repeat(bias, 64, axis=1)      # float64, as stored
+    c2, s2, b2 = oracle.requantize_matrix(plane, sb, rows, cols, bits_in, bits_out)
+    qmax = (1 << bits_out) - 1
+    for r in range(rows):
+        for g in range(G):
+            w = W[r, 64 * g:64 * (g + 1)]
+            s, b = float(_bf16_value(s2[r, g])), float(_bf16_value(b2[r, g]))
+            lo, hi = w.min(), w.max()
+            bound = s / 2 + abs(lo - b) + qmax * abs(s - (hi - lo) / qmax) + 1e-6 * max(abs(lo), abs(hi), 1e-3)
+            err = np.abs(w - (c2[r, 64 * g:64 * (g + 1)] * s + b))
+            assert err.max() <= bound, (r, g, err.max(), bound)
