@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")
     p.add_argument("--quantize", action="store_true",
                    help="measure quantise-from-float (moe_quantize_matrix) instead of the expert path")
+    p.add_argument("--retier", action="store_true",
+                   help="measure the tiered-store policy (usage over the routed token bank, hot order, "
+                        "requantisation of the cold experts) instead of the expert path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run device-to-device copies of 1 GiB (reference for the HBM byte counters)")
     p.add_argument("--traffic-from", metavar="DIR",
@@ -204,10 +207,127 @@ def quantize_bench(a):
     print(json.dumps(line), flush=True)
 
 
+def retier_bench(a):
+    """Re-tiering a layer of 512 experts of 4096 x 1024 at 4 bits into hot 4-bit / cold 2-bit (the
+    tiered store of the pages): a step is moe_expert_usage over the routing indices of a 4096-token
+    stream (routed once beforehand with the Zipf(1.1) prior, 256 tokens per moe_route call), then
+    moe_hot_order, then moe_retier with 128 hot experts, the other 384 requantised to 2 bits.
+    Algorithmic bytes per step: each cold expert's 4-bit blob read once and its 2-bit blob written
+    once.  The requantisation kernel is timed on its own with HIP events around moe_retier (which
+    adds one small table kernel).  Parity: the first and last cold experts bit-exact against the
+    oracle; the hot set's share of the stream's selections beside that of the prior's hot set."""
+    import torch
+    import bit_expert_dequant_amd as M
+    import oracle
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from moe_cases import act_tensor, build_layer
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.WORKLOADS[4]
+    H, I, E, K, n_hot, T, chunk = wl.H, wl.I, wl.E, wl.K, synth.N_HOT, 4096, 256
+    d = M.make_dims(H, I, E, K)
+    dl = build_layer(wl)
+    stream = torch.cuda.current_stream()
+    bank = wl.tokens_bank(T)
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    wts = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    ws = M.workspace(M.MOE_OP_ROUTE, d, chunk, 1)
+    for c in range(0, T, chunk):
+        M.moe_route(d, dl.L, act_tensor(wl, bank[c:c + chunk]), idx[c:c + chunk], wts[c:c + chunk], ws=ws)
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    order = torch.empty(E, dtype=torch.int32, device="cuda")
+    cold_bytes = M.lib().moe_packed_expert_bytes(H, I, 2)
+    base_bytes = M.lib().moe_packed_expert_bytes(H, I, 4)
+    cold = torch.empty((E - n_hot) * cold_bytes, dtype=torch.uint8, device="cuda")
+    tiered = torch.zeros_like(dl.table)
+
+    def step():
+        counts.zero_()
+        M.moe_expert_usage(idx, E, counts)
+        M.moe_hot_order(counts, order)
+        M.moe_retier(d, dl.table, order, n_hot, 2, cold, tiered)
+
+    steps, warm = max(1, min(a.steps, 16)), max(1, min(a.warmup, 4))
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = ev[0].elapsed_time(ev[1]) / steps
+    for i in range(steps):
+        counts.zero_()
+        M.moe_expert_usage(idx, E, counts)
+        M.moe_hot_order(counts, order)
+        ev[2 + 2 * i].record(stream)
+        M.moe_retier(d, dl.table, order, n_hot, 2, cold, tiered)
+        ev[3 + 2 * i].record(stream)
+    torch.cuda.synchronize()
+    rq_ms = [ev[2 + 2 * i].elapsed_time(ev[3 + 2 * i]) for i in range(steps)]
+    rq = float(np.median(rq_ms))
+    algo = (E - n_hot) * (base_bytes + cold_bytes)
+    gbps_step = algo / (step_ms * 1e-3) / 1e9
+    gbps_rq = algo / (rq * 1e-3) / 1e9
+    c_np = counts.cpu().numpy().astype(np.int64)
+    o_np = order.cpu().numpy()
+    total = int(c_np.sum())
+    share = float(c_np[o_np[:n_hot]].sum()) / total
+    prior_share = float(c_np[synth.hot_set(wl.seed, E)].sum()) / total
+    # parity on two cold experts (inputs: the seeded base blobs)
+    parity_ok = True
+    for r in (n_hot, E - 1):
+        e = int(o_np[r])
+        slot = r - n_hot
+        gpu = cold[slot * cold_bytes:(slot + 1) * cold_bytes].cpu().numpy()
+        ref = oracle.requantize_expert(synth.expert_blob(wl.seed, 0, e, H, I, 4), H, I, 4, 2)
+        off, _ = synth.blob_layout(H, I, 2)
+        sizes = synth.plane_sizes(H, I, 2)
+        for m, (rows, cols) in enumerate([(I, H), (I, H), (H, I)]):
+            plane = gpu[off[2 * m]:off[2 * m] + sizes[2 * m]].reshape(rows, cols // 4)
+            codes = np.empty((rows, cols), dtype=np.uint8)
+            for k in range(4):
+                codes[:, k::4] = (plane >> (2 * k)) & 3
+            sb = gpu[off[2 * m + 1]:off[2 * m + 1] + sizes[2 * m + 1]].view(np.uint16).reshape(rows, cols // 64, 2)
+            parity_ok &= bool(np.array_equal(codes, ref[m][0]) and np.array_equal(sb[:, :, 0], ref[m][1])
+                              and np.array_equal(sb[:, :, 1], ref[m][2]))
+    cpu = None
+    if not a.no_cpu:
+        cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        blob0 = synth.expert_blob(wl.seed, 0, 0, H, I, 4)
+        n_cpu, t0 = 0, time.perf_counter()
+        while n_cpu < 1 or (time.perf_counter() - t0 < 10.0 and n_cpu < 8):
+            oracle.requantize_expert(blob0, H, I, 4, 2)
+            n_cpu += 1
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(n_cpu * (base_bytes + cold_bytes) / cpu_s / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle", "sample": f"{n_cpu} experts requantised 4 -> 2 bits (oracle.requantize_expert: "
+                                           f"fp32 dequantisation with OpenMP, then the single-threaded quantiser)"}
+    line = {"metric": "re-tier GB/s (4-bit base -> hot 4-bit / cold 2-bit store)", "value": round(gbps_step, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(step_ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"{E} experts H{H} I{I} 4-bit, usage over {T} routed tokens (top-{K}, Zipf(1.1) "
+                                   f"prior), {n_hot} hot, {E - n_hot} requantised to 2 bits",
+                       "hidden": H, "inter": I, "experts": E, "hot": n_hot, "tokens": T},
+            "roofline": {"bound": "hbm", "kernel": "k_requant", "achieved": round(gbps_rq, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps_rq / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "bytes_per_launch": algo, "us_per_launch": round(rq * 1e3, 2),
+                         "timing": "HIP events around moe_retier on the launch stream (requantisation + table)"},
+            "hot_share": {"measured_hot_set": round(share, 4), "prior_hot_set": round(prior_share, 4),
+                          "selections": total},
+            "parity": {"experts": 2, "bit_exact": parity_ok}, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.quantize:
         quantize_bench(a)
+        return
+    if a.retier:
+        retier_bench(a)
         return
     if a.copy_calibration:
         copy_calibration()

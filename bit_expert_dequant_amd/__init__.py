@@ -25,6 +25,7 @@ MOE_FLAG_RESIDUAL = 1
 MOE_FLAG_SEPARATE_KERNELS = 2
 GROUP = 64
 MAX_TOPK = 8
+MAX_EXPERTS = 2048
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_BITS",
           5: "MOE_ERR_ALIGN", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_LAUNCH", 8: "MOE_ERR_UNSUPPORTED",
           9: "MOE_ERR_BUFFER", 10: "MOE_ERR_DEVICE"}
@@ -82,6 +83,9 @@ def lib():
             "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
             "moe_stream_read": (I32, [P, SZ, P, P]),
             "moe_quantize_matrix": (I32, [P, I32, I32, I32, I32, P, P, P]),
+            "moe_expert_usage": (I32, [P, I32, I32, P, P]),
+            "moe_hot_order": (I32, [P, I32, P, P]),
+            "moe_retier": (I32, [P, P, P, I32, I32, P, SZ, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -96,7 +100,7 @@ def exported_symbols() -> List[str]:
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
             "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read",
-            "moe_quantize_matrix"]
+            "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier"]
 
 
 def _check(status: int):
@@ -277,6 +281,27 @@ def moe_quantize_matrix(w, bits: int, codes, sb, stream=None) -> None:
     rows, cols = w.shape
     _check(lib().moe_quantize_matrix(_tptr(w), _dtype_code(w), rows, cols, bits, _tptr(codes), _tptr(sb),
                                      _stream(stream)))
+
+
+def moe_expert_usage(idx, n_experts: int, counts, stream=None) -> None:
+    """counts[e] += selections of expert e in the int32 device tensor `idx` (any shape; entries
+    outside [0, n_experts) are not counted); `counts` is a uint32/int32 device tensor of n_experts."""
+    _check(lib().moe_expert_usage(_tptr(idx), idx.numel(), n_experts, _tptr(counts), _stream(stream)))
+
+
+def moe_hot_order(counts, order, stream=None) -> None:
+    """order = experts by counts, largest first, equal counts lower index first (device tensors of
+    n_experts uint32/int32 counts and int32 order)."""
+    _check(lib().moe_hot_order(_tptr(counts), counts.numel(), _tptr(order), _stream(stream)))
+
+
+def moe_retier(dims: moe_dims, base, order, n_hot: int, cold_bits: int, store, tiered, stream=None) -> None:
+    """Hot experts (order[:n_hot]) keep their base blobs; the others are requantised at cold_bits into
+    `store` (a uint8 device tensor) in rank order; `tiered` (device table, may be `base`) gets the
+    new descriptors.  See moe_retier in the header."""
+    _check(lib().moe_retier(ctypes.byref(dims), _tptr(base), _tptr(order), n_hot, cold_bits, _tptr(store),
+                            0 if store is None else store.numel() * store.element_size(), _tptr(tiered),
+                            _stream(stream)))
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,

@@ -455,6 +455,48 @@ int moe_quantize_matrix(const void *w, int w_dtype, int rows, int cols, int bits
     return ok();
 }
 
+int moe_expert_usage(const int32_t *idx, int n, int n_experts, uint32_t *counts, void *stream) {
+    if (!counts || (n > 0 && !idx)) return fail(MOE_ERR_NULL, "counts (and idx when n > 0) are required");
+    if (n < 0) return fail(MOE_ERR_SHAPE, "n=%d is negative", n);
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, MOE_MAX_EXPERTS);
+    if (!aligned(counts, 4) || (idx && !aligned(idx, 4))) return fail(MOE_ERR_ALIGN, "idx and counts must be 4-byte aligned");
+    if (int s = launched(moe::launch_usage(idx, (size_t)n, n_experts, counts, (hipStream_t)stream), "usage")) return s;
+    return ok();
+}
+
+int moe_hot_order(const uint32_t *counts, int n_experts, int32_t *order, void *stream) {
+    if (!counts || !order) return fail(MOE_ERR_NULL, "counts and order are required");
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, MOE_MAX_EXPERTS);
+    if (!aligned(counts, 4) || !aligned(order, 4)) return fail(MOE_ERR_ALIGN, "counts and order must be 4-byte aligned");
+    if (int s = launched(moe::launch_hot_order(counts, n_experts, order, (hipStream_t)stream), "hot order")) return s;
+    return ok();
+}
+
+int moe_retier(const moe_dims *dims, const moe_expert_desc *base, const int32_t *order, int n_hot, int cold_bits,
+               void *store, size_t store_bytes, moe_expert_desc *tiered, void *stream) {
+    if (int s = check_dims(dims)) return s;
+    if (!base || !order || !tiered) return fail(MOE_ERR_NULL, "base, order and tiered are required");
+    const int E = dims->n_experts;
+    if (n_hot < 0 || n_hot > E) return fail(MOE_ERR_SHAPE, "n_hot=%d outside [0, n_experts=%d]", n_hot, E);
+    if (!bits_ok(cold_bits)) return fail(MOE_ERR_BITS, "cold_bits=%d (2 or 4)", cold_bits);
+    if (!aligned(base, 16) || !aligned(tiered, 16) || !aligned(order, 4))
+        return fail(MOE_ERR_ALIGN, "base and tiered must be 16-byte aligned, order 4-byte aligned");
+    const size_t cold = moe_packed_expert_bytes(dims->hidden, dims->inter, cold_bits);
+    const size_t need = (size_t)(E - n_hot) * cold;
+    if (need) {
+        if (!store) return fail(MOE_ERR_NULL, "store is NULL (%d cold experts need %zu bytes)", E - n_hot, need);
+        if (!aligned(store, MOE_BLOB_ALIGN)) return fail(MOE_ERR_ALIGN, "store must be %d-byte aligned", MOE_BLOB_ALIGN);
+        if (store_bytes < need)
+            return fail(MOE_ERR_BUFFER, "store_bytes=%zu < %zu (%d cold experts of %zu bytes)", store_bytes, need,
+                        E - n_hot, cold);
+    }
+    moe::RetierLaunch r{base, order, E, dims->hidden, dims->inter, n_hot, cold_bits, store, cold, tiered};
+    if (int s = launched(moe::launch_retier(r, (hipStream_t)stream), "retier")) return s;
+    return ok();
+}
+
 // Start/stop events of kernel j of a timed call: events[2j], events[2j+1].
 static moe::KernelEvents kernel_events(void *const *events, int j) {
     moe::KernelEvents ev;

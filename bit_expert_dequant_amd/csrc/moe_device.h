@@ -33,6 +33,46 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Quantise-from-float of one group of 64 (moe_quantize_matrix, and the requantisation of a cold
+// expert): the (scale, bias) pair from the group's minimum and maximum, scale = bf16((hi - lo) /
+// (2^BITS - 1)) and bias = bf16(lo), then a weight's code under the stored pair: the nearest
+// integer (ties to even) to the fp32 quotient (w - bias) / scale under IEEE division, clamped to
+// [0, 2^BITS - 1], 0 when the scale is 0.
+//
+// quant_code is that definition.  quant_code_fast takes the quotient as (w - bias) * rcp(scale)
+// instead (v_rcp_f32, within 1 ulp): for |quotient| < 32 it is within 2^-17 of the IEEE quotient,
+// so both round to the same integer unless the fast one lies within 2^-15 of a half-integer; at
+// |quotient| >= 32 every code clamps to 0 or 2^BITS - 1 either way.  A lane that meets such a near
+// tie, or a scale outside [2^-64, 2^64] (where the reciprocal may leave the normal range), sets
+// `redo` and recomputes its codes with quant_code, so the codes equal the definition's.
+struct QPair {
+    uint32_t word;      // scale bits | bias bits << 16, as the sb plane stores it
+    float s, b;
+    float r;            // rcp(s), or 0 when s is 0 or outside [2^-64, 2^64]
+    bool slow;          // s is nonzero and outside [2^-64, 2^64]
+};
+template <int BITS>
+__device__ __forceinline__ QPair quant_pair(float lo, float hi) {
+    constexpr float kQMax = (float)((1 << BITS) - 1);
+    const uint32_t sbits = bf16_rne((hi - lo) / kQMax), bbits = bf16_rne(lo);
+    const float s = bf16_f32(sbits);
+    const bool fast = s >= 0x1p-64f && s <= 0x1p64f;
+    return {sbits | (bbits << 16), s, bf16_f32(bbits), fast ? __builtin_amdgcn_rcpf(s) : 0.f, !fast && s != 0.f};
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t quant_code(float w, const QPair &p) {
+    constexpr float kQMax = (float)((1 << BITS) - 1);
+    return p.s > 0.f ? (uint32_t)fminf(fmaxf(rintf((w - p.b) / p.s), 0.f), kQMax) : 0u;
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t quant_code_fast(float w, const QPair &p, bool &redo) {
+    constexpr float kQMax = (float)((1 << BITS) - 1);
+    const float q = (w - p.b) * p.r;
+    const float n = rintf(q);
+    redo |= fabsf(q - n) > 0.5f - 0x1p-15f;           // |q - n| <= 1/2: within 2^-15 of a half-integer
+    return (uint32_t)fminf(fmaxf(n, 0.f), kQMax);
+}
 __device__ __forceinline__ float load_act(const void *x, int dtype, size_t i) {
     return dtype == MOE_BF16 ? bf16_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
 }

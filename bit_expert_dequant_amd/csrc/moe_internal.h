@@ -196,6 +196,19 @@ struct QuantLaunch {
 };
 hipError_t launch_quantize(const QuantLaunch &a, hipStream_t s);
 
+// Tiered store policy: usage histogram, hot order, re-tiering (moe_tier.hip).
+hipError_t launch_usage(const int32_t *idx, size_t n, int E, uint32_t *counts, hipStream_t s);
+hipError_t launch_hot_order(const uint32_t *counts, int E, int32_t *order, hipStream_t s);
+struct RetierLaunch {
+    const moe_expert_desc *base;                   // [E] the base table (blobs read)
+    const int32_t *order;                          // [E] experts by rank; the first n_hot are hot
+    int E, H, I, n_hot, cold_bits;
+    void *store;                                   // (E - n_hot) cold blobs, cold_bytes apart
+    size_t cold_bytes;
+    moe_expert_desc *tiered;                       // [E] written last (may be base)
+};
+hipError_t launch_retier(const RetierLaunch &r, hipStream_t s);
+
 // Read-stream reference kernel (XOR of every dword of buf into *sink).
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 

@@ -18,25 +18,10 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace moe {
 namespace {
-
-#define GLOBAL_AS __attribute__((address_space(1)))
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t bf16_bits(float f) {       // round to nearest even (finite)
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 
 // The matrix is a flat run of rows * cols / 64 groups of 64 consecutive weights, and both planes
 // follow the same flat group order (a row's codes and pairs are contiguous, rows follow each
@@ -45,7 +30,6 @@ __device__ __forceinline__ float dpp(float v) {
 // (bf16) contiguous, and the 16 lanes of a DPP row hold group 4k + l/16 between them.
 template <int BITS, int DT>
 __global__ void __launch_bounds__(256) k_quantize(QuantLaunch a) {
-    constexpr float kQMax = (float)((1 << BITS) - 1);
     const size_t ng = (size_t)a.rows * (a.cols / 64);
     const int lane = threadIdx.x & 63, r16 = lane >> 4, c16 = lane & 15;
     const size_t g0 = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
@@ -72,27 +56,28 @@ __global__ void __launch_bounds__(256) k_quantize(QuantLaunch a) {
         float lo = fminf(fminf(v[k][0], v[k][1]), fminf(v[k][2], v[k][3]));
         float hi = fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3]));
         // minimum and maximum over the 16 lanes of the DPP row (the group's 64 weights)
-        lo = fminf(lo, dpp<0xB1>(lo));      // quad_perm [1,0,3,2]
-        hi = fmaxf(hi, dpp<0xB1>(hi));
-        lo = fminf(lo, dpp<0x4E>(lo));      // quad_perm [2,3,0,1]
-        hi = fmaxf(hi, dpp<0x4E>(hi));
-        lo = fminf(lo, dpp<0x141>(lo));     // row_half_mirror
-        hi = fmaxf(hi, dpp<0x141>(hi));
-        lo = fminf(lo, dpp<0x140>(lo));     // row_mirror
-        hi = fmaxf(hi, dpp<0x140>(hi));
+        lo = fminf(lo, dppf<0xB1>(lo));     // quad_perm [1,0,3,2]
+        hi = fmaxf(hi, dppf<0xB1>(hi));
+        lo = fminf(lo, dppf<0x4E>(lo));     // quad_perm [2,3,0,1]
+        hi = fmaxf(hi, dppf<0x4E>(hi));
+        lo = fminf(lo, dppf<0x141>(lo));    // row_half_mirror
+        hi = fmaxf(hi, dppf<0x141>(hi));
+        lo = fminf(lo, dppf<0x140>(lo));    // row_mirror
+        hi = fmaxf(hi, dppf<0x140>(hi));
         if (gk >= ng) continue;
-        const uint32_t sbits = bf16_bits((hi - lo) / kQMax), bbits = bf16_bits(lo);
-        const float s = bf16_value(sbits), b = bf16_value(bbits);
+        const QPair p = quant_pair<BITS>(lo, hi);
         uint32_t packed = 0;
+        bool redo = p.slow;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t c = 0;
-            if (s > 0.f) c = (uint32_t)fminf(fmaxf(rintf((v[k][j] - b) / s), 0.f), kQMax);
-            packed |= c << (j * BITS);
+        for (int j = 0; j < 4; ++j) packed |= quant_code_fast<BITS>(v[k][j], p, redo) << (j * BITS);
+        if (redo) {
+            packed = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) packed |= quant_code<BITS>(v[k][j], p) << (j * BITS);
         }
         if (BITS == 4) *(GLOBAL_AS uint16_t *)(a.codes + gk * 32 + 2 * c16) = (uint16_t)packed;
         else *(GLOBAL_AS uint8_t *)(a.codes + gk * 16 + c16) = (uint8_t)packed;
-        if (c16 == 0) *(GLOBAL_AS uint32_t *)(a.sb + 2 * gk) = sbits | (bbits << 16);   // scale, then bias
+        if (c16 == 0) *(GLOBAL_AS uint32_t *)(a.sb + 2 * gk) = p.word;   // scale, then bias
     }
 }
 

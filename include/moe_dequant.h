@@ -65,7 +65,7 @@ typedef enum moe_status {
     MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes() */
     MOE_ERR_LAUNCH = 7,      /* the HIP runtime refused a kernel launch */
     MOE_ERR_UNSUPPORTED = 8, /* valid request this build does not implement */
-    MOE_ERR_BUFFER = 9,      /* a host output buffer is too small */
+    MOE_ERR_BUFFER = 9,      /* an output buffer is too small */
     MOE_ERR_DEVICE = 10      /* no usable gfx950 device / HIP runtime error */
 } moe_status;
 
@@ -180,6 +180,50 @@ int moe_pack_expert(const uint8_t *const codes[3], const uint16_t *const scale[3
  * MOE_ERR_DTYPE, MOE_ERR_BITS, MOE_ERR_ALIGN, MOE_ERR_LAUNCH. */
 int moe_quantize_matrix(const void *w, int w_dtype, int rows, int cols, int bits, uint8_t *codes,
                         uint16_t *sb, void *stream);
+
+/* --------------------------------------------------------------------------- tiered store policy */
+/* The pages keep the experts a model uses often at 4 bits and store the rest at 2 bits
+ * (nzkcom.pages.dev, "flash-moe-romance-vs-utility", adopted-optimisation table; an MLX 4-bit
+ * base: tomo3141592653.github.io, "iPhone 17 Proで400Bパラメータ LLM を動かす「flash-moe」",
+ * section "ハイブリッド量子化"), without saying how use is measured or how a 2-bit expert is made.
+ * The three calls below are the plain reading: count routing selections over a token stream,
+ * rank the experts by count, requantise the cold ones from their base blobs.  All device in,
+ * device out, asynchronous on `stream`. */
+
+/* counts[e] += number of entries of idx equal to e, for e in [0, n_experts); entries outside that
+ * range are not counted.  Accumulates, so a token stream may span many calls: zero counts
+ * before the first.  Counts wrap modulo 2^32.
+ *   idx    device [n] int32, e.g. the [T][K] routing indices moe_route writes (n = T * K)
+ *   counts device [n_experts] uint32
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n < 0, n_experts outside [1, MOE_MAX_EXPERTS]),
+ * MOE_ERR_ALIGN, MOE_ERR_LAUNCH. */
+int moe_expert_usage(const int32_t *idx, int n, int n_experts, uint32_t *counts, void *stream);
+
+/* order = the experts ranked by counts, largest first; equal counts rank the lower expert index
+ * first.  The first n entries of order are the hot set of size n.
+ *   counts device [n_experts] uint32;  order device [n_experts] int32 (a permutation)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_LAUNCH. */
+int moe_hot_order(const uint32_t *counts, int n_experts, int32_t *order, void *stream);
+
+/* Re-tier a layer: the experts order[0 .. n_hot-1] are hot and keep their base blobs; the expert
+ * of rank r >= n_hot is cold: each of its three matrices is dequantised from its base blob (any
+ * width, w = q * scale + bias in fp32) and quantised again at cold_bits with the rounding of
+ * moe_quantize_matrix, into the cold blob at store + (r - n_hot) * moe_packed_expert_bytes(H, I,
+ * cold_bits).  Then tiered[e] = base[e] for a hot expert and {its cold blob, cold_bits} for a
+ * cold one.
+ *   dims   host; hidden, inter, n_experts of the layer (top_k is only validated)
+ *   base   device [n_experts] descriptor table of the base blobs (validate it with
+ *          moe_check_experts; its blobs are read, not changed)
+ *   order  device [n_experts] int32, a permutation of the experts (as moe_hot_order writes);
+ *          an entry outside [0, n_experts) is skipped (its slot stays unwritten)
+ *   store  device, 256-byte aligned, store_bytes >= (n_experts - n_hot) cold blobs; it must not
+ *          overlap the base blobs
+ *   tiered device [n_experts] descriptor table, written after every cold blob; it may be base
+ *          itself (re-tiering in place)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_BITS, MOE_ERR_ALIGN, MOE_ERR_BUFFER (store too
+ * small), MOE_ERR_LAUNCH. */
+int moe_retier(const moe_dims *dims, const moe_expert_desc *base, const int32_t *order, int n_hot,
+               int cold_bits, void *store, size_t store_bytes, moe_expert_desc *tiered, void *stream);
 
 /* Copy a device descriptor table to the host (synchronously, on the null stream) and
  * check it: non-NULL, 256-byte aligned blobs, bits in {2,4}, reserved == 0.

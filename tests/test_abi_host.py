@@ -189,3 +189,37 @@ def test_quantize_matrix_validates_before_launch(L):
     assert q(w, M.MOE_F32, 4, 64, 2, P(0x200008), sb, None) == 5
     assert q(w, M.MOE_F32, 4, 64, 2, codes, P(0x300002), None) == 5
     assert b"bits" in L.moe_last_error() or b"align" in L.moe_last_error()
+
+
+def test_tier_calls_validate_before_launch(L):
+    """moe_expert_usage, moe_hot_order and moe_retier refuse bad arguments with a status before
+    anything is enqueued (every call below fails validation, so no device pointer is touched)."""
+    P = ctypes.c_void_p
+    idx, counts, order = P(0x100000), P(0x200000), P(0x300000)
+    u = L.moe_expert_usage
+    assert u(idx, 16, 8, None, None) == 1                                    # MOE_ERR_NULL
+    assert u(None, 16, 8, counts, None) == 1
+    assert u(idx, -1, 8, counts, None) == 2                                  # MOE_ERR_SHAPE
+    assert u(idx, 16, 0, counts, None) == 2
+    assert u(idx, 16, M.MAX_EXPERTS + 1, counts, None) == 2
+    assert u(P(0x100002), 16, 8, counts, None) == 5                          # MOE_ERR_ALIGN
+    h = L.moe_hot_order
+    assert h(None, 8, order, None) == 1
+    assert h(counts, 8, None, None) == 1
+    assert h(counts, 0, order, None) == 2
+    assert h(counts, 8, P(0x300001), None) == 5
+    dims = M.moe_dims(256, 128, 16, 2)
+    base, tiered, store = P(0x400000), P(0x500000), P(0x600000)
+    cold2 = L.moe_packed_expert_bytes(256, 128, 2)
+    r = L.moe_retier
+    assert r(ctypes.byref(dims), None, order, 4, 2, store, 12 * cold2, tiered, None) == 1
+    assert r(ctypes.byref(dims), base, order, 4, 2, None, 12 * cold2, tiered, None) == 1   # cold experts, no store
+    assert r(ctypes.byref(dims), base, order, 17, 2, store, 12 * cold2, tiered, None) == 2
+    assert r(ctypes.byref(dims), base, order, -1, 2, store, 12 * cold2, tiered, None) == 2
+    assert r(ctypes.byref(dims), base, order, 4, 3, store, 12 * cold2, tiered, None) == 4
+    assert r(ctypes.byref(dims), base, order, 4, 2, P(0x600080), 12 * cold2, tiered, None) == 5
+    assert r(ctypes.byref(dims), P(0x400008), order, 4, 2, store, 12 * cold2, tiered, None) == 5
+    assert r(ctypes.byref(dims), base, order, 4, 2, store, 12 * cold2 - 1, tiered, None) == 9   # MOE_ERR_BUFFER
+    assert b"store_bytes" in L.moe_last_error()
+    bad = M.moe_dims(100, 128, 16, 2)
+    assert r(ctypes.byref(bad), base, order, 4, 2, store, 12 * cold2, tiered, None) == 2

@@ -35,6 +35,10 @@ def weights(rows: int, cols: int, seed: int) -> np.ndarray:
         lambda: 100.3 + rng.uniform(0, 1e-3, 64),                    # far from zero, narrow
         lambda: np.concatenate([rng.normal(0, 1, 63), [40.0]]),      # one outlier
         lambda: np.zeros(64),                                        # all zero
+        # exact half-integer quotients (w - bias) / scale = k + 1/2 under a scale whose reciprocal is
+        # inexact (3 * 2^-6): the codes follow ties-to-even only if the IEEE quotient decides them
+        lambda: np.concatenate([[-1.0, -1.0 + 15 * 3 * 2.0 ** -6],
+                                -1.0 + (np.arange(62) % 15 + 0.5) * 3 * 2.0 ** -6]),
     ]
     for i, f in enumerate(special):
         g = (7 * i + 3) % G
