@@ -105,7 +105,6 @@ __device__ __forceinline__ void requant_wave(const GLOBAL_AS uint8_t *src, GLOBA
                                              const uint64_t (&oout)[6], int m, uint32_t g0, uint32_t gm, int lane) {
     constexpr int kIn = 1 << BIN;                       // input codes
     constexpr int kPer = kIn / 4;                       // table entries per quad lane
-    constexpr uint32_t kOutMask = (1u << BOUT) - 1;
     const int j = lane & 3;
     uint32_t w[kRqGroups][2], sb[kRqGroups];
 #pragma unroll
@@ -126,22 +125,23 @@ __device__ __forceinline__ void requant_wave(const GLOBAL_AS uint8_t *src, GLOBA
     for (int k = 0; k < kRqGroups; ++k) {
         const uint32_t g = g0 + 16 * k + (lane >> 2);
         if (g0 + 16 * k >= gm) break;                    // uniform: gm is a multiple of 16
-        uint32_t c[16];
+        // t[i] = BOUT * (input code of weight i): the bit offset of its table entry
+        uint32_t t[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            c[i] = BIN == 4 ? (w[k][i >> 3] >> (4 * (i & 7))) & 15u : (w[k][0] >> (2 * i)) & 3u;
-        uint32_t cmin = c[0], cmax = c[0];
+            t[i] = (BIN == 4 ? (w[k][i >> 3] >> (4 * (i & 7))) & 15u : (w[k][0] >> (2 * i)) & 3u) * BOUT;
+        uint32_t tmin = t[0], tmax = t[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
-            cmin = min(cmin, c[i]);
-            cmax = max(cmax, c[i]);
+            tmin = min(tmin, t[i]);
+            tmax = max(tmax, t[i]);
         }
-        cmin = min(cmin, dppu<0xB1>(cmin));             // quad_perm [1,0,3,2]
-        cmax = max(cmax, dppu<0xB1>(cmax));
-        cmin = min(cmin, dppu<0x4E>(cmin));             // quad_perm [2,3,0,1]
-        cmax = max(cmax, dppu<0x4E>(cmax));
+        tmin = min(tmin, dppu<0xB1>(tmin));             // quad_perm [1,0,3,2]
+        tmax = max(tmax, dppu<0xB1>(tmax));
+        tmin = min(tmin, dppu<0x4E>(tmin));             // quad_perm [2,3,0,1]
+        tmax = max(tmax, dppu<0x4E>(tmax));
         const float s = bf16_f32(sb[k] & 0xFFFFu), b = bf16_f32(sb[k] >> 16);
-        const float wa = (float)cmin * s + b, wb = (float)cmax * s + b;
+        const float wa = (float)(tmin / BOUT) * s + b, wb = (float)(tmax / BOUT) * s + b;
         const QPair p = quant_pair<BOUT>(fminf(wa, wb), fmaxf(wa, wb));
         // this lane's table entries: input codes kPer * j .. kPer * j + kPer - 1
         uint32_t tab[2] = {0, 0};
@@ -172,12 +172,8 @@ __device__ __forceinline__ void requant_wave(const GLOBAL_AS uint8_t *src, GLOBA
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             uint32_t o;
-            if (kIn * BOUT <= 32) {
-                o = (tab[0] >> (BOUT * c[i])) & kOutMask;
-            } else {                                    // 16 entries of 4 bits: two words
-                const uint32_t t = c[i] < 8 ? tab[0] : tab[1];
-                o = (t >> (4 * (c[i] & 7))) & kOutMask;
-            }
+            if (kIn * BOUT <= 32) o = __builtin_amdgcn_ubfe(tab[0], t[i], BOUT);
+            else o = __builtin_amdgcn_ubfe(t[i] < 32 ? tab[0] : tab[1], t[i] & 31, BOUT);   // 16 entries of 4 bits
             const int bit = BOUT * i;
             out[bit >> 5] |= o << (bit & 31);
         }
