@@ -14,7 +14,8 @@ Where the Flash-MoE pages define a step (affine dequantisation and its FMA form,
 "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE", section "Metal Compute Shaders")
 this follows them; where they are silent it takes the plain reading written in the
 header of ``moe_oracle.c``.  Beside the per-token path: quantise-from-float (``quantize``) and the
-policy side of the tiered store (``expert_usage``, ``hot_order``, ``requantize_expert``).
+policy side of the tiered store (``expert_usage``, ``hot_order``, ``requantize_expert``) and the
+replacement policy of an expert cache (``ExpertCacheModel``).
 """
 from __future__ import annotations
 
@@ -260,6 +261,66 @@ def requantize_expert(blob: np.ndarray, H: int, I: int, bits_in: int, bits_out: 
         sb = blob[s0:s0 + sb_bytes(rows, cols)].view(np.uint16)
         out.append(requantize_matrix(codes, sb, rows, cols, bits_in, bits_out))
     return out
+
+
+# ----------------------------------------------------------------------------- expert cache policy
+# The pages stream each selected expert from SSD once routing is known and let the OS page cache keep
+# recently read experts in memory (lilting.ch, "397Bパラメータモデルを48GB MacBookで動かすFlash-MoE",
+# section "コア技術: SSDエキスパートストリーミング"); they do not define the replacement policy.  Plain
+# reading for a store held in host memory with a cache of expert slots in device memory: least
+# recently used replacement, one call per routing step.
+
+class ExpertCacheModel:
+    """Residency of experts in n_slots slots.  fetch(requests) processes one routing step: its
+    distinct experts in [0, E) (first occurrence order; others are ignored) are each a hit when
+    resident, else a miss loaded into the lowest free slot or, with no free slot, into the slot used
+    least recently among those this call has not touched (equal times: the lower slot).  A call
+    with more distinct experts than slots is refused (ValueError) and changes nothing."""
+
+    def __init__(self, E: int, n_slots: int):
+        self.E, self.n_slots = E, n_slots
+        self.slot_of = {}                      # expert -> slot
+        self.expert_of = [-1] * n_slots        # slot -> expert, -1 free
+        self.last_use = [0] * n_slots
+        self.tick = 0
+        self.hits = self.misses = 0
+
+    def fetch(self, requests):
+        """Returns (hits, misses, loads, evicted): loads = [(expert, slot)] in load order,
+        evicted = experts removed by this call."""
+        distinct = []
+        for e in requests:
+            e = int(e)
+            if 0 <= e < self.E and e not in distinct:
+                distinct.append(e)
+        if len(distinct) > self.n_slots:
+            raise ValueError("more distinct experts than slots")
+        self.tick += 1
+        hits, missing = 0, []
+        for e in distinct:
+            if e in self.slot_of:
+                hits += 1
+                self.last_use[self.slot_of[e]] = self.tick
+            else:
+                missing.append(e)
+        loads, evicted = [], []
+        for e in missing:
+            free = [s for s in range(self.n_slots) if self.expert_of[s] < 0]
+            if free:
+                s = free[0]
+            else:
+                s = min((s for s in range(self.n_slots) if self.last_use[s] < self.tick),
+                        key=lambda s: (self.last_use[s], s))
+                old = self.expert_of[s]
+                del self.slot_of[old]
+                evicted.append(old)
+            self.slot_of[e] = s
+            self.expert_of[s] = e
+            self.last_use[s] = self.tick
+            loads.append((e, s))
+        self.hits += hits
+        self.misses += len(missing)
+        return hits, len(missing), loads, evicted
 
 
 def silu(z: float) -> float:

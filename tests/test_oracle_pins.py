@@ -572,3 +572,48 @@ def test_requantize_error_bound(orc, bits_in, bits_out):
             bound = s / 2 + abs(lo - b) + qmax * abs(s - (hi - lo) / qmax) + 1e-6 * max(abs(lo), abs(hi), 1e-3)
             err = np.abs(w - (c2[r, 64 * g:64 * (g + 1)] * s + b))
             assert err.max() <= bound, (r, g, err.max(), bound)
+
+
+# --------------------------------------------------------------------------- expert cache policy
+def test_expert_cache_model_hand_trace():
+    """Pins oracle.ExpertCacheModel on a trace worked out by hand with 3 slots:
+    {1,2} -> misses into slots 0,1; {2,3} -> 2 hit, 3 into free slot 2; {4,1} -> 1 hit (slot 0, now
+    newest), 4 evicts the least recently used untouched slot: slot 1 (expert 2, last used in call 2)
+    ties with slot 2 (expert 3, call 2) -> the lower slot 1; {3,5,5,-1,9} with E = 8 -> 3 hit,
+    5 evicts slot 0 (expert 1, call 3) vs slot 1 (expert 4, call 3) -> slot 0."""
+    import oracle
+    m = oracle.ExpertCacheModel(8, 3)
+    assert m.fetch([1, 2]) == (0, 2, [(1, 0), (2, 1)], [])
+    assert m.fetch([2, 3]) == (1, 1, [(3, 2)], [])
+    assert m.fetch([4, 1]) == (1, 1, [(4, 1)], [2])
+    assert m.fetch([3, 5, 5, -1, 9]) == (1, 1, [(5, 0)], [1])
+    assert m.slot_of == {3: 2, 4: 1, 5: 0} and m.hits == 3 and m.misses == 5
+    with pytest.raises(ValueError):
+        m.fetch([0, 1, 2, 6])
+    assert m.slot_of == {3: 2, 4: 1, 5: 0} and m.tick == 4
+
+
+def test_expert_cache_model_properties():
+    """On random routing traces: every expert of a call is resident after it; a call never evicts
+    one of its own experts; no eviction while a slot is free; an expert requested in two
+    consecutive calls is a hit the second time; with at least as many slots as experts, the misses
+    are exactly the first requests of each expert."""
+    import oracle
+    rng = np.random.default_rng(31)
+    for E, n_slots, K in [(16, 4, 2), (40, 9, 4), (12, 12, 3)]:
+        m = oracle.ExpertCacheModel(E, n_slots)
+        seen, prev = set(), set()
+        for _ in range(300):
+            req = rng.choice(E, size=K, replace=False)
+            occupied = sum(1 for x in m.expert_of if x >= 0)
+            hits, misses, loads, evicted = m.fetch(req)
+            cur = set(int(e) for e in req)
+            assert all(e in m.slot_of for e in cur)
+            assert not (set(evicted) & cur)
+            if occupied + misses <= n_slots:
+                assert not evicted
+            assert all(e in m.slot_of for e in prev & cur) and hits >= len(prev & cur)
+            if n_slots >= E:
+                assert misses == len(cur - seen)
+            seen |= cur
+            prev = cur
