@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--retier", action="store_true",
                    help="measure the tiered-store policy (usage over the routed token bank, hot order, "
                         "requantisation of the cold experts) instead of the expert path")
+    p.add_argument("--cache", type=int, default=0, metavar="SLOTS",
+                   help="decode with the experts in pinned host memory and SLOTS of them cached in device "
+                        "memory (moe_cache_fetch before each step's expert FFN)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run device-to-device copies of 1 GiB (reference for the HBM byte counters)")
     p.add_argument("--traffic-from", metavar="DIR",
@@ -321,8 +324,103 @@ def retier_bench(a):
     print(json.dumps(line), flush=True)
 
 
+def cache_bench(a):
+    """Decode with the store in host memory: the 512 experts of a 4096 x 1024 4-bit layer (3.6 GB)
+    in pinned host memory, a cache of a.cache slots in device memory, Zipf(1.1)-biased routing (the
+    tiered workload's prior).  A step is one token: moe_route, the indices copied to the host,
+    moe_cache_fetch (host-to-device copies of the missing experts, table update), moe_expert_ffn
+    through the cache's table, moe_combine; steps are dependent (each waits for its indices).
+    Reported beside it: the hit rate, the copy rate of the misses, a plain pinned host-to-device copy
+    of 64 MiB as the link's reference, and the same steps with every expert resident."""
+    import torch
+    import bit_expert_dequant_amd as M
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from moe_cases import act_tensor, build_layer
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = dataclasses.replace(synth.WORKLOADS[4], tokens=1)
+    H, I, E, K = wl.H, wl.I, wl.E, wl.K
+    d = M.make_dims(H, I, E, K)
+    dl = build_layer(wl)
+    n_slots = a.cache
+    host = torch.empty(dl.store.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(dl.store)
+    slots = torch.empty(n_slots * dl.stride, dtype=torch.uint8, device="cuda")
+    table = torch.zeros_like(dl.table)
+    cache = M.ExpertCache(d, [host.data_ptr() + e * dl.stride for e in range(E)], [4] * E, slots, dl.stride,
+                          n_slots, table)
+    Lc = M.Layer(dl.router, table, dl.logit_bias, dl.norm_w, wl.norm_eps)
+    bank = act_tensor(wl, wl.tokens_bank(4096))
+    idx = torch.empty(1, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(1, K, dtype=torch.float32, device="cuda")
+    y = torch.empty(1, K, H, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, H, dtype=torch.float32, device="cuda")
+    ws_r = M.workspace(M.MOE_OP_ROUTE, d, 1, 1)
+    ws_f = M.workspace(M.MOE_OP_EXPERT_FFN, d, 1, 1)
+    idx_h = torch.empty(1, K, dtype=torch.int32, pin_memory=True)
+
+    def step(t, cached=True):
+        x = bank[t % 4096:t % 4096 + 1]
+        M.moe_route(d, dl.L, x, idx, w, ws=ws_r)
+        if cached:
+            idx_h.copy_(idx)                     # synchronous: the step needs its routing on the host
+            cache.fetch(idx_h.numpy())
+        M.moe_expert_ffn(d, Lc if cached else dl.L, x, idx, y, ws_f)
+        M.moe_combine(y, w, out)
+
+    warm, steps = max(a.warmup, 64), max(min(a.steps, 2048), 64)
+    for t in range(warm):
+        step(t)
+    torch.cuda.synchronize()
+    h0, m0, b0 = cache.stats()
+    t0 = time.perf_counter()
+    for t in range(warm, warm + steps):
+        step(t)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    h1, m1, b1 = cache.stats()
+    t0 = time.perf_counter()
+    for t in range(warm, warm + steps):
+        step(t, cached=False)
+    torch.cuda.synchronize()
+    dt_res = time.perf_counter() - t0
+    # the link's reference: pinned host-to-device copies of 64 MiB
+    src = torch.empty(64 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(16):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    link = 16 * (64 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    hits, misses, copied = h1 - h0, m1 - m0, b1 - b0
+    copy_gbps = copied / dt / 1e9
+    line = {"metric": "decode tok/s with the expert store in host memory (device expert cache)",
+            "value": round(steps / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+            "ms_per_step": round(dt / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"one layer H{H} I{I} E{E} top-{K} 4-bit (3.6 GB) in pinned host memory, "
+                                   f"{n_slots} device slots, Zipf(1.1) routing, 1 token per step",
+                       "slots": n_slots, "experts": E},
+            "cache": {"hit_rate": round(hits / max(1, hits + misses), 4), "misses_per_token": round(misses / steps, 3),
+                      "copy_GBps": round(copy_gbps, 2), "bytes_copied": copied},
+            "roofline": {"bound": "pcie", "kernel": "host-to-device copies of missing experts",
+                         "achieved": round(copy_gbps, 2), "peak": round(link, 2), "unit": "GB/s",
+                         "frac": round(copy_gbps / link, 4), "traffic": None,
+                         "peak_is": "measured pinned host-to-device copy rate (64 MiB copies)"},
+            "resident_tok_s": round(steps / dt_res, 1)}
+    cache.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.cache:
+        cache_bench(a)
+        return
     if a.quantize:
         quantize_bench(a)
         return

@@ -26,6 +26,7 @@ MOE_FLAG_SEPARATE_KERNELS = 2
 GROUP = 64
 MAX_TOPK = 8
 MAX_EXPERTS = 2048
+MOE_CACHE_DRY_RUN = 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_BITS",
           5: "MOE_ERR_ALIGN", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_LAUNCH", 8: "MOE_ERR_UNSUPPORTED",
           9: "MOE_ERR_BUFFER", 10: "MOE_ERR_DEVICE"}
@@ -86,6 +87,11 @@ def lib():
             "moe_expert_usage": (I32, [P, I32, I32, P, P]),
             "moe_hot_order": (I32, [P, I32, P, P]),
             "moe_retier": (I32, [P, P, P, I32, I32, P, SZ, P, P]),
+            "moe_cache_create": (I32, [P, P, P, SZ, I32, P, U, P, P]),
+            "moe_cache_fetch": (I32, [P, P, I32, P, P]),
+            "moe_cache_stats": (I32, [P, P, P, P]),
+            "moe_cache_slot": (I32, [P, I32]),
+            "moe_cache_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -100,7 +106,8 @@ def exported_symbols() -> List[str]:
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
             "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read",
-            "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier"]
+            "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier", "moe_cache_create",
+            "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy"]
 
 
 def _check(status: int):
@@ -302,6 +309,55 @@ def moe_retier(dims: moe_dims, base, order, n_hot: int, cold_bits: int, store, t
     _check(lib().moe_retier(ctypes.byref(dims), _tptr(base), _tptr(order), n_hot, cold_bits, _tptr(store),
                             0 if store is None else store.numel() * store.element_size(), _tptr(tiered),
                             _stream(stream)))
+
+
+class ExpertCache:
+    """A device-memory cache of experts whose blobs live in host memory (see moe_cache_create in the
+    header).  ``host_ptrs``/``bits``: host address and width of each expert's blob (pinned memory,
+    e.g. a torch tensor allocated with pin_memory=True); ``slots``: a uint8 device tensor of
+    n_slots * slot_bytes bytes; ``table``: the device descriptor table the layer uses (e.g. from
+    :func:`expert_table`), which the cache owns from now on.  ``dry_run`` runs the policy only."""
+
+    def __init__(self, dims: moe_dims, host_ptrs: Sequence[int], bits: Sequence[int], slots=None,
+                 slot_bytes: int = 0, n_slots: int = 0, table=None, dry_run: bool = False, stream=None):
+        E = dims.n_experts
+        host = np.zeros((E, 2), dtype=np.uint64)
+        host[:, 0] = np.asarray(host_ptrs, dtype=np.uint64)
+        host[:, 1] = np.asarray(bits, dtype=np.uint64)
+        self._keep = (host, slots, table)
+        self._dry = dry_run
+        self._c = ctypes.c_void_p()
+        _check(lib().moe_cache_create(ctypes.byref(dims), _np_ptr(host), _tptr(slots), slot_bytes, n_slots,
+                                      _tptr(table), MOE_CACHE_DRY_RUN if dry_run else 0,
+                                      None if dry_run else _stream(stream), ctypes.byref(self._c)))
+
+    def fetch(self, idx, stream=None) -> int:
+        """Make the experts named in ``idx`` (host int array, any shape) resident; returns the misses."""
+        a = np.ascontiguousarray(idx, dtype=np.int32).reshape(-1)
+        miss = ctypes.c_int(0)
+        _check(lib().moe_cache_fetch(self._c, _np_ptr(a), a.size, None if self._dry else _stream(stream),
+                                     ctypes.byref(miss)))
+        return miss.value
+
+    def stats(self):
+        """(hits, misses, bytes copied) since creation."""
+        h, m, b = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().moe_cache_stats(self._c, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)))
+        return h.value, m.value, b.value
+
+    def slot(self, expert: int) -> int:
+        return lib().moe_cache_slot(self._c, expert)
+
+    def close(self):
+        if self._c:
+            lib().moe_cache_destroy(self._c)
+            self._c = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_dequant.so")
 
-SOURCES = ["moe_api.cpp", "moe_batched8.hip", "moe_decode.hip", "moe_grouped.hip", "moe_layer.hip", "moe_quant.hip", "moe_tier.hip"]
+SOURCES = ["moe_api.cpp", "moe_batched8.hip", "moe_decode.hip", "moe_grouped.hip", "moe_layer.hip", "moe_quant.hip", "moe_tier.hip", "moe_cache.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

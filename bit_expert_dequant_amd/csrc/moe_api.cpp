@@ -9,7 +9,9 @@
 #include <algorithm>
 #include <cstring>
 #include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "moe_dequant.h"
@@ -496,6 +498,183 @@ int moe_retier(const moe_dims *dims, const moe_expert_desc *base, const int32_t 
     if (int s = launched(moe::launch_retier(r, (hipStream_t)stream), "retier")) return s;
     return ok();
 }
+
+// ----------------------------------------------------------------------------- expert cache
+// Least recently used replacement over n_slots device slots; a call touches its distinct experts
+// first (hits), then loads each missing one into the lowest free slot or, with none free, into the
+// slot used least recently among those the call has not touched (equal times: the lower slot).
+struct moe_expert_cache {
+    int E = 0, n_slots = 0;
+    unsigned flags = 0;
+    std::vector<moe_expert_desc> host;            // host blob address and width per expert
+    std::vector<size_t> bytes;                    // blob bytes per expert
+    uint8_t *slots = nullptr;
+    size_t slot_bytes = 0;
+    moe_expert_desc *table = nullptr;
+    std::vector<int> slot_of, expert_of;
+    std::vector<uint64_t> last_use, mark;
+    std::set<std::pair<uint64_t, int>> lru;       // (last use, slot) of occupied slots
+    std::set<int> free_slots;
+    uint64_t tick = 0, epoch = 0;
+    uint64_t hits = 0, misses = 0, copied = 0;
+    bool broken = false;
+    // per-call scratch
+    std::vector<int> req;
+    std::vector<int32_t> upd_e;
+    std::vector<uint64_t> upd_blob;
+    std::vector<uint32_t> upd_bits;
+};
+
+int moe_cache_create(const moe_dims *dims, const moe_expert_desc *host_experts, void *slots, size_t slot_bytes,
+                     int n_slots, moe_expert_desc *table, unsigned flags, void *stream, moe_expert_cache **cache) {
+    if (!cache) return fail(MOE_ERR_NULL, "cache is NULL");
+    *cache = nullptr;
+    if (int s = check_dims(dims)) return s;
+    if (flags & ~MOE_CACHE_DRY_RUN) return fail(MOE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool dry = flags & MOE_CACHE_DRY_RUN;
+    if (!host_experts) return fail(MOE_ERR_NULL, "host_experts is NULL");
+    const int E = dims->n_experts;
+    if (n_slots < dims->top_k || n_slots > (1 << 20))
+        return fail(MOE_ERR_SHAPE, "n_slots=%d outside [top_k=%d, 2^20]", n_slots, dims->top_k);
+    if (!dry) {
+        if (!slots || !table) return fail(MOE_ERR_NULL, "slots and table are required");
+        if (!aligned(slots, MOE_BLOB_ALIGN) || slot_bytes % MOE_BLOB_ALIGN != 0)
+            return fail(MOE_ERR_ALIGN, "slots and slot_bytes must be multiples of %d", MOE_BLOB_ALIGN);
+        if (!aligned(table, 16)) return fail(MOE_ERR_ALIGN, "table must be 16-byte aligned");
+    }
+    auto c = new moe_expert_cache;
+    c->E = E;
+    c->n_slots = n_slots;
+    c->flags = flags;
+    c->host.assign(host_experts, host_experts + E);
+    c->bytes.resize(E);
+    for (int e = 0; e < E; ++e) {
+        const moe_expert_desc &d = c->host[e];
+        int st = MOE_OK;
+        if (!d.blob) st = fail(MOE_ERR_NULL, "host_experts[%d].blob is NULL", e);
+        else if (!bits_ok((int)d.bits)) st = fail(MOE_ERR_BITS, "host_experts[%d].bits=%u (2 or 4)", e, d.bits);
+        else if (d.reserved) st = fail(MOE_ERR_SHAPE, "host_experts[%d].reserved must be 0", e);
+        else if ((c->bytes[e] = moe_packed_expert_bytes(dims->hidden, dims->inter, (int)d.bits)) > slot_bytes && !dry)
+            st = fail(MOE_ERR_BUFFER, "slot_bytes=%zu < expert %d's blob of %zu bytes", slot_bytes, e, c->bytes[e]);
+        if (st) {
+            delete c;
+            return st;
+        }
+    }
+    c->slots = (uint8_t *)slots;
+    c->slot_bytes = slot_bytes;
+    c->table = table;
+    c->slot_of.assign(E, -1);
+    c->mark.assign(E, 0);
+    c->expert_of.assign(n_slots, -1);
+    c->last_use.assign(n_slots, 0);
+    for (int s = 0; s < n_slots; ++s) c->free_slots.insert(s);
+    if (!dry) {
+        if (int st = launched(moe::launch_table_absent(table, E, (hipStream_t)stream), "cache table")) {
+            delete c;
+            return st;
+        }
+    }
+    *cache = c;
+    return ok();
+}
+
+int moe_cache_fetch(moe_expert_cache *c, const int32_t *idx, int n, void *stream, int *misses_out) {
+    if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
+    if (c->broken) return fail(MOE_ERR_LAUNCH, "an earlier enqueue on this cache failed; destroy it");
+    if (n < 0) return fail(MOE_ERR_SHAPE, "n=%d is negative", n);
+    if (n > 0 && !idx) return fail(MOE_ERR_NULL, "idx is NULL");
+    const uint64_t ep = ++c->epoch;
+    c->req.clear();
+    for (int i = 0; i < n; ++i) {
+        const int e = idx[i];
+        if (e >= 0 && e < c->E && c->mark[e] != ep) {
+            c->mark[e] = ep;
+            c->req.push_back(e);
+        }
+    }
+    if ((int)c->req.size() > c->n_slots)
+        return fail(MOE_ERR_SHAPE, "%zu distinct experts exceed the %d slots", c->req.size(), c->n_slots);
+    const uint64_t t = ++c->tick;
+    int hit = 0;
+    for (int e : c->req) {
+        const int s = c->slot_of[e];
+        if (s < 0) continue;
+        ++hit;
+        c->lru.erase({c->last_use[s], s});
+        c->last_use[s] = t;
+        c->lru.insert({t, s});
+    }
+    c->upd_e.clear();
+    c->upd_blob.clear();
+    c->upd_bits.clear();
+    const bool dry = c->flags & MOE_CACHE_DRY_RUN;
+    int miss = 0;
+    for (int e : c->req) {
+        if (c->slot_of[e] >= 0) continue;
+        ++miss;
+        int s;
+        if (!c->free_slots.empty()) {
+            s = *c->free_slots.begin();
+            c->free_slots.erase(c->free_slots.begin());
+        } else {
+            // the least recent (last use, slot); a slot touched by this call has last use t and is
+            // never first while an untouched one exists, which the slot count guarantees
+            const auto it = c->lru.begin();
+            s = it->second;
+            c->lru.erase(it);
+            const int old = c->expert_of[s];
+            c->slot_of[old] = -1;
+            c->upd_e.push_back(old);
+            c->upd_blob.push_back(0);
+            c->upd_bits.push_back(4);
+        }
+        c->slot_of[e] = s;
+        c->expert_of[s] = e;
+        c->last_use[s] = t;
+        c->lru.insert({t, s});
+        uint8_t *dst = c->slots + (size_t)s * c->slot_bytes;
+        c->upd_e.push_back(e);
+        c->upd_blob.push_back((uint64_t)(uintptr_t)dst);
+        c->upd_bits.push_back(c->host[e].bits);
+        c->copied += c->bytes[e];
+        if (!dry) {
+            const hipError_t err = hipMemcpyAsync(dst, (const void *)(uintptr_t)c->host[e].blob, c->bytes[e],
+                                                  hipMemcpyHostToDevice, (hipStream_t)stream);
+            if (err != hipSuccess) {
+                c->broken = true;
+                return fail(MOE_ERR_LAUNCH, "copy of expert %d: %s", e, hipGetErrorString(err));
+            }
+        }
+    }
+    c->hits += hit;
+    c->misses += miss;
+    if (!dry && !c->upd_e.empty()) {
+        const hipError_t err = moe::launch_table_update(c->table, (int)c->upd_e.size(), c->upd_e.data(),
+                                                        c->upd_blob.data(), c->upd_bits.data(), (hipStream_t)stream);
+        if (err != hipSuccess) {
+            c->broken = true;
+            return fail(MOE_ERR_LAUNCH, "cache table update: %s", hipGetErrorString(err));
+        }
+    }
+    if (misses_out) *misses_out = miss;
+    return ok();
+}
+
+int moe_cache_stats(const moe_expert_cache *c, uint64_t *hits, uint64_t *misses, uint64_t *bytes) {
+    if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
+    if (hits) *hits = c->hits;
+    if (misses) *misses = c->misses;
+    if (bytes) *bytes = c->copied;
+    return ok();
+}
+
+int moe_cache_slot(const moe_expert_cache *c, int expert) {
+    if (!c || expert < 0 || expert >= c->E) return -2;
+    return c->slot_of[expert];
+}
+
+void moe_cache_destroy(moe_expert_cache *c) { delete c; }
 
 // Start/stop events of kernel j of a timed call: events[2j], events[2j+1].
 static moe::KernelEvents kernel_events(void *const *events, int j) {

@@ -174,11 +174,12 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
         uint32_t key = 0xFFFFFFFFu;          // padding and pairs naming no expert sort last
         if (p < P) {
             const int e = a.idx[p];
-            if (e >= 0 && e < E) {
+            if (e >= 0 && e < E && a.experts[e].blob != 0) {
                 key = (uint32_t)e * (uint32_t)P + (uint32_t)p;
                 atomicAdd(&s_cnt[e], 1);
             } else {
-                // such pairs are a caller error and get a zero output row, as in the decode path
+                // an index outside [0, E) or an absent expert (blob 0, e.g. not resident in an expert
+                // cache) gets a zero output row, as in the decode path
                 for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
             }
         }

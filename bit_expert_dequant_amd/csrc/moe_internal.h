@@ -209,6 +209,12 @@ struct RetierLaunch {
 };
 hipError_t launch_retier(const RetierLaunch &r, hipStream_t s);
 
+// Expert cache: descriptor-table writes (moe_cache.hip).  An update list names each expert at most
+// once; entries with blob 0 mark absent experts.
+hipError_t launch_table_absent(moe_expert_desc *table, int E, hipStream_t s);
+hipError_t launch_table_update(moe_expert_desc *table, int n, const int32_t *expert, const uint64_t *blob,
+                               const uint32_t *bits, hipStream_t s);
+
 // Read-stream reference kernel (XOR of every dword of buf into *sink).
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 

@@ -225,6 +225,65 @@ int moe_hot_order(const uint32_t *counts, int n_experts, int32_t *order, void *s
 int moe_retier(const moe_dims *dims, const moe_expert_desc *base, const int32_t *order, int n_hot,
                int cold_bits, void *store, size_t store_bytes, moe_expert_desc *tiered, void *stream);
 
+/* --------------------------------------------------------------------------- expert cache */
+/* For stores larger than device memory: the experts stay in host memory and a cache of slots in
+ * device memory holds the recently used ones.  The pages stream each selected expert from SSD once
+ * routing is known and let the OS page cache keep recently read experts (lilting.ch, "397Bパラメータ
+ * モデルを48GB MacBookで動かすFlash-MoE", section "コア技術: SSDエキスパートストリーミング"); here a
+ * routing step's indices, copied to the host, drive host-to-device copies of the missing experts
+ * into least recently used slots.  A step: moe_route -> copy idx to the host -> moe_cache_fetch ->
+ * moe_expert_ffn with the cache's table as the layer's experts -> moe_combine.
+ * A cache object is host state; calls on one cache must not overlap (serialise them). */
+typedef struct moe_expert_cache moe_expert_cache;
+
+#define MOE_CACHE_DRY_RUN 1u   /* policy only: no copies and no device writes (planning, host tests) */
+
+/* Create a cache.
+ *   dims          host; hidden, inter, n_experts (E), top_k of the layer
+ *   host_experts  HOST [E]: blob = host address of expert e's packed blob, bits 2 or 4, reserved 0.
+ *                 The list is copied; the blobs are read by later fetches and must stay valid and
+ *                 unchanged until moe_cache_destroy.  Allocate them pinned (hipHostMalloc) so the
+ *                 copies are asynchronous DMA.
+ *   slots         device, n_slots * slot_bytes bytes, 256-byte aligned; slot_bytes a multiple of 256
+ *                 and at least the largest expert blob (moe_packed_expert_bytes)
+ *   n_slots       in [top_k, 2^20]
+ *   table         device [E] descriptor table for the expert kernels (the moe_layer's experts).
+ *                 Create enqueues on `stream` a fill marking every expert absent (blob 0); from then
+ *                 on entry e is {its slot, its bits} while e is resident and blob 0 otherwise.  The
+ *                 expert kernels give a zero output row for an absent expert (moe_check_experts,
+ *                 which requires blobs, does not apply to such a table).
+ *   flags         0 or MOE_CACHE_DRY_RUN (then slots, table and stream are not used and may be NULL)
+ *   cache         out: the new cache, or NULL on error
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_BITS, MOE_ERR_ALIGN, MOE_ERR_BUFFER (slot too small),
+ * MOE_ERR_UNSUPPORTED (flags), MOE_ERR_LAUNCH. */
+int moe_cache_create(const moe_dims *dims, const moe_expert_desc *host_experts, void *slots,
+                     size_t slot_bytes, int n_slots, moe_expert_desc *table, unsigned flags,
+                     void *stream, moe_expert_cache **cache);
+
+/* Make resident every distinct expert named in idx (HOST [n] int32, e.g. one routing step's [T][K]
+ * indices; entries outside [0, E) are ignored).  First every such expert already resident is a
+ * hit and becomes most recently used; then each missing one (in first-occurrence order) takes the
+ * lowest free slot or, with none free, the slot used least recently among those this call has not
+ * touched (equal times: the lower slot), evicting its expert.  Each miss enqueues a host-to-device
+ * copy of the blob into its slot, then one small kernel writes the changed table entries (evicted
+ * experts become absent), all on `stream` after the work already there: kernels enqueued earlier
+ * still see a slot's previous expert.  misses (out, may be NULL): this call's misses.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n < 0, or more distinct experts than slots: nothing
+ * changes), MOE_ERR_LAUNCH (an enqueue failed; the cache is then unusable: destroy it). */
+int moe_cache_fetch(moe_expert_cache *cache, const int32_t *idx, int n, void *stream, int *misses);
+
+/* Totals since creation: distinct-expert hits and misses, bytes copied to the device.  Any output
+ * may be NULL.  Errors: MOE_ERR_NULL. */
+int moe_cache_stats(const moe_expert_cache *cache, uint64_t *hits, uint64_t *misses, uint64_t *bytes);
+
+/* Slot holding `expert`, -1 when it is not resident, -2 for a NULL cache or an expert outside
+ * [0, E). */
+int moe_cache_slot(const moe_expert_cache *cache, int expert);
+
+/* Free the cache's host state (device memory belongs to the caller; pending copies read host
+ * blobs, so synchronise the stream before freeing those).  NULL is ignored. */
+void moe_cache_destroy(moe_expert_cache *cache);
+
 /* Copy a device descriptor table to the host (synchronously, on the null stream) and
  * check it: non-NULL, 256-byte aligned blobs, bits in {2,4}, reserved == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_BITS, MOE_ERR_SHAPE, MOE_ERR_DEVICE. */

@@ -223,3 +223,70 @@ def test_tier_calls_validate_before_launch(L):
     assert b"store_bytes" in L.moe_last_error()
     bad = M.moe_dims(100, 128, 16, 2)
     assert r(ctypes.byref(bad), base, order, 4, 2, store, 12 * cold2, tiered, None) == 2
+
+
+def test_cache_dry_run_follows_the_policy_model(L):
+    """The expert cache's replacement decisions (dry run: policy only, no device) against the
+    oracle's LRU model, step by step: hits, misses and the slot of every expert."""
+    import oracle
+    rng = np.random.default_rng(41)
+    for E, K, n_slots, T in [(16, 2, 4, 1), (64, 4, 20, 3), (512, 4, 128, 1), (40, 8, 40, 2)]:
+        dims = M.moe_dims(128, 64, E, K)
+        host = [0x10000 + 0x100 * e for e in range(E)]
+        c = M.ExpertCache(dims, host, [4 if e % 3 else 2 for e in range(E)], n_slots=n_slots, dry_run=True)
+        model = oracle.ExpertCacheModel(E, n_slots)
+        zipf = 1.0 / np.arange(1, E + 1) ** 1.1
+        zipf /= zipf.sum()
+        for step in range(400):
+            idx = np.stack([rng.choice(E, size=K, replace=False, p=zipf) for _ in range(T)])
+            if step % 50 == 7:
+                idx[0, 0] = -1                       # ignored entries
+            if step % 50 == 9:
+                idx[-1, -1] = E + 3
+            miss = c.fetch(idx)
+            _, m_miss, _, _ = model.fetch(idx.reshape(-1))
+            assert miss == m_miss, (E, step)
+            assert [c.slot(e) for e in range(E)] == [model.slot_of.get(e, -1) for e in range(E)], (E, step)
+        hits, misses, _ = c.stats()
+        assert (hits, misses) == (model.hits, model.misses)
+        c.close()
+
+
+def test_cache_validates_and_refuses_oversized_steps(L):
+    """Create refuses bad arguments before touching anything; a step naming more distinct experts
+    than slots is refused and leaves the residency unchanged."""
+    dims = M.moe_dims(128, 64, 8, 2)
+    host = [0x10000 + 0x100 * e for e in range(8)]
+    with pytest.raises(M.MoeError) as ei:
+        M.ExpertCache(dims, host, [4] * 8, n_slots=1, dry_run=True)          # fewer slots than top_k
+    assert ei.value.status == 2
+    with pytest.raises(M.MoeError) as ei:
+        M.ExpertCache(dims, host, [4] * 7 + [3], n_slots=4, dry_run=True)
+    assert ei.value.status == 4
+    with pytest.raises(M.MoeError) as ei:
+        M.ExpertCache(dims, [0] + host[1:], [4] * 8, n_slots=4, dry_run=True)
+    assert ei.value.status == 1
+    P = ctypes.c_void_p
+    out = P()
+    hs = np.zeros((8, 2), dtype=np.uint64)
+    hs[:, 0] = host
+    hs[:, 1] = 4
+    blob4 = L.moe_packed_expert_bytes(128, 64, 4)
+    slot = (blob4 + 255) // 256 * 256
+    args = (ctypes.byref(dims), P(hs.ctypes.data))
+    assert L.moe_cache_create(*args, None, slot, 4, None, 0, None, ctypes.byref(out)) == 1   # no device buffers
+    assert L.moe_cache_create(*args, P(0x100080), slot, 4, P(0x200000), 0, None, ctypes.byref(out)) == 5
+    assert L.moe_cache_create(*args, P(0x100000), slot - 256, 4, P(0x200000), 0, None, ctypes.byref(out)) == 9
+    assert L.moe_cache_create(*args, P(0x100000), slot, 4, P(0x200000), 4, None, ctypes.byref(out)) == 8
+    assert not out.value
+    c = M.ExpertCache(dims, host, [4] * 8, n_slots=3, dry_run=True)
+    assert c.fetch([1, 2]) == 2
+    with pytest.raises(M.MoeError) as ei:
+        c.fetch([3, 4, 5, 6])
+    assert ei.value.status == 2
+    assert [c.slot(e) for e in range(8)] == [-1, 0, 1, -1, -1, -1, -1, -1]
+    assert c.slot(8) == -2 and c.slot(-1) == -2
+    assert c.fetch(np.array([], dtype=np.int32)) == 0
+    c.close()
+    assert L.moe_cache_fetch(None, None, 0, None, None) == 1
+    L.moe_cache_destroy(None)
