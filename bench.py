@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--traffic-from", metavar="DIR",
                    help="read rocprofv3 --pmc output under DIR/{fetch,write,copy_fetch,copy_write} and write "
                         "profiles/traffic.json for this workload")
+    p.add_argument("--traffic-key", default="",
+                   help="workload key for --traffic-from (default config<N>; 'quantize' and 'retier' for "
+                        "those modes)")
     return p.parse_args()
 
 
@@ -138,7 +141,7 @@ def traffic_from(d: str, workload_key: str):
     write = read_counter_csv(os.path.join(d, "write"), "WRITE_SIZE")
     res = {}
     for short in ("k_route_gateup", "k_router", "k_gateup", "k_down", "k_router_mfma", "k_group", "k_gu_mfma",
-                  "k_dn_mfma", "k_dn_res", "k_gu8", "k_dn8"):
+                  "k_dn_mfma", "k_dn_res", "k_gu8", "k_dn8", "k_quantize", "k_requant"):
         fk = [k for k in fetch if f"{short}<" in k or f"{short}(" in k]
         wk = [k for k in write if f"{short}<" in k or f"{short}(" in k]
         if not fk or not wk:
@@ -203,7 +206,8 @@ def quantize_bench(a):
             "config": {"workload": f"{n} fp32 matrices of {rows} x {cols}, 4-bit, group 64, {per} per launch",
                        "rows": per * rows, "cols": cols, "bits": bits},
             "roofline": {"bound": "hbm", "kernel": "k_quantize", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("k_quantize", "quantize"),
                          "bytes_per_launch": per_launch, "us_per_launch": round(us, 3),
                          "timing": "HIP events around back-to-back launches on the launch stream"},
             "parity": {"matrices": 1, "bit_exact": parity_ok}}
@@ -315,7 +319,8 @@ def retier_bench(a):
                                    f"prior), {n_hot} hot, {E - n_hot} requantised to 2 bits",
                        "hidden": H, "inter": I, "experts": E, "hot": n_hot, "tokens": T},
             "roofline": {"bound": "hbm", "kernel": "k_requant", "achieved": round(gbps_rq, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(gbps_rq / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbps_rq / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("k_requant", "retier"),
                          "bytes_per_launch": algo, "us_per_launch": round(rq * 1e3, 2),
                          "timing": "HIP events around moe_retier on the launch stream (requantisation + table)"},
             "hot_share": {"measured_hot_set": round(share, 4), "prior_hot_set": round(prior_share, 4),
@@ -358,13 +363,21 @@ def cache_bench(a):
     ws_r = M.workspace(M.MOE_OP_ROUTE, d, 1, 1)
     ws_f = M.workspace(M.MOE_OP_EXPERT_FFN, d, 1, 1)
     idx_h = torch.empty(1, K, dtype=torch.int32, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    fetch_ev = []                                # (start, stop) events around fetches that copied
 
-    def step(t, cached=True):
+    def step(t, cached=True, timed=False):
         x = bank[t % 4096:t % 4096 + 1]
         M.moe_route(d, dl.L, x, idx, w, ws=ws_r)
         if cached:
             idx_h.copy_(idx)                     # synchronous: the step needs its routing on the host
-            cache.fetch(idx_h.numpy())
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+            if ev:
+                ev[0].record(stream)
+            miss = cache.fetch(idx_h.numpy())
+            if ev and miss:
+                ev[1].record(stream)
+                fetch_ev.append(ev)
         M.moe_expert_ffn(d, Lc if cached else dl.L, x, idx, y, ws_f)
         M.moe_combine(y, w, out)
 
@@ -379,6 +392,13 @@ def cache_bench(a):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     h1, m1, b1 = cache.stats()
+    # the copies' own rate: events around each fetch that copied (its copies and table kernel)
+    b2 = cache.stats()[2]
+    for t in range(warm + steps, warm + 2 * steps):
+        step(t, timed=True)
+    torch.cuda.synchronize()
+    fetch_s = sum(e0.elapsed_time(e1) for e0, e1 in fetch_ev) * 1e-3
+    fetch_gbps = (cache.stats()[2] - b2) / fetch_s / 1e9 if fetch_s > 0 else 0.0
     t0 = time.perf_counter()
     for t in range(warm, warm + steps):
         step(t, cached=False)
@@ -406,10 +426,12 @@ def cache_bench(a):
                                    f"{n_slots} device slots, Zipf(1.1) routing, 1 token per step",
                        "slots": n_slots, "experts": E},
             "cache": {"hit_rate": round(hits / max(1, hits + misses), 4), "misses_per_token": round(misses / steps, 3),
-                      "copy_GBps": round(copy_gbps, 2), "bytes_copied": copied},
-            "roofline": {"bound": "pcie", "kernel": "host-to-device copies of missing experts",
-                         "achieved": round(copy_gbps, 2), "peak": round(link, 2), "unit": "GB/s",
-                         "frac": round(copy_gbps / link, 4), "traffic": None,
+                      "bytes_copied": copied, "copied_per_second_of_decode_GBps": round(copy_gbps, 2)},
+            "roofline": {"bound": "pcie", "kernel": "host-to-device copies of missing experts (moe_cache_fetch)",
+                         "achieved": round(fetch_gbps, 2), "peak": round(link, 2), "unit": "GB/s",
+                         "frac": round(fetch_gbps / link, 4), "traffic": None,
+                         "timing": f"HIP events around the {len(fetch_ev)} fetches that copied, in {steps} further "
+                                   "steps (copies plus the table kernel)",
                          "peak_is": "measured pinned host-to-device copy rate (64 MiB copies)"},
             "resident_tok_s": round(steps / dt_res, 1)}
     cache.close()
@@ -431,7 +453,7 @@ def main():
         copy_calibration()
         return
     if a.traffic_from:
-        traffic_from(a.traffic_from, f"config{a.config}")
+        traffic_from(a.traffic_from, a.traffic_key or f"config{a.config}")
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU (the expert path of one device); multi-GPU runs are not "
@@ -607,6 +629,19 @@ def main():
                 "timing": f"start/stop HIP events of each dispatch (hipExtLaunchKernel), {n_t} eager steps"}
         log(f"[bench] kernel us: {kernel_us}; three-kernel schedule: {kernel_us_3k}; "
             f"router + gate/up {achieved:,.1f} GB/s")
+
+    if batched:
+        # a batch runs several kernels on two streams, so its roofline is the whole batch's: the
+        # distinct expert bytes (each read once at best) over the batch time; traffic sums the HBM
+        # bytes its kernels read and wrote, from the committed counters
+        ks = ("k_router_mfma", "k_group", "k_gu8", "k_dn8", "k_gu_mfma", "k_dn_res")
+        tr = [load_traffic(k, f"config{a.config}") for k in ks]
+        roof = {"bound": "hbm", "kernel": "whole batch (" + ", ".join(ks) + ", k_combine)",
+                "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": float(sum(tr)) if all(t is not None for t in tr) else None,
+                "bytes_per_launch": bytes_per_step, "us_per_launch": round(ms_per_step * 1e3, 3),
+                "timing": "HIP events around the timed batches (graph replays)"}
 
     # measured read-stream reference: moe_stream_read over 4 GiB (best of 5 after 2 warm-ups)
     sbuf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev)
