@@ -25,9 +25,12 @@
  * this library takes the plain readings written above and in the format section below.
  *
  * Conventions (all entry points):
- *   - Every device buffer is allocated, owned and freed by the caller.  The library never
- *     allocates device memory, never synchronises the stream and keeps no global state
- *     apart from a thread-local error message.
+ *   - Every device buffer is allocated, owned and freed by the caller; the library never
+ *     allocates device memory and never synchronises a compute stream.  Its state: a
+ *     thread-local error message; per device, one side stream and two events that the first
+ *     batched moe_expert_ffn call creates (kept until the process ends); and the host objects
+ *     of the expert cache, which the caller creates and destroys.  moe_check_experts, a host
+ *     check, copies the table synchronously.
  *   - Compute calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  They validate every argument the host can see first; on any failure they
  *     return a non-zero moe_status and enqueue nothing.  Device faults surface at the
