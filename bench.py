@@ -421,6 +421,24 @@ def cache_bench(a):
     link = 16 * (64 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     hits, misses, copied = h1 - h0, m1 - m0, b1 - b0
     copy_gbps = copied / dt / 1e9
+    # parity: 16 more tokens through the cache against the resident store (same kernels: bit-exact),
+    # and two of them against the oracle
+    import oracle
+    from moe_cases import act_f64, oracle_layer
+    exact, errs = True, []
+    ol = oracle_layer(wl)
+    bank_np = wl.tokens_bank(4096)
+    for t in range(warm + 2 * steps, warm + 2 * steps + 16):
+        step(t)
+        out_c = out.clone()
+        idx_c = idx.clone()
+        step(t, cached=False)
+        torch.cuda.synchronize()
+        exact &= bool(torch.equal(out_c, out) and torch.equal(idx_c, idx))
+        if len(errs) < 2:
+            ref = oracle.layer_token(act_f64(wl, bank_np[t % 4096]), ol, H, I, K)
+            got = out_c.cpu().numpy()[0].astype(np.float64)
+            errs.append(float(np.abs(got - ref.out).max() / (np.linalg.norm(ref.out) / math.sqrt(H))))
     line = {"metric": "decode tok/s with the expert store in host memory (device expert cache)",
             "value": round(steps / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warm,
             "ms_per_step": round(dt / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
@@ -436,7 +454,9 @@ def cache_bench(a):
                          "timing": f"HIP events around the {len(fetch_ev)} fetches that copied, in {steps} further "
                                    "steps (copies plus the table kernel)",
                          "peak_is": "measured pinned host-to-device copy rate (64 MiB copies)"},
-            "resident_tok_s": round(steps / dt_res, 1)}
+            "resident_tok_s": round(steps / dt_res, 1),
+            "parity": {"tokens_vs_resident": 16, "bit_exact_vs_resident": exact, "tokens_vs_oracle": len(errs),
+                       "max_err_over_rms": max(errs), "tolerance": 2e-3, "ok": bool(exact and max(errs) <= 2e-3)}}
     cache.close()
     print(json.dumps(line), flush=True)
 
