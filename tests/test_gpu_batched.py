@@ -48,6 +48,9 @@ BATCH = [
     ("t5_h1024_i512_e16_k4_norm_per_token", 5, 1024, 512, 16, 4, 4, {"norm": True, "x_bf16": False}),
     # from 64 tokens the router runs as MFMA tiles; with a norm weight on normalised fp32 rows
     ("t80_h1024_i256_e32_k4_norm_mfma_router", 80, 1024, 256, 32, 4, 4, {"norm": True}),
+    # the limits: K * I at the LDS bound (K = 8), and the widest intermediate
+    ("t30_h512_i4608_e12_k8_lds_limit", 30, 512, 4608, 12, 8, 4, {}),
+    ("t40_h256_i8192_e8_k4_2b_max_inter", 40, 256, 8192, 8, 4, 2, {}),
 ]
 
 

@@ -66,6 +66,9 @@ SMALL = [
     ("h256_i64_e1_k1", 256, 64, 1, 1, 2, {}),
     ("h4096_i4096_e8_k8_4b", 4096, 4096, 8, 8, 4, {"x_bf16": False}),
     ("h256_i128_e1000_k6", 256, 128, 1000, 6, 4, {}),
+    # the limits: K * I exactly at the down projection's LDS bound, and the widest intermediate
+    ("h512_i4608_e10_k8_lds_limit", 512, 4608, 10, 8, 4, {}),
+    ("h256_i8192_e6_k4_2b_max_inter", 256, 8192, 6, 4, 2, {}),
 ]
 
 
