@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--graph-steps", type=int, default=0, help="steps per captured graph (0: auto)")
     p.add_argument("--no-graph", action="store_true", help="issue steps eagerly instead of via HIP graphs")
     p.add_argument("--graph", action="store_true",
-                   help="replay HIP graphs for batched configs too (by default their steps are issued eagerly: "
-                        "a batch's fork onto the side stream runs faster eager, 547 vs 581 us at 256 tokens)")
+                   help="replay HIP graphs for batched configs too (by default their steps are issued eagerly; "
+                        "both measure the same at 256 tokens, 547 us per batch)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")
@@ -73,26 +73,43 @@ def parse():
     return p.parse_args()
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
+# The source file that defines each measured kernel; every kernel also includes the shared headers.
+KERNEL_SOURCES = {
+    "k_route_gateup": "moe_layer.hip",
+    "k_router": "moe_decode.hip", "k_gateup": "moe_decode.hip", "k_down": "moe_decode.hip",
+    "k_router_mfma": "moe_grouped.hip", "k_group": "moe_grouped.hip", "k_gu_mfma": "moe_grouped.hip",
+    "k_dn_mfma": "moe_grouped.hip", "k_dn_res": "moe_grouped.hip",
+    "k_gu8": "moe_batched8.hip", "k_dn8": "moe_batched8.hip",
+    "k_quantize": "moe_quant.hip", "k_requant": "moe_tier.hip",
+}
+SHARED_HEADERS = ("moe_device.h", "moe_internal.h")
+
+
+def source_hash(kernel: str = "") -> str:
+    """Hash of the sources a kernel is built from (its file and the shared headers); with no kernel,
+    of every device source."""
     d = os.path.join(ROOT, "bit_expert_dequant_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    if kernel:
+        files = sorted({KERNEL_SOURCES[kernel], *SHARED_HEADERS})
+    else:
+        files = sorted(f for f in os.listdir(d) if f.endswith((".hip", ".h", ".cpp")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload_key: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, valid only while the
-    kernel sources are unchanged since the counters were taken."""
+    kernel's sources (its file and the shared headers) are unchanged since the counters were taken."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
         e = d.get(workload_key, {}).get(kernel)
-        if e and e.get("source_hash") == source_hash():
+        if e and e.get("source_hash") == source_hash(kernel):
             return e.get("bytes_per_launch")
     except Exception:
         return None
@@ -152,7 +169,7 @@ def traffic_from(d: str, workload_key: str):
         f = float(np.mean([v for k in fk for v in fetch[k]])) * 1024 * scale["FETCH_SIZE"]
         w = float(np.mean([v for k in wk for v in write[k]])) * 1024 * scale["WRITE_SIZE"]
         res[short] = {"bytes_per_launch": f + w, "fetch_bytes": f, "write_bytes": w,
-                      "dispatches": sum(len(fetch[k]) for k in fk), "source_hash": source_hash(),
+                      "dispatches": sum(len(fetch[k]) for k in fk), "source_hash": source_hash(short),
                       "scale_fetch": scale["FETCH_SIZE"], "scale_write": scale["WRITE_SIZE"]}
     p = os.path.join(ROOT, "profiles", "traffic.json")
     allp = json.load(open(p)) if os.path.exists(p) else {}
