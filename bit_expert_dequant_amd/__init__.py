@@ -92,6 +92,7 @@ def lib():
             "moe_cache_stats": (I32, [P, P, P, P]),
             "moe_cache_slot": (I32, [P, I32]),
             "moe_cache_destroy": (None, [P]),
+            "moe_debug_inject_launch_failure": (I32, [I32, I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -107,7 +108,8 @@ def exported_symbols() -> List[str]:
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
             "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read",
             "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier", "moe_cache_create",
-            "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy"]
+            "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy",
+            "moe_debug_inject_launch_failure"]
 
 
 def _check(status: int):

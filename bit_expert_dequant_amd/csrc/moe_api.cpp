@@ -85,6 +85,23 @@ int launched(hipError_t e, const char *what) {
     return MOE_OK;
 }
 
+// Test hook (moe_debug_inject_launch_failure): the next g_pass launch steps proceed, then g_fail are
+// refused before anything is enqueued, as if the runtime had rejected them.
+std::mutex g_inject_mu;
+int g_pass = 0, g_fail = 0;
+bool injected(const char *what) {
+    std::lock_guard<std::mutex> lock(g_inject_mu);
+    if (g_fail <= 0) return false;
+    if (g_pass > 0) {
+        --g_pass;
+        return false;
+    }
+    --g_fail;
+    fail(MOE_ERR_LAUNCH, "%s: injected launch failure (test hook)", what);
+    return true;
+}
+#define MOE_LAUNCH(expr, what) (injected(what) ? MOE_ERR_LAUNCH : launched((expr), (what)))
+
 // Workspace carving (each region 256-byte aligned).
 struct Carve {
     char *base;
@@ -336,7 +353,7 @@ int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
     if (!buf || !sink) return fail(MOE_ERR_NULL, "buf and sink are required");
     if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(MOE_ERR_ALIGN, "buf must be 16-byte, sink 4-byte aligned");
     if (bytes == 0 || bytes % 16) return fail(MOE_ERR_SHAPE, "bytes=%zu is not a positive multiple of 16", bytes);
-    if (int s = launched(moe::launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream read")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream read")) return s;
     return ok();
 }
 
@@ -373,9 +390,9 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
     hipStream_t st = (hipStream_t)stream;
     moe::RouterLaunch ra{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, layer->router,
                          layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T, xn};
-    if (int s = launched(moe::launch_router(ra, st), "router")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_router(ra, st), "router")) return s;
     moe::TopkLaunch ta{lg, dims->n_experts, dims->top_k, T, idx, w};
-    if (int s = launched(moe::launch_topk(ta, st), "top-k")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_topk(ta, st), "top-k")) return s;
     return ok();
 }
 
@@ -398,7 +415,7 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
         const void *xa = x;
         int xdt = x_dtype;
         if (layer->norm_w) {
-            if (int s = launched(moe::launch_norm_rows(x, x_dtype, layer->norm_w, layer->norm_eps, dims->hidden, T,
+            if (int s = MOE_LAUNCH(moe::launch_norm_rows(x, x_dtype, layer->norm_w, layer->norm_eps, dims->hidden, T,
                                                        g.xn, st), "norm"))
                 return s;
             xa = g.xn;
@@ -407,7 +424,7 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
         const bool small = moe::small_path_fits(dims->hidden, dims->inter);
         moe::GroupLaunch gl{idx, T, dims->top_k, dims->n_experts, layer->experts, g.off, g.perm, g.tiles, g.ntiles,
                             g.small, g.nsmall, small ? moe::kSmallTokens : 0, y, dims->hidden};
-        if (int s = launched(moe::launch_group(gl, st), "group")) return s;
+        if (int s = MOE_LAUNCH(moe::launch_group(gl, st), "group")) return s;
         moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, g.off, g.perm,
                               g.tiles, g.ntiles, g.small, g.nsmall, g.hbuf, y, {}, {}};
         const moe::SideStream *side = nullptr;
@@ -415,7 +432,7 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
             if (int s = side_stream(&side)) return s;
         // the fork/join events are shared per device: enqueue the forked section under the lock
         std::lock_guard<std::mutex> lock(g_side_mu);
-        if (int s = launched(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts),
+        if (int s = MOE_LAUNCH(moe::launch_grouped_ffn(ga, moe::grouped_max_tiles(T, dims->top_k, dims->n_experts),
                                                      small ? grouped_max_small(dims, T) : 0, st, side),
                              "grouped ffn"))
             return s;
@@ -426,9 +443,9 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     uint64_t *sel = c.take<uint64_t>((size_t)T * dims->top_k);
     moe::GateUpLaunch ga{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, nullptr, idx, nullptr, nullptr,
                          sel, nullptr, layer->experts, h, dims->hidden, dims->inter, dims->n_experts, dims->top_k, T};
-    if (int s = launched(moe::launch_gateup(ga, st), "gate/up")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_gateup(ga, st), "gate/up")) return s;
     moe::DownLaunch da{h, nullptr, nullptr, sel, nullptr, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter, dims->top_k, T};
-    if (int s = launched(moe::launch_down(da, st), "down")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_down(da, st), "down")) return s;
     return ok();
 }
 
@@ -439,7 +456,7 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
     if (!aligned(y, 4) || !aligned(w, 4) || !aligned(out, 4) || (residual && !aligned(residual, 4)))
         return fail(MOE_ERR_ALIGN, "arrays must be 4-byte aligned");
     moe::CombineLaunch ca{y, w, residual, out, T, K, H};
-    if (int s = launched(moe::launch_combine(ca, (hipStream_t)stream), "combine")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_combine(ca, (hipStream_t)stream), "combine")) return s;
     return ok();
 }
 
@@ -453,7 +470,7 @@ int moe_quantize_matrix(const void *w, int w_dtype, int rows, int cols, int bits
     if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(sb, 4))
         return fail(MOE_ERR_ALIGN, "w and codes must be 16-byte aligned, sb 4-byte aligned");
     moe::QuantLaunch qa{w, w_dtype, rows, cols, bits, codes, sb};
-    if (int s = launched(moe::launch_quantize(qa, (hipStream_t)stream), "quantize")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_quantize(qa, (hipStream_t)stream), "quantize")) return s;
     return ok();
 }
 
@@ -463,7 +480,7 @@ int moe_expert_usage(const int32_t *idx, int n, int n_experts, uint32_t *counts,
     if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
         return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, MOE_MAX_EXPERTS);
     if (!aligned(counts, 4) || (idx && !aligned(idx, 4))) return fail(MOE_ERR_ALIGN, "idx and counts must be 4-byte aligned");
-    if (int s = launched(moe::launch_usage(idx, (size_t)n, n_experts, counts, (hipStream_t)stream), "usage")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_usage(idx, (size_t)n, n_experts, counts, (hipStream_t)stream), "usage")) return s;
     return ok();
 }
 
@@ -472,7 +489,7 @@ int moe_hot_order(const uint32_t *counts, int n_experts, int32_t *order, void *s
     if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
         return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, MOE_MAX_EXPERTS);
     if (!aligned(counts, 4) || !aligned(order, 4)) return fail(MOE_ERR_ALIGN, "counts and order must be 4-byte aligned");
-    if (int s = launched(moe::launch_hot_order(counts, n_experts, order, (hipStream_t)stream), "hot order")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_hot_order(counts, n_experts, order, (hipStream_t)stream), "hot order")) return s;
     return ok();
 }
 
@@ -495,7 +512,7 @@ int moe_retier(const moe_dims *dims, const moe_expert_desc *base, const int32_t 
                         E - n_hot, cold);
     }
     moe::RetierLaunch r{base, order, E, dims->hidden, dims->inter, n_hot, cold_bits, store, cold, tiered};
-    if (int s = launched(moe::launch_retier(r, (hipStream_t)stream), "retier")) return s;
+    if (int s = MOE_LAUNCH(moe::launch_retier(r, (hipStream_t)stream), "retier")) return s;
     return ok();
 }
 
@@ -570,7 +587,7 @@ int moe_cache_create(const moe_dims *dims, const moe_expert_desc *host_experts, 
     c->last_use.assign(n_slots, 0);
     for (int s = 0; s < n_slots; ++s) c->free_slots.insert(s);
     if (!dry) {
-        if (int st = launched(moe::launch_table_absent(table, E, (hipStream_t)stream), "cache table")) {
+        if (int st = MOE_LAUNCH(moe::launch_table_absent(table, E, (hipStream_t)stream), "cache table")) {
             delete c;
             return st;
         }
@@ -676,6 +693,14 @@ int moe_cache_slot(const moe_expert_cache *c, int expert) {
 
 void moe_cache_destroy(moe_expert_cache *c) { delete c; }
 
+int moe_debug_inject_launch_failure(int after, int count) {
+    if (after < 0 || count < 0) return fail(MOE_ERR_SHAPE, "after=%d count=%d must be >= 0", after, count);
+    std::lock_guard<std::mutex> lock(g_inject_mu);
+    g_pass = after;
+    g_fail = count;
+    return ok();
+}
+
 // Start/stop events of kernel j of a timed call: events[2j], events[2j+1].
 static moe::KernelEvents kernel_events(void *const *events, int j) {
     moe::KernelEvents ev;
@@ -732,17 +757,17 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
             la.seq = W.sync;
             la.err = W.sync + 1;
             la.slots = W.slots;
-            if (int s = launched(moe::launch_layer(la, st, kernel_events(events, 2 * l)), "router + gate/up")) return s;
+            if (int s = MOE_LAUNCH(moe::launch_layer(la, st, kernel_events(events, 2 * l)), "router + gate/up")) return s;
             moe::DownLaunch da{W.h, W.sync, W.sync + 1, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
-            if (int s = launched(moe::launch_down(da, st, kernel_events(events, 2 * l + 1)), "down")) return s;
+            if (int s = MOE_LAUNCH(moe::launch_down(da, st, kernel_events(events, 2 * l + 1)), "down")) return s;
             continue;
         }
-        if (int s = launched(moe::launch_router(ra, st, kernel_events(events, 3 * l)), "router")) return s;
+        if (int s = MOE_LAUNCH(moe::launch_router(ra, st, kernel_events(events, 3 * l)), "router")) return s;
         moe::GateUpLaunch ga{xl, xdt, H, L.norm_w, L.norm_eps, W.logits, nullptr, idx_l, w_l, W.sel, W.w,
                              L.experts, W.h, H, I, E, K, 1};
-        if (int s = launched(moe::launch_gateup(ga, st, kernel_events(events, 3 * l + 1)), "gate/up")) return s;
+        if (int s = MOE_LAUNCH(moe::launch_gateup(ga, st, kernel_events(events, 3 * l + 1)), "gate/up")) return s;
         moe::DownLaunch da{W.h, nullptr, nullptr, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
-        if (int s = launched(moe::launch_down(da, st, kernel_events(events, 3 * l + 2)), "down")) return s;
+        if (int s = MOE_LAUNCH(moe::launch_down(da, st, kernel_events(events, 3 * l + 2)), "down")) return s;
     }
     return ok();
 }

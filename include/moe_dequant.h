@@ -287,6 +287,14 @@ int moe_cache_slot(const moe_expert_cache *cache, int expert);
  * blobs, so synchronise the stream before freeing those).  NULL is ignored. */
 void moe_cache_destroy(moe_expert_cache *cache);
 
+/* --------------------------------------------------------------------------- test hook */
+/* Failure handling test hook: of the launch steps that compute calls make from now on (each kernel
+ * launch, or group of launches, that the call checks), the next `after` proceed and the `count`
+ * after them are refused before anything is enqueued, returning MOE_ERR_LAUNCH with a message
+ * naming the injection.  (0, 0) switches it off.  Process-wide; tests only.
+ * Errors: MOE_ERR_SHAPE (a negative argument). */
+int moe_debug_inject_launch_failure(int after, int count);
+
 /* Copy a device descriptor table to the host (synchronously, on the null stream) and
  * check it: non-NULL, 256-byte aligned blobs, bits in {2,4}, reserved == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_BITS, MOE_ERR_SHAPE, MOE_ERR_DEVICE. */
@@ -305,6 +313,8 @@ int moe_check_experts(const moe_expert_desc *experts_dev, int n_experts);
  * moe_layer_decode call to the next (a launch counter and hand-over words of the two-launch
  * layer schedule): zero-fill it once before its first moe_layer_decode call, and again
  * before going back to moe_layer_decode after using the same memory for anything else.
+ * A moe_layer_decode call that returned MOE_ERR_LAUNCH may have run only part of a layer's launches:
+ * zero-fill its workspace again before the next moe_layer_decode call.
  * Calls sharing a workspace must be ordered (same stream, or synchronised); two calls that
  * may run concurrently need separate workspaces. */
 size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers);

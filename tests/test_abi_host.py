@@ -290,3 +290,23 @@ def test_cache_validates_and_refuses_oversized_steps(L):
     c.close()
     assert L.moe_cache_fetch(None, None, 0, None, None) == 1
     L.moe_cache_destroy(None)
+
+
+def test_injected_launch_failure_enqueues_nothing(L):
+    """With the test hook armed, calls whose arguments pass validation return MOE_ERR_LAUNCH at their
+    first launch step, before anything is enqueued (their fake device pointers are never touched);
+    the hook counts down, and (0, 0) switches it off."""
+    P = ctypes.c_void_p
+    assert L.moe_debug_inject_launch_failure(-1, 1) == 2
+    assert L.moe_debug_inject_launch_failure(0, 2) == 0
+    try:
+        assert L.moe_combine(P(0x100000), P(0x200000), 4, 2, 64, None, P(0x300000), None) == 7
+        assert b"injected" in L.moe_last_error() and b"combine" in L.moe_last_error()
+        assert L.moe_quantize_matrix(P(0x100000), M.MOE_F32, 4, 64, 4, P(0x200000), P(0x300000), None) == 7
+        assert b"injected" in L.moe_last_error() and b"quantize" in L.moe_last_error()
+        # validation still comes first: an invalid call fails as such and does not use up an injection
+        assert L.moe_debug_inject_launch_failure(0, 1) == 0
+        assert L.moe_combine(None, P(0x200000), 4, 2, 64, None, P(0x300000), None) == 1
+        assert L.moe_combine(P(0x100000), P(0x200000), 4, 2, 64, None, P(0x300000), None) == 7
+    finally:
+        assert L.moe_debug_inject_launch_failure(0, 0) == 0

@@ -196,3 +196,30 @@ def test_batched_graph_replays_match_eager():
         got = (idx.cpu().numpy(), y.cpu().numpy(), out.cpu().numpy())
         for a_, b_, what in zip(got, eager[j], ("idx", "y", "out")):
             assert np.array_equal(a_, b_), f"replay of batch {j}: {what} differs"
+
+
+def test_batched_launch_failure_then_same_result():
+    """A batched expert FFN refused after its grouping step reports MOE_ERR_LAUNCH; the same call
+    made again gives exactly the bytes of a call made before the failure."""
+    wl = small_workload("inject_b", 0x1F2, 1024, 512, 24, 4, 4)
+    dl = build_layer(wl)
+    T = 40
+    x = act_tensor(wl, wl.tokens_bank(T))
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    idx = torch.empty(T, wl.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.K, dtype=torch.float32, device="cuda")
+    M.moe_route(d, dl.L, x, idx, w, ws=M.workspace(M.MOE_OP_ROUTE, d, T))
+    ws = M.workspace(M.MOE_OP_EXPERT_FFN, d, T)
+    y0 = torch.empty(T, wl.K, wl.H, dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(d, dl.L, x, idx, y0, ws)
+    y1 = torch.full_like(y0, float("nan"))
+    M.lib().moe_debug_inject_launch_failure(1, 1)
+    try:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_expert_ffn(d, dl.L, x, idx, y1, ws)
+        assert ei.value.status == 7 and "injected" in str(ei.value)
+    finally:
+        M.lib().moe_debug_inject_launch_failure(0, 0)
+    M.moe_expert_ffn(d, dl.L, x, idx, y1, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)

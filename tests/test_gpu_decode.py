@@ -338,3 +338,32 @@ def test_stream_read_xor():
         assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host)), n
     with pytest.raises(M.MoeError):        # 12 bytes: not a multiple of 16
         M.moe_stream_read(torch.zeros(3, dtype=torch.int32, device="cuda"), sink)
+
+
+def test_launch_failure_between_kernels_then_recovery():
+    """A decode call refused at its second launch (router + gate/up ran, down did not) reports
+    MOE_ERR_LAUNCH; after the workspace is zero-filled again, as the header asks, the next calls are
+    correct."""
+    wl = small_workload("inject_dec", 0x1F1, 1024, 512, 16, 4, 4)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    bank = wl.tokens_bank(3)
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    out, idx, w = run_decode(dl, act_tensor(wl, bank[0]), ws=ws)
+    check_token(wl, ol, None, act_f64(wl, bank[0]), out, idx, w, what="before")
+    o = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    i = torch.empty(wl.K, dtype=torch.int32, device="cuda")
+    ww = torch.empty(wl.K, dtype=torch.float32, device="cuda")
+    M.lib().moe_debug_inject_launch_failure(1, 1)
+    try:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_layer_decode(d, [dl.L], act_tensor(wl, bank[1]), o, i, ww, ws=ws)
+        assert ei.value.status == 7 and "injected" in str(ei.value)
+    finally:
+        M.lib().moe_debug_inject_launch_failure(0, 0)
+    torch.cuda.synchronize()
+    ws.zero_()
+    for t in (1, 2):
+        out, idx, w = run_decode(dl, act_tensor(wl, bank[t]), ws=ws)
+        check_token(wl, ol, None, act_f64(wl, bank[t]), out, idx, w, what=f"after, token {t}")
