@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <set>
@@ -89,14 +90,16 @@ int launched(hipError_t e, const char *what) {
 // refused before anything is enqueued, as if the runtime had rejected them.
 std::mutex g_inject_mu;
 int g_pass = 0, g_fail = 0;
+std::atomic<bool> g_armed{false};       // lets unarmed launches skip the lock
 bool injected(const char *what) {
+    if (!g_armed.load(std::memory_order_acquire)) return false;
     std::lock_guard<std::mutex> lock(g_inject_mu);
     if (g_fail <= 0) return false;
     if (g_pass > 0) {
         --g_pass;
         return false;
     }
-    --g_fail;
+    if (--g_fail == 0) g_armed.store(false, std::memory_order_release);
     fail(MOE_ERR_LAUNCH, "%s: injected launch failure (test hook)", what);
     return true;
 }
@@ -698,6 +701,7 @@ int moe_debug_inject_launch_failure(int after, int count) {
     std::lock_guard<std::mutex> lock(g_inject_mu);
     g_pass = after;
     g_fail = count;
+    g_armed.store(count > 0, std::memory_order_release);
     return ok();
 }
 
