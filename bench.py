@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="issue steps eagerly instead of via HIP graphs")
     p.add_argument("--graph", action="store_true",
                    help="replay HIP graphs for batched configs too (by default their steps are issued eagerly; "
-                        "both measure the same at 256 tokens, 547 us per batch)")
+                        "both measure the same at 256 tokens, 540 us per batch)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--timing-steps", type=int, default=256, help="steps of the per-kernel timing pass")

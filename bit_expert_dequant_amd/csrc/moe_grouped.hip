@@ -153,37 +153,35 @@ __device__ __forceinline__ int bin_of(const uint32_t (&w)[4], int n) {
 }
 static_assert(kSmallTokens <= 8, "the small-list ranking packs eight token-count bins");
 
-// Counting sort of the T*K (token, slot) pairs by expert, stable in the pair index, in one
-// 1024-thread workgroup: an LDS histogram, block scans of the counts, of the 32-token MFMA tiles
-// of busy experts and of the small experts binned by token count, and a bitonic sort of the keys
-// expert * P + pair (their ascending order is exactly the stable order by expert); then the MFMA
-// work list of (expert, tile) and the small-expert records, most tokens first, so that the longest
-// workgroups of the small-expert kernels start first.
+// Counting sort of the T*K (token, slot) pairs by expert in one 1024-thread workgroup: an LDS
+// histogram, block scans of the counts, of the 32-token MFMA tiles of busy experts and of the small
+// experts binned by token count, then a scatter of the pairs into their experts' ranges (through
+// per-expert cursors, so the order inside a range is arbitrary: every output row depends on its own
+// token only); then the MFMA work list of (expert, tile) and the small-expert records, most tokens
+// first, so that the longest workgroups of the small-expert kernels start first.  (A bitonic sort
+// of the keys expert * P + pair, which kept each range in pair order, took 8 us more per
+// 256-token batch.)
 __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
     extern __shared__ int s_all[];
     __shared__ uint32_t s_w[64];
     const int P = a.T * a.K, E = a.E, NP2 = pow2_at_least(P);
-    uint32_t *s_key = (uint32_t *)s_all;     // [NP2]
+    uint32_t *s_key = (uint32_t *)s_all;     // [NP2] pair index at each sorted position
     int *s_cnt = s_all + NP2;                // [E]
     int *s_off = s_cnt + E;                  // [E + 1]
     int *s_toff = s_off + E + 1;             // [E + 1]
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
     __syncthreads();
-    for (int p = tid; p < NP2; p += blockDim.x) {
-        uint32_t key = 0xFFFFFFFFu;          // padding and pairs naming no expert sort last
-        if (p < P) {
-            const int e = a.idx[p];
-            if (e >= 0 && e < E && a.experts[e].blob != 0) {
-                key = (uint32_t)e * (uint32_t)P + (uint32_t)p;
-                atomicAdd(&s_cnt[e], 1);
-            } else {
-                // an index outside [0, E) or an absent expert (blob 0, e.g. not resident in an expert
-                // cache) gets a zero output row, as in the decode path
-                for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
-            }
+    auto valid = [&](int e) { return e >= 0 && e < E && a.experts[e].blob != 0; };
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = a.idx[p];
+        if (valid(e)) {
+            atomicAdd(&s_cnt[e], 1);
+        } else {
+            // an index outside [0, E) or an absent expert (blob 0, e.g. not resident in an expert
+            // cache) gets a zero output row, as in the decode path
+            for (int c = 0; c < a.H; ++c) a.y[(size_t)p * a.H + c] = 0.f;
         }
-        s_key[p] = key;
     }
     __syncthreads();
     // thread t owns experts 2t and 2t+1 (E <= 2048)
@@ -218,32 +216,18 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
         if (sm1) pos1 = start[c1] + bin_of(p, c1) + (sm0 && c0 == c1 ? 1 : 0);
         if (tid == 0) *a.nsmall = nsm;
     }
-    // bitonic sort, ascending: exchange distances of 64 and more through LDS (one barrier each),
-    // the rest of each merge inside the wave with shuffles (one barrier for all of them)
-    for (int k = 2; k <= NP2; k <<= 1) {
-        int j = k >> 1;
-        for (; j >= 64; j >>= 1) {
-            for (int i = tid; i < NP2; i += blockDim.x) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t x = s_key[i], y = s_key[ixj];
-                    if ((x > y) == ((i & k) == 0)) { s_key[i] = y; s_key[ixj] = x; }
-                }
-            }
-            __syncthreads();
-        }
-        for (int i = tid; i < NP2; i += blockDim.x) {       // whole waves, or all of NP2 < 64
-            uint32_t v = s_key[i];
-            for (int jj = j; jj > 0; jj >>= 1) {
-                const uint32_t o = (uint32_t)__shfl_xor((int)v, jj);
-                v = (((i & jj) == 0) == ((i & k) == 0)) ? min(v, o) : max(v, o);
-            }
-            s_key[i] = v;
-        }
-        __syncthreads();
+    // scatter: each valid pair takes the next position of its expert's range (the order inside an
+    // expert's range does not matter: every output row depends on its own token only)
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = a.idx[p];
+        if (valid(e)) s_key[s_off[e] + atomicAdd(&s_cnt[e], 1)] = (uint32_t)p;
     }
+    __syncthreads();
     const int nv = s_off[E];
-    for (int i = tid; i < nv; i += blockDim.x) a.perm[i] = (int)(s_key[i] % (uint32_t)P);
+    for (int i = tid; i < nv; i += blockDim.x) a.perm[i] = (int)s_key[i];
     for (int e = tid; e <= E; e += blockDim.x) a.off[e] = s_off[e];
     for (int e = tid; e < E; e += blockDim.x) {
         const int nt = s_toff[e + 1] - s_toff[e];
@@ -262,7 +246,7 @@ __global__ void __launch_bounds__(1024) k_group(GroupLaunch a) {
         r.bits = d.bits == 2 ? 2 : 4;
         r.pad[0] = r.pad[1] = 0;
 #pragma unroll
-        for (int t = 0; t < kSmallTokens; ++t) r.pair[t] = (int)(s_key[r.base + min(t, n - 1)] % (uint32_t)P);
+        for (int t = 0; t < kSmallTokens; ++t) r.pair[t] = (int)s_key[r.base + min(t, n - 1)];
         a.small[pos] = r;
     };
     if (sm0) small_rec(e0, c0, pos0);
