@@ -361,6 +361,30 @@ __global__ void __launch_bounds__(kBlock) k_stream_read(const u32x4 *p, size_t n
     if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
 }
 
+// out[t][c] = sum_k w[t][k] * y[t][k][c] (+ residual[t][c]), k in order.  k_combine4: one token per
+// grid row, four columns per thread with 16-byte loads and stores (H a multiple of 4, buffers 16-byte
+// aligned); k_combine: any shape, one element per thread.
+typedef float fv4 __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(kBlock) k_combine4(CombineLaunch a) {
+    const int t = blockIdx.y;
+    const int c4 = blockIdx.x * kBlock + threadIdx.x;
+    if (c4 * 4 >= a.H) return;
+    const size_t row = (size_t)t * a.H;
+    fv4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < a.K; ++k) {
+        const float wk = a.w[t * a.K + k];
+        const fv4 y = __builtin_nontemporal_load((const fv4 *)(a.y + (row * a.K + (size_t)k * a.H)) + c4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += wk * y[j];
+    }
+    if (a.residual) {
+        const fv4 r = ((const fv4 *)(a.residual + row))[c4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += r[j];
+    }
+    ((fv4 *)(a.out + row))[c4] = acc;
+}
+
 __global__ void __launch_bounds__(kBlock) k_combine(CombineLaunch a) {
     const size_t n = (size_t)a.T * a.H;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
@@ -513,6 +537,12 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hip
 }
 
 hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (a.H % 4 == 0 && al16(a.y) && al16(a.out) && (!a.residual || al16(a.residual)) && a.T <= 65535) {
+        const dim3 grid((unsigned)((a.H / 4 + kBlock - 1) / kBlock), (unsigned)a.T);
+        hipLaunchKernelGGL(k_combine4, grid, dim3(kBlock), 0, s, a);
+        return hipGetLastError();
+    }
     const size_t n = (size_t)a.T * a.H;
     size_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 4096) blocks = 4096;
