@@ -71,7 +71,7 @@ __device__ bool wait_logits(const uint64_t *slots, int E, uint32_t tag, float *s
     int it = 0;
     for (; it < kSpinLimit; ++it) {
         if ((uint32_t)(ld_word64(slots + E - 1) >> 32) == tag) break;
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(16);   // back-off 1, 4, 8, 16, 32, 64, 127: 17.47, 17.44, 17.39, 17.28, 17.26, 17.53, 19.15 us per step
     }
     for (; it < kSpinLimit; ++it) {
         uint64_t v[NP];
