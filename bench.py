@@ -16,6 +16,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
 import hashlib
 import json
@@ -247,8 +248,7 @@ def retier_bench(a):
     import bit_expert_dequant_amd as M
     import oracle
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from moe_cases import act_tensor, build_layer
+    from synth.device import act_tensor, build_layer
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = synth.WORKLOADS[4]
     H, I, E, K, n_hot, T, chunk = wl.H, wl.I, wl.E, wl.K, synth.N_HOT, 4096, 256
@@ -360,8 +360,7 @@ def cache_bench(a):
     import torch
     import bit_expert_dequant_amd as M
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from moe_cases import act_tensor, build_layer
+    from synth.device import act_tensor, build_layer
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = dataclasses.replace(synth.WORKLOADS[4], tokens=1)
     H, I, E, K = wl.H, wl.I, wl.E, wl.K
@@ -441,9 +440,9 @@ def cache_bench(a):
     # parity: 16 more tokens through the cache against the resident store (same kernels: bit-exact),
     # and two of them against the oracle
     import oracle
-    from moe_cases import act_f64, oracle_layer
+    from synth.device import act_f64
     exact, errs = True, []
-    ol = oracle_layer(wl)
+    ol = oracle.workload_layer(wl)
     bank_np = wl.tokens_bank(4096)
     for t in range(warm + 2 * steps, warm + 2 * steps + 16):
         step(t)
@@ -459,7 +458,11 @@ def cache_bench(a):
     line = {"metric": "decode tok/s with the expert store in host memory (device expert cache)",
             "value": round(steps / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warm,
             "ms_per_step": round(dt / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "vs_baseline": None, "dtype": "i4-dot-i32+f32", "data": "synthetic",
+        "dtype_note": ("expert matvecs: 4-bit (or 2-bit) codes times 16-bit fixed-point activation digits per "
+                       "32-column slot as exact int32 dot products (v_dot8_i32_i4), scale and bias applied in fp32; "
+                       "router: bf16 pairs (hi + lo split when the activation is not bf16) with fp32 accumulation; "
+                       "batched busy experts: bf16 MFMA with fp32 accumulation; inputs bf16, outputs fp32"),
             "config": {"workload": f"one layer H{H} I{I} E{E} top-{K} 4-bit (3.6 GB) in pinned host memory, "
                                    f"{n_slots} device slots, Zipf(1.1) routing, 1 token per step",
                        "slots": n_slots, "experts": E},
@@ -503,8 +506,7 @@ def main():
     import torch
     import bit_expert_dequant_amd as M
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from moe_cases import act_f64, build_layer, oracle_layer, to_bf16_tensor
+    from synth.device import act_f64, build_layer, to_bf16_tensor
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -564,43 +566,66 @@ def main():
             M.moe_expert_ffn(d, L[0], bank_b[j], idxs[j], y, ws_f)
             M.moe_combine(y, wts[j], outs)
 
-    # eager warm-up (also sets kernel attributes before any capture)
-    for i in range(min(8, a.warmup) or 1):
+    # eager warm-up: exactly --warmup steps (at least one, which also sets kernel attributes before
+    # any capture); the tokens continue through the bank after the warm-up's
+    n_cycle = n_bank if not batched else n_bank // wl.tokens
+    for i in range(max(1, a.warmup)):
         step(i, i % G)
     torch.cuda.synchronize()
 
-    graphs = []
-    # single-token steps replay graphs (launch-bound); batched steps are issued eagerly unless --graph
+    # timed region: exactly --steps steps.  Single-token steps replay HIP graphs of G steps (launch
+    # bound otherwise), cycling through the bank, plus one graph for the remainder when G does not
+    # divide the step count; every graph is uploaded to the device (hipGraphUpload, nothing runs)
+    # before the timed region.  Batched steps are issued eagerly unless --graph.
     use_graph = not a.no_graph and (not batched or a.graph)
-    n_cycle = n_bank if not batched else n_bank // wl.tokens
+    graphs = []
+    timed_tokens = list(range(a.steps))         # bank position of each timed step (mod the bank)
     if use_graph:
-        n_graphs = max(1, n_cycle // G)
+        G = max(1, min(G, a.steps))
+        n_full, rem = divmod(a.steps, G)
+        n_graphs = max(1, min(n_full, n_cycle // G)) if n_full else 0
+        plan = []                                   # graph of each replay, in timed order
+        timed_tokens = []
         for gi in range(n_graphs):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for s in range(G):
                     step(gi * G + s, s)
             graphs.append(g)
+        for r in range(n_full):
+            plan.append(r % n_graphs)
+            timed_tokens.extend((r % n_graphs) * G + s for s in range(G))
+        if rem:
+            timed_tokens.extend(n_full * G + s for s in range(rem))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(rem):
+                    step(n_full * G + s, s)
+            graphs.append(g)
+            plan.append(len(graphs) - 1)
+        hip = ctypes.CDLL("libamdhip64.so")
+        for g in graphs:
+            rc = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()), ctypes.c_void_p(stream.cuda_stream))
+            assert rc == 0, f"hipGraphUpload failed ({rc})"
         torch.cuda.synchronize()
-        log(f"[bench] captured {len(graphs)} graph(s) of {G} step(s)")
+        log(f"[bench] captured {len(graphs)} graph(s): {n_full} replay(s) of {G} step(s)"
+            + (f" + one of {rem}" if rem else ""))
 
-    def run(n_steps, offset=0):
+    def run():
         if use_graph:
-            reps = max(1, n_steps // G)
-            for r in range(reps):
-                graphs[(offset // G + r) % len(graphs)].replay()
-            return reps * G
-        for i in range(n_steps):
-            step(offset + i, (offset + i) % G)
-        return n_steps
+            for gi in plan:
+                graphs[gi].replay()
+            return a.steps
+        for i in range(a.steps):
+            step(i, i % G)
+        return a.steps
 
-    run(a.warmup)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
     w0 = time.perf_counter()
-    done = run(a.steps, offset=0)
+    done = run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -610,19 +635,15 @@ def main():
 
     # exact weight bytes per step from the routing the timed steps used
     idx_h = idxs.cpu().numpy()
-    steps_idx = [(i % (n_cycle)) for i in range(done)]
+    steps_idx = [t % n_cycle for t in timed_tokens]
     if not batched:
-        per_tok = np.array([sum(router_bytes + norm_bytes + blob_bytes[idx_h[t, l]].sum()
-                                for l in range(wl.n_layers)) for t in range(n_bank)], dtype=np.float64)
-        bytes_per_step = float(np.mean(per_tok[[s % n_bank for s in steps_idx]]))
+        per_tok = {t: float(sum(router_bytes + norm_bytes + blob_bytes[idx_h[t, l]].sum()
+                                for l in range(wl.n_layers))) for t in set(steps_idx)}
+        bytes_per_step = float(np.mean([per_tok[t] for t in steps_idx]))
         tokens_per_step = 1
     else:
-        per_b = []
-        for j in range(n_cycle):
-            sel = np.unique(idx_h[j].reshape(-1))
-            per_b.append(router_bytes + blob_bytes[sel].sum())
-        per_b = np.array(per_b, dtype=np.float64)
-        bytes_per_step = float(np.mean(per_b[[s % n_cycle for s in steps_idx]]))
+        per_b = {j: float(router_bytes + blob_bytes[np.unique(idx_h[j].reshape(-1))].sum()) for j in set(steps_idx)}
+        bytes_per_step = float(np.mean([per_b[j] for j in steps_idx]))
         tokens_per_step = wl.tokens
     tok_s = tokens_per_step / (ms_per_step * 1e-3)
     gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
@@ -657,6 +678,7 @@ def main():
 
         kernel_us = timed_pass(False)
         kernel_us_3k = timed_pass(True)
+        idx_h = idxs.cpu().numpy()          # the timing passes routed tokens 0 .. n_t-1
         # algorithmic bytes of the router + gate/up launch: router matrix, norm weight and the gate
         # and up planes of the K selected experts
         rg_b = [router_bytes + norm_bytes + gu_bytes[idx_h[t, l]].sum() for t in range(n_t) for l in range(wl.n_layers)]
@@ -713,7 +735,7 @@ def main():
         import oracle
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-        ols = [oracle_layer(wl, l) for l in range(wl.n_layers)]
+        ols = [oracle.workload_layer(wl, l) for l in range(wl.n_layers)]
         x0 = act_f64(wl, bank_np[0])
         # one token first to size the sample
         t1 = time.perf_counter()
@@ -725,7 +747,11 @@ def main():
             n_s = min(n_s, wl.tokens)
         # pre-generate the expert blobs the sample needs, so that only the oracle is timed
         sample = list(range(n_s))
+        routed = ({t % n_cycle for t in timed_tokens} | {t % n_cycle for t in range(max(1, a.warmup))}
+                  | (set(range(n_t)) if not batched else set()))
         for t in sample:
+            if (t if not batched else 0) not in routed:
+                continue                     # routing of this token not known yet: generated when used
             for l in range(wl.n_layers):
                 for e in (idx_h[t, l] if not batched else idx_h[0, t]):
                     ols[l].blob(int(e))
@@ -771,7 +797,11 @@ def main():
         "metric": "MoE decode tok/s and weight GB/s (% of HBM peak), 4-bit, 512 experts top-4",
         "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": done, "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "i4-dot-i32+f32", "data": "synthetic",
+        "dtype_note": ("expert matvecs: 4-bit (or 2-bit) codes times 16-bit fixed-point activation digits per "
+                       "32-column slot as exact int32 dot products (v_dot8_i32_i4), scale and bias applied in fp32; "
+                       "router: bf16 pairs (hi + lo split when the activation is not bf16) with fp32 accumulation; "
+                       "batched busy experts: bf16 MFMA with fp32 accumulation; inputs bf16, outputs fp32"),
         "config": cfg,
         "weight_bytes_per_step": bytes_per_step, "weight_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),

@@ -1,9 +1,10 @@
 // moe_grouped.hip -- batched (T > 1) expert FFN: token grouping and MFMA grouped dequant-GEMM.
 //
 //   k_group    : counting sort of the T*K (token, slot) pairs by expert -- histogram (LDS integer
-//                atomics), exclusive prefix sum, and a stable scatter (one wavefront per expert,
-//                ballot + popcount over the pairs in index order, so the order is deterministic and
-//                follows the token id); also emits the work list of (expert, 32-token tile).
+//                atomics), exclusive prefix sum, and a scatter of the pairs into their experts'
+//                ranges through per-expert LDS cursors (the order inside a range is arbitrary: each
+//                output row depends on its own token only, so results do not depend on it); also
+//                emits the work list of (expert, 32-token tile) and the small-expert records.
 //   k_norm_rows: RMSNorm of every token row (only when the layer has a norm weight).
 //   k_gu_mfma  : per (expert, token tile, 128 rows of I): G = X W_g^T and U = X W_u^T with
 //                v_mfma_f32_32x32x16_bf16, then h = silu(G) * U.

@@ -342,6 +342,25 @@ class LayerWeights:
     norm_eps: float = 1e-6
 
 
+def workload_layer(wl, layer_id: int = 0, cache_size: Optional[int] = None) -> LayerWeights:
+    """Host inputs of one layer of a seeded workload (any object with the seeded generator's
+    methods: expert_bits(), blob(layer, e), router(layer), logit_bias(), norm_w(layer), and the
+    fields router_bf16, norm_eps and n_layers).  Expert blobs are regenerated on demand and the most
+    recent `cache_size` of them kept (default: 512 shared out over the workload's layers)."""
+    import functools
+    bits = wl.expert_bits()
+    if cache_size is None:
+        cache_size = max(8, 512 // max(1, int(getattr(wl, "n_layers", 1))))
+
+    @functools.lru_cache(maxsize=cache_size)
+    def blob(e: int) -> np.ndarray:
+        return wl.blob(layer_id, int(e))
+
+    return LayerWeights(router=wl.router(layer_id), router_is_bf16=wl.router_bf16,
+                        blob=lambda e: blob(int(e)), bits=lambda e: int(bits[e]),
+                        logit_bias=wl.logit_bias(), norm_w=wl.norm_w(layer_id), norm_eps=wl.norm_eps)
+
+
 @dataclass
 class LayerResult:
     idx: np.ndarray        # int32 [K]

@@ -152,38 +152,52 @@ void orc_router_logits(const void *Wr, int wr_is_bf16, int E, int H, const doubl
 
 /* Softmax over all E logits, top-K by logit (descending; equal logits -> lower
  * expert index first), weights renormalised over the K selected.  *margin is the
- * gap between the K-th and (K+1)-th largest logit (+inf when K == E). */
+ * gap between the K-th and (K+1)-th largest logit (+inf when K == E).
+ *
+ * The pages say nothing about non-finite logits.  Reading taken here: a NaN logit
+ * counts as -inf, in the selection and in the softmax alike (so a NaN expert is
+ * chosen only after every finite one, and then in index order among the -inf ones,
+ * with weight 0).  When every logit is -inf (or NaN) the softmax has no maximum to
+ * subtract; the weights are then the limit of K equal logits, 1/K each. */
 void orc_route(const double *logits, int E, int K, int32_t *idx, double *w, double *margin) {
-    double mx = logits[0];
-    for (int e = 1; e < E; ++e)
-        if (logits[e] > mx) mx = logits[e];
+    double *lv = (double *)malloc(sizeof(double) * (size_t)E);
     double *p = (double *)malloc(sizeof(double) * (size_t)E);
     char *taken = (char *)calloc((size_t)E, 1);
-    double z = 0.0;
+    double mx = -INFINITY;
     for (int e = 0; e < E; ++e) {
-        p[e] = exp(logits[e] - mx);
-        z += p[e];
+        lv[e] = isnan(logits[e]) ? -INFINITY : logits[e];
+        if (lv[e] > mx) mx = lv[e];
     }
-    for (int e = 0; e < E; ++e) p[e] /= z;
     /* selection: K passes of "largest remaining logit, lowest index on ties" */
     for (int k = 0; k < K; ++k) {
         int best = -1;
         for (int e = 0; e < E; ++e) {
             if (taken[e]) continue;
-            if (best < 0 || logits[e] > logits[best]) best = e;
+            if (best < 0 || lv[e] > lv[best]) best = e;
         }
         taken[best] = 1;
         idx[k] = best;
     }
-    double sel = 0.0;
-    for (int k = 0; k < K; ++k) sel += p[idx[k]];
-    for (int k = 0; k < K; ++k) w[k] = p[idx[k]] / sel;
+    if (mx == -INFINITY) {
+        for (int k = 0; k < K; ++k) w[k] = 1.0 / (double)K;
+    } else {
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp(lv[e] - mx);
+            z += p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        double sel = 0.0;
+        for (int k = 0; k < K; ++k) sel += p[idx[k]];
+        for (int k = 0; k < K; ++k) w[k] = p[idx[k]] / sel;
+    }
     if (margin) {
         double next = -INFINITY;
         for (int e = 0; e < E; ++e)
-            if (!taken[e] && logits[e] > next) next = logits[e];
-        *margin = (K < E) ? logits[idx[K - 1]] - next : INFINITY;
+            if (!taken[e] && lv[e] > next) next = lv[e];
+        *margin = (K < E) ? lv[idx[K - 1]] - next : INFINITY;
     }
+    free(lv);
     free(p);
     free(taken);
 }

@@ -278,12 +278,52 @@ def test_layer_decode_routing_ties(E, K, separate):
     for _ in range(2):                     # the second call reuses the workspace
         M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, separate_kernels=separate)
         torch.cuda.synchronize()
-        lg = col.astype(np.float64)
-        lg[np.isnan(lg)] = -np.inf
-        ri, rw, _ = oracle.route(lg, K)
+        ri, rw, _ = oracle.route(col.astype(np.float64), K)
         assert list(idx.cpu().numpy()) == list(ri)
         assert_close(w.cpu().numpy(), rw, "tie weights")
     assert ws_error_word(ws) == 0
+
+
+@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+@pytest.mark.parametrize("case", ["nan_in_topk", "all_nan"])
+def test_layer_decode_nan_logits_against_oracle(case, separate):
+    """NaN logits inside the top K, and a row with no finite logit, routed by moe_layer_decode and
+    moe_route on the very logits the oracle gets (NaN ranks as -inf with weight 0; no finite logit
+    gives weights 1/K).  The output is checked too, for the experts with nonzero weight."""
+    H, I, E, K = 64, 64, 16, 4
+    col = np.full(E, np.nan, dtype=np.float32)
+    if case == "nan_in_topk":
+        col[1], col[4], col[2] = 2.0, 1.0, -np.inf
+    wl = small_workload("nan_" + case, 77, H, I, E, K, 4, router_bf16=False, x_bf16=False)
+    dl = build_layer(wl)
+    router = np.zeros((E, H), dtype=np.float32)
+    router[:, 0] = col
+    L = M.Layer(torch.from_numpy(router).cuda(), dl.table)
+    x_np = np.zeros(H, dtype=np.float32)
+    x_np[0] = 1.0
+    x = torch.from_numpy(x_np).cuda()
+    d = M.make_dims(H, I, E, K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    out = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, separate_kernels=separate)
+    torch.cuda.synchronize()
+    ri, rw, _ = oracle.route(col.astype(np.float64), K)
+    assert list(idx.cpu().numpy()) == list(ri)
+    assert_close(w.cpu().numpy(), rw, "NaN weights")
+    ol = oracle_layer(wl)
+    ol.router = router
+    ref = oracle.layer_token(x_np.astype(np.float64), ol, H, I, K)
+    assert list(ref.idx) == list(ri)
+    assert_close(out.cpu().numpy(), ref.out, "out with NaN logits")
+    assert ws_error_word(ws) == 0
+    idx2 = torch.empty(1, K, dtype=torch.int32, device="cuda")
+    w2 = torch.empty(1, K, dtype=torch.float32, device="cuda")
+    M.moe_route(d, L, x.view(1, H), idx2, w2)
+    torch.cuda.synchronize()
+    assert list(idx2.cpu().numpy()[0]) == list(ri)
+    assert_close(w2.cpu().numpy()[0], rw, "NaN weights (moe_route)")
 
 
 @pytest.mark.parametrize("E", [40, 700])
@@ -319,11 +359,9 @@ def test_route_ties_zeros_and_infinities(E):
     L2 = M.Layer(torch.from_numpy(router).cuda(), table)
     M.moe_route(d, L2, torch.from_numpy(x).cuda(), idx, w, logits)
     torch.cuda.synchronize()
-    lg2 = col2.astype(np.float64)
-    lg2[np.isnan(lg2)] = -np.inf
-    ri2, rw2, _ = oracle.route(lg2, K)
+    ri2, rw2, _ = oracle.route(col2.astype(np.float64), K)
     assert list(idx.cpu().numpy()[0]) == list(ri2)
-    assert np.all(np.isfinite(w.cpu().numpy()))
+    assert_close(w.cpu().numpy()[0], rw2, "NaN weights")
 
 
 def test_stream_read_xor():
@@ -367,3 +405,120 @@ def test_launch_failure_between_kernels_then_recovery():
     for t in (1, 2):
         out, idx, w = run_decode(dl, act_tensor(wl, bank[t]), ws=ws)
         check_token(wl, ol, None, act_f64(wl, bank[t]), out, idx, w, what=f"after, token {t}")
+
+
+def test_error_word_forces_nan_until_zero_fill():
+    """The header's contract for a timed-out logit wait, forced from the host (no wait has to time
+    out): with a nonzero error word every call writes NaN outputs and leaves the word set; after the
+    workspace is zero-filled the calls match the oracle again."""
+    wl = small_workload("errword", 0x2E2, 1024, 512, 16, 4, 4)
+    dl = build_layer(wl)
+    ol = oracle_layer(wl)
+    bank = wl.tokens_bank(2)
+    d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    out, idx, w = run_decode(dl, act_tensor(wl, bank[0]), ws=ws)
+    check_token(wl, ol, None, act_f64(wl, bank[0]), out, idx, w, what="before")
+    ws[4:8] = torch.tensor(np.array([3], dtype=np.uint32).view(np.uint8), device="cuda")
+    o = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        o.fill_(0.0)
+        M.moe_layer_decode(d, [dl.L], act_tensor(wl, bank[1]), o, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(o).all(), "outputs must be NaN while the error word is set"
+        assert ws_error_word(ws) != 0
+    ws.zero_()
+    out, idx, w = run_decode(dl, act_tensor(wl, bank[1]), ws=ws)
+    check_token(wl, ol, None, act_f64(wl, bank[1]), out, idx, w, what="after zero-fill")
+
+
+@pytest.mark.parametrize("H", [66, 4096])
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("resid", ["none", "separate", "aliased"])
+def test_combine_shapes_offsets_and_residual(H, offset, resid):
+    """moe_combine on rows that are not a multiple of 4 and on views one float off 16-byte
+    alignment (the one-element-per-thread kernel), and on aligned rows (the 16-byte kernel); the
+    residual as its own buffer and with out aliasing it, as the header allows."""
+    T, K = 3, 4
+    rng = np.random.default_rng(H * 10 + offset)
+    y_np = rng.standard_normal((T, K, H)).astype(np.float32)
+    w_np = rng.random((T, K)).astype(np.float32)
+    r_np = rng.standard_normal((T, H)).astype(np.float32)
+    ybuf = torch.zeros(T * K * H + offset, dtype=torch.float32, device="cuda")
+    y = ybuf[offset:].view(T, K, H)
+    y.copy_(torch.from_numpy(y_np))
+    w = torch.from_numpy(w_np).cuda()
+    obuf = torch.zeros(T * H + offset, dtype=torch.float32, device="cuda")
+    out = obuf[offset:].view(T, H)
+    residual = None
+    if resid == "separate":
+        rbuf = torch.zeros(T * H + offset, dtype=torch.float32, device="cuda")
+        residual = rbuf[offset:].view(T, H)
+        residual.copy_(torch.from_numpy(r_np))
+    elif resid == "aliased":
+        out.copy_(torch.from_numpy(r_np))
+        residual = out
+    M.moe_combine(y, w, out, residual=residual)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t in range(T):
+        ref = oracle.combine(y_np[t].astype(np.float64), w_np[t].astype(np.float64),
+                             None if resid == "none" else r_np[t].astype(np.float64))
+        assert_close(got[t], ref, f"combine t={t}")
+    if resid == "separate":
+        assert np.array_equal(residual.cpu().numpy(), r_np)
+
+
+@pytest.mark.parametrize("bits_mix", ["4bit", "mixed"])
+def test_decode_through_packer_blobs(bits_mix):
+    """Experts packed by moe_pack_expert from code, scale and bias arrays (not by the seeded
+    generator's own byte placement), decoded on the GPU: routing against the oracle on the same
+    blobs, and each expert's output against a float64 product of the raw arrays themselves."""
+    H, I, E, K = 1024, 512, 8, 4
+    rng = np.random.default_rng(0x9AC + len(bits_mix))
+    bits = [4] * E if bits_mix == "4bit" else [4, 2, 2, 4, 2, 4, 4, 2]
+    stride = M.moe_packed_expert_bytes(H, I, 4)
+    host = np.zeros((E, stride), dtype=np.uint8)
+    dense = []
+    for e in range(E):
+        mats, Ws = [], []
+        for R, C in [(I, H), (I, H), (H, I)]:
+            codes = rng.integers(0, 1 << bits[e], (R, C)).astype(np.uint8)
+            s = synth.f32_to_bf16_rne(rng.uniform(0.002, 0.02, R * C // 64).astype(np.float32))
+            b = synth.f32_to_bf16_rne(rng.uniform(-0.1, 0.1, R * C // 64).astype(np.float32))
+            mats.append((codes, s, b))
+            sf = np.repeat(synth.bf16_to_f32(s).reshape(R, -1), 64, 1).astype(np.float64)
+            bf = np.repeat(synth.bf16_to_f32(b).reshape(R, -1), 64, 1).astype(np.float64)
+            Ws.append(codes.astype(np.float64) * sf + bf)
+        blob = M.moe_pack_expert(mats, H, I, bits[e])
+        host[e, :blob.size] = blob
+        dense.append(Ws)
+    store = torch.from_numpy(host.reshape(-1)).cuda()
+    table = M.expert_table([store.data_ptr() + e * stride for e in range(E)], bits)
+    router_np = synth.f32_to_bf16_rne((rng.standard_normal((E, H)) * 0.02).astype(np.float32))
+    router = torch.from_numpy(router_np.view(np.int16)).cuda().view(torch.bfloat16)
+    L = M.Layer(router, table)
+    ol = oracle.LayerWeights(router_np, True, lambda e: host[e], lambda e: bits[e])
+    d = M.make_dims(H, I, E, K)
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
+    for t in range(3):
+        x_u16 = synth.f32_to_bf16_rne(rng.standard_normal(H).astype(np.float32))
+        x = torch.from_numpy(x_u16.view(np.int16)).cuda().view(torch.bfloat16)
+        x64 = synth.bf16_to_f32(x_u16).astype(np.float64)
+        out = torch.empty(H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(K, dtype=torch.int32, device="cuda")
+        w = torch.empty(K, dtype=torch.float32, device="cuda")
+        M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws)
+        y = torch.empty(1, K, H, dtype=torch.float32, device="cuda")
+        M.moe_expert_ffn(d, L, x.view(1, H), idx.view(1, K), y, M.workspace(M.MOE_OP_EXPERT_FFN, d, 1))
+        torch.cuda.synchronize()
+        ref = oracle.layer_token(x64, ol, H, I, K)
+        assert ref.margin > MIN_MARGIN
+        assert list(idx.cpu().numpy()) == list(ref.idx)
+        assert_close(out.cpu().numpy(), ref.out, f"token {t} out")
+        yk = y.cpu().numpy()[0]
+        for k, e in enumerate(ref.idx):
+            Wg, Wu, Wd = dense[int(e)]
+            g, u = Wg @ x64, Wu @ x64
+            y_ref = Wd @ (g / (1.0 + np.exp(-g)) * u)
+            assert_close(yk[k], y_ref, f"token {t} expert {int(e)} ({bits[int(e)]}-bit) y from the raw arrays")

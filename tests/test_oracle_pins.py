@@ -280,6 +280,33 @@ def test_route_zero_logits_and_ties(orc):
     assert list(idx) == [1, 2] and np.allclose(w, 0.5)
 
 
+def test_route_nan_counts_as_minus_inf(orc):
+    """Reading for non-finite logits (the pages are silent): NaN ranks as -inf in the selection and
+    weighs exp(-inf) = 0; with no finite logit at all the weights are 1/K.  Hand cases."""
+    nan, inf = np.nan, np.inf
+    # NaN at index 0, two finite logits: the finite ones win, softmax over them
+    idx, w, margin = orc.route(np.array([nan, 2.0, 1.0, nan, 0.5]), 2)
+    assert list(idx) == [1, 2]
+    e = np.exp(-1.0)
+    assert np.allclose(w, [1 / (1 + e), e / (1 + e)], rtol=1e-15) and np.all(np.isfinite(w))
+    assert margin == pytest.approx(0.5)
+    # K beyond the finite logits: NaN and -inf follow in index order, with weight exactly 0
+    idx, w, _ = orc.route(np.array([nan, 2.0, -inf, nan, 1.0]), 4)
+    assert list(idx) == [1, 4, 0, 2]
+    assert np.allclose(w[:2], [1 / (1 + e), e / (1 + e)], rtol=1e-15) and w[2] == 0.0 and w[3] == 0.0
+    # no finite logit: lower indices first, equal weights
+    idx, w, _ = orc.route(np.array([nan, -inf, nan, -inf]), 3)
+    assert list(idx) == [0, 1, 2] and np.array_equal(w, np.full(3, 1 / 3))
+    # the NaN reading equals routing the same logits with NaN replaced by -inf
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        lg = rng.standard_normal(12)
+        lg[rng.random(12) < 0.4] = nan
+        a_i, a_w, _ = orc.route(lg, 4)
+        b_i, b_w, _ = orc.route(np.where(np.isnan(lg), -inf, lg), 4)
+        assert list(a_i) == list(b_i) and np.array_equal(a_w, b_w)
+
+
 def test_route_permutation_equivariance(orc):
     rng = np.random.default_rng(7)
     logits = rng.standard_normal(32)
