@@ -320,7 +320,8 @@ def test_layer_decode_nan_logits_against_oracle(case, separate):
     assert ws_error_word(ws) == 0
     idx2 = torch.empty(1, K, dtype=torch.int32, device="cuda")
     w2 = torch.empty(1, K, dtype=torch.float32, device="cuda")
-    M.moe_route(d, L, x.view(1, H), idx2, w2)
+    lg2 = torch.empty(1, E, dtype=torch.float32, device="cuda")
+    M.moe_route(d, L, x.view(1, H), idx2, w2, lg2)
     torch.cuda.synchronize()
     assert list(idx2.cpu().numpy()[0]) == list(ri)
     assert_close(w2.cpu().numpy()[0], rw, "NaN weights (moe_route)")
