@@ -48,6 +48,8 @@ def parse():
                    help="tokens per call through the batched path (2..4096) instead of the config's own; "
                         "for single-layer configs (small-T multi-token decode)")
     p.add_argument("--graph-steps", type=int, default=0, help="steps per captured graph (0: auto)")
+    p.add_argument("--schedule", default="two_launch", choices=["two_launch", "single_launch", "three_kernels"],
+                   help="layer schedule of the decode steps: two launches (default), one, or three kernels")
     p.add_argument("--no-graph", action="store_true", help="issue steps eagerly instead of via HIP graphs")
     p.add_argument("--graph", action="store_true",
                    help="replay HIP graphs for batched configs too (by default their steps are issued eagerly; "
@@ -76,6 +78,7 @@ def parse():
 
 # The source file that defines each measured kernel; every kernel also includes the shared headers.
 KERNEL_SOURCES = {
+    "k_layer": "moe_fused.hip",
     "k_route_gateup": "moe_layer.hip",
     "k_router": "moe_decode.hip", "k_gateup": "moe_decode.hip", "k_down": "moe_decode.hip",
     "k_router_mfma": "moe_grouped.hip", "k_group": "moe_grouped.hip", "k_gu_mfma": "moe_grouped.hip",
@@ -83,7 +86,7 @@ KERNEL_SOURCES = {
     "k_gu8": "moe_batched8.hip", "k_dn8": "moe_batched8.hip",
     "k_quantize": "moe_quant.hip", "k_requant": "moe_tier.hip",
 }
-SHARED_HEADERS = ("moe_device.h", "moe_internal.h")
+SHARED_HEADERS = ("moe_device.h", "moe_internal.h", "moe_handoff.h")
 
 
 def source_hash(kernel: str = "") -> str:
@@ -546,9 +549,11 @@ def main():
         wts = torch.empty(n_bank, wl.n_layers, K, dtype=torch.float32, device=dev)
         residual = wl.norm
 
+        sched = {"separate_kernels": a.schedule == "three_kernels", "single_launch": a.schedule == "single_launch"}
+
         def step(i, g):
             M.moe_layer_decode(d, L, bank[i % n_bank], outs[g], idxs[i % n_bank], wts[i % n_bank],
-                               residual=residual, ws=ws)
+                               residual=residual, ws=ws, **sched)
     else:
         T = wl.tokens
         G = a.graph_steps or 1
@@ -654,12 +659,14 @@ def main():
     # and, for the breakdown, on the three-kernel schedule
     roof = None
     kernel_us = {}
-    kernel_us_3k = {}
+    kernel_us_other = {}
     if not batched:
         n_t = min(a.timing_steps, n_bank)
 
-        def timed_pass(separate):
-            names = ["router", "gateup", "down"] if separate else ["route_gateup", "down"]
+        def timed_pass(schedule):
+            names = {"single_launch": ["layer"], "two_launch": ["route_gateup", "down"],
+                     "three_kernels": ["router", "gateup", "down"]}[schedule]
+            kw = {"separate_kernels": schedule == "three_kernels", "single_launch": schedule == "single_launch"}
             nk = len(names) * wl.n_layers
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(n_t)]
             for row in evs:      # torch creates the HIP event on first record
@@ -668,7 +675,7 @@ def main():
             torch.cuda.synchronize()
             for t in range(n_t):  # ROCm records no event nodes inside captured graphs: eager issue
                 M.moe_layer_decode_timed(d, L, bank[t], outs[t % G], evs[t], idxs[t], wts[t], residual=wl.norm,
-                                         ws=ws, separate_kernels=separate)
+                                         ws=ws, **kw)
             torch.cuda.synchronize()
             dur = {n: [] for n in names}
             for t in range(n_t):
@@ -676,22 +683,34 @@ def main():
                     dur[names[j % len(names)]].append(evs[t][2 * j].elapsed_time(evs[t][2 * j + 1]) * 1e3)
             return {n: float(np.mean(v)) for n, v in dur.items()}
 
-        kernel_us = timed_pass(False)
-        kernel_us_3k = timed_pass(True)
+        kernel_us = timed_pass(a.schedule)
+        kernel_us_other = {sc: timed_pass(sc) for sc in ("two_launch", "single_launch", "three_kernels") if sc != a.schedule}
         idx_h = idxs.cpu().numpy()          # the timing passes routed tokens 0 .. n_t-1
-        # algorithmic bytes of the router + gate/up launch: router matrix, norm weight and the gate
-        # and up planes of the K selected experts
-        rg_b = [router_bytes + norm_bytes + gu_bytes[idx_h[t, l]].sum() for t in range(n_t) for l in range(wl.n_layers)]
-        rg_us = kernel_us["route_gateup"]
-        achieved = float(np.mean(rg_b)) / (rg_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_route_gateup (router, top-K, gate/up + SwiGLU of the K experts)",
+        if a.schedule == "single_launch":
+            # the dominant (only) kernel of a step: router matrix, norm weight and the whole blobs
+            # (gate, up and down planes) of the K selected experts
+            kb = [router_bytes + norm_bytes + blob_bytes[idx_h[t, l]].sum() for t in range(n_t)
+                  for l in range(wl.n_layers)]
+            k_us = kernel_us["layer"]
+            kname, kdesc = "k_layer", "k_layer (router, top-K, gate/up + SwiGLU, down + combine of the K experts; one launch)"
+        else:
+            # router + gate/up launch: router matrix, norm weight and the gate and up planes
+            kb = [router_bytes + norm_bytes + gu_bytes[idx_h[t, l]].sum() for t in range(n_t)
+                  for l in range(wl.n_layers)]
+            k_us = kernel_us["route_gateup" if a.schedule == "two_launch" else "gateup"]
+            kname, kdesc = "k_route_gateup", "k_route_gateup (router, top-K, gate/up + SwiGLU of the K experts)"
+            if a.schedule == "three_kernels":
+                kb = [gu_bytes[idx_h[t, l]].sum() for t in range(n_t) for l in range(wl.n_layers)]
+                kname, kdesc = "k_gateup", "k_gateup (top-K, gate/up + SwiGLU of the K experts)"
+        achieved = float(np.mean(kb)) / (k_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kdesc,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic("k_route_gateup", f"config{a.config}"),
-                "bytes_per_launch": float(np.mean(rg_b)), "us_per_launch": round(rg_us, 3),
+                "traffic": load_traffic(kname, f"config{a.config}"),
+                "bytes_per_launch": float(np.mean(kb)), "us_per_launch": round(k_us, 3),
                 "timing": f"start/stop HIP events of each dispatch (hipExtLaunchKernel), {n_t} eager steps"}
-        log(f"[bench] kernel us: {kernel_us}; three-kernel schedule: {kernel_us_3k}; "
-            f"router + gate/up {achieved:,.1f} GB/s")
+        log(f"[bench] kernel us ({a.schedule}): {kernel_us}; other schedules: {kernel_us_other}; "
+            f"{kname} {achieved:,.1f} GB/s")
 
     if batched:
         # a batch runs several kernels on two streams, so its roofline is the whole batch's: the
@@ -793,6 +812,8 @@ def main():
     cfg = {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": K,
            "layers": wl.n_layers, "tokens_per_step": tokens_per_step, "bits": sorted(set(bits.tolist())),
            "group": 64, "graph_steps": G if use_graph else 0, "bank_tokens": n_bank}
+    if not batched:
+        cfg["schedule"] = a.schedule
     line = {
         "metric": "MoE decode tok/s and weight GB/s (% of HBM peak), 4-bit, 512 experts top-4",
         "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": done, "warmup": a.warmup,
@@ -807,7 +828,7 @@ def main():
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "stream_frac": round(gbps / stream_gbps, 4), "stream": stream,
         "kernel_us": {k: round(v, 3) for k, v in kernel_us.items()},
-        "kernel_us_three_kernel_schedule": {k: round(v, 3) for k, v in kernel_us_3k.items()},
+        "kernel_us_other_schedules": {sc: {k: round(v, 3) for k, v in ku.items()} for sc, ku in kernel_us_other.items()},
         "roofline": roof, "cpu_baseline": cpu, "parity": parity,
         "source_hash": source_hash(),
     }

@@ -23,6 +23,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_OP_ROUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE = 1, 2, 3
 MOE_FLAG_RESIDUAL = 1
 MOE_FLAG_SEPARATE_KERNELS = 2
+MOE_FLAG_SINGLE_LAUNCH = 4
 GROUP = 64
 MAX_TOPK = 8
 MAX_EXPERTS = 2048
@@ -266,12 +267,13 @@ def moe_combine(y, w, out, residual=None, stream=None) -> None:
 
 
 def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, w=None, residual: bool = False,
-                     ws=None, stream=None, separate_kernels: bool = False) -> None:
+                     ws=None, stream=None, separate_kernels: bool = False, single_launch: bool = False) -> None:
     """One decode token through the layers.  ``ws`` must come from :func:`workspace` (zero-filled)
-    and be reused only by stream-ordered calls; ``separate_kernels`` selects the three-kernel
-    schedule instead of the default two launches per layer."""
+    and be reused only by stream-ordered calls.  A layer is two launches by default (router + gate/up,
+    down); ``separate_kernels`` selects three, ``single_launch`` one (a persistent grid)."""
     arr = (moe_layer * len(layers))(*[L.c for L in layers])
-    flags = (MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
+    flags = ((MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
+             | (MOE_FLAG_SINGLE_LAUNCH if single_launch else 0))
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                   _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
@@ -363,20 +365,22 @@ class ExpertCache:
 
 
 def moe_layer_decode_timed(dims: moe_dims, layers: Sequence[Layer], x, out, events: Sequence, idx=None, w=None,
-                           residual: bool = False, ws=None, stream=None, separate_kernels: bool = False) -> None:
+                           residual: bool = False, ws=None, stream=None, separate_kernels: bool = False,
+                           single_launch: bool = False) -> None:
     """As moe_layer_decode, with a start/stop pair of ``events`` (torch.cuda.Event objects with
     timing enabled) per kernel: events[2j].elapsed_time(events[2j+1]) is kernel j's execution time.
-    Two kernels per layer on the default schedule (router + gate/up, down), three with
-    ``separate_kernels`` (router, gate/up, down)."""
+    Two kernels per layer on the default schedule (router + gate/up, down), one with ``single_launch``,
+    three with ``separate_kernels`` (router, gate/up, down)."""
     arr = (moe_layer * len(layers))(*[L.c for L in layers])
-    need = 2 * (3 if separate_kernels else 2) * len(layers)
+    need = 2 * (3 if separate_kernels else 1 if single_launch else 2) * len(layers)
     if len(events) < need:
         raise ValueError(f"{need} events needed, {len(events)} given")
     handles = [e.cuda_event for e in events]
     if not all(handles):
         raise ValueError("events must have been recorded once (torch creates HIP events lazily)")
     ev = (ctypes.c_void_p * len(events))(*handles)
-    flags = (MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
+    flags = ((MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
+             | (MOE_FLAG_SINGLE_LAUNCH if single_launch else 0))
     _check(lib().moe_layer_decode_timed(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                         _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                         _stream(stream), ev))

@@ -9,8 +9,10 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <set>
+#include <tuple>
 #include <string>
 #include <utility>
 #include <vector>
@@ -188,6 +190,7 @@ size_t ffn_ws(const moe_dims *d, int T) {
 struct DecodeWs {
     uint32_t *sync;      // [0] launch counter, [1] error word
     uint64_t *slots;     // [copies][E] tagged logits
+    uint32_t *flags;     // single launch: [copies][max workgroups] "h stored" flags
     float *logits;
     uint64_t *sel;
     float *w;
@@ -200,6 +203,7 @@ DecodeWs decode_layout(const moe_dims *d, void *ws) {
     DecodeWs r;
     r.sync = c.take<uint32_t>(2);
     r.slots = c.take<uint64_t>((size_t)moe::layer_logit_copies() * d->n_experts);
+    r.flags = c.take<uint32_t>((size_t)moe::fused_flag_copies() * moe::fused_max_workgroups());
     r.logits = c.take<float>(d->n_experts);
     r.sel = c.take<uint64_t>(d->top_k);
     r.w = c.take<float>(d->top_k);
@@ -207,6 +211,33 @@ DecodeWs decode_layout(const moe_dims *d, void *ws) {
     r.xbuf = c.take<float>(2 * (size_t)d->hidden);
     r.bytes = c.off;
     return r;
+}
+
+// Workgroups of the single-launch layer kernel for a shape on the current device (an occupancy query
+// the first time, then remembered).
+std::mutex g_nw_mu;
+std::map<std::tuple<int, int, int, int, int>, int> g_nw;
+int fused_workgroups_cached(const moe_dims *d, int *nw) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    const auto key = std::make_tuple(dev, d->hidden, d->inter, d->n_experts, d->top_k);
+    {
+        std::lock_guard<std::mutex> lock(g_nw_mu);
+        const auto it = g_nw.find(key);
+        if (it != g_nw.end()) {
+            *nw = it->second;
+            return MOE_OK;
+        }
+    }
+    int n = 0;
+    if (hipError_t e = moe::fused_workgroups(d->hidden, d->inter, d->n_experts, d->top_k, &n))
+        return fail(MOE_ERR_DEVICE, "occupancy of the layer kernel: %s", hipGetErrorString(e));
+    if (n < 1) return fail(MOE_ERR_UNSUPPORTED, "the single-launch layer kernel does not fit this shape on this "
+                                                "device; use the default schedule");
+    std::lock_guard<std::mutex> lock(g_nw_mu);
+    g_nw[key] = n;
+    *nw = n;
+    return MOE_OK;
 }
 
 size_t decode_ws(const moe_dims *d) {
@@ -717,7 +748,7 @@ static moe::KernelEvents kernel_events(void *const *events, int j) {
 
 static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
                              int x_dtype, unsigned flags, float *out, int32_t *idx, float *w, void *ws,
-                             size_t ws_bytes, void *stream, void *const *events) {
+                             size_t ws_bytes, void *stream, void *const *events, bool per_call_errors) {
     if (int s = check_dims(dims)) return s;
     if (!layers) return fail(MOE_ERR_NULL, "layers is NULL");
     if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_SHAPE, "n_layers=%d outside [1, 4096]", n_layers);
@@ -726,8 +757,10 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
     if (int s = check_dtype(x_dtype, "x")) return s;
     if (!x || !out) return fail(MOE_ERR_NULL, "x and out are required");
     if ((idx == nullptr) != (w == nullptr)) return fail(MOE_ERR_NULL, "idx and w must both be given or both NULL");
-    if (flags & ~(MOE_FLAG_RESIDUAL | MOE_FLAG_SEPARATE_KERNELS))
+    if (flags & ~(MOE_FLAG_RESIDUAL | MOE_FLAG_SEPARATE_KERNELS | MOE_FLAG_SINGLE_LAUNCH))
         return fail(MOE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if ((flags & MOE_FLAG_SEPARATE_KERNELS) && (flags & MOE_FLAG_SINGLE_LAUNCH))
+        return fail(MOE_ERR_UNSUPPORTED, "MOE_FLAG_SEPARATE_KERNELS and MOE_FLAG_SINGLE_LAUNCH exclude each other");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_ALIGN, "x and out must be 16-byte aligned");
     if ((idx && !aligned(idx, 4)) || (w && !aligned(w, 4))) return fail(MOE_ERR_ALIGN, "idx/w not 4-byte aligned");
     if (out == x) return fail(MOE_ERR_SHAPE, "out must not alias x");
@@ -738,6 +771,10 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
     hipStream_t st = (hipStream_t)stream;
     const bool residual = flags & MOE_FLAG_RESIDUAL;
     const bool separate = flags & MOE_FLAG_SEPARATE_KERNELS;
+    const bool single = flags & MOE_FLAG_SINGLE_LAUNCH;
+    int nw = 0;
+    if (single)
+        if (int s = fused_workgroups_cached(dims, &nw)) return s;
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer &L = layers[l];
         const void *xl = l == 0 ? x : (const void *)(W.xbuf + (size_t)((l - 1) & 1) * H);
@@ -760,7 +797,20 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
             la.split = !(xdt == MOE_BF16 && L.norm_w == nullptr);
             la.seq = W.sync;
             la.err = W.sync + 1;
+            la.clear_err = per_call_errors && l == 0;
             la.slots = W.slots;
+            if (single) {
+                moe::FusedLaunch fa{};
+                fa.L = la;
+                fa.residual = residual ? xl : nullptr;
+                fa.residual_dtype = xdt;
+                fa.out = ol;
+                fa.flags = W.flags;
+                fa.seq = W.sync;
+                fa.nw = nw;
+                if (int s = MOE_LAUNCH(moe::launch_layer_fused(fa, st, kernel_events(events, l)), "layer")) return s;
+                continue;
+            }
             if (int s = MOE_LAUNCH(moe::launch_layer(la, st, kernel_events(events, 2 * l)), "router + gate/up")) return s;
             moe::DownLaunch da{W.h, W.sync, W.sync + 1, W.sel, W.w, residual ? xl : nullptr, xdt, H, ol, H, I, K, 1};
             if (int s = MOE_LAUNCH(moe::launch_down(da, st, kernel_events(events, 2 * l + 1)), "down")) return s;
@@ -778,7 +828,8 @@ static int layer_decode_impl(const moe_dims *dims, const moe_layer *layers, int 
 
 int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
                      unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
-    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, nullptr);
+    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, nullptr,
+                             false);
 }
 
 int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
@@ -786,13 +837,27 @@ int moe_layer_decode_timed(const moe_dims *dims, const moe_layer *layers, int n_
                            void *stream, void *const *events) {
     if (!events) return fail(MOE_ERR_NULL, "events is NULL");
     if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_SHAPE, "n_layers=%d outside [1, 4096]", n_layers);
-    const int per_layer = (flags & MOE_FLAG_SEPARATE_KERNELS) ? 3 : 2;
+    const int per_layer = (flags & MOE_FLAG_SEPARATE_KERNELS) ? 3 : (flags & MOE_FLAG_SINGLE_LAUNCH) ? 1 : 2;
     for (int i = 0; i < 2 * per_layer * n_layers; ++i)
         if (!events[i]) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
         return fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode_timed cannot be captured into a graph");
-    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, events);
+    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, events,
+                             false);
 }
 
 }  // extern "C"
+
+namespace moe {
+int layer_decode_entry(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
+                       unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream,
+                       void *const *events, bool per_call_errors) {
+    return layer_decode_impl(dims, layers, n_layers, x, x_dtype, flags, out, idx, w, ws, ws_bytes, stream, events,
+                             per_call_errors);
+}
+size_t layer_decode_ws_bytes(const moe_dims *dims) {
+    return check_dims(dims) == MOE_OK ? decode_ws(dims) : 0;
+}
+int set_error(int status, const char *msg) { return fail(status, "%s", msg); }
+}  // namespace moe

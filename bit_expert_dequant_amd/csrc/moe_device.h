@@ -172,15 +172,22 @@ __device__ __forceinline__ uint64_t lookup_sel(int e, int E, bool use_tab, const
 // dword of eight weight codes then meets one such "plane" dword per v_dot8_i32_i4, which does eight
 // multiply-adds in the time a bf16 dot2 does two.
 //
-// Slot layout (kSlotDw dwords): plane p occupies dwords 4p .. 4p+3.  4-bit order: dword 4p + j holds
+// Slot layout (kSlotDw dwords): plane p occupies dwords 4q .. 4q+3, q = p ^ plane_swz(slot) (below).
+// 4-bit order: dword 4p + j (p the plane, unswizzled) holds
 // columns 8j .. 8j+7 (nibble n = column 8j+n), matching code dword j of the slot.  2-bit order: dword
 // 4p + 2j + e holds columns 16j + 2n + e (n < 8), matching the even (e = 0) and odd (e = 1) codes of
 // code dword j once they are spread to nibbles.  A thread stages one 16-column chunk m = 2s + h;
 // in both orders it owns dwords 4p + 2h and 4p + 2h + 1 of every plane.
 //
 // Precision: a column's rounding error is at most sx/2, 2^-16 of the slot's largest |x|.
+//
+// LDS banks.  A lane reads its slot's four planes as 16-byte loads, and neighbouring lanes own
+// neighbouring slots, 64 bytes apart; stored in plane order every lane of a load would hit the same
+// four banks.  Plane p of slot s therefore sits at plane position p ^ plane_swz(s), which spreads the
+// 16-byte loads of any 8 (32 banks) or 16 (64 banks) consecutive slots over distinct banks.
 constexpr int kSlotDw = 16;
 constexpr float kXMax = 30583.f;
+__device__ __forceinline__ int plane_swz(int s) { return ((s >> 1) ^ (s >> 2)) & 3; }
 
 // A chunk of 16 consecutive activations (32 bytes of bf16 or 64 of fp32) is loaded in two steps:
 // issue_chunk16 starts four 16-byte loads with no data-dependent branch (bf16 repeats its second
@@ -257,6 +264,7 @@ __device__ __forceinline__ void stage_chunk(int m, bool valid, const float (&v)[
         y[i] = __float_as_uint(t) - (0x4B400000u - 0x8888u);
     }
     const int h = m & 1;
+    const int swz = plane_swz(m >> 1);
     uint32_t *base4 = d4 ? d4 + (m >> 1) * kSlotDw + 2 * h : nullptr;
     uint32_t *base2 = d2 ? d2 + (m >> 1) * kSlotDw + 2 * h : nullptr;
     if (base4) {
@@ -266,7 +274,7 @@ __device__ __forceinline__ void stage_chunk(int m, bool valid, const float (&v)[
         planes8(a, pa);
         planes8(b, pb);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) *(u32x2 *)(base4 + 4 * p) = u32x2{pa[p], pb[p]};
+        for (int p = 0; p < 4; ++p) *(u32x2 *)(base4 + 4 * (p ^ swz)) = u32x2{pa[p], pb[p]};
     }
     if (base2) {
         uint32_t a[8], b[8], pa[4], pb[4];
@@ -275,7 +283,7 @@ __device__ __forceinline__ void stage_chunk(int m, bool valid, const float (&v)[
         planes8(a, pa);
         planes8(b, pb);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) *(u32x2 *)(base2 + 4 * p) = u32x2{pa[p], pb[p]};
+        for (int p = 0; p < 4; ++p) *(u32x2 *)(base2 + 4 * (p ^ swz)) = u32x2{pa[p], pb[p]};
     }
     if (!h) xs[m >> 1] = float2{mant > 0.f ? ldexpf(mant / kXMax, ex) : 0.f, sum};
 }
@@ -288,9 +296,10 @@ struct ActView {
 
 // Loads slot s of a view into registers, for a lane whose slot exists.
 __device__ __forceinline__ void load_act_slot_full(const ActView &av, int s, uint32_t (&D)[kSlotDw], float2 &xs) {
+    const int swz = plane_swz(s);
 #pragma unroll
     for (int i = 0; i < kSlotDw; i += 4) {
-        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + i);
+        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + 4 * ((i >> 2) ^ swz));
         D[i] = d.x; D[i + 1] = d.y; D[i + 2] = d.z; D[i + 3] = d.w;
     }
     xs = av.xs[s];
@@ -298,9 +307,10 @@ __device__ __forceinline__ void load_act_slot_full(const ActView &av, int s, uin
 // Loads slot ss of a view into registers (zeros when !ok: an idle lane's slot adds nothing).
 __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok, uint32_t (&D)[kSlotDw], float2 &xs) {
     const int s = ok ? ss : 0;
+    const int swz = plane_swz(s);
 #pragma unroll
     for (int i = 0; i < kSlotDw; i += 4) {
-        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + i);
+        const u32x4 d = *(const u32x4 *)(av.d + s * kSlotDw + 4 * ((i >> 2) ^ swz));
         D[i] = ok ? d.x : 0u; D[i + 1] = ok ? d.y : 0u; D[i + 2] = ok ? d.z : 0u; D[i + 3] = ok ? d.w : 0u;
     }
     const float2 t = av.xs[s];
@@ -312,21 +322,21 @@ __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok
 // activation.  4-bit codes enter v_dot8_i32_i4 as q - 8 (the code XOR 8 read as a signed nibble),
 // so the bias becomes b + 8 s; 2-bit codes spread to nibbles are already in [0, 3].  Per plane
 // the integer sums are at most 32 * 8 * 8, so the combined sum is exact in int32 and in fp32.
-// The four digit planes are combined in Horner form, acc = ((A3 * 16 + A2) * 16 + A1) * 16 + A0,
-// with every plane's dot products accumulated straight into acc.
+// Each digit plane accumulates in its own register (four independent chains of four dot products,
+// instead of one chain of sixteen: with one or two waves per SIMD the chain latency, not the issue
+// rate, bounds a decode unit), then the planes combine in Horner form,
+// acc = ((A3 * 16 + A2) * 16 + A1) * 16 + A0.
 template <int BITS>
 __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
-    int acc = 0;
+    int a[4] = {0, 0, 0, 0};
     if (BITS == 4) {
         int c[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) c[j] = (int)(q[j] ^ 0x88888888u);
 #pragma unroll
-        for (int p = 3; p >= 0; --p) {
-            acc *= 16;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], acc, false);
-        }
+            for (int p = 0; p < 4; ++p) a[p] = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], a[p], false);
     } else {
         int e[2][2];
 #pragma unroll
@@ -335,15 +345,14 @@ __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSl
             e[j][1] = (int)((q[j] >> 2) & 0x33333333u);
         }
 #pragma unroll
-        for (int p = 3; p >= 0; --p) {
-            acc *= 16;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                acc = __builtin_amdgcn_sdot8(e[j][0], (int)D[4 * p + 2 * j], acc, false);
-                acc = __builtin_amdgcn_sdot8(e[j][1], (int)D[4 * p + 2 * j + 1], acc, false);
+            for (int p = 0; p < 4; ++p) {
+                a[p] = __builtin_amdgcn_sdot8(e[j][0], (int)D[4 * p + 2 * j], a[p], false);
+                a[p] = __builtin_amdgcn_sdot8(e[j][1], (int)D[4 * p + 2 * j + 1], a[p], false);
             }
-        }
     }
+    const int acc = ((a[3] * 16 + a[2]) * 16 + a[1]) * 16 + a[0];
     const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
     const float bb = BITS == 4 ? fmaf(8.f, s, b) : b;
     return fmaf(s * xs.x, (float)acc, bb * xs.y);
@@ -462,10 +471,61 @@ __device__ __forceinline__ Top2 top2_range(const uint32_t *key, uint32_t taken, 
     }
 }
 
+// The K rounds for few keys per lane (NP <= 8): each lane keeps its best untaken key; a round takes
+// the wave maximum, the lowest lane holding it (one ballot), and that lane drops the key and takes
+// its next best -- with eight keys or fewer a lane recomputes that from scratch in a handful of
+// compares, branch-free, which costs less per round than keeping a second-best list.  Winners are
+// read back as scalars (readlane), so no cross-lane shuffle is needed at the end.
+template <int NP>
+__device__ __forceinline__ void wave_topk_lean(const uint32_t (&key_in)[NP], int K, uint32_t &my_key, int &my_pos) {
+    const int lane = threadIdx.x & 63;
+    uint32_t key[NP];
+#pragma unroll
+    for (int t = 0; t < NP; ++t) key[t] = key_in[t];
+    uint32_t bk = key[0];
+    int bs = 0;
+#pragma unroll
+    for (int t = 1; t < NP; ++t) {
+        const bool gt = key[t] > bk;
+        bk = gt ? key[t] : bk;
+        bs = gt ? t : bs;
+    }
+    my_key = 0;
+    my_pos = 0;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t m = wave_max_all(bk);
+        const int wl = __ffsll((unsigned long long)__ballot(bk == m)) - 1;
+        const int ws = __builtin_amdgcn_readlane(bs, wl);
+        my_key = lane == k ? m : my_key;
+        my_pos = lane == k ? wl * NP + ws : my_pos;
+        if (NP > 1) {
+            const bool win = lane == wl;
+#pragma unroll
+            for (int t = 0; t < NP; ++t) key[t] = (win && t == ws) ? 0u : key[t];
+            uint32_t nk = key[0];
+            int ns = 0;
+#pragma unroll
+            for (int t = 1; t < NP; ++t) {
+                const bool gt = key[t] > nk;
+                nk = gt ? key[t] : nk;
+                ns = gt ? t : ns;
+            }
+            bk = win ? nk : bk;
+            bs = win ? ns : bs;
+        } else {
+            bk = lane == wl ? 0u : bk;
+        }
+    }
+}
+
 // The K rounds.  `key`: this lane's NP keys (positions NP*lane + t of the wave).  Lane k < K
 // returns the k-th largest key and its position (equal keys: lower position first).
 template <int NP>
 __device__ __forceinline__ void wave_topk_core(const uint32_t (&key)[NP], int K, uint32_t &my_key, int &my_pos) {
+    if constexpr (NP <= 8) {
+        wave_topk_lean<NP>(key, K, my_key, my_pos);
+        return;
+    }
     constexpr int FW = NP <= 8 ? 3 : 5;                            // bits per recorded slot
     typedef typename std::conditional<NP <= 8, uint32_t, uint64_t>::type rec_t;
     const int lane = threadIdx.x & 63;
@@ -778,6 +838,30 @@ __device__ __forceinline__ void gu_finish(const Geo &g, int I, int r0, int RB, c
         pu = group_sum(pu, g.gsz);
         const int rr = gi * g.rpi + g.lrow;
         if (g.lsl == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu(pg) * pu;
+    }
+}
+
+// The RG SwiGLU values of one unit, in every lane of each row group (no store).
+template <int BITS, int NJ, int RG>
+__device__ __forceinline__ void gu_values(const Geo &g, const ActView &av, const GULoads<NJ, RG> &L, float (&hv)[RG]) {
+    uint32_t D[NJ][kSlotDw];
+    float2 XS[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int slot = g.lsl + 64 * j;
+        load_act_slot(av, slot, slot < g.spr, D[j], XS[j]);
+    }
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+        float pg = 0.f, pu = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            pg += slot_dot<BITS>(L.qg[gi][j], D[j], L.sg[gi][j], XS[j]);
+            pu += slot_dot<BITS>(L.qu[gi][j], D[j], L.su[gi][j], XS[j]);
+        }
+        pg = group_sum(pg, g.gsz);
+        pu = group_sum(pu, g.gsz);
+        hv[gi] = silu(pg) * pu;
     }
 }
 

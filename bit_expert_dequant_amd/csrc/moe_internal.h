@@ -173,6 +173,7 @@ struct LayerLaunch {
     const uint32_t *seq;                           // launch counter (advanced by the down kernel)
     uint64_t *slots;                               // [layer_logit_copies()][E] tag << 32 | logit bits
     uint32_t *err;                                 // timed-out waits (nonzero: the down kernel writes NaN)
+    int clear_err;                                 // nonzero: the first workgroup zeroes *err first (per-call errors)
     int nr, ng;                                    // workgroups per group (set by launch_layer)
     RowGeo geo; PlaneTable pt;                     // gate/up geometry (set by launch_layer)
 };
@@ -180,6 +181,34 @@ void layer_grid(int H, int I, int E, int K, int *nr, int *ng);
 int layer_logit_copies();
 size_t layer_lds_bytes(int H, int E);
 hipError_t launch_layer(const LayerLaunch &a, hipStream_t s, const KernelEvents &ev = {});
+
+// One decode layer in a single launch of a persistent grid (moe_fused.hip): nw workgroups, all
+// resident at once, each computing router rows, its gate/up and down units; the logits and h pass
+// between them through tagged workspace words.
+struct FusedLaunch {
+    LayerLaunch L;                                 // router + gate/up part (nr, ng, sel_ws, w_ws unused)
+    const void *residual; int residual_dtype;      // [H] added to the output, or NULL
+    float *out;                                    // [H]
+    uint32_t *flags;                               // [fused_flag_copies()][fused_max_workgroups()]
+    uint32_t *seq;                                 // the launch counter (L.seq), advanced by workgroup 0
+    int nw;                                        // workgroups (fused_workgroups)
+    RowGeo dgeo;                                   // down geometry (set by launch_layer_fused)
+};
+int fused_flag_copies();
+int fused_max_workgroups();
+// Workgroups for a layer of this shape on the current device: as many as the layer has router rows
+// or units of four waves, at most as many as can be resident at once.
+hipError_t fused_workgroups(int H, int I, int E, int K, int *nw);
+hipError_t launch_layer_fused(const FusedLaunch &a, hipStream_t s, const KernelEvents &ev = {});
+
+// moe_layer_decode behind its argument checks, on a given workspace.  per_call_errors: a timed-out
+// wait makes only the call it happens in write NaN (the error word is cleared at each call's start)
+// instead of every later call on the workspace.
+int layer_decode_entry(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x, int x_dtype,
+                       unsigned flags, float *out, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream,
+                       void *const *events, bool per_call_errors);
+size_t layer_decode_ws_bytes(const moe_dims *dims);   // 0 for invalid dims
+int set_error(int status, const char *msg);           // records the thread's error message, returns status
 
 struct CombineLaunch {
     const float *y; const float *w; const float *residual; float *out;

@@ -360,6 +360,7 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
 
 #define MOE_FLAG_RESIDUAL 1u          /* out = x + MoE(x) (pre-norm residual block) */
 #define MOE_FLAG_SEPARATE_KERNELS 2u  /* run each layer as three kernels (router, gate/up, down) */
+#define MOE_FLAG_SINGLE_LAUNCH 4u     /* run each layer as one launch of a persistent grid */
 
 /* One decode token through n_layers layers (1 <= n_layers <= 4096); layer l's output is
  * layer l+1's input.  Per layer: [RMSNorm] -> router -> top-K -> gate/up/SwiGLU for all K
@@ -370,7 +371,11 @@ int moe_combine(const float *y, const float *w, int T, int K, int H, const float
  * workgroups only wait for router workgroups started before them, and the wait is bounded: if it
  * ever runs out, the workspace's error word becomes nonzero and this and every later call with
  * that workspace write NaN outputs until it is zero-filled again.  MOE_FLAG_SEPARATE_KERNELS
- * selects three launches per layer (router, gate/up, down) with the same arithmetic.
+ * selects three launches per layer (router, gate/up, down); MOE_FLAG_SINGLE_LAUNCH one launch of a
+ * grid whose workgroups each compute router rows, gate/up and down units, handing the logits and h
+ * over through the workspace (the grid is sized to what the device can hold resident at once; every
+ * wait is bounded as above).  Same arithmetic in all three, except that the single launch hands h
+ * over truncated to 19 mantissa bits (a relative change below 2^-19).  The flags exclude each other.
  *   layers host [n_layers]
  *   x      device [H] x_dtype (input of the first layer), 16-byte aligned
  *   out    device [H] fp32 output of the last layer
@@ -387,6 +392,7 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
  * events[2j], events[2j+1]:
  *   default (two launches per layer): 4*n_layers events; layer l's router + gate/up launch is
  *           kernel 2l and its down kernel 2l+1;
+ *   MOE_FLAG_SINGLE_LAUNCH: 2*n_layers events; layer l's launch is kernel l;
  *   MOE_FLAG_SEPARATE_KERNELS: 6*n_layers events; layer l's router, gate/up and down kernels are
  *           kernels 3l, 3l+1, 3l+2.
  * Each kernel is launched through hipExtLaunchKernel with its pair, which the runtime stamps with

@@ -28,14 +28,22 @@ def ws_error_word(ws) -> int:
     return int(ws[4:8].cpu().numpy().view(np.uint32)[0])
 
 
-def run_decode(dl, x, residual=False, separate=False, ws=None):
+SCHEDULES = ["two_launch", "single_launch", "three_kernels"]
+
+
+def sched_kw(schedule: str) -> dict:
+    """moe_layer_decode keyword arguments of a layer schedule: one launch (default), two, three."""
+    return {"separate_kernels": schedule == "three_kernels", "single_launch": schedule == "single_launch"}
+
+
+def run_decode(dl, x, residual=False, schedule="two_launch", ws=None):
     wl = dl.wl
     d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
     ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1) if ws is None else ws
     out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
     idx = torch.empty(wl.K, dtype=torch.int32, device="cuda")
     w = torch.empty(wl.K, dtype=torch.float32, device="cuda")
-    M.moe_layer_decode(d, [dl.L], x, out, idx, w, residual=residual, ws=ws, separate_kernels=separate)
+    M.moe_layer_decode(d, [dl.L], x, out, idx, w, residual=residual, ws=ws, **sched_kw(schedule))
     torch.cuda.synchronize()
     assert ws_error_word(ws) == 0
     return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
@@ -72,11 +80,11 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_layer_decode_small_shapes(case, separate):
+def test_layer_decode_small_shapes(case, schedule):
     name, H, I, E, K, bits, extra = case
-    say(f"[decode small] {name} separate={separate}")
+    say(f"[decode small] {name} schedule={schedule}")
     wl = small_workload(name, 0xC0DE + H + I + E, H, I, E, K, bits, **extra)
     dl = build_layer(wl)
     ol = oracle_layer(wl)
@@ -86,11 +94,12 @@ def test_layer_decode_small_shapes(case, separate):
     for t in range(3):
         residual = t == 2
         x = act_tensor(wl, bank[t])
-        out, idx, w = run_decode(dl, x, residual=residual, separate=separate, ws=ws)
+        out, idx, w = run_decode(dl, x, residual=residual, schedule=schedule, ws=ws)
         check_token(wl, ol, x, act_f64(wl, bank[t]), out, idx, w, residual, f"{name} token {t}")
 
 
-def test_two_launch_many_calls_one_workspace():
+@pytest.mark.parametrize("schedule", ["two_launch", "single_launch"])
+def test_many_calls_one_workspace(schedule):
     """Back-to-back calls on one workspace (each launch must see only its own hand-over words):
     every call matches the three-kernel schedule on the same token, and repeats are bit-identical."""
     wl = small_workload("seq", 4711, 1024, 512, 64, 4, 4, norm=True)
@@ -103,10 +112,10 @@ def test_two_launch_many_calls_one_workspace():
     for i in range(48):
         t = (i * 5) % 8
         x = act_tensor(wl, bank[t])
-        out, idx, w = run_decode(dl, x, residual=True, ws=ws)
-        ref, ridx, rw = run_decode(dl, x, residual=True, separate=True, ws=ws2)
+        out, idx, w = run_decode(dl, x, residual=True, schedule=schedule, ws=ws)
+        ref, ridx, rw = run_decode(dl, x, residual=True, schedule="three_kernels", ws=ws2)
         assert list(idx) == list(ridx), f"call {i} token {t}"
-        assert_close(out, ref, f"call {i} token {t} two launches vs three kernels", rel=2e-5)
+        assert_close(out, ref, f"call {i} token {t} {schedule} vs three kernels", rel=2e-5)
         if t in first:
             assert np.array_equal(first[t], out), f"call {i} token {t} not reproducible"
         first.setdefault(t, out)
@@ -214,8 +223,8 @@ def test_two_layer_stack_small():
         assert_close(out.cpu().numpy(), ref_out, "stack out")
 
 
-@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
-def test_timed_decode_matches_untimed(separate):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_timed_decode_matches_untimed(schedule):
     """moe_layer_decode_timed runs the same schedule as moe_layer_decode (bit-identical outputs and
     routing on a 2-layer stack) and stamps a start/stop event pair per kernel, in stream order."""
     wl = small_workload("timed", 777, 1024, 512, 16, 4, 4, norm=True, n_layers=2)
@@ -230,16 +239,15 @@ def test_timed_decode_matches_untimed(separate):
         idx = torch.empty(2, wl.K, dtype=torch.int32, device="cuda")
         w = torch.empty(2, wl.K, dtype=torch.float32, device="cuda")
         if timed:
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (3 if separate else 2) * 2)]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range({'two_launch': 4, 'single_launch': 2, 'three_kernels': 6}[schedule]) for _ in range(2)]
             for e in evs:
                 e.record()
             torch.cuda.synchronize()
             with pytest.raises(ValueError):
-                M.moe_layer_decode_timed(d, L, x, out, evs[:-1], idx, w, residual=True, ws=ws,
-                                         separate_kernels=separate)
-            M.moe_layer_decode_timed(d, L, x, out, evs, idx, w, residual=True, ws=ws, separate_kernels=separate)
+                M.moe_layer_decode_timed(d, L, x, out, evs[:-1], idx, w, residual=True, ws=ws, **sched_kw(schedule))
+            M.moe_layer_decode_timed(d, L, x, out, evs, idx, w, residual=True, ws=ws, **sched_kw(schedule))
         else:
-            M.moe_layer_decode(d, L, x, out, idx, w, residual=True, ws=ws, separate_kernels=separate)
+            M.moe_layer_decode(d, L, x, out, idx, w, residual=True, ws=ws, **sched_kw(schedule))
         torch.cuda.synchronize()
         res.append((out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()))
         if timed:
@@ -252,9 +260,9 @@ def test_timed_decode_matches_untimed(separate):
     assert ws_error_word(ws) == 0
 
 
-@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("E,K", [(40, 8), (512, 4), (700, 8), (2048, 3)])
-def test_layer_decode_routing_ties(E, K, separate):
+def test_layer_decode_routing_ties(E, K, schedule):
     """Routing inside moe_layer_decode on logits with exact ties, +0/-0, -inf and NaN: an fp32
     router and a one-hot fp32 token make each logit equal to one router entry, so the selection
     (equal logits -> lower index; NaN ranks as -inf) and the weights are fixed exactly."""
@@ -276,7 +284,7 @@ def test_layer_decode_routing_ties(E, K, separate):
     idx = torch.empty(K, dtype=torch.int32, device="cuda")
     w = torch.empty(K, dtype=torch.float32, device="cuda")
     for _ in range(2):                     # the second call reuses the workspace
-        M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, separate_kernels=separate)
+        M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, **sched_kw(schedule))
         torch.cuda.synchronize()
         ri, rw, _ = oracle.route(col.astype(np.float64), K)
         assert list(idx.cpu().numpy()) == list(ri)
@@ -284,9 +292,9 @@ def test_layer_decode_routing_ties(E, K, separate):
     assert ws_error_word(ws) == 0
 
 
-@pytest.mark.parametrize("separate", [False, True], ids=["two_launch", "three_kernels"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("case", ["nan_in_topk", "all_nan"])
-def test_layer_decode_nan_logits_against_oracle(case, separate):
+def test_layer_decode_nan_logits_against_oracle(case, schedule):
     """NaN logits inside the top K, and a row with no finite logit, routed by moe_layer_decode and
     moe_route on the very logits the oracle gets (NaN ranks as -inf with weight 0; no finite logit
     gives weights 1/K).  The output is checked too, for the experts with nonzero weight."""
@@ -307,7 +315,7 @@ def test_layer_decode_nan_logits_against_oracle(case, separate):
     out = torch.empty(H, dtype=torch.float32, device="cuda")
     idx = torch.empty(K, dtype=torch.int32, device="cuda")
     w = torch.empty(K, dtype=torch.float32, device="cuda")
-    M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, separate_kernels=separate)
+    M.moe_layer_decode(d, [L], x, out, idx, w, ws=ws, **sched_kw(schedule))
     torch.cuda.synchronize()
     ri, rw, _ = oracle.route(col.astype(np.float64), K)
     assert list(idx.cpu().numpy()) == list(ri)
@@ -379,33 +387,45 @@ def test_stream_read_xor():
         M.moe_stream_read(torch.zeros(3, dtype=torch.int32, device="cuda"), sink)
 
 
-def test_launch_failure_between_kernels_then_recovery():
-    """A decode call refused at its second launch (router + gate/up ran, down did not) reports
-    MOE_ERR_LAUNCH; after the workspace is zero-filled again, as the header asks, the next calls are
-    correct."""
-    wl = small_workload("inject_dec", 0x1F1, 1024, 512, 16, 4, 4)
-    dl = build_layer(wl)
-    ol = oracle_layer(wl)
+@pytest.mark.parametrize("schedule", ["two_launch", "single_launch"])
+def test_launch_failure_between_kernels_then_recovery(schedule):
+    """A decode call refused at its second launch step (two launches: router + gate/up ran, down did
+    not; one launch: the first of two stacked layers ran, the second did not) reports MOE_ERR_LAUNCH;
+    after the workspace is zero-filled again, as the header asks, the next calls are correct."""
+    n_layers = 2 if schedule == "single_launch" else 1
+    wl = small_workload("inject_dec", 0x1F1, 1024, 512, 16, 4, 4, n_layers=n_layers, norm=n_layers > 1)
+    dls = [build_layer(wl, l) for l in range(n_layers)]
+    ols = [oracle_layer(wl, l) for l in range(n_layers)]
     bank = wl.tokens_bank(3)
     d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
-    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, 1)
-    out, idx, w = run_decode(dl, act_tensor(wl, bank[0]), ws=ws)
-    check_token(wl, ol, None, act_f64(wl, bank[0]), out, idx, w, what="before")
+    ws = M.workspace(M.MOE_OP_LAYER_DECODE, d, 1, n_layers)
+    kw = sched_kw(schedule)
+    res = n_layers > 1
+
+    def run_check(t, what):
+        out = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(n_layers, wl.K, dtype=torch.int32, device="cuda")
+        w = torch.empty(n_layers, wl.K, dtype=torch.float32, device="cuda")
+        M.moe_layer_decode(d, [dl.L for dl in dls], act_tensor(wl, bank[t]), out, idx, w, residual=res, ws=ws, **kw)
+        torch.cuda.synchronize()
+        ref_out, refs = oracle.stack_token(act_f64(wl, bank[t]), ols, wl.H, wl.I, wl.K, residual=res)
+        for l, r in enumerate(refs):
+            assert list(idx.cpu().numpy()[l]) == list(r.idx), f"{what} layer {l}"
+        assert_close(out.cpu().numpy(), ref_out, f"{what} out")
+
+    run_check(0, "before")
     o = torch.empty(wl.H, dtype=torch.float32, device="cuda")
-    i = torch.empty(wl.K, dtype=torch.int32, device="cuda")
-    ww = torch.empty(wl.K, dtype=torch.float32, device="cuda")
     M.lib().moe_debug_inject_launch_failure(1, 1)
     try:
         with pytest.raises(M.MoeError) as ei:
-            M.moe_layer_decode(d, [dl.L], act_tensor(wl, bank[1]), o, i, ww, ws=ws)
+            M.moe_layer_decode(d, [dl.L for dl in dls], act_tensor(wl, bank[1]), o, residual=res, ws=ws, **kw)
         assert ei.value.status == 7 and "injected" in str(ei.value)
     finally:
         M.lib().moe_debug_inject_launch_failure(0, 0)
     torch.cuda.synchronize()
     ws.zero_()
     for t in (1, 2):
-        out, idx, w = run_decode(dl, act_tensor(wl, bank[t]), ws=ws)
-        check_token(wl, ol, None, act_f64(wl, bank[t]), out, idx, w, what=f"after, token {t}")
+        run_check(t, f"after, token {t}")
 
 
 def test_error_word_forces_nan_until_zero_fill():
