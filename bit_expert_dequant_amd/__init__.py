@@ -83,6 +83,7 @@ def lib():
             "moe_combine": (I32, [P, P, I32, I32, I32, P, P, P]),
             "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
             "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
+            "moe_layer_decode_static": (I32, [P, P, I32, P, I32, U, P, P, P, P]),
             "moe_stream_read": (I32, [P, SZ, P, P]),
             "moe_quantize_matrix": (I32, [P, I32, I32, I32, I32, P, P, P]),
             "moe_expert_usage": (I32, [P, I32, I32, P, P]),
@@ -107,7 +108,8 @@ def exported_symbols() -> List[str]:
     return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
-            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed", "moe_stream_read",
+            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
+            "moe_layer_decode_static", "moe_stream_read",
             "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier", "moe_cache_create",
             "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy",
             "moe_debug_inject_launch_failure"]
@@ -277,6 +279,18 @@ def moe_layer_decode(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, 
     _check(lib().moe_layer_decode(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
                                   _tptr(out), _tptr(idx), _tptr(w), _tptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
+
+
+def moe_layer_decode_static(dims: moe_dims, layers: Sequence[Layer], x, out, idx=None, w=None,
+                            residual: bool = False, stream=None, separate_kernels: bool = False,
+                            single_launch: bool = False) -> None:
+    """moe_layer_decode with the library's per-device static workspace (allocates nothing; calls on
+    one device must not overlap)."""
+    arr = (moe_layer * len(layers))(*[L.c for L in layers])
+    flags = ((MOE_FLAG_RESIDUAL if residual else 0) | (MOE_FLAG_SEPARATE_KERNELS if separate_kernels else 0)
+             | (MOE_FLAG_SINGLE_LAUNCH if single_launch else 0))
+    _check(lib().moe_layer_decode_static(ctypes.byref(dims), arr, len(layers), _tptr(x), _dtype_code(x), flags,
+                                         _tptr(out), _tptr(idx), _tptr(w), _stream(stream)))
 
 
 def moe_stream_read(buf, sink, stream=None) -> None:

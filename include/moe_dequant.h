@@ -386,6 +386,20 @@ int moe_layer_decode(const moe_dims *dims, const moe_layer *layers, int n_layers
                      int x_dtype, unsigned flags, float *out, int32_t *idx, float *w,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving loops that forbid
+ * allocation): moe_layer_decode with its workspace in a device array the library holds, one per
+ * device, MOE_STATIC_SCRATCH_BYTES (256 KiB) large, so the caller passes inputs and outputs only and
+ * the call allocates nothing.  The array starts zeroed and keeps the state of the last call on the
+ * device (launch counter, hand-over words); calls on one device that may overlap (different streams
+ * without ordering) race on it and must not be issued.  Unlike moe_layer_decode, a timed-out wait
+ * makes only the call it happens in write NaN outputs.  Arguments as moe_layer_decode.
+ * Errors as moe_layer_decode; MOE_ERR_WORKSPACE when the dims need more than the array holds
+ * (moe_workspace_bytes(MOE_OP_LAYER_DECODE, ...) > MOE_STATIC_SCRATCH_BYTES), MOE_ERR_DEVICE when the
+ * array's device address cannot be obtained. */
+#define MOE_STATIC_SCRATCH_BYTES (1u << 18)
+int moe_layer_decode_static(const moe_dims *dims, const moe_layer *layers, int n_layers, const void *x,
+                            int x_dtype, unsigned flags, float *out, int32_t *idx, float *w, void *stream);
+
 /* moe_layer_decode with per-kernel timing, the library's counterpart of the pages' per-layer
  * timing breakdown (lilting.ch page, "遅延GPU実行" section, per-layer time table).  It runs the
  * schedule `flags` selects, kernel j of the call (in issue order) getting the start/stop pair
