@@ -24,6 +24,7 @@ MOE_OP_ROUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE = 1, 2, 3
 MOE_FLAG_RESIDUAL = 1
 MOE_FLAG_SEPARATE_KERNELS = 2
 MOE_FLAG_SINGLE_LAUNCH = 4
+MOE_FFN_AUTO, MOE_FFN_PER_TOKEN, MOE_FFN_SHARED, MOE_FFN_GROUPED = 0, 1, 2, 3
 GROUP = 64
 MAX_TOPK = 8
 MAX_EXPERTS = 2048
@@ -80,6 +81,7 @@ def lib():
             "moe_workspace_bytes": (SZ, [I32, P, I32, I32]),
             "moe_route": (I32, [P, P, P, I32, I32, P, P, P, P, SZ, P]),
             "moe_expert_ffn": (I32, [P, P, P, I32, I32, P, P, P, SZ, P]),
+            "moe_expert_ffn_path": (I32, [P, P, P, I32, I32, P, P, P, SZ, I32, P]),
             "moe_combine": (I32, [P, P, I32, I32, I32, P, P, P]),
             "moe_layer_decode": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P]),
             "moe_layer_decode_timed": (I32, [P, P, I32, P, I32, U, P, P, P, P, SZ, P, P]),
@@ -108,7 +110,7 @@ def exported_symbols() -> List[str]:
     return ["moe_status_string", "moe_last_error", "moe_version", "moe_packed_codes_bytes",
             "moe_packed_sb_bytes", "moe_packed_expert_bytes", "moe_expert_plane_offsets", "moe_pack_matrix",
             "moe_unpack_matrix", "moe_pack_expert", "moe_check_experts", "moe_workspace_bytes", "moe_route",
-            "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
+            "moe_expert_ffn", "moe_expert_ffn_path", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
             "moe_layer_decode_static", "moe_stream_read",
             "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier", "moe_cache_create",
             "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy",
@@ -257,10 +259,16 @@ def moe_route(dims: moe_dims, layer: Layer, x, idx, w, logits=None, ws=None, str
                            _tptr(w), _tptr(logits), _tptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def moe_expert_ffn(dims: moe_dims, layer: Layer, x, idx, y, ws, stream=None) -> None:
+def moe_expert_ffn(dims: moe_dims, layer: Layer, x, idx, y, ws, stream=None, path: int = 0) -> None:
+    """``path``: MOE_FFN_AUTO (0, what moe_expert_ffn chooses), MOE_FFN_PER_TOKEN, MOE_FFN_SHARED or
+    MOE_FFN_GROUPED."""
     T = x.shape[0] if x.dim() == 2 else 1
-    _check(lib().moe_expert_ffn(ctypes.byref(dims), ctypes.byref(layer.c), _tptr(x), _dtype_code(x), T,
-                                _tptr(idx), _tptr(y), _tptr(ws), ws.numel(), _stream(stream)))
+    if path == MOE_FFN_AUTO:
+        _check(lib().moe_expert_ffn(ctypes.byref(dims), ctypes.byref(layer.c), _tptr(x), _dtype_code(x), T,
+                                    _tptr(idx), _tptr(y), _tptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(lib().moe_expert_ffn_path(ctypes.byref(dims), ctypes.byref(layer.c), _tptr(x), _dtype_code(x), T,
+                                         _tptr(idx), _tptr(y), _tptr(ws), ws.numel(), path, _stream(stream)))
 
 
 def moe_combine(y, w, out, residual=None, stream=None) -> None:

@@ -177,13 +177,58 @@ constexpr int kMaxGroupedPairs = 32768;   // the grouping kernel keeps every pai
 // config-1 layer: 29 against 78 us at 2 tokens, 114 against 133 at 16, 206 against 195 at 32.
 constexpr int kPerTokenMaxT = 24;
 bool grouped_ffn(int T) { return T > kPerTokenMaxT; }
+// From 2 to kSharedMaxT tokens (T*K <= kSharedMaxPairs) the shared-read kernels stream each
+// selected expert once for all the pairs that chose it.
+bool shared_ffn(const moe_dims *d, int T) {
+    return T >= 2 && T <= moe::kSharedMaxT && T * d->top_k <= moe::kSharedMaxPairs &&
+           moe::shared_path_fits(d->hidden, d->inter, d->n_experts, T);
+}
+// Shared-read workspace: SwiGLU outputs of every pair in expert order, then the normalised rows.
+struct SharedWs {
+    float *hbuf, *xn;
+    size_t bytes;
+};
+SharedWs shared_ws(const moe_dims *d, int T, void *base) {
+    Carve c{(char *)base};
+    SharedWs r;
+    r.hbuf = c.take<float>((size_t)T * d->top_k * d->inter);
+    r.xn = c.take<float>((size_t)T * d->hidden);
+    r.bytes = c.off;
+    return r;
+}
 
-size_t ffn_ws(const moe_dims *d, int T) {
-    if (grouped_ffn(T)) return grouped_ws(d, T, nullptr).bytes;
+size_t per_token_ws(const moe_dims *d, int T) {
     Carve c{nullptr};
     c.take<float>((size_t)T * d->top_k * d->inter);
     c.take<uint64_t>((size_t)T * d->top_k);
     return c.off;
+}
+// Which kernels run a call (MOE_FFN_AUTO resolved), or -1 when the forced path cannot take T.
+int ffn_path(const moe_dims *d, int T, int path) {
+    switch (path) {
+        case MOE_FFN_AUTO:
+            if (grouped_ffn(T)) return T * d->top_k <= kMaxGroupedPairs ? MOE_FFN_GROUPED : -1;
+            return shared_ffn(d, T) ? MOE_FFN_SHARED : MOE_FFN_PER_TOKEN;
+        case MOE_FFN_PER_TOKEN: return T <= kPerTokenMaxT ? path : -1;
+        case MOE_FFN_SHARED: return shared_ffn(d, T) ? path : -1;
+        case MOE_FFN_GROUPED: return T >= 2 && T * d->top_k <= kMaxGroupedPairs ? path : -1;
+        default: return -1;
+    }
+}
+size_t path_ws(const moe_dims *d, int T, int path) {
+    switch (path) {
+        case MOE_FFN_GROUPED: return grouped_ws(d, T, nullptr).bytes;
+        case MOE_FFN_SHARED: return shared_ws(d, T, nullptr).bytes;
+        case MOE_FFN_PER_TOKEN: return per_token_ws(d, T);
+        default: return 0;
+    }
+}
+// Enough for every path that can take T.
+size_t ffn_ws(const moe_dims *d, int T) {
+    size_t b = 0;
+    for (int p : {MOE_FFN_PER_TOKEN, MOE_FFN_SHARED, MOE_FFN_GROUPED})
+        if (ffn_path(d, T, p) == p) b = std::max(b, path_ws(d, T, p));
+    return b;
 }
 // Layer-decode workspace: the two-launch schedule's hand-over words first (they must start
 // zeroed), then the buffers both schedules use.
@@ -430,8 +475,8 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
     return ok();
 }
 
-int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
-                   const int32_t *idx, float *y, void *ws, size_t ws_bytes, void *stream) {
+int moe_expert_ffn_path(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+                        const int32_t *idx, float *y, void *ws, size_t ws_bytes, int path, void *stream) {
     if (int s = check_dims(dims)) return s;
     if (int s = check_layer(layer, 0)) return s;
     if (int s = check_dtype(x_dtype, "x")) return s;
@@ -439,11 +484,20 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     if (T < 1 || T > 65535) return fail(MOE_ERR_SHAPE, "T=%d outside [1, 65535]", T);
     if (!aligned(x, 16)) return fail(MOE_ERR_ALIGN, "x not 16-byte aligned");
     if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MOE_ERR_ALIGN, "idx/y not 4-byte aligned");
-    if (grouped_ffn(T) && T * dims->top_k > kMaxGroupedPairs)
-        return fail(MOE_ERR_UNSUPPORTED, "T*top_k=%d exceeds %d for the grouped path", T * dims->top_k, kMaxGroupedPairs);
-    if (int s = check_ws(ws, ws_bytes, ffn_ws(dims, T))) return s;
+    if (path < MOE_FFN_AUTO || path > MOE_FFN_GROUPED) return fail(MOE_ERR_UNSUPPORTED, "unknown path %d", path);
+    const int run = ffn_path(dims, T, path);
+    if (run < 0) {
+        if (path == MOE_FFN_AUTO || path == MOE_FFN_GROUPED)
+            return fail(MOE_ERR_UNSUPPORTED, "T*top_k=%d: the grouped path takes 2 <= T and T*top_k <= %d",
+                        T * dims->top_k, kMaxGroupedPairs);
+        if (path == MOE_FFN_PER_TOKEN)
+            return fail(MOE_ERR_UNSUPPORTED, "T=%d: the per-token path takes T <= %d", T, kPerTokenMaxT);
+        return fail(MOE_ERR_UNSUPPORTED, "T=%d top_k=%d: the shared-read path takes 2 <= T <= %d, T*top_k <= %d "
+                    "and staged rows that fit in LDS", T, dims->top_k, moe::kSharedMaxT, moe::kSharedMaxPairs);
+    }
+    if (int s = check_ws(ws, ws_bytes, path_ws(dims, T, run))) return s;
     hipStream_t st = (hipStream_t)stream;
-    if (grouped_ffn(T)) {
+    if (run == MOE_FFN_GROUPED) {
         // batched: group the (token, slot) pairs by expert, then the grouped kernels
         GroupedWs g = grouped_ws(dims, T, ws);
         const void *xa = x;
@@ -472,6 +526,22 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
             return s;
         return ok();
     }
+    if (run == MOE_FFN_SHARED) {
+        SharedWs sw = shared_ws(dims, T, ws);
+        const void *xa = x;
+        int xdt = x_dtype;
+        if (layer->norm_w) {
+            if (int s = MOE_LAUNCH(moe::launch_norm_rows(x, x_dtype, layer->norm_w, layer->norm_eps, dims->hidden, T,
+                                                       sw.xn, st), "norm"))
+                return s;
+            xa = sw.xn;
+            xdt = MOE_F32;
+        }
+        moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, nullptr, sw.hbuf, y, {}, {}, 0, idx, T, dims->n_experts, 0};
+        if (int s = MOE_LAUNCH(moe::launch_shared_ffn(ga, st), "shared-read ffn")) return s;
+        return ok();
+    }
     Carve c{(char *)ws};
     float *h = c.take<float>((size_t)T * dims->top_k * dims->inter);
     uint64_t *sel = c.take<uint64_t>((size_t)T * dims->top_k);
@@ -481,6 +551,11 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
     moe::DownLaunch da{h, nullptr, nullptr, sel, nullptr, nullptr, MOE_F32, 0, y, dims->hidden, dims->inter, dims->top_k, T};
     if (int s = MOE_LAUNCH(moe::launch_down(da, st), "down")) return s;
     return ok();
+}
+
+int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+                   const int32_t *idx, float *y, void *ws, size_t ws_bytes, void *stream) {
+    return moe_expert_ffn_path(dims, layer, x, x_dtype, T, idx, y, ws, ws_bytes, MOE_FFN_AUTO, stream);
 }
 
 int moe_combine(const float *y, const float *w, int T, int K, int H, const float *residual, float *out,

@@ -19,6 +19,9 @@
 // Flash-MoE", section "Metal Compute Shaders"), with sum(q x) an exact integer dot product.
 #include "moe_device.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace moe {
 namespace {
 
@@ -46,17 +49,21 @@ struct DigitStage {
 // --------------------------------------------------------------------------- gate/up
 // GS: lanes per row group when it is a compile-time 32 or 64 and every lane's slots exist, else 0
 // (run-time group size, idle slots masked).
-template <int BITS, int NJ, int GS>
-__device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const SmallRec &se, uint32_t *lds) {
+// Units of one workgroup: slice `sl` of an expert's matrix takes units [sl, sl + 1) * kWaves * upw;
+// unit i of a wave is ub + i * kWaves, nu of them (0 for a wave past the matrix).  The small-expert
+// list runs with sl = blockIdx.x and upw = kGuUPW / kDnUPW (GUARD false); the shared-read path
+// sizes both per expert (GUARD true: the loads past nu are skipped).
+template <int BITS, int NJ, int GS, bool GUARD, int CAP>
+__device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CAP> &se, int sl, int upw,
+                                         uint32_t *lds) {
     constexpr int RG = gu_rg<NJ>();
     const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const Geo g = make_geo(a.geo);
     const int RB = a.geo.rb, nblk = a.geo.nblk;
     Planes pl[3];
     expert_planes(se.blob, BITS, a.pt, pl);
-    // unit i of this wave: ub + i * kWaves; nu of them (0 for a wave past the matrix)
-    const int ub = blockIdx.x * kWaves * kGuUPW + wave;
-    const int nu = max(0, min(kGuUPW, (nblk - ub + kWaves - 1) / kWaves));
+    const int ub = sl * kWaves * upw + wave;
+    const int nu = max(0, min(upw, (nblk - ub + kWaves - 1) / kWaves));
     const int last = max(nu - 1, 0);
     auto r0_of = [&](int i) { return min(ub + min(i, last) * kWaves, nblk - 1) * RB; };
 
@@ -70,12 +77,12 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const SmallRec 
     static_for<0, kGuNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging (registers first, so the weight loads stay in flight)
-    stage_finish(row_addr, se.n, H, a.x_dtype, sb, DigitStage<BITS>{lds, H});
+    stage_finish<CAP / 4>(row_addr, se.n, H, a.x_dtype, sb, DigitStage<BITS>{lds, H});
     __syncthreads();
 
     // 3. units: each loaded unit meets every token
     const int rd = row_dw(H);
-    unit_pipeline<kGuUPW>(nu, L, issue, [&](int i, const GULoads<NJ, RG> &B) {
+    unit_pipeline<kGuUPW, kGuNB, GUARD>(nu, L, issue, [&](int i, const GULoads<NJ, RG> &B) {
         const int r0 = r0_of(i);
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
@@ -126,8 +133,8 @@ __global__ void __launch_bounds__(kBlock) k_gu8(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     SmallRec se;
     if (!small_entry(a, se)) return;
-    if (se.bits == 2) gu8_body<2, NJ, GS>(a, se, lds);
-    else gu8_body<4, NJ, GS>(a, se, lds);
+    if (se.bits == 2) gu8_body<2, NJ, GS, false>(a, se, blockIdx.x, kGuUPW, lds);
+    else gu8_body<4, NJ, GS, false>(a, se, blockIdx.x, kGuUPW, lds);
 }
 
 // --------------------------------------------------------------------------- down
@@ -152,16 +159,17 @@ __device__ __forceinline__ void dn8_issue(const Planes &pl, const Geo &g, int H,
     }
 }
 
-template <int BITS, int NJ, int GS>
-__device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const SmallRec &se, uint32_t *lds) {
+template <int BITS, int NJ, int GS, bool GUARD, int CAP>
+__device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CAP> &se, int sl, int upw,
+                                         uint32_t *lds) {
     constexpr int RG = dn8_rg<NJ>();
     const int H = a.H, I = a.I, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const Geo g = make_geo(a.geo);
     const int RB = a.geo.rb, nblk = a.geo.nblk;
     Planes pl[3];
     expert_planes(se.blob, BITS, a.pt, pl);
-    const int ub = blockIdx.x * kWaves * kDnUPW + wave;
-    const int nu = max(0, min(kDnUPW, (nblk - ub + kWaves - 1) / kWaves));
+    const int ub = sl * kWaves * upw + wave;
+    const int nu = max(0, min(upw, (nblk - ub + kWaves - 1) / kWaves));
     const int last = max(nu - 1, 0);
     auto r0_of = [&](int i) { return min(ub + min(i, last) * kWaves, nblk - 1) * RB; };
 
@@ -174,12 +182,12 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const SmallRec 
     static_for<0, kDnNB - 1>([&](auto ic) { issue(decltype(ic)::value, L[decltype(ic)::value]); });
 
     // 2. staging
-    stage_finish(row_addr, se.n, I, MOE_F32, sb, DigitStage<BITS>{lds, I});
+    stage_finish<CAP / 4>(row_addr, se.n, I, MOE_F32, sb, DigitStage<BITS>{lds, I});
     __syncthreads();
 
     // 3. units
     const int rd = row_dw(I);
-    unit_pipeline<kDnUPW>(nu, L, issue, [&](int i, const D8Loads<NJ, RG> &B) {
+    unit_pipeline<kDnUPW, kDnNB, GUARD>(nu, L, issue, [&](int i, const D8Loads<NJ, RG> &B) {
         const int r0 = r0_of(i);
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
@@ -195,7 +203,7 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const SmallRec 
             }
             float *yrow = a.y + (size_t)se.pair[0] * H;
 #pragma unroll
-            for (int q = 1; q < kSmallTokens; ++q) yrow = t == q ? a.y + (size_t)se.pair[q] * H : yrow;
+            for (int q = 1; q < CAP; ++q) yrow = t == q ? a.y + (size_t)se.pair[q] * H : yrow;
             if constexpr (GS != 0) {
 #pragma unroll
                 for (int q = 0; q < RG / 2; ++q) {
@@ -221,8 +229,182 @@ __global__ void __launch_bounds__(kBlock) k_dn8(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     SmallRec se;
     if (!small_entry(a, se)) return;
-    if (se.bits == 2) dn8_body<2, NJ, GS>(a, se, lds);
-    else dn8_body<4, NJ, GS>(a, se, lds);
+    if (se.bits == 2) dn8_body<2, NJ, GS, false>(a, se, blockIdx.x, kDnUPW, lds);
+    else dn8_body<4, NJ, GS, false>(a, se, blockIdx.x, kDnUPW, lds);
+}
+
+// --------------------------------------------------------------------------- shared-read path
+// A call with a few tokens (T*K <= kSharedMaxPairs pairs) takes no grouping pass: wavefront 0 of
+// every workgroup derives the call's distinct experts from idx by itself.  Each valid pair marks a
+// two-word LDS entry of its expert (first pair, pair count) with LDS atomics, so the pairs that
+// their entry names first stand for the distinct experts, in order of first appearance.  Expert d
+// with its pairs in pair order is one entry of the work list (an expert with more than `cap` pairs
+// becomes several entries of at most cap pairs, each streaming the expert once); its rows of the
+// expert-ordered h buffer start after the pairs of the experts that appear before it.  The grid's
+// workgroups are dealt round-robin over the entries; an entry's workgroups (slices) split its
+// matrix, with enough units per wave that a slice's weight stream outweighs the staging of its
+// rows.  Gate/up and down derive the same entries, so the h rows match between them.
+struct SharedWork {
+    TokRec<kSharedCap> r;
+    int sl, upw;            // slice of the expert's matrix and units per wave (upw 0: no work)
+    uint64_t inval;         // pairs whose index is outside [0, E) or whose expert is absent
+};
+constexpr int kSharedRecDw = 32;
+__host__ __device__ __forceinline__ int shared_rec_off(int cols, int cap, int E) {
+    const int st = cap * row_dw(cols), tb = 2 * E;
+    return ((st > tb ? st : tb) + 3) & ~3;
+}
+__host__ __device__ __forceinline__ int shared_cap(int T) {
+    const int c = (T + 3) & ~3;
+    return c < kSharedCap ? c : kSharedCap;
+}
+
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The work of this workgroup; every thread calls it (it ends with a barrier).  lds: the staging area
+// (its first 2E dwords serve as the expert table), then the record at rec_off.
+__device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, int rec_off, uint32_t *lds,
+                                            SharedWork &w) {
+    uint32_t *rec = lds + rec_off;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, P = a.T * a.K, cap = a.cap;
+        int e = -1, bits = 4;
+        uint64_t blob = 0;
+        if (lane < P) {
+            e = a.idx[lane];
+            if (e >= 0 && e < a.E) {
+                const moe_expert_desc d = a.experts[e];
+                blob = d.blob;
+                bits = d.bits == 2 ? 2 : 4;
+            }
+        }
+        const bool valid = blob != 0;
+        uint32_t *tab = lds;            // [2e] first pair of expert e, [2e + 1] its pair count
+        if (valid) {
+            tab[2 * e] = 64u;
+            tab[2 * e + 1] = 0u;
+        }
+        if (valid) {                    // after the stores above: one wavefront's LDS operations run in order
+            atomicMin(&tab[2 * e], (uint32_t)lane);
+            atomicAdd(&tab[2 * e + 1], 1u);
+        }
+        int first = 64, cnt = 0;
+        if (valid) {
+            first = (int)tab[2 * e];
+            cnt = (int)tab[2 * e + 1];
+        }
+        const bool is_first = valid && first == lane;
+        const uint64_t fm = __ballot(is_first);
+        const uint64_t big = __ballot(is_first && cnt > cap);
+        // entries: one per distinct expert, or ceil(cnt / cap) when some expert has more than cap pairs
+        int nent = __popcll(fm);
+        if (big) {
+            nent = 0;
+            for (uint64_t m = fm; m; m &= m - 1) {
+                const int l = __ffsll((unsigned long long)m) - 1;
+                nent += (__builtin_amdgcn_readlane(cnt, l) + cap - 1) / cap;
+            }
+        }
+        int f = 0, c = 0, n = 0, base = 0, sl = 0, upw = 0, pe = 0, pbits = 4;
+        uint64_t pblob = 0;
+        uint32_t pairs[kSharedCap] = {};
+        if (nent > 0) {
+            const int G = gridDim.x, L = blockIdx.x;
+            const int j = L % nent, s = L / nent;
+            const int avail = G / nent + (j < G % nent ? 1 : 0);
+            if (!big) {
+                f = __ffsll((unsigned long long)__ballot(is_first && mbcnt64(fm) == j)) - 1;
+            } else {
+                int acc = 0;
+                for (uint64_t m = fm; m; m &= m - 1) {
+                    const int l = __ffsll((unsigned long long)m) - 1;
+                    const int nch = (__builtin_amdgcn_readlane(cnt, l) + cap - 1) / cap;
+                    if (j < acc + nch) {
+                        f = l;
+                        c = j - acc;
+                        break;
+                    }
+                    acc += nch;
+                }
+            }
+            pe = __builtin_amdgcn_readlane(e, f);
+            pblob = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(blob >> 32), f) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)blob, f);
+            pbits = __builtin_amdgcn_readlane(bits, f);
+            uint64_t m = __ballot(valid && e == pe);
+            n = min(cap, __popcll(m) - c * cap);
+            base = __popcll(__ballot(valid && first < f)) + c * cap;
+            for (int q = 0; q < c * cap; ++q) m &= m - 1;
+#pragma unroll
+            for (int t = 0; t < kSharedCap; ++t) {
+                pairs[t] = t < n ? (uint32_t)(__ffsll((unsigned long long)m) - 1) : pairs[t > 0 ? t - 1 : 0];
+                if (t < n) m &= m - 1;
+            }
+            // slices: at least (n + 1) / 2 units per wave, at most the workgroups this entry has
+            const int want = max(1, min(kGuUPW, (n + 1) / 2));
+            const int nsl = min(avail, (nblk + kWaves * want - 1) / (kWaves * want));
+            if (s < nsl) {
+                sl = s;
+                upw = (nblk + kWaves * nsl - 1) / (kWaves * nsl);
+            }
+        }
+        const uint64_t inval = __ballot(lane < P && !valid);
+        if (lane == 0) {
+            rec[0] = (uint32_t)pblob;
+            rec[1] = (uint32_t)(pblob >> 32);
+            rec[2] = (uint32_t)pe;
+            rec[3] = (uint32_t)n;
+            rec[4] = (uint32_t)base;
+            rec[5] = (uint32_t)pbits;
+            rec[6] = (uint32_t)sl;
+            rec[7] = (uint32_t)upw;
+            rec[8] = (uint32_t)inval;
+            rec[9] = (uint32_t)(inval >> 32);
+#pragma unroll
+            for (int t = 0; t < kSharedCap; ++t) rec[10 + t] = pairs[t];
+        }
+    }
+    __syncthreads();
+    // readfirstlane returns int: take the word back as unsigned before widening it into a 64-bit
+    // address or mask (a sign-extended low word would corrupt the upper half)
+    auto rd = [&](int i) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)rec[i]); };
+    w.r.blob = ((uint64_t)rd(1) << 32) | rd(0);
+    w.r.e = (int)rd(2);
+    w.r.n = (int)rd(3);
+    w.r.base = (int)rd(4);
+    w.r.bits = (int)rd(5);
+    w.sl = (int)rd(6);
+    w.upw = (int)rd(7);
+    w.inval = ((uint64_t)rd(9) << 32) | rd(8);
+#pragma unroll
+    for (int t = 0; t < kSharedCap; ++t) w.r.pair[t] = (int)rd(10 + t);
+}
+
+template <int NJ, int GS>
+__global__ void __launch_bounds__(kBlock) k_gu_sh(GroupedLaunch a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    SharedWork w;
+    shared_work(a, a.geo.nblk, shared_rec_off(a.H, a.cap, a.E), lds, w);
+    if (w.upw == 0) return;
+    if (w.r.bits == 2) gu8_body<2, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
+    else gu8_body<4, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
+}
+
+template <int NJ, int GS>
+__global__ void __launch_bounds__(kBlock) k_dn_sh(GroupedLaunch a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    SharedWork w;
+    shared_work(a, a.geo.nblk, shared_rec_off(a.I, a.cap, a.E), lds, w);
+    // zero rows for the pairs without an expert, spread over the whole grid
+    for (uint64_t m = w.inval; m; m &= m - 1) {
+        float *yr = a.y + (size_t)(__ffsll((unsigned long long)m) - 1) * a.H;
+        for (int c = blockIdx.x * kBlock + threadIdx.x; c < a.H; c += gridDim.x * kBlock) yr[c] = 0.f;
+    }
+    if (w.upw == 0) return;
+    if (w.r.bits == 2) dn8_body<2, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
+    else dn8_body<4, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
 }
 
 // Compile-time group size for rows of `cols` inputs taken NJ slots per lane: 32 or 64 when every
@@ -236,33 +418,50 @@ int small_gs(int cols, int nj) {
 
 size_t small_lds_bytes(int cols) { return (size_t)kSmallTokens * row_dw(cols) * 4; }
 
-hipError_t set_small_lds(const void *fn, size_t lds) {
-    if (lds <= 64 * 1024) return hipSuccess;
-    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+constexpr size_t kMaxLds = 160 * 1024;
+// Raise a kernel's dynamic LDS limit to the CU's whole LDS, once per kernel and device (launches
+// during stream capture then make no attribute calls).
+template <auto FN>
+hipError_t allow_full_lds() {
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    if (hipError_t e = hipFuncSetAttribute((const void *)FN, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds))
+        return e;
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+template <auto FN>
+hipError_t launch_lds(dim3 grid, size_t lds, hipStream_t s, const KernelEvents &ev, const GroupedLaunch &a) {
+    if (lds > 64 * 1024)
+        if (hipError_t e = allow_full_lds<FN>()) return e;
+    return dispatch(FN, grid, dim3(kBlock), lds, s, ev, a);
 }
 
 }  // namespace
 
 bool small_path_fits(int H, int I) {
-    return small_lds_bytes(H) <= 160 * 1024 && small_lds_bytes(I) <= 160 * 1024 && H % 64 == 0 && I % 64 == 0;
+    return small_lds_bytes(H) <= kMaxLds && small_lds_bytes(I) <= kMaxLds && H % 64 == 0 && I % 64 == 0;
 }
 
 hipError_t launch_small_gateup(const GroupedLaunch &a_in, int max_small, hipStream_t s) {
     GroupedLaunch a = a_in;
     a.geo = gateup_geo(a.H, a.I);
     a.pt = plane_table(a.H, a.I);
+    a.upw = kGuUPW;
     const dim3 grid((a.geo.nblk + kWaves * kGuUPW - 1) / (kWaves * kGuUPW), max_small);
     const size_t lds = small_lds_bytes(a.H);
-    auto launch = [&](auto fn) -> hipError_t {
-        if (hipError_t e = set_small_lds((const void *)fn, lds)) return e;
-        hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-        return hipGetLastError();
-    };
+    const KernelEvents ev{};
     const int nj = nj_for(a.H), gs = small_gs(a.H, nj);
     switch (nj) {
-        case 1: return gs == 64 ? launch(k_gu8<1, 64>) : gs == 32 ? launch(k_gu8<1, 32>) : launch(k_gu8<1, 0>);
-        case 2: return gs ? launch(k_gu8<2, 64>) : launch(k_gu8<2, 0>);
-        default: return gs ? launch(k_gu8<4, 64>) : launch(k_gu8<4, 0>);
+        case 1:
+            return gs == 64   ? launch_lds<k_gu8<1, 64>>(grid, lds, s, ev, a)
+                   : gs == 32 ? launch_lds<k_gu8<1, 32>>(grid, lds, s, ev, a)
+                              : launch_lds<k_gu8<1, 0>>(grid, lds, s, ev, a);
+        case 2: return gs ? launch_lds<k_gu8<2, 64>>(grid, lds, s, ev, a) : launch_lds<k_gu8<2, 0>>(grid, lds, s, ev, a);
+        default: return gs ? launch_lds<k_gu8<4, 64>>(grid, lds, s, ev, a) : launch_lds<k_gu8<4, 0>>(grid, lds, s, ev, a);
     }
 }
 
@@ -271,17 +470,74 @@ hipError_t launch_small_down(const GroupedLaunch &a_in, int max_small, hipStream
     const int nj = nj_for(a.I), gs = small_gs(a.I, nj);
     a.geo = row_geo(a.I, a.H, nj == 1 ? dn8_rg<1>() : nj == 2 ? dn8_rg<2>() : dn8_rg<4>());
     a.pt = plane_table(a.H, a.I);
+    a.upw = kDnUPW;
     const dim3 grid((a.geo.nblk + kWaves * kDnUPW - 1) / (kWaves * kDnUPW), max_small);
     const size_t lds = small_lds_bytes(a.I);
-    auto launch = [&](auto fn) -> hipError_t {
-        if (hipError_t e = set_small_lds((const void *)fn, lds)) return e;
-        hipLaunchKernelGGL(fn, grid, dim3(kBlock), lds, s, a);
-        return hipGetLastError();
-    };
+    const KernelEvents ev{};
     switch (nj) {
-        case 1: return gs == 64 ? launch(k_dn8<1, 64>) : gs == 32 ? launch(k_dn8<1, 32>) : launch(k_dn8<1, 0>);
-        case 2: return gs ? launch(k_dn8<2, 64>) : launch(k_dn8<2, 0>);
-        default: return gs ? launch(k_dn8<4, 64>) : launch(k_dn8<4, 0>);
+        case 1:
+            return gs == 64   ? launch_lds<k_dn8<1, 64>>(grid, lds, s, ev, a)
+                   : gs == 32 ? launch_lds<k_dn8<1, 32>>(grid, lds, s, ev, a)
+                              : launch_lds<k_dn8<1, 0>>(grid, lds, s, ev, a);
+        case 2: return gs ? launch_lds<k_dn8<2, 64>>(grid, lds, s, ev, a) : launch_lds<k_dn8<2, 0>>(grid, lds, s, ev, a);
+        default: return gs ? launch_lds<k_dn8<4, 64>>(grid, lds, s, ev, a) : launch_lds<k_dn8<4, 0>>(grid, lds, s, ev, a);
+    }
+}
+
+namespace {
+size_t shared_lds_bytes(int cols, int cap, int E) { return ((size_t)shared_rec_off(cols, cap, E) + kSharedRecDw) * 4; }
+// Workgroups of a shared-read launch: every entry (at most P of them) gets enough slices to keep
+// its units per wave within the unrolled pipeline, and the grid fills the chip at least twice.
+int shared_grid(int nblk, int upw_max, int P) {
+    const int per = (nblk + kWaves * upw_max - 1) / (kWaves * upw_max);
+    return std::max(P * per, 512);
+}
+}  // namespace
+
+bool shared_path_fits(int H, int I, int E, int T) {
+    const int cap = shared_cap(T);
+    return H % 64 == 0 && I % 64 == 0 && shared_lds_bytes(H, cap, E) <= kMaxLds &&
+           shared_lds_bytes(I, cap, E) <= kMaxLds;
+}
+
+hipError_t launch_shared_ffn(const GroupedLaunch &a_in, hipStream_t s, const KernelEvents &gu_ev,
+                             const KernelEvents &dn_ev) {
+    GroupedLaunch a = a_in;
+    const int P = a.T * a.K;
+    a.cap = shared_cap(a.T);
+    a.pt = plane_table(a.H, a.I);
+    {
+        a.geo = gateup_geo(a.H, a.I);
+        a.upw = 0;
+        const dim3 grid(shared_grid(a.geo.nblk, kGuUPW, P));
+        const size_t lds = shared_lds_bytes(a.H, a.cap, a.E);
+        const int nj = nj_for(a.H), gs = small_gs(a.H, nj);
+        hipError_t e;
+        switch (nj) {
+            case 1:
+                e = gs == 64   ? launch_lds<k_gu_sh<1, 64>>(grid, lds, s, gu_ev, a)
+                    : gs == 32 ? launch_lds<k_gu_sh<1, 32>>(grid, lds, s, gu_ev, a)
+                               : launch_lds<k_gu_sh<1, 0>>(grid, lds, s, gu_ev, a);
+                break;
+            case 2:
+                e = gs ? launch_lds<k_gu_sh<2, 64>>(grid, lds, s, gu_ev, a) : launch_lds<k_gu_sh<2, 0>>(grid, lds, s, gu_ev, a);
+                break;
+            default:
+                e = gs ? launch_lds<k_gu_sh<4, 64>>(grid, lds, s, gu_ev, a) : launch_lds<k_gu_sh<4, 0>>(grid, lds, s, gu_ev, a);
+        }
+        if (e) return e;
+    }
+    const int nj = nj_for(a.I), gs = small_gs(a.I, nj);
+    a.geo = row_geo(a.I, a.H, nj == 1 ? dn8_rg<1>() : nj == 2 ? dn8_rg<2>() : dn8_rg<4>());
+    const dim3 grid(shared_grid(a.geo.nblk, kDnUPW, P));
+    const size_t lds = shared_lds_bytes(a.I, a.cap, a.E);
+    switch (nj) {
+        case 1:
+            return gs == 64   ? launch_lds<k_dn_sh<1, 64>>(grid, lds, s, dn_ev, a)
+                   : gs == 32 ? launch_lds<k_dn_sh<1, 32>>(grid, lds, s, dn_ev, a)
+                              : launch_lds<k_dn_sh<1, 0>>(grid, lds, s, dn_ev, a);
+        case 2: return gs ? launch_lds<k_dn_sh<2, 64>>(grid, lds, s, dn_ev, a) : launch_lds<k_dn_sh<2, 0>>(grid, lds, s, dn_ev, a);
+        default: return gs ? launch_lds<k_dn_sh<4, 64>>(grid, lds, s, dn_ev, a) : launch_lds<k_dn_sh<4, 0>>(grid, lds, s, dn_ev, a);
     }
 }
 

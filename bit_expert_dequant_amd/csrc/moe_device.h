@@ -934,14 +934,18 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // The unit pipeline of one wave: UPW units, NB register buffers, the loads of unit i + NB - 1 issued
 // before unit i is finished, so NB - 1 units are in flight while one is computed.  Fully unrolled
-// (buffer indices are compile-time) and branch-free around the loads: a wave with fewer than UPW
-// units (the ragged end of a matrix) re-reads its last unit's rows instead, and only the finishing
-// step is skipped.  issue(i, buf) must clamp i itself.
-template <int UPW, int NB, typename Buf, typename Issue, typename Finish>
+// (buffer indices are compile-time).  Without GUARD it is branch-free around the loads: a wave with
+// fewer than UPW units (the ragged end of a matrix) re-reads its last unit's rows instead, and only
+// the finishing step is skipped.  With GUARD (waves whose unit count is usually well below UPW) the
+// loads past the wave's nu units are skipped too, by a wave-uniform branch.  issue(i, buf) must
+// clamp i itself.
+template <int UPW, int NB, bool GUARD = false, typename Buf, typename Issue, typename Finish>
 __device__ __forceinline__ void unit_pipeline(int nu, Buf (&B)[NB], Issue &&issue, Finish &&finish) {
     static_for<0, UPW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i + NB - 1 < UPW) issue(i + NB - 1, B[(i + NB - 1) % NB]);
+        if constexpr (i + NB - 1 < UPW) {
+            if (!GUARD || i + NB - 1 < nu) issue(i + NB - 1, B[(i + NB - 1) % NB]);
+        }
         if (i < nu) finish(i, B[i % NB]);
     });
 }
@@ -967,8 +971,8 @@ __device__ __forceinline__ bool small_entry(const GroupedLaunch &a, SmallRec &r)
 
 // Staging of an expert's token rows into LDS.  Thread `tid` takes chunk tid (+ kBlock, ... for rows
 // of more than kBlock chunks) of 16 activations of every row, so a token's index is a compile-time
-// constant everywhere and its row address a uniform value: row_addr(t) for t < kSmallTokens (t >= n
-// gives a duplicate of a present row).  Tokens go in two batches of four; the loads of the first
+// constant everywhere and its row address a uniform value: row_addr(t) for t < 4 * NBATCH (t >= n
+// gives a duplicate of a present row).  Tokens go in NBATCH batches of four; the loads of the first
 // pass's first batch are issued by stage_issue, before the caller's first weight loads, and
 // everything else happens in stage_finish, which hands every chunk to conv(t, chunk, valid, v).
 // Every thread of the workgroup calls both (conv may exchange data between the lanes of a wave);
@@ -1000,19 +1004,21 @@ template <typename RowAddr>
 __device__ __forceinline__ void stage_issue(RowAddr &&row_addr, int cols, int dtype, StageBatch &sb) {
     stage_batch_issue<0>(row_addr, dtype, min((int)threadIdx.x, cols / 16 - 1), sb);
 }
-template <typename RowAddr, typename Conv>
+template <int NBATCH, typename RowAddr, typename Conv>
 __device__ __forceinline__ void stage_finish(RowAddr &&row_addr, int n, int cols, int dtype, StageBatch &sb,
                                              Conv &&conv) {
-    static_assert(kSmallTokens == 8, "two batches of four tokens");
     const int nch = cols / 16;
     for (int m0 = 0; m0 < nch; m0 += kBlock) {                               // uniform; usually one pass
         const int m = m0 + (int)threadIdx.x, mc = min(m, nch - 1);
         if (m0 > 0) stage_batch_issue<0>(row_addr, dtype, mc, sb);
         stage_batch_convert<0>(n, nch, dtype, m, sb, conv);
-        if (n > 4) {
-            stage_batch_issue<1>(row_addr, dtype, mc, sb);
-            stage_batch_convert<1>(n, nch, dtype, m, sb, conv);
-        }
+        static_for<1, NBATCH>([&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            if (n > 4 * B) {                                                 // uniform
+                stage_batch_issue<B>(row_addr, dtype, mc, sb);
+                stage_batch_convert<B>(n, nch, dtype, m, sb, conv);
+            }
+        });
     }
 }
 

@@ -109,14 +109,26 @@ hipError_t launch_down(const DownLaunch &a, hipStream_t s, const KernelEvents &e
 // proportional to their tokens); busier experts take the MFMA tiles of 32 tokens.
 constexpr int kSmallTokens = 8;
 
-// One entry of the small-expert list: everything a workgroup needs to start, in one 64-byte load.
-struct SmallRec {
+// Work of one workgroup row of the integer dot-product kernels: an expert and up to CAP of its
+// (token, slot) pairs.  The small-expert list holds CAP = kSmallTokens records (one 64-byte load
+// each); the shared-read path builds CAP = kSharedCap records inside the kernels.
+template <int CAP>
+struct TokRec {
     uint64_t blob;                                 // the expert's blob address
-    int32_t e, n, base, bits;                      // expert, tokens (1..kSmallTokens), first sorted position, code width
+    int32_t e, n, base, bits;                      // expert, pairs (1..CAP), first sorted position, code width
     int32_t pad[2];
-    int32_t pair[kSmallTokens];                    // pair index (t*K + k) of its tokens, in expert order
+    int32_t pair[CAP];                             // pair index (t*K + k) of its tokens, in expert order
 };
+using SmallRec = TokRec<kSmallTokens>;
 static_assert(sizeof(SmallRec) == 64, "SmallRec is one 64-byte record");
+
+// Shared-read path for a few tokens (2 <= T <= kSharedMaxT, T*K <= 64): the kernels derive the
+// distinct experts of the call from idx themselves (no grouping pass) and every workgroup stages
+// the activation rows of all pairs that chose its expert, so each selected expert's weights are
+// streamed once per call whatever the overlap between the tokens' selections.
+constexpr int kSharedMaxT = 16;
+constexpr int kSharedCap = 16;                     // staged rows per workgroup at most
+constexpr int kSharedMaxPairs = 64;                // T*K: one wavefront derives the records
 
 struct GroupLaunch {
     const int32_t *idx; int T, K, E;
@@ -146,6 +158,9 @@ struct GroupedLaunch {
     float *hbuf;                                   // [T*K][I] SwiGLU outputs in expert order
     float *y;                                      // [T*K][H]
     RowGeo geo; PlaneTable pt;                     // set by the small-expert launchers
+    int upw;                                       // work units per wavefront (1..8), set by the launchers
+    // shared-read path only: the routing, and the staged rows per workgroup (4..kSharedCap)
+    const int32_t *idx; int T, E, cap;
 };
 // A second stream of the device with its fork and join events (see launch_grouped_ffn).
 struct SideStream {
@@ -158,6 +173,11 @@ hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_sma
 // not fit them (everything then takes the MFMA tiles).
 bool small_path_fits(int H, int I);
 hipError_t launch_small_gateup(const GroupedLaunch &a, int max_small, hipStream_t s);
+// Shared-read path (moe_batched8.hip): gate/up then down for T*K <= kSharedMaxPairs pairs; false
+// from shared_path_fits when the staged rows and the record table do not fit in LDS.
+bool shared_path_fits(int H, int I, int E, int T);
+hipError_t launch_shared_ffn(const GroupedLaunch &a, hipStream_t s, const KernelEvents &gu_ev = {},
+                             const KernelEvents &dn_ev = {});
 hipError_t launch_small_down(const GroupedLaunch &a, int max_small, hipStream_t s);
 
 // Router + gate/up of one decode token in one launch (two groups of workgroups; the logits pass

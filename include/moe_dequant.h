@@ -340,16 +340,45 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
  *   x   device [T][H] x_dtype (normalised inside when the layer has a norm weight)
  *   idx device [T][K] int32; an entry outside [0, E) gives a zero row of y
  *   y   device [T][K][H] fp32
- * T <= 24 runs the decode matvec kernels (all K experts in one launch per phase, one grid row
- * per token); T > 24 groups the T*K (token, slot) pairs by expert (T*K <= 32768): experts with
- * more than 8 tokens run the grouped
- * dequant-GEMM (MFMA) kernels, the others integer dot-product kernels over their staged tokens.
- * The MFMA kernels run on a second stream of the device, forked from `stream` with an event and
- * joined back to it before the call returns (graph capture follows the fork); the library
- * creates that stream on the first batched call on a device and keeps it until the process
- * ends.  Errors as moe_route. */
+ * The kernels are chosen by T (moe_expert_ffn_path below names them):
+ *   T = 1, and T <= 24 when the shared-read path does not apply: MOE_FFN_PER_TOKEN;
+ *   2 <= T <= 16 with T*K <= 64: MOE_FFN_SHARED;
+ *   T > 24: MOE_FFN_GROUPED (T*K <= 32768).
+ * Errors as moe_route, and MOE_ERR_UNSUPPORTED when T*K exceeds 32768 above 24 tokens. */
 int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
                    const int32_t *idx, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_expert_ffn with the kernels chosen by the caller (same arguments, results equal within the
+ * parity tolerance whatever the path; moe_workspace_bytes(MOE_OP_EXPERT_FFN) covers every path
+ * that can take T):
+ *   MOE_FFN_AUTO       the choice moe_expert_ffn makes.
+ *   MOE_FFN_PER_TOKEN  T <= 24: the decode matvec kernels, all K experts in one launch per phase,
+ *                      one grid row per token; every token streams the experts it selected.
+ *   MOE_FFN_SHARED     2 <= T <= 16 and T*K <= 64 (and the staged rows fit in LDS: at most 16 rows
+ *                      of H and of I inputs, 2 bytes per input, plus 8 bytes per expert): each
+ *                      distinct expert of idx is streamed once for all (token, slot) pairs that
+ *                      chose it, its workgroups staging those pairs' activations.  The kernels find
+ *                      the distinct experts themselves (no grouping pass, two launches; with a norm
+ *                      weight a row-normalisation launch first).  An expert chosen by more than 16
+ *                      pairs (only possible when tokens repeat experts within their K) is streamed
+ *                      once per 16 pairs.  Motivation: the nzkcom.pages.dev page
+ *                      "flash-moe-romance-vs-utility", section on admitting geek romance, table of
+ *                      rejected optimisations, multi-token-prediction row: MoE decoding pays expert
+ *                      I/O per token, so several tokens gain only when they share the reads.
+ *   MOE_FFN_GROUPED    2 <= T, T*K <= 32768: the T*K (token, slot) pairs are grouped by expert;
+ *                      experts with more than 8 tokens run the grouped dequant-GEMM (MFMA) kernels,
+ *                      the others integer dot-product kernels over their staged tokens.  The MFMA
+ *                      kernels run on a second stream of the device, forked from `stream` with an
+ *                      event and joined back to it before the call returns (graph capture follows
+ *                      the fork); the library creates that stream on the first grouped call on a
+ *                      device and keeps it until the process ends.
+ * Errors as moe_expert_ffn; MOE_ERR_UNSUPPORTED for an unknown path or a T the path cannot take. */
+#define MOE_FFN_AUTO 0
+#define MOE_FFN_PER_TOKEN 1
+#define MOE_FFN_SHARED 2
+#define MOE_FFN_GROUPED 3
+int moe_expert_ffn_path(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
+                        const int32_t *idx, float *y, void *ws, size_t ws_bytes, int path, void *stream);
 
 /* Weighted combine: out[t][c] = sum_k w[t][k] * y[t][k][c] (+ residual[t][c]).
  *   y device [T][K][H] fp32, w device [T][K] fp32, residual device [T][H] fp32 or NULL,

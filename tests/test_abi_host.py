@@ -154,6 +154,26 @@ def test_expert_ffn_and_decode_validation(L):
                             None) == 6
     assert L.moe_expert_ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 1, None, FAKE, FAKE, need,
                             None) == 1
+    # path selection (validated before any launch): unknown paths and T outside a path's range
+    ffn = L.moe_expert_ffn_path
+    big = 1 << 30
+
+    def path_rc(T, path):
+        return ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, T, FAKE, FAKE, FAKE, big, path, None)
+    assert path_rc(4, 7) == 8 and path_rc(4, -1) == 8
+    assert path_rc(1, M.MOE_FFN_SHARED) == 8 and path_rc(17, M.MOE_FFN_SHARED) == 8
+    assert b"shared-read" in L.moe_last_error()
+    assert path_rc(25, M.MOE_FFN_PER_TOKEN) == 8 and path_rc(1, M.MOE_FFN_GROUPED) == 8
+    d8 = dims(K=8)
+    assert ffn(ctypes.byref(d8), ctypes.byref(lay), FAKE, M.MOE_F32, 9, FAKE, FAKE, FAKE, big, M.MOE_FFN_SHARED,
+               None) == 8                                          # 72 pairs: more than one wavefront
+    # the workspace covers every path that can take T: at 2..16 tokens shared-read (h of every pair,
+    # then the rows normalised), per-token (h of every pair, then the selected experts) and grouped
+    pairs_h = 4 * 2 * 256 * 4
+    assert M.moe_workspace_bytes(M.MOE_OP_EXPERT_FFN, d, 4, 1) >= max(pairs_h + 4 * 512 * 4, pairs_h + 256)
+    wsn = pairs_h + 4 * 512 * 4
+    assert ffn(ctypes.byref(d), ctypes.byref(lay), FAKE, M.MOE_F32, 4, FAKE, FAKE, FAKE, wsn - 1, M.MOE_FFN_SHARED,
+               None) == 6
     need = M.moe_workspace_bytes(M.MOE_OP_LAYER_DECODE, d, 1, 3)
     assert need > 0 and M.moe_workspace_bytes(M.MOE_OP_LAYER_DECODE, d, 2, 3) == 0
     arr = (M.moe_layer * 3)(layer(), layer(router=None), layer())
