@@ -65,6 +65,13 @@ def parse():
     p.add_argument("--cache", type=int, default=0, metavar="SLOTS",
                    help="decode with the experts in pinned host memory and SLOTS of them cached in device "
                         "memory (moe_cache_fetch before each step's expert FFN)")
+    p.add_argument("--small-t", action="store_true",
+                   help="expert FFN of 2..16 tokens on config 1, shared-read against per-token kernels, on "
+                        "router-chosen, draft-style and identical routings (one JSON line)")
+    p.add_argument("--small-t-case", default="", metavar="T:ROUTING",
+                   help="with --small-t: only this case (e.g. 16:same), for profiler runs")
+    p.add_argument("--small-t-path", default="both", choices=["both", "shared", "per_token"],
+                   help="with --small-t: the kernels to time")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run device-to-device copies of 1 GiB (reference for the HBM byte counters)")
     p.add_argument("--traffic-from", metavar="DIR",
@@ -484,8 +491,107 @@ def cache_bench(a):
     print(json.dumps(line), flush=True)
 
 
+def small_t_bench(a):
+    """Expert FFN of a few tokens (moe_expert_ffn_path): each call's T tokens with their K experts;
+    the shared-read kernels stream every distinct expert once, the per-token kernels every (token,
+    expert) pair.  Routing is fixed before the timed region (the FFN alone is timed).  Every path
+    replays a HIP graph of 64 calls that cycles through 16 batches of T tokens."""
+    import torch
+    import bit_expert_dequant_amd as M
+    import synth
+    from synth.device import build_layer, to_bf16_tensor
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[1]
+    H, I, E, K = wl.H, wl.I, wl.E, wl.K
+    d = M.make_dims(H, I, E, K)
+    dl = build_layer(wl)
+    bits = wl.expert_bits()
+    blob_bytes = np.array([wl.blob_bytes(int(b)) for b in bits], dtype=np.int64)
+    cases = [(T, kind) for T in (2, 4, 8, 16) for kind in ("router", "draft", "same")]
+    if a.small_t_case:
+        t_s, kind_s = a.small_t_case.split(":")
+        cases = [(int(t_s), kind_s)]
+    paths = {"both": ["shared", "per_token"], "shared": ["shared"], "per_token": ["per_token"]}[a.small_t_path]
+    code = {"shared": M.MOE_FFN_SHARED, "per_token": M.MOE_FFN_PER_TOKEN}
+    NB, G = 16, 64
+    R = max(1, min(a.steps, 4096) // G)          # replays of the 64-call graph per path
+    stream = torch.cuda.current_stream()
+    hip = ctypes.CDLL("libamdhip64.so")
+    out = []
+    for T, kind in cases:
+        bank_np = wl.tokens_bank(NB * T)
+        x = to_bf16_tensor(bank_np, dev).view(NB, T, H)
+        ridx = torch.empty(NB, T, K, dtype=torch.int32, device=dev)
+        rw = torch.empty(NB, T, K, dtype=torch.float32, device=dev)
+        ws_r = M.workspace(M.MOE_OP_ROUTE, d, T)
+        for b in range(NB):
+            M.moe_route(d, dl.L, x[b], ridx[b], rw[b], ws=ws_r)
+        torch.cuda.synchronize()
+        idx_np = np.stack([synth.shared_routing(kind, r, E) for r in ridx.cpu().numpy()])
+        idx = torch.from_numpy(idx_np).to(dev)
+        distinct = [np.unique(idx_np[b]) for b in range(NB)]
+        shared_bytes = float(np.mean([blob_bytes[u].sum() for u in distinct]))
+        pair_bytes = float(np.mean([blob_bytes[idx_np[b].reshape(-1)].sum() for b in range(NB)]))
+        ws = M.workspace(M.MOE_OP_EXPERT_FFN, d, T)
+        y = torch.empty(T, K, H, dtype=torch.float32, device=dev)
+        row = {"T": T, "routing": kind, "distinct_experts": float(np.mean([u.size for u in distinct])),
+               "distinct_expert_bytes": shared_bytes, "pair_bytes": pair_bytes}
+        for path in paths:
+            def call(i):
+                M.moe_expert_ffn(d, dl.L, x[i % NB], idx[i % NB], y, ws, path=code[path])
+            for i in range(max(1, min(a.warmup, 64))):
+                call(i)
+            torch.cuda.synchronize()
+            if a.no_graph:                        # eager issue (for counter runs, one record per launch)
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                for i in range(R * G):
+                    call(i)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                us = ev0.elapsed_time(ev1) * 1e3 / (R * G)
+                row[f"{path}_eager_us"] = round(us, 2)
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(G):
+                    call(i)
+            assert hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()), ctypes.c_void_p(stream.cuda_stream)) == 0
+            g.replay()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(R):
+                g.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / (R * G)
+            row[f"{path}_us"] = round(us, 2)
+            row[f"{path}_tok_s"] = round(T / (us * 1e-6), 1)
+            del g
+        if "shared_us" in row:
+            gbps = shared_bytes / (row["shared_us"] * 1e-6) / 1e9
+            row["shared_distinct_GBps"] = round(gbps, 1)
+            row["shared_frac_of_hbm"] = round(gbps / HBM_PEAK_GBPS, 4)
+        if "shared_us" in row and "per_token_us" in row:
+            row["speedup_vs_per_token"] = round(row["per_token_us"] / row["shared_us"], 3)
+        log(f"[small-t] {row}")
+        out.append(row)
+    line = {"metric": "expert_ffn_small_t", "unit": "us per call", "higher_is_better": False,
+            "data": "synthetic", "steps_per_path": R * G, "dtype": "int4 codes x 16-bit fixed-point activations",
+            "config": {"workload": wl.name.split(",")[0], "H": H, "I": I, "E": E, "K": K,
+                       "timed": "moe_expert_ffn_path only (routing fixed beforehand)"},
+            "cases": out}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.small_t:
+        small_t_bench(a)
+        return
     if a.cache:
         cache_bench(a)
         return

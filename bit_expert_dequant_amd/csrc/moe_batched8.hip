@@ -30,6 +30,7 @@ namespace {
 // is dn8_rg wave instructions of rows (8 KiB at I = 1024).
 constexpr int kGuUPW = 8, kGuNB = 3;
 constexpr int kDnUPW = 8, kDnNB = 3;
+constexpr int kSharedUPW = 2;             // shared-read path: every unit's loads issued up front
 template <int NJ>
 __host__ __device__ constexpr int dn8_rg() { return NJ >= 4 ? 2 : NJ == 2 ? 4 : 8; }
 
@@ -50,10 +51,10 @@ struct DigitStage {
 // GS: lanes per row group when it is a compile-time 32 or 64 and every lane's slots exist, else 0
 // (run-time group size, idle slots masked).
 // Units of one workgroup: slice `sl` of an expert's matrix takes units [sl, sl + 1) * kWaves * upw;
-// unit i of a wave is ub + i * kWaves, nu of them (0 for a wave past the matrix).  The small-expert
-// list runs with sl = blockIdx.x and upw = kGuUPW / kDnUPW (GUARD false); the shared-read path
-// sizes both per expert (GUARD true: the loads past nu are skipped).
-template <int BITS, int NJ, int GS, bool GUARD, int CAP>
+// unit i of a wave is ub + i * kWaves, nu of them (0 for a wave past the matrix), upw <= UPW (the
+// unrolled pipeline's length).  The small-expert list runs with sl = blockIdx.x and upw = UPW =
+// kGuUPW / kDnUPW; the shared-read path sizes both per expert, with UPW = kSharedUPW.
+template <int BITS, int NJ, int GS, int UPW, int CAP>
 __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CAP> &se, int sl, int upw,
                                          uint32_t *lds) {
     constexpr int RG = gu_rg<NJ>();
@@ -82,7 +83,7 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
 
     // 3. units: each loaded unit meets every token
     const int rd = row_dw(H);
-    unit_pipeline<kGuUPW, kGuNB, GUARD>(nu, L, issue, [&](int i, const GULoads<NJ, RG> &B) {
+    unit_pipeline<UPW>(nu, L, issue, [&](int i, const GULoads<NJ, RG> &B) {
         const int r0 = r0_of(i);
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
@@ -133,8 +134,8 @@ __global__ void __launch_bounds__(kBlock) k_gu8(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     SmallRec se;
     if (!small_entry(a, se)) return;
-    if (se.bits == 2) gu8_body<2, NJ, GS, false>(a, se, blockIdx.x, kGuUPW, lds);
-    else gu8_body<4, NJ, GS, false>(a, se, blockIdx.x, kGuUPW, lds);
+    if (se.bits == 2) gu8_body<2, NJ, GS, kGuUPW>(a, se, blockIdx.x, kGuUPW, lds);
+    else gu8_body<4, NJ, GS, kGuUPW>(a, se, blockIdx.x, kGuUPW, lds);
 }
 
 // --------------------------------------------------------------------------- down
@@ -159,7 +160,7 @@ __device__ __forceinline__ void dn8_issue(const Planes &pl, const Geo &g, int H,
     }
 }
 
-template <int BITS, int NJ, int GS, bool GUARD, int CAP>
+template <int BITS, int NJ, int GS, int UPW, int CAP>
 __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CAP> &se, int sl, int upw,
                                          uint32_t *lds) {
     constexpr int RG = dn8_rg<NJ>();
@@ -187,7 +188,7 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CA
 
     // 3. units
     const int rd = row_dw(I);
-    unit_pipeline<kDnUPW, kDnNB, GUARD>(nu, L, issue, [&](int i, const D8Loads<NJ, RG> &B) {
+    unit_pipeline<UPW>(nu, L, issue, [&](int i, const D8Loads<NJ, RG> &B) {
         const int r0 = r0_of(i);
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
@@ -229,8 +230,8 @@ __global__ void __launch_bounds__(kBlock) k_dn8(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     SmallRec se;
     if (!small_entry(a, se)) return;
-    if (se.bits == 2) dn8_body<2, NJ, GS, false>(a, se, blockIdx.x, kDnUPW, lds);
-    else dn8_body<4, NJ, GS, false>(a, se, blockIdx.x, kDnUPW, lds);
+    if (se.bits == 2) dn8_body<2, NJ, GS, kDnUPW>(a, se, blockIdx.x, kDnUPW, lds);
+    else dn8_body<4, NJ, GS, kDnUPW>(a, se, blockIdx.x, kDnUPW, lds);
 }
 
 // --------------------------------------------------------------------------- shared-read path
@@ -238,26 +239,29 @@ __global__ void __launch_bounds__(kBlock) k_dn8(GroupedLaunch a) {
 // every workgroup derives the call's distinct experts from idx by itself.  Each valid pair marks a
 // two-word LDS entry of its expert (first pair, pair count) with LDS atomics, so the pairs that
 // their entry names first stand for the distinct experts, in order of first appearance.  Expert d
-// with its pairs in pair order is one entry of the work list (an expert with more than `cap` pairs
-// becomes several entries of at most cap pairs, each streaming the expert once); its rows of the
-// expert-ordered h buffer start after the pairs of the experts that appear before it.  The grid's
-// workgroups are dealt round-robin over the entries; an entry's workgroups (slices) split its
-// matrix, with enough units per wave that a slice's weight stream outweighs the staging of its
-// rows.  Gate/up and down derive the same entries, so the h rows match between them.
+// with its pairs in pair order is one entry of the work list (an expert with more than 2 * cap pairs
+// becomes several entries of at most that many, each streaming the expert once); its rows
+// of the expert-ordered h buffer start after the pairs of the experts that appear before it.  The
+// grid's workgroups are dealt round-robin over the entries, and an entry's workgroups split its
+// matrix into as many slices as there are of them (one or two units per wave: with many rows per
+// expert the dot products, not the weight stream, set the pace).  Gate/up and down derive the same
+// entries, so the h rows match between them.  A workgroup stages at most `cap` (4 or 8) of its
+// entry's rows at a time and makes one pass over its units per batch of rows: the second pass reads
+// the slice's weights again from L2.
 struct SharedWork {
-    TokRec<kSharedCap> r;
+    uint64_t blob;
+    int n, base, bits;      // the entry's pairs (1..kSharedCap), first h row, code width
     int sl, upw;            // slice of the expert's matrix and units per wave (upw 0: no work)
     uint64_t inval;         // pairs whose index is outside [0, E) or whose expert is absent
+    const uint32_t *pairs;  // LDS: the entry's pairs in pair order
 };
 constexpr int kSharedRecDw = 32;
 __host__ __device__ __forceinline__ int shared_rec_off(int cols, int cap, int E) {
     const int st = cap * row_dw(cols), tb = 2 * E;
     return ((st > tb ? st : tb) + 3) & ~3;
 }
-__host__ __device__ __forceinline__ int shared_cap(int T) {
-    const int c = (T + 3) & ~3;
-    return c < kSharedCap ? c : kSharedCap;
-}
+// Rows a workgroup stages at a time: 4 for up to four tokens, else 8.
+__host__ __device__ __forceinline__ int shared_cap(int T) { return T <= 4 ? 4 : kSmallTokens; }
 
 __device__ __forceinline__ int mbcnt64(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -269,7 +273,7 @@ __device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, in
                                             SharedWork &w) {
     uint32_t *rec = lds + rec_off;
     if (threadIdx.x < 64) {
-        const int lane = threadIdx.x, P = a.T * a.K, cap = a.cap;
+        const int lane = threadIdx.x, P = a.T * a.K;
         int e = -1, bits = 4;
         uint64_t blob = 0;
         if (lane < P) {
@@ -297,14 +301,15 @@ __device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, in
         }
         const bool is_first = valid && first == lane;
         const uint64_t fm = __ballot(is_first);
-        const uint64_t big = __ballot(is_first && cnt > cap);
-        // entries: one per distinct expert, or ceil(cnt / cap) when some expert has more than cap pairs
+        const int C = 2 * a.cap;        // pairs per entry: two batches of staged rows
+        const uint64_t big = __ballot(is_first && cnt > C);
+        // entries: one per distinct expert, or ceil(cnt / C) when some expert has more pairs
         int nent = __popcll(fm);
         if (big) {
             nent = 0;
             for (uint64_t m = fm; m; m &= m - 1) {
                 const int l = __ffsll((unsigned long long)m) - 1;
-                nent += (__builtin_amdgcn_readlane(cnt, l) + cap - 1) / cap;
+                nent += (__builtin_amdgcn_readlane(cnt, l) + C - 1) / C;
             }
         }
         int f = 0, c = 0, n = 0, base = 0, sl = 0, upw = 0, pe = 0, pbits = 4;
@@ -320,7 +325,7 @@ __device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, in
                 int acc = 0;
                 for (uint64_t m = fm; m; m &= m - 1) {
                     const int l = __ffsll((unsigned long long)m) - 1;
-                    const int nch = (__builtin_amdgcn_readlane(cnt, l) + cap - 1) / cap;
+                    const int nch = (__builtin_amdgcn_readlane(cnt, l) + C - 1) / C;
                     if (j < acc + nch) {
                         f = l;
                         c = j - acc;
@@ -334,17 +339,16 @@ __device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, in
                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)blob, f);
             pbits = __builtin_amdgcn_readlane(bits, f);
             uint64_t m = __ballot(valid && e == pe);
-            n = min(cap, __popcll(m) - c * cap);
-            base = __popcll(__ballot(valid && first < f)) + c * cap;
-            for (int q = 0; q < c * cap; ++q) m &= m - 1;
+            n = min(C, __popcll(m) - c * C);
+            base = __popcll(__ballot(valid && first < f)) + c * C;
+            for (int q = 0; q < c * C; ++q) m &= m - 1;
 #pragma unroll
             for (int t = 0; t < kSharedCap; ++t) {
                 pairs[t] = t < n ? (uint32_t)(__ffsll((unsigned long long)m) - 1) : pairs[t > 0 ? t - 1 : 0];
                 if (t < n) m &= m - 1;
             }
-            // slices: at least (n + 1) / 2 units per wave, at most the workgroups this entry has
-            const int want = max(1, min(kGuUPW, (n + 1) / 2));
-            const int nsl = min(avail, (nblk + kWaves * want - 1) / (kWaves * want));
+            // slices: as many as the entry has workgroups, down to one unit per wave
+            const int nsl = min(avail, (nblk + kWaves - 1) / kWaves);
             if (s < nsl) {
                 sl = s;
                 upw = (nblk + kWaves * nsl - 1) / (kWaves * nsl);
@@ -370,28 +374,58 @@ __device__ __forceinline__ void shared_work(const GroupedLaunch &a, int nblk, in
     // readfirstlane returns int: take the word back as unsigned before widening it into a 64-bit
     // address or mask (a sign-extended low word would corrupt the upper half)
     auto rd = [&](int i) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)rec[i]); };
-    w.r.blob = ((uint64_t)rd(1) << 32) | rd(0);
-    w.r.e = (int)rd(2);
-    w.r.n = (int)rd(3);
-    w.r.base = (int)rd(4);
-    w.r.bits = (int)rd(5);
+    w.blob = ((uint64_t)rd(1) << 32) | rd(0);
+    w.n = (int)rd(3);
+    w.base = (int)rd(4);
+    w.bits = (int)rd(5);
     w.sl = (int)rd(6);
     w.upw = (int)rd(7);
     w.inval = ((uint64_t)rd(9) << 32) | rd(8);
-#pragma unroll
-    for (int t = 0; t < kSharedCap; ++t) w.r.pair[t] = (int)rd(10 + t);
+    w.pairs = rec + 10;
 }
 
+// Rows tb .. tb + cap - 1 of an entry as a record of its own (tb a multiple of cap, uniform); the
+// pairs come from the entry's LDS record.
+__device__ __forceinline__ void row_batch(const SharedWork &w, int tb, int cap, TokRec<kSmallTokens> &o) {
+    o.blob = w.blob;
+    o.e = 0;
+    o.bits = w.bits;
+    o.n = min(cap, w.n - tb);
+    o.base = w.base + tb;
+#pragma unroll
+    for (int t = 0; t < kSmallTokens; ++t)
+        o.pair[t] = __builtin_amdgcn_readfirstlane((int)w.pairs[min(tb + min(t, o.n - 1), kSharedCap - 1)]);
+}
+
+// An entry's rows in at most two batches of `cap`, written out rather than looped: a loop around the
+// body keeps its hoisted addresses live throughout and spills.
+template <int NJ, int GS>
+__device__ __forceinline__ void gu_batch(const GroupedLaunch &a, const SharedWork &w, int tb, uint32_t *lds) {
+    TokRec<kSmallTokens> r;
+    row_batch(w, tb, a.cap, r);
+    if (r.bits == 2) gu8_body<2, NJ, GS, kSharedUPW>(a, r, w.sl, w.upw, lds);
+    else gu8_body<4, NJ, GS, kSharedUPW>(a, r, w.sl, w.upw, lds);
+}
 template <int NJ, int GS>
 __global__ void __launch_bounds__(kBlock) k_gu_sh(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     SharedWork w;
     shared_work(a, a.geo.nblk, shared_rec_off(a.H, a.cap, a.E), lds, w);
     if (w.upw == 0) return;
-    if (w.r.bits == 2) gu8_body<2, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
-    else gu8_body<4, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
+    gu_batch<NJ, GS>(a, w, 0, lds);
+    if (w.n > a.cap) {
+        __syncthreads();                          // the first batch's rows are no longer read
+        gu_batch<NJ, GS>(a, w, a.cap, lds);
+    }
 }
 
+template <int NJ, int GS>
+__device__ __forceinline__ void dn_batch(const GroupedLaunch &a, const SharedWork &w, int tb, uint32_t *lds) {
+    TokRec<kSmallTokens> r;
+    row_batch(w, tb, a.cap, r);
+    if (r.bits == 2) dn8_body<2, NJ, GS, kSharedUPW>(a, r, w.sl, w.upw, lds);
+    else dn8_body<4, NJ, GS, kSharedUPW>(a, r, w.sl, w.upw, lds);
+}
 template <int NJ, int GS>
 __global__ void __launch_bounds__(kBlock) k_dn_sh(GroupedLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
@@ -403,8 +437,11 @@ __global__ void __launch_bounds__(kBlock) k_dn_sh(GroupedLaunch a) {
         for (int c = blockIdx.x * kBlock + threadIdx.x; c < a.H; c += gridDim.x * kBlock) yr[c] = 0.f;
     }
     if (w.upw == 0) return;
-    if (w.r.bits == 2) dn8_body<2, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
-    else dn8_body<4, NJ, GS, true>(a, w.r, w.sl, w.upw, lds);
+    dn_batch<NJ, GS>(a, w, 0, lds);
+    if (w.n > a.cap) {
+        __syncthreads();
+        dn_batch<NJ, GS>(a, w, a.cap, lds);
+    }
 }
 
 // Compile-time group size for rows of `cols` inputs taken NJ slots per lane: 32 or 64 when every
@@ -486,10 +523,10 @@ hipError_t launch_small_down(const GroupedLaunch &a_in, int max_small, hipStream
 
 namespace {
 size_t shared_lds_bytes(int cols, int cap, int E) { return ((size_t)shared_rec_off(cols, cap, E) + kSharedRecDw) * 4; }
-// Workgroups of a shared-read launch: every entry (at most P of them) gets enough slices to keep
-// its units per wave within the unrolled pipeline, and the grid fills the chip at least twice.
-int shared_grid(int nblk, int upw_max, int P) {
-    const int per = (nblk + kWaves * upw_max - 1) / (kWaves * upw_max);
+// Workgroups of a shared-read launch: every entry (at most P of them) gets enough slices for at
+// most kSharedUPW units per wave, and the grid fills the chip at least twice.
+int shared_grid(int nblk, int P) {
+    const int per = (nblk + kWaves * kSharedUPW - 1) / (kWaves * kSharedUPW);
     return std::max(P * per, 512);
 }
 }  // namespace
@@ -509,7 +546,7 @@ hipError_t launch_shared_ffn(const GroupedLaunch &a_in, hipStream_t s, const Ker
     {
         a.geo = gateup_geo(a.H, a.I);
         a.upw = 0;
-        const dim3 grid(shared_grid(a.geo.nblk, kGuUPW, P));
+        const dim3 grid(shared_grid(a.geo.nblk, P));
         const size_t lds = shared_lds_bytes(a.H, a.cap, a.E);
         const int nj = nj_for(a.H), gs = small_gs(a.H, nj);
         hipError_t e;
@@ -529,7 +566,7 @@ hipError_t launch_shared_ffn(const GroupedLaunch &a_in, hipStream_t s, const Ker
     }
     const int nj = nj_for(a.I), gs = small_gs(a.I, nj);
     a.geo = row_geo(a.I, a.H, nj == 1 ? dn8_rg<1>() : nj == 2 ? dn8_rg<2>() : dn8_rg<4>());
-    const dim3 grid(shared_grid(a.geo.nblk, kDnUPW, P));
+    const dim3 grid(shared_grid(a.geo.nblk, P));
     const size_t lds = shared_lds_bytes(a.I, a.cap, a.E);
     switch (nj) {
         case 1:

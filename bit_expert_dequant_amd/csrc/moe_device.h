@@ -934,18 +934,15 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // The unit pipeline of one wave: UPW units, NB register buffers, the loads of unit i + NB - 1 issued
 // before unit i is finished, so NB - 1 units are in flight while one is computed.  Fully unrolled
-// (buffer indices are compile-time).  Without GUARD it is branch-free around the loads: a wave with
-// fewer than UPW units (the ragged end of a matrix) re-reads its last unit's rows instead, and only
-// the finishing step is skipped.  With GUARD (waves whose unit count is usually well below UPW) the
-// loads past the wave's nu units are skipped too, by a wave-uniform branch.  issue(i, buf) must
-// clamp i itself.
-template <int UPW, int NB, bool GUARD = false, typename Buf, typename Issue, typename Finish>
+// (buffer indices are compile-time) and branch-free around the loads: a wave with fewer than UPW
+// units (the ragged end of a matrix) re-reads its last unit's rows instead, and only the finishing
+// step is skipped.  (Skipping those loads behind a branch instead keeps every buffer live across
+// the branch and spills.)  issue(i, buf) must clamp i itself.
+template <int UPW, int NB, typename Buf, typename Issue, typename Finish>
 __device__ __forceinline__ void unit_pipeline(int nu, Buf (&B)[NB], Issue &&issue, Finish &&finish) {
     static_for<0, UPW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i + NB - 1 < UPW) {
-            if (!GUARD || i + NB - 1 < nu) issue(i + NB - 1, B[(i + NB - 1) % NB]);
-        }
+        if constexpr (i + NB - 1 < UPW) issue(i + NB - 1, B[(i + NB - 1) % NB]);
         if (i < nu) finish(i, B[i % NB]);
     });
 }

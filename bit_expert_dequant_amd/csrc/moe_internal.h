@@ -127,7 +127,7 @@ static_assert(sizeof(SmallRec) == 64, "SmallRec is one 64-byte record");
 // the activation rows of all pairs that chose its expert, so each selected expert's weights are
 // streamed once per call whatever the overlap between the tokens' selections.
 constexpr int kSharedMaxT = 16;
-constexpr int kSharedCap = 16;                     // staged rows per workgroup at most
+constexpr int kSharedCap = 16;                     // pairs of one expert per workgroup record
 constexpr int kSharedMaxPairs = 64;                // T*K: one wavefront derives the records
 
 struct GroupLaunch {
@@ -159,7 +159,7 @@ struct GroupedLaunch {
     float *y;                                      // [T*K][H]
     RowGeo geo; PlaneTable pt;                     // set by the small-expert launchers
     int upw;                                       // work units per wavefront (1..8), set by the launchers
-    // shared-read path only: the routing, and the staged rows per workgroup (4..kSharedCap)
+    // shared-read path only: the routing, and the rows a workgroup stages at a time (4 or 8)
     const int32_t *idx; int T, E, cap;
 };
 // A second stream of the device with its fork and join events (see launch_grouped_ffn).

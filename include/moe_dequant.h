@@ -354,14 +354,14 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
  *   MOE_FFN_AUTO       the choice moe_expert_ffn makes.
  *   MOE_FFN_PER_TOKEN  T <= 24: the decode matvec kernels, all K experts in one launch per phase,
  *                      one grid row per token; every token streams the experts it selected.
- *   MOE_FFN_SHARED     2 <= T <= 16 and T*K <= 64 (and the staged rows fit in LDS: at most 16 rows
- *                      of H and of I inputs, 2 bytes per input, plus 8 bytes per expert): each
+ *   MOE_FFN_SHARED     2 <= T <= 16 and T*K <= 64 (and the staged rows fit in LDS: 8 rows (4 when
+ *                      T <= 4) of H and of I inputs at 2.25 bytes per input, and 8 bytes per expert): each
  *                      distinct expert of idx is streamed once for all (token, slot) pairs that
  *                      chose it, its workgroups staging those pairs' activations.  The kernels find
  *                      the distinct experts themselves (no grouping pass, two launches; with a norm
  *                      weight a row-normalisation launch first).  An expert chosen by more than 16
- *                      pairs (only possible when tokens repeat experts within their K) is streamed
- *                      once per 16 pairs.  Motivation: the nzkcom.pages.dev page
+ *                      pairs (8 when T <= 4; only possible when tokens repeat experts within their
+ *                      K) is streamed once per 16 (8) pairs.  Motivation: the nzkcom.pages.dev page
  *                      "flash-moe-romance-vs-utility", section on admitting geek romance, table of
  *                      rejected optimisations, multi-token-prediction row: MoE decoding pays expert
  *                      I/O per token, so several tokens gain only when they share the reads.

@@ -245,6 +245,29 @@ class Workload:
         return token_bank(self.seed, n, self.H, self.x_bf16)
 
 
+def shared_routing(kind: str, base: np.ndarray, E: int) -> np.ndarray:
+    """Routings of a few tokens for the shared-read measurements, built from the router's choice
+    `base` [T][K] on the same tokens: "router" keeps it; "draft" gives every token the first token's
+    first K-1 experts and one expert of its own (draft tokens of a speculative step that agree on
+    most experts); "same" gives every token the first token's K experts."""
+    T, K = base.shape
+    if kind == "router":
+        return base.astype(np.int32).copy()
+    if kind not in ("draft", "same"):
+        raise ValueError(f"unknown routing {kind!r}")
+    shared = [int(e) for e in base[0]]
+    idx = np.empty((T, K), dtype=np.int32)
+    for t in range(T):
+        if kind == "same":
+            idx[t] = shared
+            continue
+        own = (shared[-1] + 37 * t) % E
+        while own in shared[:-1]:
+            own = (own + 1) % E
+        idx[t] = shared[:-1] + [own]
+    return idx
+
+
 WORKLOADS: Dict[int, Workload] = {
     0: Workload("tiny: H512 I256 E8 top2, 4-bit, fp32 router and x", 0, 512, 256, 8, 2,
                 router_bf16=False, x_bf16=False),

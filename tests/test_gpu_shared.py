@@ -50,23 +50,6 @@ def check_rows(wl, ol, x64, idx_h, y, what, absent=()):
             assert_close(y[t, k], outs[key], f"{what}: token {t} slot {k} expert {e}")
 
 
-def routing(kind, base, T, K, E):
-    """Caller-side routings built from the router's choice `base` [T][K] on the same tokens."""
-    if kind == "router":
-        return base.copy()
-    idx = np.empty((T, K), dtype=np.int32)
-    shared = [int(e) for e in base[0]]
-    for t in range(T):
-        if kind == "same":
-            idx[t] = shared
-        else:                                     # "draft": K-1 experts shared, the last one per token
-            own = (shared[-1] + 37 * t) % E
-            while own in shared[:-1]:
-                own = (own + 1) % E
-            idx[t] = shared[:-1] + [own]
-    return idx
-
-
 @pytest.fixture(scope="module")
 def cfg1():
     wl = synth.WORKLOADS[1]
@@ -97,7 +80,7 @@ def test_shared_read_config1(cfg1, T, kind):
         for t in range(T):
             ri, _, margin = oracle.route(oracle.router_logits(ol.router, x64[t], ol.logit_bias, wl.router_bf16), wl.K)
             assert margin > MIN_MARGIN and list(base[t]) == list(ri), f"token {t}"
-    idx_h = routing(kind, base, T, wl.K, wl.E)
+    idx_h = synth.shared_routing(kind, base, wl.E)
     idx = torch.from_numpy(idx_h).to("cuda")
     y = run_ffn(d, dl, x, idx, M.MOE_FFN_SHARED)
     say(f"[shared]   {len(set(idx_h.reshape(-1).tolist()))} distinct experts over {T * wl.K} pairs")
