@@ -91,9 +91,10 @@ KERNEL_SOURCES = {
     "k_router_mfma": "moe_grouped.hip", "k_group": "moe_grouped.hip", "k_gu_mfma": "moe_grouped.hip",
     "k_dn_mfma": "moe_grouped.hip", "k_dn_res": "moe_grouped.hip",
     "k_gu8": "moe_batched8.hip", "k_dn8": "moe_batched8.hip",
+    "k_stage_rows": "moe_shared_gu.hip", "k_gu_sh": "moe_shared_gu.hip", "k_dn_sh": "moe_shared_dn.hip",
     "k_quantize": "moe_quant.hip", "k_requant": "moe_tier.hip",
 }
-SHARED_HEADERS = ("moe_device.h", "moe_internal.h", "moe_handoff.h")
+SHARED_HEADERS = ("moe_device.h", "moe_internal.h", "moe_handoff.h", "moe_small.h")
 
 
 def source_hash(kernel: str = "") -> str:

@@ -178,21 +178,28 @@ constexpr int kMaxGroupedPairs = 32768;   // the grouping kernel keeps every pai
 constexpr int kPerTokenMaxT = 24;
 bool grouped_ffn(int T) { return T > kPerTokenMaxT; }
 // From 2 to kSharedMaxT tokens (T*K <= kSharedMaxPairs) the shared-read kernels stream each
-// selected expert once for all the pairs that chose it.
+// selected expert once for all the pairs that chose it; the automatic choice takes them from
+// kSharedAutoMinT tokens.  Measured on the config-1 layer (H4096 I1024 E512 K4), per call, shared-read
+// against per-token: 25.2 / 21.1 us at 2 tokens (router's choice), 32.1 / 31.9 at 4 (all tokens on
+// the same 4 experts), 53.2 / 57.8 at 8 (router), 83.0 / 106.9 at 16 (router), 79.7 / 100.3 at 16
+// (same experts): below 8 tokens the per-token kernels' shorter prologue wins even with overlap.
+constexpr int kSharedAutoMinT = 8;
 bool shared_ffn(const moe_dims *d, int T) {
     return T >= 2 && T <= moe::kSharedMaxT && T * d->top_k <= moe::kSharedMaxPairs &&
            moe::shared_path_fits(d->hidden, d->inter, d->n_experts, T);
 }
-// Shared-read workspace: SwiGLU outputs of every pair in expert order, then the normalised rows.
+// Shared-read workspace: SwiGLU outputs of every pair in expert order, then the activation rows
+// staged as digit planes in both code widths.
 struct SharedWs {
-    float *hbuf, *xn;
+    float *hbuf;
+    uint32_t *planes;
     size_t bytes;
 };
 SharedWs shared_ws(const moe_dims *d, int T, void *base) {
     Carve c{(char *)base};
     SharedWs r;
     r.hbuf = c.take<float>((size_t)T * d->top_k * d->inter);
-    r.xn = c.take<float>((size_t)T * d->hidden);
+    r.planes = c.take<uint32_t>((size_t)T * (d->hidden + d->hidden / 16));
     r.bytes = c.off;
     return r;
 }
@@ -208,7 +215,7 @@ int ffn_path(const moe_dims *d, int T, int path) {
     switch (path) {
         case MOE_FFN_AUTO:
             if (grouped_ffn(T)) return T * d->top_k <= kMaxGroupedPairs ? MOE_FFN_GROUPED : -1;
-            return shared_ffn(d, T) ? MOE_FFN_SHARED : MOE_FFN_PER_TOKEN;
+            return T >= kSharedAutoMinT && shared_ffn(d, T) ? MOE_FFN_SHARED : MOE_FFN_PER_TOKEN;
         case MOE_FFN_PER_TOKEN: return T <= kPerTokenMaxT ? path : -1;
         case MOE_FFN_SHARED: return shared_ffn(d, T) ? path : -1;
         case MOE_FFN_GROUPED: return T >= 2 && T * d->top_k <= kMaxGroupedPairs ? path : -1;
@@ -528,17 +535,9 @@ int moe_expert_ffn_path(const moe_dims *dims, const moe_layer *layer, const void
     }
     if (run == MOE_FFN_SHARED) {
         SharedWs sw = shared_ws(dims, T, ws);
-        const void *xa = x;
-        int xdt = x_dtype;
-        if (layer->norm_w) {
-            if (int s = MOE_LAUNCH(moe::launch_norm_rows(x, x_dtype, layer->norm_w, layer->norm_eps, dims->hidden, T,
-                                                       sw.xn, st), "norm"))
-                return s;
-            xa = sw.xn;
-            xdt = MOE_F32;
-        }
-        moe::GroupedLaunch ga{xa, xdt, dims->hidden, dims->inter, dims->top_k, layer->experts, nullptr, nullptr,
-                              nullptr, nullptr, nullptr, nullptr, sw.hbuf, y, {}, {}, 0, idx, T, dims->n_experts, 0};
+        moe::GroupedLaunch ga{x, x_dtype, dims->hidden, dims->inter, dims->top_k, layer->experts, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, nullptr, sw.hbuf, y, {}, {}, 0, idx, T, dims->n_experts, 0, 0,
+                              layer->norm_w, layer->norm_eps, sw.planes};
         if (int s = MOE_LAUNCH(moe::launch_shared_ffn(ga, st), "shared-read ffn")) return s;
         return ok();
     }

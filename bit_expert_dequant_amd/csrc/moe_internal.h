@@ -159,8 +159,12 @@ struct GroupedLaunch {
     float *y;                                      // [T*K][H]
     RowGeo geo; PlaneTable pt;                     // set by the small-expert launchers
     int upw;                                       // work units per wavefront (1..8), set by the launchers
-    // shared-read path only: the routing, and the rows a workgroup stages at a time (4 or 8)
-    const int32_t *idx; int T, E, cap;
+    // shared-read path only: the routing, the rows a gate/up (4 or 8) and a down (cap or 2 cap)
+    // workgroup stages at a time, the
+    // layer's norm weight, and the pre-staged rows [T][H + H/16]
+    const int32_t *idx; int T, E, cap, cap_dn;
+    const uint16_t *norm_w; float norm_eps;
+    uint32_t *planes;
 };
 // A second stream of the device with its fork and join events (see launch_grouped_ffn).
 struct SideStream {
@@ -176,6 +180,8 @@ hipError_t launch_small_gateup(const GroupedLaunch &a, int max_small, hipStream_
 // Shared-read path (moe_batched8.hip): gate/up then down for T*K <= kSharedMaxPairs pairs; false
 // from shared_path_fits when the staged rows and the record table do not fit in LDS.
 bool shared_path_fits(int H, int I, int E, int T);
+// The staging and gate/up launches of the path (moe_shared_gu.hip); a.cap, a.geo and a.pt set.
+hipError_t launch_shared_gateup(const GroupedLaunch &a, hipStream_t s, const KernelEvents &ev);
 hipError_t launch_shared_ffn(const GroupedLaunch &a, hipStream_t s, const KernelEvents &gu_ev = {},
                              const KernelEvents &dn_ev = {});
 hipError_t launch_small_down(const GroupedLaunch &a, int max_small, hipStream_t s);

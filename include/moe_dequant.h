@@ -341,8 +341,8 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
  *   idx device [T][K] int32; an entry outside [0, E) gives a zero row of y
  *   y   device [T][K][H] fp32
  * The kernels are chosen by T (moe_expert_ffn_path below names them):
- *   T = 1, and T <= 24 when the shared-read path does not apply: MOE_FFN_PER_TOKEN;
- *   2 <= T <= 16 with T*K <= 64: MOE_FFN_SHARED;
+ *   T < 8, and T <= 24 when the shared-read path does not apply: MOE_FFN_PER_TOKEN;
+ *   8 <= T <= 16 with T*K <= 64: MOE_FFN_SHARED (faster from 8 tokens on, measured);
  *   T > 24: MOE_FFN_GROUPED (T*K <= 32768).
  * Errors as moe_route, and MOE_ERR_UNSUPPORTED when T*K exceeds 32768 above 24 tokens. */
 int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
@@ -355,11 +355,12 @@ int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, 
  *   MOE_FFN_PER_TOKEN  T <= 24: the decode matvec kernels, all K experts in one launch per phase,
  *                      one grid row per token; every token streams the experts it selected.
  *   MOE_FFN_SHARED     2 <= T <= 16 and T*K <= 64 (and the staged rows fit in LDS: 8 rows (4 when
- *                      T <= 4) of H and of I inputs at 2.25 bytes per input, and 8 bytes per expert): each
- *                      distinct expert of idx is streamed once for all (token, slot) pairs that
- *                      chose it, its workgroups staging those pairs' activations.  The kernels find
- *                      the distinct experts themselves (no grouping pass, two launches; with a norm
- *                      weight a row-normalisation launch first).  An expert chosen by more than 16
+ *                      T <= 4) of H and of I inputs at 2.25 bytes per input, and 8 bytes per
+ *                      expert): each distinct expert of idx is streamed once for all (token, slot)
+ *                      pairs that chose it, its workgroups staging those pairs' activations.  Three
+ *                      launches: the T rows (normalised when the layer has a norm weight) converted
+ *                      once to the kernels' 16-bit fixed-point layout, then gate/up and down, which
+ *                      find the distinct experts themselves (no grouping pass).  An expert chosen by more than 16
  *                      pairs (8 when T <= 4; only possible when tokens repeat experts within their
  *                      K) is streamed once per 16 (8) pairs.  Motivation: the nzkcom.pages.dev page
  *                      "flash-moe-romance-vs-utility", section on admitting geek romance, table of
