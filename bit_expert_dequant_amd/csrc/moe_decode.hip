@@ -444,17 +444,12 @@ PlaneTable plane_table(int H, int I) {
 size_t gateup_lds_bytes(int H) { return ((size_t)H + H / 16) * 4; }   // both orders + xs
 size_t down_lds_bytes(int I, int K) { return (size_t)K * down_lds_per_expert(I) * 4; }
 
-static hipError_t set_lds(const void *fn, size_t lds) {
-    if (lds <= 64 * 1024) return hipSuccess;
-    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
 template <int RDT, bool SPLIT>
 static hipError_t router_impl(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev) {
     dim3 grid((a.E + kWaves - 1) / kWaves, a.T);
     const size_t lds = (size_t)a.H * 4;
     auto fn = k_router<RDT, SPLIT>;
-    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    if (hipError_t e = lds_for<k_router<RDT, SPLIT>>(lds)) return e;
     return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
@@ -477,7 +472,7 @@ static hipError_t gateup_impl_np(const GateUpLaunch &a, hipStream_t s, const Ker
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = gateup_lds_bytes(a.H);
     auto fn = k_gateup<NJ, NP>;
-    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    if (hipError_t e = lds_for<k_gateup<NJ, NP>>(lds)) return e;
     return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 
@@ -503,7 +498,7 @@ static hipError_t down_impl_k(const DownLaunch &a, hipStream_t s, const KernelEv
     dim3 grid((units + kWaves - 1) / kWaves, a.T);
     const size_t lds = down_lds_bytes(a.I, a.K);
     auto fn = k_down<NJ, COMBINE, KM>;
-    if (hipError_t e = set_lds((const void *)fn, lds)) return e;
+    if (hipError_t e = lds_for<k_down<NJ, COMBINE, KM>>(lds)) return e;
     return dispatch(fn, grid, dim3(kBlock), lds, s, ev, a);
 }
 

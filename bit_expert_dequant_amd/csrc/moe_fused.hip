@@ -373,10 +373,7 @@ template <int NP, int NJ, int DNJ, int KM>
 struct RunLaunch {
     static hipError_t run(const FusedLaunch &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
         auto fn = k_layer<NP, NJ, DNJ, KM>;
-        if (lds > 64 * 1024)
-            if (hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)lds))
-                return e;
+        if (hipError_t e = lds_for<k_layer<NP, NJ, DNJ, KM>>(lds)) return e;
         return dispatch(fn, dim3(a.nw), dim3(kBlock), lds, s, ev, a);
     }
 };
@@ -384,10 +381,7 @@ template <int NP, int NJ, int DNJ, int KM>
 struct RunOcc {
     static hipError_t run(int *blocks, size_t lds) {
         auto fn = k_layer<NP, NJ, DNJ, KM>;
-        if (lds > 64 * 1024)
-            if (hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)lds))
-                return e;
+        if (hipError_t e = lds_for<k_layer<NP, NJ, DNJ, KM>>(lds)) return e;
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fn, kBlock, lds);
     }
 };

@@ -751,10 +751,7 @@ size_t group_lds_bytes(int T, int K, int E) { return ((size_t)pow2_at_least(T * 
 hipError_t launch_group(const GroupLaunch &a, hipStream_t s) {
     if (grouped_max_tiles(a.T, a.K, a.E) >= (1 << 16)) return hipErrorInvalidValue;   // packed scan word
     const size_t lds = group_lds_bytes(a.T, a.K, a.E);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_group, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    if (hipError_t e = lds_for<k_group>(lds)) return e;
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), lds, s, a);
     return hipGetLastError();
 }
@@ -835,10 +832,7 @@ hipError_t launch_grouped_ffn(const GroupedLaunch &a, int max_tiles, int max_sma
 static hipError_t grouped_down_mfma(const GroupedLaunch &a, int max_tiles, hipStream_t s) {
     if (a.I <= kDnResI) {
         const size_t lds = dn_res_lds_bytes(a.I);
-        if (lds > 64 * 1024)
-            if (hipError_t e = hipFuncSetAttribute((const void *)k_dn_res, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)lds))
-                return e;
+        if (hipError_t e = lds_for<k_dn_res>(lds)) return e;
         dim3 g2(((a.H + kTN - 1) / kTN + kDnRB - 1) / kDnRB, max_tiles);
         hipLaunchKernelGGL(k_dn_res, g2, dim3(256), lds, s, a);
         return hipGetLastError();

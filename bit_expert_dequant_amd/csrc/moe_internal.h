@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "moe_dequant.h"
 
 namespace moe {
@@ -18,6 +21,26 @@ constexpr int kGroup = 64;
 struct KernelEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
+
+// Dynamic LDS beyond the default 64 KiB: the kernel's limit is raised only when a launch needs more
+// than it was last raised to on this device (a per-kernel, per-device high-water mark), so repeated
+// launches -- those recorded under stream capture included -- make no attribute call.
+constexpr size_t kCuLds = 160 * 1024;
+template <auto FN>
+inline hipError_t lds_for(size_t lds) {
+    if (lds <= 64 * 1024) return hipSuccess;
+    static std::atomic<uint32_t> mark[64];
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return e;
+    if (dev >= 0 && dev < 64 && mark[dev].load(std::memory_order_acquire) >= lds) return hipSuccess;
+    static std::mutex mu;                         // raises are serialised: the limit only grows
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && mark[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
+    if (hipError_t e = hipFuncSetAttribute((const void *)FN, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
+        return e;
+    if (dev >= 0 && dev < 64) mark[dev].store((uint32_t)lds, std::memory_order_release);
+    return hipSuccess;
+}
 
 template <typename F, typename A>
 inline hipError_t dispatch(F fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, const KernelEvents &ev,

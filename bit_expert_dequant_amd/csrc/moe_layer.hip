@@ -62,9 +62,7 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
 template <int NP, int NJ>
 hipError_t layer_impl(const LayerLaunch &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
     auto fn = k_route_gateup<NP, NJ>;
-    if (lds > 64 * 1024)
-        if (hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
-            return e;
+    if (hipError_t e = lds_for<k_route_gateup<NP, NJ>>(lds)) return e;
     return dispatch(fn, dim3(a.nr + a.ng), dim3(kBlock), lds, s, ev, a);
 }
 

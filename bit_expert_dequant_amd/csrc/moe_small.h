@@ -428,25 +428,10 @@ int small_gs(int cols, int nj) {
 
 size_t small_lds_bytes(int cols) { return (size_t)kSmallTokens * row_dw(cols) * 4; }
 
-constexpr size_t kMaxLds = 160 * 1024;
-// Raise a kernel's dynamic LDS limit to the CU's whole LDS, once per kernel and device (launches
-// during stream capture then make no attribute calls).
-template <auto FN>
-hipError_t allow_full_lds() {
-    static std::atomic<uint64_t> done{0};
-    int dev = 0;
-    if (hipError_t e = hipGetDevice(&dev)) return e;
-    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-    if (hipError_t e = hipFuncSetAttribute((const void *)FN, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds))
-        return e;
-    done.fetch_or(bit, std::memory_order_release);
-    return hipSuccess;
-}
+constexpr size_t kMaxLds = kCuLds;
 template <auto FN>
 hipError_t launch_lds(dim3 grid, size_t lds, hipStream_t s, const KernelEvents &ev, const GroupedLaunch &a) {
-    if (lds > 64 * 1024)
-        if (hipError_t e = allow_full_lds<FN>()) return e;
+    if (hipError_t e = lds_for<FN>(lds)) return e;
     return dispatch(FN, grid, dim3(kBlock), lds, s, ev, a);
 }
 
