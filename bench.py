@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--retier", action="store_true",
                    help="measure the tiered-store policy (usage over the routed token bank, hot order, "
                         "requantisation of the cold experts) instead of the expert path")
+    p.add_argument("--cache-device", action="store_true",
+                   help="with --cache: the device-side policy (moe_cache_fetch_device, no host round trip)")
     p.add_argument("--cache", type=int, default=0, metavar="SLOTS",
                    help="decode with the experts in pinned host memory and SLOTS of them cached in device "
                         "memory (moe_cache_fetch before each step's expert FFN)")
@@ -384,6 +386,9 @@ def cache_bench(a):
     table = torch.zeros_like(dl.table)
     cache = M.ExpertCache(d, [host.data_ptr() + e * dl.stride for e in range(E)], [4] * E, slots, dl.stride,
                           n_slots, table)
+    dev = a.cache_device
+    if dev:
+        cache.attach_device()
     Lc = M.Layer(dl.router, table, dl.logit_bias, dl.norm_w, wl.norm_eps)
     bank = act_tensor(wl, wl.tokens_bank(4096))
     idx = torch.empty(1, K, dtype=torch.int32, device="cuda")
@@ -399,7 +404,16 @@ def cache_bench(a):
     def step(t, cached=True, timed=False):
         x = bank[t % 4096:t % 4096 + 1]
         M.moe_route(d, dl.L, x, idx, w, ws=ws_r)
-        if cached:
+        if cached and dev:
+            # no host step: the policy kernel reads the routing where moe_route left it
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+            if ev:
+                ev[0].record(stream)
+            cache.fetch_device(idx)
+            if ev:
+                ev[1].record(stream)
+                fetch_ev.append(ev)
+        elif cached:
             idx_h.copy_(idx)                     # synchronous: the step needs its routing on the host
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
             if ev:
@@ -466,6 +480,8 @@ def cache_bench(a):
             ref = oracle.layer_token(act_f64(wl, bank_np[t % 4096]), ol, H, I, K)
             got = out_c.cpu().numpy()[0].astype(np.float64)
             errs.append(float(np.abs(got - ref.out).max() / (np.linalg.norm(ref.out) / math.sqrt(H))))
+    policy = ("device-side policy (moe_cache_fetch_device: policy kernel + zero-copy copy kernel, no host step)"
+              if dev else "host policy (indices copied to the host, moe_cache_fetch: DMA copies + table kernel)")
     line = {"metric": "decode tok/s with the expert store in host memory (device expert cache)",
             "value": round(steps / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warm,
             "ms_per_step": round(dt / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
@@ -479,11 +495,16 @@ def cache_bench(a):
                        "slots": n_slots, "experts": E},
             "cache": {"hit_rate": round(hits / max(1, hits + misses), 4), "misses_per_token": round(misses / steps, 3),
                       "bytes_copied": copied, "copied_per_second_of_decode_GBps": round(copy_gbps, 2)},
-            "roofline": {"bound": "pcie", "kernel": "host-to-device copies of missing experts (moe_cache_fetch)",
+            "policy": policy,
+            "roofline": {"bound": "pcie",
+                         "kernel": ("k_cache_policy + k_cache_copy (every step's device fetch)" if dev else
+                                    "host-to-device copies of missing experts (moe_cache_fetch)"),
                          "achieved": round(fetch_gbps, 2), "peak": round(link, 2), "unit": "GB/s",
                          "frac": round(fetch_gbps / link, 4), "traffic": None,
-                         "timing": f"HIP events around the {len(fetch_ev)} fetches that copied, in {steps} further "
-                                   "steps (copies plus the table kernel)",
+                         "timing": (f"HIP events around the device fetch of each of {steps} further steps "
+                                    "(policy kernel + copy kernel, hits-only steps included)" if dev else
+                                    f"HIP events around the {len(fetch_ev)} fetches that copied, in {steps} further "
+                                    "steps (copies plus the table kernel)"),
                          "peak_is": "measured pinned host-to-device copy rate (64 MiB copies)"},
             "resident_tok_s": round(steps / dt_res, 1),
             "parity": {"tokens_vs_resident": 16, "bit_exact_vs_resident": exact, "tokens_vs_oracle": len(errs),

@@ -96,6 +96,10 @@ def lib():
             "moe_cache_stats": (I32, [P, P, P, P]),
             "moe_cache_slot": (I32, [P, I32]),
             "moe_cache_destroy": (None, [P]),
+            "moe_cache_device_state_bytes": (SZ, [P]),
+            "moe_cache_attach_device": (I32, [P, P, SZ, P]),
+            "moe_cache_fetch_device": (I32, [P, P, I32, P]),
+            "moe_cache_device_refused": (I32, [P]),
             "moe_debug_inject_launch_failure": (I32, [I32, I32]),
         }
         for name, (res, args) in sig.items():
@@ -114,7 +118,8 @@ def exported_symbols() -> List[str]:
             "moe_layer_decode_static", "moe_stream_read",
             "moe_quantize_matrix", "moe_expert_usage", "moe_hot_order", "moe_retier", "moe_cache_create",
             "moe_cache_fetch", "moe_cache_stats", "moe_cache_slot", "moe_cache_destroy",
-            "moe_debug_inject_launch_failure"]
+            "moe_cache_device_state_bytes", "moe_cache_attach_device", "moe_cache_fetch_device",
+            "moe_cache_device_refused", "moe_debug_inject_launch_failure"]
 
 
 def _check(status: int):
@@ -373,6 +378,23 @@ class ExpertCache:
 
     def slot(self, expert: int) -> int:
         return lib().moe_cache_slot(self._c, expert)
+
+    def attach_device(self, stream=None) -> None:
+        """Move the policy to the device (see moe_cache_attach_device): a device state buffer is
+        allocated here and kept; from now on use :meth:`fetch_device`."""
+        import torch
+        nb = lib().moe_cache_device_state_bytes(self._c)
+        if nb == 0:
+            raise MoeError(8, "the device policy does not apply to this cache")
+        self._state = torch.empty((nb + 255) // 256 * 64, dtype=torch.int32, device="cuda")
+        _check(lib().moe_cache_attach_device(self._c, _tptr(self._state), self._state.numel() * 4, _stream(stream)))
+
+    def fetch_device(self, idx, stream=None) -> None:
+        """Make the experts named in ``idx`` (a device int32 tensor, any shape) resident, on the device."""
+        _check(lib().moe_cache_fetch_device(self._c, _tptr(idx), idx.numel(), _stream(stream)))
+
+    def refused(self) -> int:
+        return lib().moe_cache_device_refused(self._c)
 
     def close(self):
         if self._c:

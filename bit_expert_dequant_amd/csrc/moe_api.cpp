@@ -643,6 +643,8 @@ struct moe_expert_cache {
     uint64_t tick = 0, epoch = 0;
     uint64_t hits = 0, misses = 0, copied = 0;
     bool broken = false;
+    uint32_t *dev_state = nullptr;                // device-side policy state once attached
+    int dev_device = -1;
     // per-call scratch
     std::vector<int> req;
     std::vector<int32_t> upd_e;
@@ -706,6 +708,7 @@ int moe_cache_create(const moe_dims *dims, const moe_expert_desc *host_experts, 
 
 int moe_cache_fetch(moe_expert_cache *c, const int32_t *idx, int n, void *stream, int *misses_out) {
     if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
+    if (c->dev_state) return fail(MOE_ERR_UNSUPPORTED, "the cache's policy runs on the device: use moe_cache_fetch_device");
     if (c->broken) return fail(MOE_ERR_LAUNCH, "an earlier enqueue on this cache failed; destroy it");
     if (n < 0) return fail(MOE_ERR_SHAPE, "n=%d is negative", n);
     if (n > 0 && !idx) return fail(MOE_ERR_NULL, "idx is NULL");
@@ -788,15 +791,113 @@ int moe_cache_fetch(moe_expert_cache *c, const int32_t *idx, int n, void *stream
 
 int moe_cache_stats(const moe_expert_cache *c, uint64_t *hits, uint64_t *misses, uint64_t *bytes) {
     if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
-    if (hits) *hits = c->hits;
-    if (misses) *misses = c->misses;
-    if (bytes) *bytes = c->copied;
+    uint64_t h = c->hits, m = c->misses, b = c->copied;
+    if (c->dev_state) {
+        uint32_t hdr[moe::kCacheHdr];
+        if (hipError_t e = hipMemcpy(hdr, c->dev_state, sizeof(hdr), hipMemcpyDeviceToHost))
+            return fail(MOE_ERR_DEVICE, "reading the device cache state: %s", hipGetErrorString(e));
+        h = hdr[6] | ((uint64_t)hdr[7] << 32);
+        m = hdr[8] | ((uint64_t)hdr[9] << 32);
+        b = hdr[10] | ((uint64_t)hdr[11] << 32);
+    }
+    if (hits) *hits = h;
+    if (misses) *misses = m;
+    if (bytes) *bytes = b;
     return ok();
 }
 
 int moe_cache_slot(const moe_expert_cache *c, int expert) {
     if (!c || expert < 0 || expert >= c->E) return -2;
+    if (c->dev_state) {
+        int32_t v = -2;
+        const moe::CacheLayout L = moe::cache_layout(c->E, c->n_slots);
+        if (hipMemcpy(&v, c->dev_state + L.slot_of + expert, 4, hipMemcpyDeviceToHost) != hipSuccess) return -2;
+        return v;
+    }
     return c->slot_of[expert];
+}
+
+size_t moe_cache_device_state_bytes(const moe_expert_cache *c) {
+    if (!c || (c->flags & MOE_CACHE_DRY_RUN) || c->n_slots > moe::kCacheMaxSlots) return 0;
+    return moe::cache_layout(c->E, c->n_slots).words * 4;
+}
+
+int moe_cache_attach_device(moe_expert_cache *c, void *state, size_t state_bytes, void *stream) {
+    if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
+    if (c->dev_state) return fail(MOE_ERR_UNSUPPORTED, "the cache is already attached to a device state");
+    if (c->flags & MOE_CACHE_DRY_RUN) return fail(MOE_ERR_UNSUPPORTED, "a dry-run cache has no device side");
+    if (c->broken) return fail(MOE_ERR_LAUNCH, "an earlier enqueue on this cache failed; destroy it");
+    if (c->n_slots > moe::kCacheMaxSlots)
+        return fail(MOE_ERR_UNSUPPORTED, "n_slots=%d exceeds the device policy's %d", c->n_slots, moe::kCacheMaxSlots);
+    if (!state) return fail(MOE_ERR_NULL, "state is NULL");
+    if (!aligned(state, 256)) return fail(MOE_ERR_ALIGN, "state must be 256-byte aligned");
+    const moe::CacheLayout L = moe::cache_layout(c->E, c->n_slots);
+    if (state_bytes < L.words * 4) return fail(MOE_ERR_WORKSPACE, "state_bytes=%zu < %zu", state_bytes, L.words * 4);
+    // every host blob must be pinned memory the device can read
+    std::vector<uint32_t> w(L.words, 0u);
+    for (int e = 0; e < c->E; ++e) {
+        void *dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, (void *)(uintptr_t)c->host[e].blob, 0) != hipSuccess || !dp) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_UNSUPPORTED, "expert %d's host blob is not pinned device-accessible memory "
+                                             "(allocate the store with hipHostMalloc)", e);
+        }
+        const uint64_t a = (uint64_t)(uintptr_t)dp;
+        w[L.src + 2 * (size_t)e] = (uint32_t)a;
+        w[L.src + 2 * (size_t)e + 1] = (uint32_t)(a >> 32);
+        w[L.nbytes + e] = (uint32_t)c->bytes[e];
+        w[L.bits + e] = c->host[e].bits;
+    }
+    // the host state so far: occupied slots are 0 .. n_used - 1 (the lowest free slot is always taken)
+    int n_used = 0;
+    for (int s = 0; s < c->n_slots; ++s) n_used += c->expert_of[s] >= 0 ? 1 : 0;
+    w[0] = (uint32_t)n_used;
+    int prev = -1, head = -1;
+    for (const auto &ls : c->lru) {                 // least recent first
+        const int s = ls.second;
+        w[L.prev + s] = (uint32_t)prev;
+        if (prev >= 0) w[L.next + prev] = (uint32_t)s; else head = s;
+        prev = s;
+    }
+    if (prev >= 0) w[L.next + prev] = (uint32_t)-1;
+    w[1] = (uint32_t)head;
+    w[2] = (uint32_t)prev;
+    for (int s = 0; s < c->n_slots; ++s) {
+        w[L.expert_of + s] = (uint32_t)c->expert_of[s];
+        if (c->expert_of[s] < 0) w[L.prev + s] = w[L.next + s] = (uint32_t)-1;
+    }
+    for (int e = 0; e < c->E; ++e) w[L.slot_of + e] = (uint32_t)c->slot_of[e];
+    w[6] = (uint32_t)c->hits; w[7] = (uint32_t)(c->hits >> 32);
+    w[8] = (uint32_t)c->misses; w[9] = (uint32_t)(c->misses >> 32);
+    w[10] = (uint32_t)c->copied; w[11] = (uint32_t)(c->copied >> 32);
+    hipStream_t st = (hipStream_t)stream;
+    if (hipError_t e = hipMemcpyAsync(state, w.data(), L.words * 4, hipMemcpyHostToDevice, st))
+        return fail(MOE_ERR_DEVICE, "state upload: %s", hipGetErrorString(e));
+    if (hipError_t e = hipStreamSynchronize(st)) return fail(MOE_ERR_DEVICE, "state upload: %s", hipGetErrorString(e));
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    c->dev_state = (uint32_t *)state;
+    c->dev_device = dev;
+    return ok();
+}
+
+int moe_cache_fetch_device(moe_expert_cache *c, const int32_t *idx, int n, void *stream) {
+    if (!c) return fail(MOE_ERR_NULL, "cache is NULL");
+    if (!c->dev_state) return fail(MOE_ERR_UNSUPPORTED, "the cache has no device state: call moe_cache_attach_device");
+    if (n < 0) return fail(MOE_ERR_SHAPE, "n=%d is negative", n);
+    if (n > 0 && !idx) return fail(MOE_ERR_NULL, "idx is NULL");
+    if (idx && !aligned(idx, 4)) return fail(MOE_ERR_ALIGN, "idx must be 4-byte aligned");
+    moe::CacheDevLaunch cl{c->dev_state, c->E, c->n_slots, c->table, c->slots, c->slot_bytes};
+    if (int st = MOE_LAUNCH(moe::launch_cache_fetch_device(cl, idx, n, (hipStream_t)stream), "device cache fetch"))
+        return st;
+    return ok();
+}
+
+int moe_cache_device_refused(const moe_expert_cache *c) {
+    if (!c || !c->dev_state) return -1;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, c->dev_state + 4, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    return (int)v;
 }
 
 void moe_cache_destroy(moe_expert_cache *c) { delete c; }

@@ -293,6 +293,42 @@ hipError_t launch_table_absent(moe_expert_desc *table, int E, hipStream_t s);
 hipError_t launch_table_update(moe_expert_desc *table, int n, const int32_t *expert, const uint64_t *blob,
                                const uint32_t *bits, hipStream_t s);
 
+// Device-side cache policy (moe_cache.hip).  The state is one device buffer of 32-bit words:
+//   header [kCacheHdr]: n_used, head, tail (LRU list ends, -1 when empty), n_copy, refused steps,
+//                       then hits, misses, bytes as 64-bit counters
+//   slot_of [E] (slot of each expert or -1), expert_of [S], prev [S], next [S] (the LRU list of
+//   occupied slots, least recent first), copy [2 S] (slot, expert of this step's loads),
+//   src [E] 64-bit device addresses of the pinned host blobs, nbytes [E], bits [E].
+constexpr int kCacheHdr = 16;
+constexpr int kCacheMaxSlots = 2048;
+struct CacheLayout {
+    size_t slot_of, expert_of, prev, next, copy, src, nbytes, bits, words;
+};
+__host__ __device__ inline CacheLayout cache_layout(int E, int S) {
+    CacheLayout l;
+    size_t o = kCacheHdr;
+    l.slot_of = o; o += (size_t)E;
+    l.expert_of = o; o += (size_t)S;
+    l.prev = o; o += (size_t)S;
+    l.next = o; o += (size_t)S;
+    l.copy = o; o += 2 * (size_t)S;
+    o = (o + 1) & ~(size_t)1;                      // 8-byte alignment of the addresses
+    l.src = o; o += 2 * (size_t)E;
+    l.nbytes = o; o += (size_t)E;
+    l.bits = o; o += (size_t)E;
+    l.words = o;
+    return l;
+}
+struct CacheDevLaunch {
+    uint32_t *state;
+    int E, S;
+    moe_expert_desc *table;
+    uint8_t *slots;
+    uint64_t slot_bytes;
+};
+size_t cache_policy_lds_bytes(int E, int S);
+hipError_t launch_cache_fetch_device(const CacheDevLaunch &c, const int32_t *idx, int n, hipStream_t s);
+
 // Read-stream reference kernel (XOR of every dword of buf into *sink).
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 

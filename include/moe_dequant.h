@@ -283,6 +283,30 @@ int moe_cache_stats(const moe_expert_cache *cache, uint64_t *hits, uint64_t *mis
  * [0, E). */
 int moe_cache_slot(const moe_expert_cache *cache, int expert);
 
+/* Device-side policy: the same policy as moe_cache_fetch, run by a kernel on device indices, with
+ * the missing blobs copied by a kernel that reads the pinned host store directly (zero-copy loads
+ * at the host link's rate), so a routing step needs no host round trip:
+ *   moe_route -> moe_cache_fetch_device -> moe_expert_ffn with the cache's table -> moe_combine.
+ * moe_cache_device_state_bytes: bytes of device state for this cache (0: the device policy does not
+ *   apply: a dry-run cache, or more than 2048 slots).
+ * moe_cache_attach_device: copies the cache's residency so far into `state` (device, 256-byte
+ *   aligned, state_bytes >= moe_cache_device_state_bytes) and synchronises `stream`.  From then on
+ *   the policy state lives on the device: moe_cache_fetch is refused (MOE_ERR_UNSUPPORTED), and
+ *   moe_cache_stats and moe_cache_slot read the device state (synchronous copies, so call them after
+ *   the fetches they should see have completed).  Every host blob must be pinned memory the device
+ *   can read (hipHostMalloc, or a pinned torch tensor): MOE_ERR_UNSUPPORTED otherwise.  Errors:
+ *   MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE.
+ * moe_cache_fetch_device: idx device [n] int32 (entries outside [0, E) ignored).  Enqueues on
+ *   `stream` one single-workgroup policy kernel (which also rewrites the changed table entries) and
+ *   one copy kernel; calls on one cache must be stream-ordered.  A step naming more distinct experts
+ *   than slots changes nothing and is counted (moe_cache_device_refused).  Errors: MOE_ERR_NULL,
+ *   MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED (not attached), MOE_ERR_LAUNCH.
+ * moe_cache_device_refused: refused steps so far (synchronous read), -1 when not attached. */
+size_t moe_cache_device_state_bytes(const moe_expert_cache *cache);
+int moe_cache_attach_device(moe_expert_cache *cache, void *state, size_t state_bytes, void *stream);
+int moe_cache_fetch_device(moe_expert_cache *cache, const int32_t *idx, int n, void *stream);
+int moe_cache_device_refused(const moe_expert_cache *cache);
+
 /* Free the cache's host state (device memory belongs to the caller; pending copies read host
  * blobs, so synchronise the stream before freeing those).  NULL is ignored. */
 void moe_cache_destroy(moe_expert_cache *cache);

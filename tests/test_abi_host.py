@@ -269,6 +269,11 @@ def test_cache_dry_run_follows_the_policy_model(L):
             assert [c.slot(e) for e in range(E)] == [model.slot_of.get(e, -1) for e in range(E)], (E, step)
         hits, misses, _ = c.stats()
         assert (hits, misses) == (model.hits, model.misses)
+        # a dry-run cache has no device side: no state size, attach and device fetch refused
+        assert L.moe_cache_device_state_bytes(c._c) == 0
+        assert L.moe_cache_attach_device(c._c, FAKE, 1 << 20, None) == 8
+        assert L.moe_cache_fetch_device(c._c, FAKE, 4, None) == 8
+        assert L.moe_cache_device_refused(c._c) == -1
         c.close()
 
 

@@ -125,3 +125,92 @@ def test_absent_expert_gives_zero_rows(T):
     absent = torch.from_numpy(idx_h % 2 == 1).cuda()
     assert torch.all(y[absent] == 0)
     assert torch.equal(y[~absent], y_ref[~absent])
+
+
+# --------------------------------------------------------------------------- device-side policy
+def check_state(hs, model, dl, what):
+    """The device state's residency equals the model's; table entries point at the slots; every
+    resident slot holds its expert's blob byte for byte."""
+    wl = dl.wl
+    tab = hs.table.cpu().numpy().view(np.uint64).reshape(-1, 2)
+    base = hs.slots.data_ptr()
+    store = dl.store.cpu().numpy().reshape(wl.E, dl.stride)
+    slots = hs.slots.cpu().numpy().reshape(-1, dl.stride)
+    bits = wl.expert_bits()
+    for e in range(wl.E):
+        s = hs.cache.slot(e)
+        assert s == model.slot_of.get(e, -1), f"{what}: expert {e} in slot {s}, model {model.slot_of.get(e, -1)}"
+        if s < 0:
+            assert tab[e, 0] == 0, f"{what}: absent expert {e} has a blob"
+        else:
+            assert tab[e, 0] == base + s * dl.stride and (tab[e, 1] & 0xFFFFFFFF) == bits[e], f"{what}: table {e}"
+            nb = wl.blob_bytes(int(bits[e]))
+            assert np.array_equal(slots[s, :nb], store[e, :nb]), f"{what}: slot {s} bytes of expert {e}"
+
+
+def test_device_policy_matches_model():
+    """The device policy against the oracle's cache model, step by step: 16 experts, 5 slots, top-2;
+    three host fetches first (the state moves to the device with them), then 40 device steps of 1-2
+    tokens with out-of-range indices, and two steps with more distinct experts than slots (refused)."""
+    wl = small_workload("cache_device", 0xCAC7, 256, 128, 16, 2)
+    dl = build_layer(wl)
+    hs = HostStore(dl, 5)
+    model = oracle.ExpertCacheModel(16, 5)
+    rng = np.random.default_rng(7)
+    for step in ([0, 3], [3, 5, 7], [9, 0]):
+        hs.cache.fetch(np.array(step, dtype=np.int32))
+        model.fetch(step)
+    hs.cache.attach_device()
+    check_state(hs, model, dl, "after attach")
+    with pytest.raises(M.MoeError):
+        hs.cache.fetch(np.array([1], dtype=np.int32))          # the host policy is off now
+    refused = 0
+    for t in range(40):
+        T = int(rng.integers(1, 3))
+        idx_h = rng.integers(-2, 18, size=(T, 2)).astype(np.int32)
+        if t in (11, 27):
+            idx_h = np.arange(12, dtype=np.int32).reshape(6, 2)  # 12 distinct > 5 slots
+        try:
+            model.fetch(idx_h.reshape(-1))
+        except ValueError:
+            refused += 1
+        h0, m0, _ = hs.cache.stats()
+        hs.cache.fetch_device(torch.from_numpy(idx_h).cuda())
+        torch.cuda.synchronize()
+        h1, m1, _ = hs.cache.stats()
+        assert (h1, m1) == (model.hits, model.misses), f"step {t}: hits/misses {(h1, m1)} vs model"
+        check_state(hs, model, dl, f"step {t}")
+    assert hs.cache.refused() == refused and refused == 2
+    say(f"[cache device] hits {model.hits} misses {model.misses}")
+
+
+@pytest.mark.parametrize("T", [1, 32], ids=["decode", "grouped"])
+def test_device_fetch_matches_resident(T):
+    """Route on the device -> device fetch -> expert FFN through the cache table, with no host step:
+    outputs equal the resident store's byte for byte (decode steps over 16 experts with 3 slots;
+    batches of 32 over 64 experts with 60 slots)."""
+    if T == 1:
+        wl = small_workload("cache_dev_decode", 0xCAC9, 512, 256, 16, 2, tiered=True, n_hot=6, zipf=True)
+        n_slots, steps = 3, 24
+    else:
+        wl = small_workload("cache_dev_batched", 0xCACB, 256, 128, 64, 2)
+        n_slots, steps = 60, 5
+    dl = build_layer(wl)
+    hs = HostStore(dl, n_slots)
+    hs.cache.attach_device()
+    bank = wl.tokens_bank(T * steps)
+    done = 0
+    for t in range(steps):
+        x = act_tensor(wl, bank[T * t:T * (t + 1)])
+        idx, _ = route(dl, x, T)
+        if T > 1 and len(set(idx.cpu().numpy().reshape(-1).tolist())) > n_slots:
+            continue
+        hs.cache.fetch_device(idx)
+        y = ffn(hs.dims, hs.L, x, idx, T, wl.H, wl.K)
+        y_ref = ffn(hs.dims, dl.L, x, idx, T, wl.H, wl.K)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"step {t}: cached and resident outputs differ"
+        done += 1
+    hits, misses, nbytes = hs.cache.stats()
+    say(f"[cache device T={T}] steps {done} hits {hits} misses {misses} bytes {nbytes}")
+    assert done >= 3 and misses > n_slots
