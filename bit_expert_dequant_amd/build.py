@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_dequant.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["moe_api.cpp", "moe_batched8.hip", "moe_shared_gu.hip", "moe_shared_dn.hip", "moe_decode.hip", "moe_grouped.hip", "moe_layer.hip", "moe_quant.hip", "moe_tier.hip", "moe_cache.hip", "moe_static.hip", "moe_fused.hip"]
+SOURCES = ["moe_api.cpp", "moe_batched8.hip", "moe_shared_gu.hip", "moe_shared_gux.hip", "moe_shared_dn.hip", "moe_decode.hip", "moe_grouped.hip", "moe_layer.hip", "moe_quant.hip", "moe_tier.hip", "moe_cache.hip", "moe_static.hip", "moe_fused.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

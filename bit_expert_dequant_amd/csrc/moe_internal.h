@@ -203,8 +203,10 @@ hipError_t launch_small_gateup(const GroupedLaunch &a, int max_small, hipStream_
 // Shared-read path (moe_batched8.hip): gate/up then down for T*K <= kSharedMaxPairs pairs; false
 // from shared_path_fits when the staged rows and the record table do not fit in LDS.
 bool shared_path_fits(int H, int I, int E, int T);
-// The staging and gate/up launches of the path (moe_shared_gu.hip); a.cap, a.geo and a.pt set.
+// The staging and gate/up launches of the path (moe_shared_gu.hip), or the gate/up launch staging its
+// rows from x (moe_shared_gux.hip: no norm weight); a.cap, a.geo and a.pt set.
 hipError_t launch_shared_gateup(const GroupedLaunch &a, hipStream_t s, const KernelEvents &ev);
+hipError_t launch_shared_gateup_direct(const GroupedLaunch &a, hipStream_t s, const KernelEvents &ev);
 hipError_t launch_shared_ffn(const GroupedLaunch &a, hipStream_t s, const KernelEvents &gu_ev = {},
                              const KernelEvents &dn_ev = {});
 hipError_t launch_small_down(const GroupedLaunch &a, int max_small, hipStream_t s);

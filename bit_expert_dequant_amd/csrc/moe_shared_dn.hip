@@ -53,7 +53,9 @@ hipError_t launch_shared_ffn(const GroupedLaunch &a_in, hipStream_t s, const Ker
     a.pt = plane_table(a.H, a.I);
     a.upw = 0;
     a.geo = gateup_geo(a.H, a.I);
-    if (hipError_t e = launch_shared_gateup(a, s, gu_ev)) return e;
+    // up to four tokens without a norm weight: no staging launch (measured faster there)
+    const bool direct = a.T <= kSharedDirectMaxT && a.norm_w == nullptr;
+    if (hipError_t e = direct ? launch_shared_gateup_direct(a, s, gu_ev) : launch_shared_gateup(a, s, gu_ev)) return e;
     const int nj = nj_for(a.I), gs = small_gs(a.I, nj);
     a.geo = row_geo(a.I, a.H, nj == 1 ? dn8_rg<1>() : nj == 2 ? dn8_rg<2>() : dn8_rg<4>());
     const dim3 grid(shared_grid(a.geo.nblk, a.T * a.K));

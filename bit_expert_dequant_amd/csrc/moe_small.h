@@ -262,6 +262,7 @@ __host__ __device__ __forceinline__ int shared_rec_off(int cols, int cap, int E)
     const int st = cap * row_dw(cols), tb = 2 * E;
     return ((st > tb ? st : tb) + 3) & ~3;
 }
+constexpr int kSharedDirectMaxT = 4;      // up to this many tokens (no norm): rows staged by each workgroup
 // Rows a workgroup stages at a time: 4 for up to four tokens, else 8.
 __host__ __device__ __forceinline__ int shared_cap(int T) { return T <= 4 ? 4 : kSmallTokens; }
 
@@ -448,5 +449,56 @@ int shared_grid(int nblk, int P) {
     const int per = (nblk + kWaves * kGuUPW - 1) / (kWaves * kGuUPW);
     return std::max(P * per, 512);
 }
+// An entry's rows in at most two batches of `cap`, written out rather than looped: a loop around the
+// body keeps its hoisted addresses live throughout and spills.
+// UPW: the unrolled pipeline's length, kSharedUPW when upw <= kSharedUPW (many rows per expert:
+// many short slices) else kGuUPW / kDnUPW.
+// PRE: the rows come pre-staged by k_stage_rows (a.planes); otherwise every workgroup converts its
+// rows from x itself (few tokens and no norm weight: no staging launch).
+template <int NJ, int GS, int UPW, bool PRE>
+__device__ __forceinline__ void gu_batch(const GroupedLaunch &a, const SharedWork &w, int tb, uint32_t *lds) {
+    TokRec<kSmallTokens> r;
+    row_batch(w, tb, a.cap, r);
+    if (r.bits == 2) gu8_body<2, NJ, GS, UPW, kSmallTokens, PRE>(a, r, w.sl, w.upw, lds);
+    else gu8_body<4, NJ, GS, UPW, kSmallTokens, PRE>(a, r, w.sl, w.upw, lds);
+}
+template <int NJ, int GS, int UPW, bool PRE>
+__device__ __forceinline__ void gu_entry(const GroupedLaunch &a, const SharedWork &w, uint32_t *lds) {
+    gu_batch<NJ, GS, UPW, PRE>(a, w, 0, lds);
+    if (w.n > a.cap) {
+        __syncthreads();                          // the first batch's rows are no longer read
+        gu_batch<NJ, GS, UPW, PRE>(a, w, a.cap, lds);
+    }
+}
+template <int NJ, int GS, bool PRE>
+__global__ void __launch_bounds__(kBlock) k_gu_sh(GroupedLaunch a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    SharedWork w;
+    shared_work(a, a.geo.nblk, shared_rec_off(a.H, a.cap, a.E), lds, w);
+    if (w.upw == 0) return;
+    if (w.upw <= kSharedUPW) gu_entry<NJ, GS, kSharedUPW, PRE>(a, w, lds);
+    else gu_entry<NJ, GS, kGuUPW, PRE>(a, w, lds);
+}
+
+// The gate/up launch of the shared-read path with PRE staging or without.
+template <bool PRE>
+hipError_t launch_gu_sh(const GroupedLaunch &a, hipStream_t s, const KernelEvents &ev) {
+    const dim3 grid(shared_grid(a.geo.nblk, a.T * a.K));
+    const size_t lds = shared_lds_bytes(a.H, a.cap, a.E);
+    const int nj = nj_for(a.H), gs = small_gs(a.H, nj);
+    switch (nj) {
+        case 1:
+            return gs == 64   ? launch_lds<k_gu_sh<1, 64, PRE>>(grid, lds, s, ev, a)
+                   : gs == 32 ? launch_lds<k_gu_sh<1, 32, PRE>>(grid, lds, s, ev, a)
+                              : launch_lds<k_gu_sh<1, 0, PRE>>(grid, lds, s, ev, a);
+        case 2:
+            return gs ? launch_lds<k_gu_sh<2, 64, PRE>>(grid, lds, s, ev, a)
+                      : launch_lds<k_gu_sh<2, 0, PRE>>(grid, lds, s, ev, a);
+        default:
+            return gs ? launch_lds<k_gu_sh<4, 64, PRE>>(grid, lds, s, ev, a)
+                      : launch_lds<k_gu_sh<4, 0, PRE>>(grid, lds, s, ev, a);
+    }
+}
+
 }  // namespace
 }  // namespace moe

@@ -4,7 +4,9 @@ against the CPU oracle, for every (token, slot) row of y.
 
 Routings: the router's own choice on seeded tokens (mostly distinct experts), draft-style tokens
 that share K-1 experts with the first token and differ in one, and tokens that all choose the same
-K experts (every expert staged with T rows).  Plus the edge cases of the in-kernel expert list:
+K experts (every expert staged with T rows).  Up to four tokens without a norm weight every
+workgroup stages its rows from x itself; otherwise one launch stages them for all.  Plus the edge
+cases of the in-kernel expert list:
 an expert chosen by more pairs than a workgroup stages, repeated experts within a token,
 indices outside [0, E) and absent experts (zero rows), 2-bit and tiered experts, fp32 and
 normalised activations, ragged and widest rows."""
@@ -96,12 +98,12 @@ def test_shared_read_repeated_and_missing_experts(cfg1):
     a token, indices outside [0, E) and an absent expert (blob 0 in a copy of the table)."""
     wl, dl, ol = cfg1
     d = M.make_dims(wl.H, wl.I, wl.E, wl.K)
-    T = 16
-    bank = wl.tokens_bank(T)
-    x, x64 = act_tensor(wl, bank), act_f64(wl, bank)
-    idx_h = np.full((T, wl.K), 300, dtype=np.int32)
-    y = run_ffn(d, dl, x, torch.from_numpy(idx_h).to("cuda"), M.MOE_FFN_SHARED)
-    check_rows(wl, ol, x64, idx_h, y, "one expert, 64 pairs")
+    for T in (16, 4):        # 16: four records of 16 pairs (staged rows); 4: two of 8 (rows staged in-kernel)
+        bank = wl.tokens_bank(T)
+        x, x64 = act_tensor(wl, bank), act_f64(wl, bank)
+        idx_h = np.full((T, wl.K), 300, dtype=np.int32)
+        y = run_ffn(d, dl, x, torch.from_numpy(idx_h).to("cuda"), M.MOE_FFN_SHARED)
+        check_rows(wl, ol, x64, idx_h, y, f"one expert, {T * wl.K} pairs")
 
     T = 5
     idx_h = np.array([[7, 7, 8, 9], [-1, 7, 500, 511], [9, 9, 9, 9], [512, 3, 1 << 30, 7], [8, 500, 3, 2]],
@@ -125,6 +127,8 @@ def test_shared_read_repeated_and_missing_experts(cfg1):
 SMALL = [
     # name, T, H, I, E, K, bits, extra
     ("t3_h512_i256_e8_k2_2b", 3, 512, 256, 8, 2, 2, {}),
+    ("t3_h1024_i512_e16_k4_norm_staged", 3, 1024, 512, 16, 4, 4, {"norm": True}),
+    ("t4_h1024_i512_e16_k4_fp32_direct", 4, 1024, 512, 16, 4, 4, {"x_bf16": False}),
     ("t6_h1024_i512_e16_k4_tiered_fp32", 6, 1024, 512, 16, 4, 4, {"tiered": True, "n_hot": 5, "x_bf16": False}),
     ("t9_h192_i320_e5_k3_ragged", 9, 192, 320, 5, 3, 4, {}),
     ("t12_h2048_i768_e40_k4_norm", 12, 2048, 768, 40, 4, 4, {"norm": True}),
