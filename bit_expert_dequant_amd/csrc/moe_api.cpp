@@ -142,10 +142,16 @@ int side_stream(const moe::SideStream **out) {
 }
 
 // Router workspace: logits (when the caller passes none), then for T >= kRouterMfmaMinT the
-// normalised rows that the MFMA router reads (optional: without room for them the matvec router
-// normalises in place).
+// normalised rows that the MFMA router reads and the partial logits of its K splits (both optional:
+// without room for the rows the matvec router normalises in place, without room for the partials
+// the MFMA router runs unsplit).
+size_t route_split_bytes(const moe_dims *d, int T) {
+    const int ns = moe::router_mfma_splits(d->hidden, d->n_experts, T);
+    return ns > 1 ? r256((size_t)ns * T * d->n_experts * 4) : 0;
+}
 size_t route_ws(const moe_dims *d, int T) {
-    return r256((size_t)T * d->n_experts * 4) + (T >= moe::kRouterMfmaMinT ? r256((size_t)T * d->hidden * 4) : 0);
+    return r256((size_t)T * d->n_experts * 4) +
+           (T >= moe::kRouterMfmaMinT ? r256((size_t)T * d->hidden * 4) + route_split_bytes(d, T) : 0);
 }
 // Batched path workspace: grouping tables, SwiGLU outputs in expert order, normalised rows.
 struct GroupedWs {
@@ -468,16 +474,22 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
     Carve c{(char *)ws};
     float *lg = logits ? logits : c.take<float>((size_t)T * dims->n_experts);
     if (int s = check_ws(ws, ws_bytes, c.off)) return s;
-    float *xn = nullptr;
+    float *xn = nullptr, *part = nullptr;
     if (T >= moe::kRouterMfmaMinT && ws) {
         float *p = c.take<float>((size_t)T * dims->hidden);
         if (ws_bytes >= c.off) xn = p;
+        if (const size_t pb = route_split_bytes(dims, T)) {
+            float *q = (float *)c.take<char>(pb);
+            if (ws_bytes >= c.off) part = q;
+        }
     }
     hipStream_t st = (hipStream_t)stream;
     moe::RouterLaunch ra{x, x_dtype, dims->hidden, layer->norm_w, layer->norm_eps, layer->router,
-                         layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T, xn};
+                         layer->router_dtype, layer->logit_bias, lg, dims->hidden, dims->n_experts, T, xn, part};
+    if (!moe::router_mfma_fits(ra)) ra.part_ws = nullptr;       // partial rows only from the MFMA router
     if (int s = MOE_LAUNCH(moe::launch_router(ra, st), "router")) return s;
-    moe::TopkLaunch ta{lg, dims->n_experts, dims->top_k, T, idx, w};
+    const int ns = ra.part_ws ? moe::router_mfma_splits(dims->hidden, dims->n_experts, T) : 1;
+    moe::TopkLaunch ta{lg, dims->n_experts, dims->top_k, T, idx, w, ra.part_ws, ns, layer->logit_bias, lg};
     if (int s = MOE_LAUNCH(moe::launch_topk(ta, st), "top-k")) return s;
     return ok();
 }

@@ -48,11 +48,31 @@ __global__ void __launch_bounds__(kBlock) k_router(RouterLaunch a) {
         a.logits[(size_t)blockIdx.y * a.E + blockIdx.x * kWaves + (threadIdx.x >> 6)] = lg;
 }
 
-template <int NP>
+// NS > 1: the row is first summed from the batched router's NS partial rows (split order, then the
+// bias) and written out.
+template <int NP, int NS>
 __global__ void __launch_bounds__(64) k_topk(TopkLaunch a) {
     const int t = blockIdx.x;
     float lg[NP];
-    issue_logits<NP>(a.logits + (size_t)t * a.E, a.E, lg);
+    if constexpr (NS == 1) {
+        issue_logits<NP>(a.logits + (size_t)t * a.E, a.E, lg);
+    } else {
+        const int lane = threadIdx.x & 63;
+        float p[NS][NP];
+#pragma unroll
+        for (int q = 0; q < NS; ++q) issue_logits<NP>(a.part + ((size_t)q * a.T + t) * a.E, a.E, p[q]);
+        float b[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) b[i] = a.bias ? a.bias[min(NP * lane + i, a.E - 1)] : 0.f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            float v = p[0][i];
+#pragma unroll
+            for (int q = 1; q < NS; ++q) v += p[q][i];
+            lg[i] = v + b[i];
+            if (NP * lane + i < a.E) a.logits_out[(size_t)t * a.E + NP * lane + i] = lg[i];
+        }
+    }
     uint32_t key[NP];
     logit_keys<NP>(lg, a.E, key);
     int my_idx;
@@ -460,10 +480,28 @@ hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvent
     return split ? router_impl<MOE_BF16, true>(a, s, ev) : router_impl<MOE_BF16, false>(a, s, ev);
 }
 
-hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
-    if (a.E <= 512) hipLaunchKernelGGL(k_topk<8>, dim3(a.T), dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(k_topk<32>, dim3(a.T), dim3(64), 0, s, a);
+// Partial rows per lane are held in registers: up to 8 splits at E <= 512, 2 above (the split
+// count of the batched router keeps to these).
+template <int NP, int MAXS>
+static hipError_t topk_np(const TopkLaunch &a, hipStream_t s) {
+    switch (a.nsplit) {
+        case 0:
+        case 1: hipLaunchKernelGGL((k_topk<NP, 1>), dim3(a.T), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_topk<NP, 2>), dim3(a.T), dim3(64), 0, s, a); break;
+        case 4:
+            if constexpr (MAXS >= 4) { hipLaunchKernelGGL((k_topk<NP, (MAXS >= 4 ? 4 : 1)>), dim3(a.T), dim3(64), 0, s, a); break; }
+            return hipErrorInvalidValue;
+        case 8:
+            if constexpr (MAXS >= 8) { hipLaunchKernelGGL((k_topk<NP, (MAXS >= 8 ? 8 : 1)>), dim3(a.T), dim3(64), 0, s, a); break; }
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkLaunch &a, hipStream_t s) {
+    if (a.nsplit > 1 && (!a.part || !a.logits_out)) return hipErrorInvalidValue;
+    return a.E <= 512 ? topk_np<8, 8>(a, s) : topk_np<32, 2>(a, s);
 }
 
 template <int NJ, int NP>

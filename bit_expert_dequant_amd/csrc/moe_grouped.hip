@@ -656,8 +656,10 @@ __global__ void __launch_bounds__(256) k_dn_res(GroupedLaunch a) {
 
 // --------------------------------------------------------------------------- batched router
 // logits[t][e] = sum_c x[t][c] R[e][c] (+ bias[e]) for a bf16 router R, as v_mfma_f32_32x32x16_bf16
-// tiles of 32 tokens (A rows) by 32 experts (B columns).  The kRtWaves waves of a workgroup take
-// equal parts of the K range and meet in LDS in a fixed order (8 waves measured slower than 4).  Both operands come straight from
+// tiles of 32 tokens (A rows) by 32 experts (B columns).  With K splits (grid z) each workgroup
+// takes an equal part of the K range and writes a partial row for the top-K kernel to sum; the
+// kRtWaves waves of a workgroup take equal parts of its range and meet in LDS in a fixed order
+// (8 waves measured slower than 4).  Both operands come straight from
 // memory with cached loads (the router rows of an expert tile are re-read by the tiles of the other
 // tokens, which run on the same XCD since the grid has 16 expert tiles per token tile, and the
 // token rows by the other expert tiles; 26.7 -> 22.2 us at 256 tokens against non-temporal loads):
@@ -668,7 +670,9 @@ __global__ void __launch_bounds__(256) k_dn_res(GroupedLaunch a) {
 // are split into hi + lo bf16 parts, two MFMAs per step, as in the matvec router.
 constexpr int kRtTile = 32;
 constexpr int kRtWaves = 4;                            // waves per workgroup, each a 1/kRtWaves of K
-template <bool SPLIT>
+constexpr int kRtMaxSplit = 8;                         // K splits across workgroups, at most
+constexpr long kRtTargetWg = 256;                      // workgroups the splits aim for
+template <bool SPLIT, int NB>
 __global__ void __launch_bounds__(64 * kRtWaves) k_router_mfma(RouterLaunch a) {
     __shared__ float s_red[kRtWaves - 1][16][64];
     constexpr int XB = SPLIT ? 4 : 2;                  // activation bytes
@@ -677,13 +681,13 @@ __global__ void __launch_bounds__(64 * kRtWaves) k_router_mfma(RouterLaunch a) {
     const int H = a.H, E = a.E, T = a.T;
     const int t0 = blockIdx.y * kRtTile, e0 = blockIdx.x * kRtTile;
     const int tok = min(t0 + m, T - 1), ex = min(e0 + m, E - 1);      // clamped rows are not written
-    const int kq = H / kRtWaves, k0 = wave * kq, nblk = kq / 64;
+    const int ns = gridDim.z;                          // K splits: this workgroup takes split blockIdx.z
+    const int kq = H / (kRtWaves * ns), k0 = (blockIdx.z * kRtWaves + wave) * kq, nblk = kq / 64;
     const GLOBAL_AS uint8_t *rrow = (const GLOBAL_AS uint8_t *)a.router + ((size_t)ex * H + k0 + 32 * h) * 2;
     const GLOBAL_AS uint8_t *xrow = (const GLOBAL_AS uint8_t *)a.x + ((size_t)tok * a.x_stride + k0 + 32 * h) * XB;
-    constexpr int NB = 4;                              // blocks in flight per wave
+    // NB blocks in flight per wave; NB divides nblk, so no load runs past the wave's range
     u32x4 bq[NB][4], xq[NB][XQ];
     auto load = [&](int blk, int buf) {
-        blk = min(blk, nblk - 1);                      // past the end: a harmless re-read
 #pragma unroll
         for (int i = 0; i < 4; ++i) bq[buf][i] = *(const GLOBAL_AS u32x4 *)(rrow + (size_t)blk * 128 + 16 * i);
 #pragma unroll
@@ -713,10 +717,15 @@ __global__ void __launch_bounds__(64 * kRtWaves) k_router_mfma(RouterLaunch a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) load(i, i);
     for (int b = 0; b < nblk; b += NB) {
+        if (b + NB < nblk) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            if (b + i < nblk) compute(i);
-            load(b + NB + i, i);
+            for (int i = 0; i < NB; ++i) {
+                compute(i);
+                load(b + NB + i, i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) compute(i);
         }
     }
     if (wave > 0) {
@@ -726,14 +735,16 @@ __global__ void __launch_bounds__(64 * kRtWaves) k_router_mfma(RouterLaunch a) {
     __syncthreads();
     if (wave == 0) {
         const int e = e0 + m;
-        const float bias = (a.logit_bias && e < E) ? a.logit_bias[e] : 0.f;
+        const bool part = ns > 1;                      // partial row of this split, no bias
+        const float bias = (!part && a.logit_bias && e < E) ? a.logit_bias[e] : 0.f;
+        float *out = part ? a.part_ws + (size_t)blockIdx.z * T * E : a.logits;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             float sum = acc[v];
 #pragma unroll
             for (int q = 0; q < kRtWaves - 1; ++q) sum += s_red[q][v][lane];
             const int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (t < T && e < E) a.logits[(size_t)t * E + e] = sum + bias;
+            if (t < T && e < E) out[(size_t)t * E + e] = sum + bias;
         }
     }
 }
@@ -762,6 +773,17 @@ hipError_t launch_norm_rows(const void *x, int x_dtype, const uint16_t *norm_w, 
     return hipGetLastError();
 }
 
+int router_mfma_splits(int H, int E, int T) {
+    // a workgroup per CU at least: a 32 x 32 tile over the whole K range reads 512 KiB at H = 4096,
+    // and with 128 tiles (256 tokens) half the CUs would carry it (21.5 -> 17.7 us for the route call
+    // of 256 tokens of 512 experts with two splits; four and eight measured the same within 0.5 %)
+    const long tiles = (long)((E + kRtTile - 1) / kRtTile) * ((T + kRtTile - 1) / kRtTile);
+    const int maxs = E <= 512 ? kRtMaxSplit : 2;       // the top-K kernel's registers per partial row
+    int ns = 1;
+    while (ns < maxs && tiles * ns < kRtTargetWg && H % (64 * kRtWaves * ns * 2) == 0) ns *= 2;
+    return ns;
+}
+
 bool router_mfma_fits(const RouterLaunch &a) {
     return a.router_dtype == MOE_BF16 && a.T >= kRouterMfmaMinT && a.H % (64 * kRtWaves) == 0 &&
            (a.norm_w == nullptr || a.xn_ws != nullptr);
@@ -777,9 +799,21 @@ hipError_t launch_router_mfma(const RouterLaunch &a_in, hipStream_t s) {
         a.x_stride = a.H;
         a.norm_w = nullptr;
     }
-    const dim3 grid((a.E + kRtTile - 1) / kRtTile, (a.T + kRtTile - 1) / kRtTile);
-    if (a.x_dtype == MOE_BF16) hipLaunchKernelGGL(k_router_mfma<false>, grid, dim3(64 * kRtWaves), 0, s, a);
-    else hipLaunchKernelGGL(k_router_mfma<true>, grid, dim3(64 * kRtWaves), 0, s, a);
+    const int ns = a.part_ws ? router_mfma_splits(a.H, a.E, a.T) : 1;
+    const dim3 grid((a.E + kRtTile - 1) / kRtTile, (a.T + kRtTile - 1) / kRtTile, ns);
+    const int nblk = a.H / (64 * kRtWaves * ns);       // 64-column blocks per wave
+    const dim3 blk(64 * kRtWaves);
+    const bool bf = a.x_dtype == MOE_BF16;
+    if (nblk % 4 == 0) {
+        if (bf) hipLaunchKernelGGL((k_router_mfma<false, 4>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_router_mfma<true, 4>), grid, blk, 0, s, a);
+    } else if (nblk % 2 == 0) {
+        if (bf) hipLaunchKernelGGL((k_router_mfma<false, 2>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_router_mfma<true, 2>), grid, blk, 0, s, a);
+    } else {
+        if (bf) hipLaunchKernelGGL((k_router_mfma<false, 1>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_router_mfma<true, 1>), grid, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 

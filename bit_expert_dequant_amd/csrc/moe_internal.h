@@ -83,6 +83,8 @@ struct RouterLaunch {
     float *logits;                                 // [T][E]
     int H, E, T;
     float *xn_ws;                                  // [T][H] workspace for normalised rows, or NULL
+    float *part_ws;                                // [splits][T][E] partial logits of the MFMA router's K
+                                                   // splits (then summed by the top-K kernel), or NULL
 };
 hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvents &ev = {});
 // Batched bf16 router as MFMA tiles (moe_grouped.hip); false when the shape does not fit it.  From
@@ -91,11 +93,18 @@ hipError_t launch_router(const RouterLaunch &a, hipStream_t s, const KernelEvent
 // is faster.
 constexpr int kRouterMfmaMinT = 64;
 bool router_mfma_fits(const RouterLaunch &a);
+// K splits of the MFMA router for T tokens (1: one workgroup per 32 x 32 tile sums the whole K range
+// and writes the logits itself).  With more than one, each split writes a partial row and the top-K
+// kernel adds them in split order.
+int router_mfma_splits(int H, int E, int T);
 hipError_t launch_router_mfma(const RouterLaunch &a, hipStream_t s);
 
 struct TopkLaunch {
     const float *logits; int E, K, T;
     int32_t *idx; float *w;                        // [T][K]
+    // nsplit > 1: the logits are the sum of nsplit partial rows part[s][T][E] (in split order) plus
+    // bias (nullable), written to logits_out; `logits` is not read
+    const float *part; int nsplit; const float *bias; float *logits_out;
 };
 hipError_t launch_topk(const TopkLaunch &a, hipStream_t s);
 

@@ -143,6 +143,18 @@ def test_route_rejects_bad_arguments(L):
     assert call_route(L, d, layer(), logits=None) == 6
     assert call_route(L, d, layer(), logits=None, ws=FAKE, wsb=16) == 6
     assert call_route(L, d, layer(), logits=None, ws=FAKE + 16, wsb=1 << 20) == 5
+    # route workspace: logits, then from 64 tokens the normalised rows and the partial logit rows of
+    # the MFMA router's K splits (as many splits as bring its grid to 256 workgroups: 8 at 64 tokens
+    # of 512 experts, 2 at 256 tokens, none from 512; at most 2 above 512 experts)
+    r = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    d1 = dims(H=4096, I=1024, E=512, K=4)
+    ws_route = lambda dd, T: M.moe_workspace_bytes(M.MOE_OP_ROUTE, dd, T, 1)  # noqa: E731
+    assert ws_route(d1, 63) == r(63 * 512 * 4)
+    assert ws_route(d1, 64) == r(64 * 512 * 4) + r(64 * 4096 * 4) + r(8 * 64 * 512 * 4)
+    assert ws_route(d1, 256) == r(256 * 512 * 4) + r(256 * 4096 * 4) + r(2 * 256 * 512 * 4)
+    assert ws_route(d1, 512) == r(512 * 512 * 4) + r(512 * 4096 * 4)
+    dw = dims(H=2048, I=256, E=1024, K=4)
+    assert ws_route(dw, 64) == r(64 * 1024 * 4) + r(64 * 2048 * 4) + r(2 * 64 * 1024 * 4)
 
 
 def test_expert_ffn_and_decode_validation(L):
