@@ -322,37 +322,43 @@ __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok
 // activation.  4-bit codes enter v_dot8_i32_i4 as q - 8 (the code XOR 8 read as a signed nibble),
 // so the bias becomes b + 8 s; 2-bit codes spread to nibbles are already in [0, 3].  Per plane
 // the integer sums are at most 32 * 8 * 8, so the combined sum is exact in int32 and in fp32.
-// Each digit plane accumulates in its own register (four independent chains of four dot products,
-// instead of one chain of sixteen: with one or two waves per SIMD the chain latency, not the issue
-// rate, bounds a decode unit), then the planes combine in Horner form,
-// acc = ((A3 * 16 + A2) * 16 + A1) * 16 + A0.
-template <int BITS>
+// The digit planes combine in Horner form, acc = ((A3 * 16 + A2) * 16 + A1) * 16 + A0, over CH
+// dependency chains: CH = 4 gives each plane its own register (four independent chains of four dot
+// products: with one or two waves per SIMD the chain latency, not the issue rate, bounds a decode
+// unit); CH = 1 runs one chain from the top plane down, scaling by 16 between planes, and CH = 2 two
+// chains (A3, A2 and A1, A0) -- fewer instructions (no zeroed accumulator and no combination per
+// plane) where many tokens' slots interleave.  The integer sum is the same in every form.
+template <int BITS, int CH = 4>
 __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
-    int a[4] = {0, 0, 0, 0};
+    static_assert(CH == 1 || CH == 2 || CH == 4, "one, two or four chains");
+    int c[4];
     if (BITS == 4) {
-        int c[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) c[j] = (int)(q[j] ^ 0x88888888u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) a[p] = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], a[p], false);
     } else {
-        int e[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            e[j][0] = (int)(q[j] & 0x33333333u);
-            e[j][1] = (int)((q[j] >> 2) & 0x33333333u);
+            c[2 * j] = (int)(q[j] & 0x33333333u);
+            c[2 * j + 1] = (int)((q[j] >> 2) & 0x33333333u);
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                a[p] = __builtin_amdgcn_sdot8(e[j][0], (int)D[4 * p + 2 * j], a[p], false);
-                a[p] = __builtin_amdgcn_sdot8(e[j][1], (int)D[4 * p + 2 * j + 1], a[p], false);
-            }
     }
-    const int acc = ((a[3] * 16 + a[2]) * 16 + a[1]) * 16 + a[0];
+    // the four dot products of plane p added to acc (2-bit: the two nibble spreads of each code dword
+    // meet consecutive plane dwords)
+    auto plane = [&](int p, int acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], acc, false);
+        return acc;
+    };
+    int acc;
+    if constexpr (CH == 4) {
+        const int a0 = plane(0, 0), a1 = plane(1, 0), a2 = plane(2, 0), a3 = plane(3, 0);
+        acc = ((a3 * 16 + a2) * 16 + a1) * 16 + a0;
+    } else if constexpr (CH == 2) {
+        const int hi = plane(2, plane(3, 0) * 16), lo = plane(0, plane(1, 0) * 16);
+        acc = hi * 256 + lo;
+    } else {
+        acc = plane(0, plane(1, plane(2, plane(3, 0) * 16) * 16) * 16);
+    }
     const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
     const float bb = BITS == 4 ? fmaf(8.f, s, b) : b;
     return fmaf(s * xs.x, (float)acc, bb * xs.y);

@@ -31,6 +31,11 @@ namespace {
 constexpr int kGuUPW = 8, kGuNB = 3;
 constexpr int kDnUPW = 8, kDnNB = 3;
 constexpr int kSharedUPW = 2;             // shared-read path: every unit's loads issued up front
+// Dependency chains of a slot's dot products (slot_dot): the token loop interleaves the slots of a
+// unit, so fewer chains than planes save the zeroed accumulators and the combination (250 instead of
+// 282 vector instructions per unit and token).  Config-4 batch: two chains 525-526 us, one chain
+// 530-531, four 531-532 (two runs each).
+constexpr int kSmallDotCh = 2;
 template <int NJ>
 __host__ __device__ constexpr int dn8_rg() { return NJ >= 4 ? 2 : NJ == 2 ? 4 : 8; }
 
@@ -116,8 +121,8 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
                 pg[gi] = pu[gi] = 0.f;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    pg[gi] += slot_dot<BITS>(B.qg[gi][j], D[j], B.sg[gi][j], XS[j]);
-                    pu[gi] += slot_dot<BITS>(B.qu[gi][j], D[j], B.su[gi][j], XS[j]);
+                    pg[gi] += slot_dot<BITS, kSmallDotCh>(B.qg[gi][j], D[j], B.sg[gi][j], XS[j]);
+                    pu[gi] += slot_dot<BITS, kSmallDotCh>(B.qu[gi][j], D[j], B.su[gi][j], XS[j]);
                 }
             }
             float *hout = a.hbuf + (size_t)(se.base + t) * I;
@@ -211,7 +216,8 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CA
             for (int gi = 0; gi < RG; ++gi) {
                 part[gi] = 0.f;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) part[gi] += slot_dot<BITS>(B.q[gi][j], D[j], B.sb[gi][j], XS[j]);
+                for (int j = 0; j < NJ; ++j)
+                    part[gi] += slot_dot<BITS, kSmallDotCh>(B.q[gi][j], D[j], B.sb[gi][j], XS[j]);
             }
             float *yrow = a.y + (size_t)se.pair[0] * H;
 #pragma unroll
