@@ -186,9 +186,12 @@ bool grouped_ffn(int T) { return T > kPerTokenMaxT; }
 // From 2 to kSharedMaxT tokens (T*K <= kSharedMaxPairs) the shared-read kernels stream each
 // selected expert once for all the pairs that chose it; the automatic choice takes them from
 // kSharedAutoMinT tokens.  Measured on the config-1 layer (H4096 I1024 E512 K4), per call, shared-read
-// against per-token: 25.2 / 21.1 us at 2 tokens (router's choice), 32.1 / 31.9 at 4 (all tokens on
-// the same 4 experts), 53.2 / 57.8 at 8 (router), 83.0 / 106.9 at 16 (router), 79.7 / 100.3 at 16
-// (same experts): below 8 tokens the per-token kernels' shorter prologue wins even with overlap.
+// against per-token: 23.1 / 19.7 us at 2 tokens (router's choice), 29.0 / 29.8 at 4 (all tokens on
+// the same 4 experts), 53.2 / 53.7 at 8 (router), 52.5 / 51.3 at 8 (three experts shared), 46.4 /
+// 50.5 at 8 (same experts), 65.5 / 64.6 at 10 (router), 58.0 / 61.9 at 10 (three shared), 73.2 / 75.3
+// at 12 (router), 82.6 / 98.8 at 16 (router): below 8 tokens the per-token kernels' shorter prologue
+// wins even with overlap; at 8-10 the two are within 2 % on distinct experts and shared experts favour
+// the shared-read kernels by up to 9 %; from 12 tokens these win on every routing measured.
 constexpr int kSharedAutoMinT = 8;
 bool shared_ffn(const moe_dims *d, int T) {
     return T >= 2 && T <= moe::kSharedMaxT && T * d->top_k <= moe::kSharedMaxPairs &&

@@ -366,7 +366,9 @@ int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x
  *   y   device [T][K][H] fp32
  * The kernels are chosen by T (moe_expert_ffn_path below names them):
  *   T < 8, and T <= 24 when the shared-read path does not apply: MOE_FFN_PER_TOKEN;
- *   8 <= T <= 16 with T*K <= 64: MOE_FFN_SHARED (faster from 8 tokens on, measured);
+ *   8 <= T <= 16 with T*K <= 64: MOE_FFN_SHARED (measured on a 4096 x 1024, 512-expert top-4 layer:
+ *     within 2 % of the per-token kernels at 8-10 tokens with distinct experts, up to 9 % faster when
+ *     tokens share experts, faster on every routing from 12 tokens);
  *   T > 24: MOE_FFN_GROUPED (T*K <= 32768).
  * Errors as moe_route, and MOE_ERR_UNSUPPORTED when T*K exceeds 32768 above 24 tokens. */
 int moe_expert_ffn(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
