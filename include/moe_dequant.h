@@ -353,7 +353,10 @@ size_t moe_workspace_bytes(int op, const moe_dims *dims, int T, int n_layers);
  * For T >= 64 with a bf16 router (H a multiple of 256) the logits come from MFMA tiles; with a norm
  * weight the normalised rows are first written to the workspace after the logits (the size from
  * moe_workspace_bytes includes them; a smaller workspace that still holds the logits makes the
- * matvec router normalise in registers instead).
+ * matvec router normalise in registers instead).  While the tiles are fewer than 256 the tiles'
+ * K range is split across 2 to 8 workgroups, whose partial logit rows follow the normalised rows in
+ * the workspace and are summed in split order by the top-K step (without room for them the tiles
+ * run unsplit; the logits may then differ in the last bits).
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE,
  * MOE_ERR_LAUNCH. */
 int moe_route(const moe_dims *dims, const moe_layer *layer, const void *x, int x_dtype, int T,
