@@ -259,6 +259,13 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
         wk[k] = k < K ? wk[k] : 0.f;
         if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
     }
+    // the first unit's load offsets while the selections and h are in flight
+    const Geo g = make_geo(a.geo);
+    const int RB = a.geo.rb;
+    const int nblk = a.geo.nblk;
+    int u = blockIdx.x * kWaves + wave;
+    DNOffs<NJ, RG> o;
+    dn_offsets<NJ, RG>(a.pt, g, H, I, min(u, nblk - 1) * RB, o);
     float v[2][16];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -266,12 +273,8 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[j][i]));   // materialised here
     }
-    const Geo g = make_geo(a.geo);
-    const int RB = a.geo.rb;
-    const int nblk = a.geo.nblk;
-    int u = blockIdx.x * kWaves + wave;
     DLoads<NJ, RG, KM> L;
-    if (u < nblk) dn_issue_all<NJ, RG, KM>(sel, K, g, H, I, u * RB, a.pt, L);
+    if (u < nblk) dn_issue_all_at<NJ, RG, KM>(sel, K, o, L);
 
     // 2. stage h of every expert in its code width's digit-plane order.  The first pass works on
     //    registers only, so the weight loads just issued stay in flight meanwhile.

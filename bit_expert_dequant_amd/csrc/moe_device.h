@@ -77,6 +77,11 @@ __device__ __forceinline__ float load_act(const void *x, int dtype, size_t i) {
     return dtype == MOE_BF16 ? bf16_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
 }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu with the hardware exponential (2^x) and reciprocal, about 2^-21 relative error: for kernels
+// that evaluate it once per row and token, where the IEEE division's dozen instructions show.
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 
 // Sum over aligned groups of GS lanes (GS a power of two <= 64); every lane gets its group's sum.
 // Butterfly in registers: quad permutes and row mirrors (DPP) inside 16-lane rows, then the gfx950
@@ -328,25 +333,38 @@ __device__ __forceinline__ void load_act_slot(const ActView &av, int ss, bool ok
 // unit); CH = 1 runs one chain from the top plane down, scaling by 16 between planes, and CH = 2 two
 // chains (A3, A2 and A1, A0) -- fewer instructions (no zeroed accumulator and no combination per
 // plane) where many tokens' slots interleave.  The integer sum is the same in every form.
-template <int BITS, int CH = 4>
-__device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
-    static_assert(CH == 1 || CH == 2 || CH == 4, "one, two or four chains");
+// The token-independent part of a slot: its code dwords as v_dot8_i32_i4 operands and its scale and
+// folded bias.  Kernels that meet one loaded slot with several staged rows compute it once per slot.
+struct SlotOps {
     int c[4];
+    float s, bb;
+};
+template <int BITS>
+__device__ __forceinline__ SlotOps slot_ops(const u32x4 q, uint32_t sb) {
+    SlotOps o;
     if (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c[j] = (int)(q[j] ^ 0x88888888u);
+        for (int j = 0; j < 4; ++j) o.c[j] = (int)(q[j] ^ 0x88888888u);
     } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            c[2 * j] = (int)(q[j] & 0x33333333u);
-            c[2 * j + 1] = (int)((q[j] >> 2) & 0x33333333u);
+            o.c[2 * j] = (int)(q[j] & 0x33333333u);
+            o.c[2 * j + 1] = (int)((q[j] >> 2) & 0x33333333u);
         }
     }
+    o.s = bf16_f32(sb & 0xFFFFu);
+    const float b = bf16_f32(sb >> 16);
+    o.bb = BITS == 4 ? fmaf(8.f, o.s, b) : b;
+    return o;
+}
+template <int CH = 4>
+__device__ __forceinline__ float slot_dot_ops(const SlotOps &o, const uint32_t (&D)[kSlotDw], float2 xs) {
+    static_assert(CH == 1 || CH == 2 || CH == 4, "one, two or four chains");
     // the four dot products of plane p added to acc (2-bit: the two nibble spreads of each code dword
     // meet consecutive plane dwords)
     auto plane = [&](int p, int acc) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot8(c[j], (int)D[4 * p + j], acc, false);
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot8(o.c[j], (int)D[4 * p + j], acc, false);
         return acc;
     };
     int acc;
@@ -359,9 +377,11 @@ __device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSl
     } else {
         acc = plane(0, plane(1, plane(2, plane(3, 0) * 16) * 16) * 16);
     }
-    const float s = bf16_f32(sb & 0xFFFFu), b = bf16_f32(sb >> 16);
-    const float bb = BITS == 4 ? fmaf(8.f, s, b) : b;
-    return fmaf(s * xs.x, (float)acc, bb * xs.y);
+    return fmaf(o.s * xs.x, (float)acc, o.bb * xs.y);
+}
+template <int BITS, int CH = 4>
+__device__ __forceinline__ float slot_dot(const u32x4 q, const uint32_t (&D)[kSlotDw], uint32_t sb, float2 xs) {
+    return slot_dot_ops<CH>(slot_ops<BITS>(q, sb), D, xs);
 }
 
 typedef const GLOBAL_AS uint8_t *gbytes;
@@ -681,12 +701,15 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
         issue_chunk16(x, a.x_dtype, m, xc[j]);
         if (a.norm_w) issue_chunk16(a.norm_w, MOE_BF16, m, nc[j]);
     }
-    // 2. first batch of this wave's part of the row
+    // 2. first batch of this wave's part of the row.  Router rows go through the caches (unlike the
+    //    expert weights): every step reads the same rows, and a workgroup index always lands on the
+    //    same XCD, so each XCD's share of the router stays in its L2 between steps (17.58 -> 17.31 us
+    //    per H4096/E512 decode step, three alternating runs each)
     u32x4 wv[kRouterBatch];
 #pragma unroll
     for (int j = 0; j < kRouterBatch; ++j) {
         const int c = c0 + min((lane + 64 * j) * EPL, cols - EPL);   // clamped; unused lanes ignore it
-        wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
+        wv[j] = *(const GLOBAL_AS u32x4 *)(row + (size_t)c * EB);
     }
     // 3. activation (+ RMSNorm) into LDS
     float v[2][16];
@@ -748,7 +771,7 @@ __device__ __forceinline__ bool router_row(const RouterLaunch &a, int bx, int t,
 #pragma unroll
                 for (int j = 0; j < kRouterBatch; ++j) {
                     const int c = c0 + min((lane + 64 * (base + j)) * EPL, cols - EPL);
-                    wv[j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(row + (size_t)c * EB));
+                    wv[j] = *(const GLOBAL_AS u32x4 *)(row + (size_t)c * EB);
                 }
             }
 #pragma unroll
@@ -818,6 +841,64 @@ __device__ __forceinline__ void gu_issue(const Planes *pl, const Geo &g, int H, 
             const size_t sbi = (size_t)r * G + (slot >> 1);
             L.sg[gi][j] = __builtin_nontemporal_load(pl[0].sb + sbi);
             L.su[gi][j] = __builtin_nontemporal_load(pl[1].sb + sbi);
+        }
+    }
+}
+
+// Byte offsets of one gate/up unit's loads inside an expert blob of code width BITS (32 bits: a blob
+// of the largest supported shape is far below 4 GiB).  They depend on the unit and the lane only, so
+// a kernel computes them before the routing is known; once it is, every load is the expert's blob
+// address (wave-uniform, in scalar registers) plus one of these, and no address arithmetic is left
+// between the selection and the loads.
+template <int NJ, int RG>
+struct GUOffs {
+    uint32_t qg[RG][NJ], qu[RG][NJ], sg[RG][NJ], su[RG][NJ];
+};
+template <int BITS, int NJ, int RG>
+__device__ __forceinline__ void gu_offsets(const PlaneTable &t, const Geo &g, int H, int I, int r0,
+                                           GUOffs<NJ, RG> &o) {
+    const uint64_t *po = t.off[BITS == 2 ? 0 : 1];
+    const uint32_t G = (uint32_t)H / 64, rowb = (uint32_t)H * BITS / 8;
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+        const uint32_t r = (uint32_t)min(r0 + gi * g.rpi + g.lrow, I - 1);     // clamped as in gu_issue
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const uint32_t slot = (uint32_t)min(g.lsl + 64 * j, g.spr - 1);
+            const uint32_t qo = r * rowb + slot * (BITS == 4 ? 16u : 8u);
+            const uint32_t so = (r * G + (slot >> 1)) * 4u;
+            o.qg[gi][j] = (uint32_t)po[0] + qo;
+            o.qu[gi][j] = (uint32_t)po[2] + qo;
+            o.sg[gi][j] = (uint32_t)po[1] + so;
+            o.su[gi][j] = (uint32_t)po[3] + so;
+            // materialised here, ahead of the wait they are meant to precede
+            asm volatile("" : "+v"(o.qg[gi][j]), "+v"(o.qu[gi][j]), "+v"(o.sg[gi][j]), "+v"(o.su[gi][j]));
+        }
+    }
+}
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+// The loads of gu_issue from precomputed offsets; `blob` is wave-uniform.
+template <int BITS, int NJ, int RG>
+__device__ __forceinline__ void gu_issue_at(uint64_t blob, const GUOffs<NJ, RG> &o, GULoads<NJ, RG> &L) {
+    const gbytes b = (gbytes)uniform64(blob);
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (BITS == 4) {
+                L.qg[gi][j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(b + o.qg[gi][j]));
+                L.qu[gi][j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(b + o.qu[gi][j]));
+            } else {
+                const u32x2 vg = __builtin_nontemporal_load((const GLOBAL_AS u32x2 *)(b + o.qg[gi][j]));
+                const u32x2 vu = __builtin_nontemporal_load((const GLOBAL_AS u32x2 *)(b + o.qu[gi][j]));
+                L.qg[gi][j] = u32x4{vg.x, vg.y, 0u, 0u};
+                L.qu[gi][j] = u32x4{vu.x, vu.y, 0u, 0u};
+            }
+            L.sg[gi][j] = __builtin_nontemporal_load((gwords)(b + o.sg[gi][j]));
+            L.su[gi][j] = __builtin_nontemporal_load((gwords)(b + o.su[gi][j]));
         }
     }
 }
@@ -921,6 +1002,59 @@ __device__ __forceinline__ void dn_issue_all(const uint64_t (&sel)[KM], int K, c
         Planes pl[3];
         expert_planes(sel_blob(sk), sel_bits(sk), pt, pl);
         dn_issue<NJ, RG, KM>(pl[2], sel_bits(sk), g, H, I, r0, k, L);
+    }
+}
+
+// Byte offsets of one down unit's loads inside an expert blob, for both code widths ([0] 2-bit, [1]
+// 4-bit), computed before the selection is known (see GUOffs).
+template <int NJ, int RG>
+struct DNOffs {
+    uint32_t q[2][RG][NJ], sb[2][RG][NJ];
+};
+template <int NJ, int RG>
+__device__ __forceinline__ void dn_offsets(const PlaneTable &t, const Geo &g, int H, int I, int r0, DNOffs<NJ, RG> &o) {
+    const uint32_t G = (uint32_t)I / 64;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint32_t rowb = (uint32_t)I * (w ? 4u : 2u) / 8;
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi) {
+            const uint32_t r = (uint32_t)min(r0 + gi * g.rpi + g.lrow, H - 1);     // clamped; see gu_issue
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t slot = (uint32_t)min(g.lsl + 64 * j, g.spr - 1);
+                o.q[w][gi][j] = (uint32_t)t.off[w][4] + r * rowb + (slot << (w ? 4 : 3));
+                o.sb[w][gi][j] = (uint32_t)t.off[w][5] + (r * G + (slot >> 1)) * 4u;
+                asm volatile("" : "+v"(o.q[w][gi][j]), "+v"(o.sb[w][gi][j]));
+            }
+        }
+    }
+}
+// dn_issue_all from precomputed offsets: the same loads (every slot read as 16 bytes; slots past K
+// and absent experts read a present expert's rows), each the expert's blob address plus an offset.
+template <int NJ, int RG, int KM>
+__device__ __forceinline__ void dn_issue_all_at(const uint64_t (&sel)[KM], int K, const DNOffs<NJ, RG> &o,
+                                                DLoads<NJ, RG, KM> &L) {
+    uint64_t any = 0;
+#pragma unroll
+    for (int k = KM - 1; k >= 0; --k)
+        if (k < K && sel[k]) any = sel[k];
+    if (!any) return;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        const uint64_t sk = uniform64((k < K && sel[k]) ? sel[k] : any);
+        const gbytes b = (gbytes)sel_blob(sk);
+        const bool two = sel_bits(sk) == 2;
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t qo = two ? o.q[0][gi][j] : o.q[1][gi][j];
+                const uint32_t so = two ? o.sb[0][gi][j] : o.sb[1][gi][j];
+                L.q[k][gi][j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(b + qo));
+                L.sb[k][gi][j] = __builtin_nontemporal_load((gwords)(b + so));
+            }
+        }
     }
 }
 

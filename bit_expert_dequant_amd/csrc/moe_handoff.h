@@ -162,8 +162,19 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
     }
     const ActView v4{d4, xs}, v2{d2, xs};
 
-    // 3. wave 0 waits for this launch's logits and copies them to LDS; the barrier publishes the
+    // 3. the first work unit's load offsets for 4-bit experts (they do not depend on the routing), then
+    //    wave 0 waits for this launch's logits and copies them to LDS; the barrier publishes the
     //    logits, the table and the layouts
+    const Geo g = make_geo(a.geo);
+    const int RB = a.geo.rb;
+    const int nblk = a.geo.nblk;
+    const int units = K * nblk;
+    int u = gb * kWaves + wave;
+    GUOffs<NJ, RG> o4;
+    {
+        const int k = blk_of(min(u, units - 1), a.geo);
+        gu_offsets<4, NJ, RG>(a.pt, g, H, I, (min(u, units - 1) - k * nblk) * RB, o4);
+    }
     const uint32_t tag = launch_tag(seq);
     if (wave == 0) wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, tag, s_lg, a.err);
     __syncthreads();
@@ -180,38 +191,38 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         a.sel_ws[lane] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
     }
 
-    // 5. geometry of the work units
-    const Geo g = make_geo(a.geo);
-    const int RB = a.geo.rb;
-    const int nblk = a.geo.nblk;
-    const int units = K * nblk;
+    // 5. work units -> h; the first one (the only one when the grid covers every unit) is peeled so
+    //    that its loads follow the selection directly
     const int stride = a.ng * kWaves;
-    int u = gb * kWaves + wave;
     GULoads<NJ, RG> L;
-    uint64_t sel = 0;
     Planes pl[3];
-
-    // 6. work units -> h
-    for (; u < units; u += stride) {
-        const int k = blk_of(u, a.geo);
-        const int r0 = (u - k * nblk) * RB;
+    auto unit = [&](int uu, bool at) {
+        const int k = blk_of(uu, a.geo);
+        const int r0 = (uu - k * nblk) * RB;
         float *hout = a.h + (size_t)k * I;
-        sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+        const uint64_t sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
         if (!sel) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
-            continue;
+            return;
         }
         // Loads and arithmetic of one code width sit in one branch, so the arithmetic on the first
         // slots waits only for their own loads while the later ones are still arriving.
-        expert_planes(sel_blob(sel), sel_bits(sel), a.pt, pl);
         if (sel_bits(sel) == 2) {
+            expert_planes(sel_blob(sel), 2, a.pt, pl);
             gu_issue<2, NJ, RG>(pl, g, H, I, r0, RB, L);
             gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
         } else {
-            gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
+            if (at) {
+                gu_issue_at<4, NJ, RG>(sel_blob(sel), o4, L);
+            } else {
+                expert_planes(sel_blob(sel), 4, a.pt, pl);
+                gu_issue<4, NJ, RG>(pl, g, H, I, r0, RB, L);
+            }
             gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
         }
-    }
+    };
+    if (u < units) unit(u, true);
+    for (u += stride; u < units; u += stride) unit(u, false);
 }
 
 }  // namespace

@@ -110,6 +110,15 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
     const int rd = row_dw(H);
     unit_pipeline<UPW>(nu, L, issue, [&](int i, const GULoads<NJ, RG> &B) {
         const int r0 = r0_of(i);
+        // the slots' dot-product operands, once per unit for all of its tokens
+        SlotOps og[RG][NJ], ou[RG][NJ];
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                og[gi][j] = slot_ops<BITS>(B.qg[gi][j], B.sg[gi][j]);
+                ou[gi][j] = slot_ops<BITS>(B.qu[gi][j], B.su[gi][j]);
+            }
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
             uint32_t D[NJ][kSlotDw];
@@ -121,8 +130,8 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
                 pg[gi] = pu[gi] = 0.f;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    pg[gi] += slot_dot<BITS, kSmallDotCh>(B.qg[gi][j], D[j], B.sg[gi][j], XS[j]);
-                    pu[gi] += slot_dot<BITS, kSmallDotCh>(B.qu[gi][j], D[j], B.su[gi][j], XS[j]);
+                    pg[gi] += slot_dot_ops<kSmallDotCh>(og[gi][j], D[j], XS[j]);
+                    pu[gi] += slot_dot_ops<kSmallDotCh>(ou[gi][j], D[j], XS[j]);
                 }
             }
             float *hout = a.hbuf + (size_t)(se.base + t) * I;
@@ -131,7 +140,7 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
                 const float s = pair_sum<GS>(pg[0], pu[0]);
                 const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
                 const int r = r0 + g.lrow;
-                if (lane == 0 && r < I) hout[r] = silu(__uint_as_float(p[0])) * __uint_as_float(p[1]);
+                if (lane == 0 && r < I) hout[r] = silu_fast(__uint_as_float(p[0])) * __uint_as_float(p[1]);
             } else if constexpr (GS != 0) {
                 // rows 2q and 2q+1 of the unit: the lower half-group holds row 2q, the upper row 2q+1
 #pragma unroll
@@ -140,14 +149,14 @@ __device__ __forceinline__ void gu8_body(const GroupedLaunch &a, const TokRec<CA
                     const float su = pair_sum<GS>(pu[2 * q], pu[2 * q + 1]);
                     const int hi = (lane % GS) >= GS / 2;
                     const int rr = (2 * q + hi) * g.rpi + g.lrow;
-                    if (lane % (GS / 2) == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu(sg) * su;
+                    if (lane % (GS / 2) == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu_fast(sg) * su;
                 }
             } else {
 #pragma unroll
                 for (int gi = 0; gi < RG; ++gi) {
                     const float sg = group_sum(pg[gi], g.gsz), su = group_sum(pu[gi], g.gsz);
                     const int rr = gi * g.rpi + g.lrow;
-                    if (g.lsl == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu(sg) * su;
+                    if (g.lsl == 0 && rr < RB && r0 + rr < I) hout[r0 + rr] = silu_fast(sg) * su;
                 }
             }
         }
@@ -206,6 +215,11 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CA
     const int rd = row_dw(I);
     unit_pipeline<UPW>(nu, L, issue, [&](int i, const D8Loads<NJ, RG> &B) {
         const int r0 = r0_of(i);
+        SlotOps op[RG][NJ];
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) op[gi][j] = slot_ops<BITS>(B.q[gi][j], B.sb[gi][j]);
         for (int t = 0; t < se.n; ++t) {
             const uint32_t *d = lds + t * rd;
             uint32_t D[NJ][kSlotDw];
@@ -217,7 +231,7 @@ __device__ __forceinline__ void dn8_body(const GroupedLaunch &a, const TokRec<CA
                 part[gi] = 0.f;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    part[gi] += slot_dot<BITS, kSmallDotCh>(B.q[gi][j], D[j], B.sb[gi][j], XS[j]);
+                    part[gi] += slot_dot_ops<kSmallDotCh>(op[gi][j], D[j], XS[j]);
             }
             float *yrow = a.y + (size_t)se.pair[0] * H;
 #pragma unroll
