@@ -77,6 +77,40 @@ __device__ bool wait_logits(const uint64_t *slots, int E, uint32_t tag, float *s
     return false;
 }
 
+// wait_logits for a wave that ranks the logits itself: lane l ends with the order-preserving keys
+// of experts NP*l .. NP*l+NP-1 in registers (absent experts 0; after a timed-out wait the keys of
+// NaN, which rank as -inf) and nothing goes through LDS.
+template <int NP>
+__device__ bool wait_logit_keys(const uint64_t *slots, int E, uint32_t tag, uint32_t (&key)[NP], uint32_t *err) {
+    const int lane = threadIdx.x & 63;
+    int it = 0;
+    for (; it < kSpinLimit; ++it) {
+        if ((uint32_t)(ld_word64(slots + E - 1) >> 32) == tag) break;
+        __builtin_amdgcn_s_sleep(16);     // back-off as in wait_logits
+    }
+    float lg[NP];
+    for (; it < kSpinLimit; ++it) {
+        uint64_t v[NP];
+#pragma unroll
+        for (int t = 0; t < NP; ++t) v[t] = ld_word64(slots + min(NP * lane + t, E - 1));
+        bool ok = true;
+#pragma unroll
+        for (int t = 0; t < NP; ++t) ok = ok && (NP * lane + t >= E || (uint32_t)(v[t] >> 32) == tag);
+        if (__all(ok)) {
+#pragma unroll
+            for (int t = 0; t < NP; ++t) lg[t] = __uint_as_float((uint32_t)v[t]);
+            logit_keys<NP>(lg, E, key);
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int t = 0; t < NP; ++t) lg[t] = __uint_as_float(0x7FC00000u);
+    logit_keys<NP>(lg, E, key);
+    if (lane == 0) atomicAdd(err, 1u);
+    return false;
+}
+
 // ----------------------------------------------------------------------------------- router
 __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_t *lds, float *red, uint32_t seq) {
     float lg = 0.f;
@@ -176,20 +210,53 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         gu_offsets<4, NJ, RG>(a.pt, g, H, I, (min(u, units - 1) - k * nblk) * RB, o4);
     }
     const uint32_t tag = launch_tag(seq);
-    if (wave == 0) wait_logits<NP>(a.slots + (size_t)(gb % kLogitCopies) * E, E, tag, s_lg, a.err);
-    __syncthreads();
-
-    // 4. routing: each wave takes a quarter of the logits, then the candidates meet in LDS (every
-    //    wave ends with the same selection in lanes 0..K-1)
+    const uint64_t *row = a.slots + (size_t)(gb % kLogitCopies) * E;
+    // s_cand holds the K selected experts' (blob | bits) words in this path
+    uint64_t *s_sel = (uint64_t *)s_cand;
     int my_idx = 0;
-    float my_w = 0.f;
-    block_topk<NP>(s_lg, E, K, s_cand, my_idx, my_w);
-    if (gb == 0 && wave == 0 && lane < K) {
-        if (a.idx_out) a.idx_out[lane] = my_idx;
-        if (a.w_out) a.w_out[lane] = my_w;
-        a.w_ws[lane] = my_w;
-        a.sel_ws[lane] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
+    if constexpr (NP <= 8) {
+        // 4. routing by wave 0 alone, straight from the polled words (at most 8 keys per lane: the K
+        //    rounds take no list upkeep), while the other waves wait at the barrier that also publishes
+        //    the selection.  The barrier before it publishes the table and the layouts while the router
+        //    workgroups still run.
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t key[NP];
+            wait_logit_keys<NP>(row, E, tag, key, a.err);
+            uint32_t mk;
+            int pos;
+            wave_topk_core<NP>(key, K, mk, pos);
+            const float w = topk_weight(mk, K);
+            if (lane < K) {
+                const uint64_t sl = lookup_sel(pos, E, use_tab, s_tab, a.experts);
+                s_sel[lane] = sl;
+                if (gb == 0) {
+                    if (a.idx_out) a.idx_out[lane] = pos;
+                    if (a.w_out) a.w_out[lane] = w;
+                    a.w_ws[lane] = w;
+                    a.sel_ws[lane] = sl;
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        // 4. routing: wave 0 copies the logits to LDS; each wave takes a quarter of them, then the
+        //    candidates meet in LDS (every wave ends with the same selection in lanes 0..K-1)
+        if (wave == 0) wait_logits<NP>(row, E, tag, s_lg, a.err);
+        __syncthreads();
+        float my_w = 0.f;
+        block_topk<NP>(s_lg, E, K, s_cand, my_idx, my_w);
+        if (gb == 0 && wave == 0 && lane < K) {
+            if (a.idx_out) a.idx_out[lane] = my_idx;
+            if (a.w_out) a.w_out[lane] = my_w;
+            a.w_ws[lane] = my_w;
+            a.sel_ws[lane] = lookup_sel(my_idx, E, use_tab, s_tab, a.experts);
+        }
     }
+    auto sel_of = [&](int k) {
+        if constexpr (NP <= 8) return s_sel[k];
+        else return lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+    };
 
     // 5. work units -> h; the first one (the only one when the grid covers every unit) is peeled so
     //    that its loads follow the selection directly
@@ -200,7 +267,7 @@ __device__ __forceinline__ void gateup_phase(const LayerLaunch a, int gb, uint32
         const int k = blk_of(uu, a.geo);
         const int r0 = (uu - k * nblk) * RB;
         float *hout = a.h + (size_t)k * I;
-        const uint64_t sel = lookup_sel(__builtin_amdgcn_readlane(my_idx, k), E, use_tab, s_tab, a.experts);
+        const uint64_t sel = sel_of(k);
         if (!sel) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             return;

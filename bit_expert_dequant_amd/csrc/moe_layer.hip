@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ uint64_t s_tab[kTabMax];
     __shared__ float red[kWaves];
-    __shared__ uint32_t s_cand[2 * kWaves * MOE_MAX_TOPK];
+    __shared__ __align__(8) uint32_t s_cand[2 * kWaves * MOE_MAX_TOPK];
     // The launch counter is loaded through an offset the compiler cannot prove uniform, so it stays
     // in a vector register and is waited for where the tag is first used, not here.
     int zero;
