@@ -234,24 +234,23 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
     // The error word is loaded without a branch (a harmless in-bounds word stands in when there is
     // none) so that its wait falls at the output stores, not here.
     const uint32_t err_word = *(const GLOBAL_AS uint32_t *)(a.err ? a.err : (const uint32_t *)a.sel);
-    // 1. h chunks of this thread (first pass) and the selected experts + routing weights, all in
-    //    flight together (branch-free clamped loads); the chunks are converted before the first
-    //    unit's weight loads go out, so no wait for them can fall behind those loads
+    // 1. the selected experts, then this thread's h chunks (first pass) and the routing weights, all
+    //    in flight together (branch-free clamped loads).  Loads complete in issue order, so the
+    //    selections can be used -- and the first unit's weight loads issued -- while h is still on
+    //    its way.
     const int per = down_lds_per_expert(I);
     const int cpe = I / 16;                         // chunks per expert
     const int nch = K * cpe;
     const float *hrow = a.h + (size_t)t * K * I;
-    Chunk16 hc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) issue_chunk16(hrow, MOE_F32, min((int)threadIdx.x + kBlock * j, nch - 1), hc[j]);
     uint64_t sel[KM];
     float wk[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        const size_t o = (size_t)t * K + min(k, K - 1);
-        sel[k] = ((const GLOBAL_AS uint64_t *)a.sel)[o];
-        wk[k] = COMBINE ? ((const GLOBAL_AS float *)a.w)[o] : 0.f;
-    }
+    for (int k = 0; k < KM; ++k) sel[k] = ((const GLOBAL_AS uint64_t *)a.sel)[(size_t)t * K + min(k, K - 1)];
+    Chunk16 hc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) issue_chunk16(hrow, MOE_F32, min((int)threadIdx.x + kBlock * j, nch - 1), hc[j]);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) wk[k] = COMBINE ? ((const GLOBAL_AS float *)a.w)[(size_t)t * K + min(k, K - 1)] : 0.f;
     uint32_t two_mask = 0;   // bit k: expert k has 2-bit codes
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
@@ -259,22 +258,18 @@ __global__ void __launch_bounds__(kBlock) k_down(DownLaunch a) {
         wk[k] = k < K ? wk[k] : 0.f;
         if (sel_bits(sel[k]) == 2) two_mask |= 1u << k;
     }
-    // the first unit's load offsets while the selections and h are in flight
+    // the first unit's load offsets while the selections are in flight, then its weight loads
     const Geo g = make_geo(a.geo);
     const int RB = a.geo.rb;
     const int nblk = a.geo.nblk;
     int u = blockIdx.x * kWaves + wave;
     DNOffs<NJ, RG> o;
     dn_offsets<NJ, RG>(a.pt, g, H, I, min(u, nblk - 1) * RB, o);
+    DLoads<NJ, RG, KM> L;
+    dn_issue_all_at<NJ, RG, KM>(sel, K, o, a.h, L);    // a wave past the rows re-reads the last unit
     float v[2][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        chunk16_f32(hc[j], MOE_F32, v[j]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[j][i]));   // materialised here
-    }
-    DLoads<NJ, RG, KM> L;
-    if (u < nblk) dn_issue_all_at<NJ, RG, KM>(sel, K, o, L);
+    for (int j = 0; j < 2; ++j) chunk16_f32(hc[j], MOE_F32, v[j]);
 
     // 2. stage h of every expert in its code width's digit-plane order.  The first pass works on
     //    registers only, so the weight loads just issued stay in flight meanwhile.

@@ -1032,25 +1032,28 @@ __device__ __forceinline__ void dn_offsets(const PlaneTable &t, const Geo &g, in
 }
 // dn_issue_all from precomputed offsets: the same loads (every slot read as 16 bytes; slots past K
 // and absent experts read a present expert's rows), each the expert's blob address plus an offset.
+// Branch-free, so that the waits for loads issued before these (h) can count them: with no expert
+// present at all every load reads the first 16 bytes of `spare` (any buffer of at least 16 bytes)
+// and its results go unused.
 template <int NJ, int RG, int KM>
 __device__ __forceinline__ void dn_issue_all_at(const uint64_t (&sel)[KM], int K, const DNOffs<NJ, RG> &o,
-                                                DLoads<NJ, RG, KM> &L) {
+                                                const void *spare, DLoads<NJ, RG, KM> &L) {
     uint64_t any = 0;
 #pragma unroll
     for (int k = KM - 1; k >= 0; --k)
         if (k < K && sel[k]) any = sel[k];
-    if (!any) return;
+    const bool none = any == 0;
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-        const uint64_t sk = uniform64((k < K && sel[k]) ? sel[k] : any);
-        const gbytes b = (gbytes)sel_blob(sk);
+        const uint64_t sk = (k < K && sel[k]) ? sel[k] : any;
+        const gbytes b = (gbytes)uniform64(none ? (uint64_t)spare : sel_blob(sk));
         const bool two = sel_bits(sk) == 2;
 #pragma unroll
         for (int gi = 0; gi < RG; ++gi) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const uint32_t qo = two ? o.q[0][gi][j] : o.q[1][gi][j];
-                const uint32_t so = two ? o.sb[0][gi][j] : o.sb[1][gi][j];
+                const uint32_t qo = none ? 0u : two ? o.q[0][gi][j] : o.q[1][gi][j];
+                const uint32_t so = none ? 0u : two ? o.sb[0][gi][j] : o.sb[1][gi][j];
                 L.q[k][gi][j] = __builtin_nontemporal_load((const GLOBAL_AS u32x4 *)(b + qo));
                 L.sb[k][gi][j] = __builtin_nontemporal_load((gwords)(b + so));
             }
