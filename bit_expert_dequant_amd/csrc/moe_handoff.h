@@ -112,10 +112,45 @@ __device__ bool wait_logit_keys(const uint64_t *slots, int E, uint32_t tag, uint
 }
 
 // ----------------------------------------------------------------------------------- router
+// The bf16 router row for a bf16 activation without a norm, in registers only: lane l's columns of
+// the row, eight at a time ((l + 64 j) * 8 ..), meet the same columns of x loaded straight from
+// memory, already in the dot2 operand format, so there is no LDS staging and no barrier between the
+// loads and the dot products.  The same products in the same order as router_row.  H a multiple of
+// 512, at most 4096 (one batch of row loads); wave w of workgroup bx takes expert bx * kWaves + w.
+__device__ __forceinline__ bool router_row_bf16x(const RouterLaunch &a, int bx, float &logit) {
+    const int H = a.H, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = bx * kWaves + wave;
+    const int nld = H / 512;
+    const GLOBAL_AS u32x4 *row =
+        (const GLOBAL_AS u32x4 *)((const GLOBAL_AS uint8_t *)a.router + (size_t)(e < a.E ? e : 0) * H * 2);
+    const GLOBAL_AS u32x4 *xv = (const GLOBAL_AS u32x4 *)a.x;
+    const float bias = e < a.E && a.logit_bias ? a.logit_bias[e] : 0.f;
+    // pairs in issue order, so the first products wait for the first pair only (loads complete in
+    // issue order); clamped, so every load is in bounds and the extra ones are not used
+    u32x4 xq[kRouterBatch], wq[kRouterBatch];
+#pragma unroll
+    for (int j = 0; j < kRouterBatch; ++j) {
+        const int i = lane + 64 * min(j, nld - 1);
+        xq[j] = xv[i];
+        wq[j] = row[i];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRouterBatch; ++j)
+        if (j < nld) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = dot2(wq[j][q], xq[j][q], acc);
+        }
+    logit = group_sum(acc, 64) + bias;
+    return e < a.E;
+}
+
 __device__ __forceinline__ void router_phase(const LayerLaunch a, int b, uint32_t *lds, float *red, uint32_t seq) {
     float lg = 0.f;
     bool ok;
-    if (a.r.router_dtype == MOE_BF16)
+    if (kRouterWPR == 1 && a.r.router_dtype == MOE_BF16 && !a.split && a.H % 512 == 0 && a.H <= 512 * kRouterBatch)
+        ok = router_row_bf16x(a.r, b, lg);
+    else if (a.r.router_dtype == MOE_BF16)
         ok = a.split ? router_row<MOE_BF16, true, kRouterWPR>(a.r, b, 0, lds, red, lg)
                      : router_row<MOE_BF16, false, kRouterWPR>(a.r, b, 0, lds, red, lg);
     else
