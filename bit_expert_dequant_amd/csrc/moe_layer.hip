@@ -50,10 +50,9 @@ __global__ void __launch_bounds__(kBlock) k_route_gateup(LayerLaunch a) {
     const int b = blockIdx.x;
     if (a.clear_err && b == 0 && threadIdx.x == 0) st_word(a.err, 0u);
     if (b < a.nr) {
-        // the router waves issue ahead of the gate/up waves that share their CUs while staging and
-        // polling: every gate/up workgroup waits for the logits (17.63 -> 17.54 us per step, medians of
-        // five alternating runs, each within +-0.01 us)
-        __builtin_amdgcn_s_setprio(3);
+        // (a raised wave priority for the router waves helped while the router was staged through LDS;
+        // with its rows computed in registers the gate/up staging it delayed is the later of the two:
+        // 15.83 -> 15.65 us per H4096/E512 step without it, three alternating runs)
         router_phase(a, b, lds, red, seq);
     } else {
         gateup_phase<NJ, NP>(a, b - a.nr, lds, s_tab, s_cand, red, seq);
