@@ -214,8 +214,8 @@ __global__ void __launch_bounds__(kBlock) k_gateup(GateUpLaunch a) {
             for (int r = r0 + lane; r < r0 + RB && r < I; r += 64) hout[r] = 0.f;
             continue;
         }
-        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG>(g, I, r0, RB, v2, L, hout);
-        else gu_finish<4, NJ, RG>(g, I, r0, RB, v4, L, hout);
+        if (sel_bits(sel) == 2) gu_finish<2, NJ, RG, true>(g, I, r0, RB, v2, L, hout);
+        else gu_finish<4, NJ, RG, true>(g, I, r0, RB, v4, L, hout);
     }
 }
 
