@@ -201,7 +201,6 @@ def quantize_bench(a):
     written once.  Parity: every code and pair of the first matrix against the oracle."""
     import torch
     import bit_expert_dequant_amd as M
-    import oracle
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rows, cols, bits, n, per = 1024, 4096, 4, 64, 16
     cb, sbb = M.lib().moe_packed_codes_bytes(rows, cols, bits), M.lib().moe_packed_sb_bytes(rows, cols)
@@ -228,12 +227,17 @@ def quantize_bench(a):
     us = e0.elapsed_time(e1) * 1e3 / (reps * nl)
     per_launch = per * (rows * cols * 4 + cb + sbb)
     gbps = per_launch / (us * 1e-6) / 1e9
-    oc, os_, ob = oracle.quantize(W[0].cpu().numpy(), bits)
-    plane = codes[0].cpu().numpy().reshape(rows, cols // 2)
-    gc = np.empty((rows, cols), dtype=np.uint8)
-    gc[:, 0::2], gc[:, 1::2] = plane & 15, plane >> 4
-    gsb = sb[0].cpu().numpy().view(np.uint16).reshape(rows, cols // 64, 2)
-    parity_ok = bool(np.array_equal(gc, oc) and np.array_equal(gsb[:, :, 0], os_) and np.array_equal(gsb[:, :, 1], ob))
+    # CPU leg (skipped with --no-cpu): the oracle's quantiser on the first matrix, compared code by code
+    parity_ok = None
+    if not a.no_cpu:
+        import oracle
+        oc, os_, ob = oracle.quantize(W[0].cpu().numpy(), bits)
+        plane = codes[0].cpu().numpy().reshape(rows, cols // 2)
+        gc = np.empty((rows, cols), dtype=np.uint8)
+        gc[:, 0::2], gc[:, 1::2] = plane & 15, plane >> 4
+        gsb = sb[0].cpu().numpy().view(np.uint16).reshape(rows, cols // 64, 2)
+        parity_ok = bool(np.array_equal(gc, oc) and np.array_equal(gsb[:, :, 0], os_)
+                         and np.array_equal(gsb[:, :, 1], ob))
     line = {"metric": "quantise-from-float GB/s (fp32 weights -> 4-bit packed planes)", "value": round(gbps, 1),
             "unit": "GB/s", "n_gpus": 1, "steps": reps * nl, "warmup": nl, "ms_per_step": round(us * 1e-3, 6),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -259,7 +263,6 @@ def retier_bench(a):
     oracle; the hot set's share of the stream's selections beside that of the prior's hot set."""
     import torch
     import bit_expert_dequant_amd as M
-    import oracle
     import synth
     from synth.device import act_tensor, build_layer
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -316,25 +319,28 @@ def retier_bench(a):
     total = int(c_np.sum())
     share = float(c_np[o_np[:n_hot]].sum()) / total
     prior_share = float(c_np[synth.hot_set(wl.seed, E)].sum()) / total
-    # parity on two cold experts (inputs: the seeded base blobs)
-    parity_ok = True
-    for r in (n_hot, E - 1):
-        e = int(o_np[r])
-        slot = r - n_hot
-        gpu = cold[slot * cold_bytes:(slot + 1) * cold_bytes].cpu().numpy()
-        ref = oracle.requantize_expert(synth.expert_blob(wl.seed, 0, e, H, I, 4), H, I, 4, 2)
-        off, _ = synth.blob_layout(H, I, 2)
-        sizes = synth.plane_sizes(H, I, 2)
-        for m, (rows, cols) in enumerate([(I, H), (I, H), (H, I)]):
-            plane = gpu[off[2 * m]:off[2 * m] + sizes[2 * m]].reshape(rows, cols // 4)
-            codes = np.empty((rows, cols), dtype=np.uint8)
-            for k in range(4):
-                codes[:, k::4] = (plane >> (2 * k)) & 3
-            sb = gpu[off[2 * m + 1]:off[2 * m + 1] + sizes[2 * m + 1]].view(np.uint16).reshape(rows, cols // 64, 2)
-            parity_ok &= bool(np.array_equal(codes, ref[m][0]) and np.array_equal(sb[:, :, 0], ref[m][1])
-                              and np.array_equal(sb[:, :, 1], ref[m][2]))
+    # CPU leg (skipped with --no-cpu): the oracle's requantisation of two cold experts (inputs: the
+    # seeded base blobs), compared code by code, then its throughput on a bounded sample
+    parity_ok = None
     cpu = None
     if not a.no_cpu:
+        import oracle
+        parity_ok = True
+        for r in (n_hot, E - 1):
+            e = int(o_np[r])
+            slot = r - n_hot
+            gpu = cold[slot * cold_bytes:(slot + 1) * cold_bytes].cpu().numpy()
+            ref = oracle.requantize_expert(synth.expert_blob(wl.seed, 0, e, H, I, 4), H, I, 4, 2)
+            off, _ = synth.blob_layout(H, I, 2)
+            sizes = synth.plane_sizes(H, I, 2)
+            for m, (rows, cols) in enumerate([(I, H), (I, H), (H, I)]):
+                plane = gpu[off[2 * m]:off[2 * m] + sizes[2 * m]].reshape(rows, cols // 4)
+                codes = np.empty((rows, cols), dtype=np.uint8)
+                for k in range(4):
+                    codes[:, k::4] = (plane >> (2 * k)) & 3
+                sb = gpu[off[2 * m + 1]:off[2 * m + 1] + sizes[2 * m + 1]].view(np.uint16).reshape(rows, cols // 64, 2)
+                parity_ok &= bool(np.array_equal(codes, ref[m][0]) and np.array_equal(sb[:, :, 0], ref[m][1])
+                                  and np.array_equal(sb[:, :, 1], ref[m][2]))
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         blob0 = synth.expert_blob(wl.seed, 0, 0, H, I, 4)
         n_cpu, t0 = 0, time.perf_counter()
@@ -462,13 +468,11 @@ def cache_bench(a):
     link = 16 * (64 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     hits, misses, copied = h1 - h0, m1 - m0, b1 - b0
     copy_gbps = copied / dt / 1e9
-    # parity: 16 more tokens through the cache against the resident store (same kernels: bit-exact),
-    # and two of them against the oracle
-    import oracle
+    # parity: 16 more tokens through the cache against the resident store (same kernels: bit-exact);
+    # in the CPU leg (skipped with --no-cpu) two of them also against the oracle
     from synth.device import act_f64
     exact, errs = True, []
-    ol = oracle.workload_layer(wl)
-    bank_np = wl.tokens_bank(4096)
+    outs_c = []
     for t in range(warm + 2 * steps, warm + 2 * steps + 16):
         step(t)
         out_c = out.clone()
@@ -476,9 +480,14 @@ def cache_bench(a):
         step(t, cached=False)
         torch.cuda.synchronize()
         exact &= bool(torch.equal(out_c, out) and torch.equal(idx_c, idx))
-        if len(errs) < 2:
+        if len(outs_c) < 2:
+            outs_c.append((t, out_c.cpu().numpy()[0].astype(np.float64)))
+    if not a.no_cpu:
+        import oracle
+        ol = oracle.workload_layer(wl)
+        bank_np = wl.tokens_bank(4096)
+        for t, got in outs_c:
             ref = oracle.layer_token(act_f64(wl, bank_np[t % 4096]), ol, H, I, K)
-            got = out_c.cpu().numpy()[0].astype(np.float64)
             errs.append(float(np.abs(got - ref.out).max() / (np.linalg.norm(ref.out) / math.sqrt(H))))
     policy = ("device-side policy (moe_cache_fetch_device: policy kernel + zero-copy copy kernel, no host step)"
               if dev else "host policy (indices copied to the host, moe_cache_fetch: DMA copies + table kernel)")
@@ -508,7 +517,8 @@ def cache_bench(a):
                          "peak_is": "measured pinned host-to-device copy rate (64 MiB copies)"},
             "resident_tok_s": round(steps / dt_res, 1),
             "parity": {"tokens_vs_resident": 16, "bit_exact_vs_resident": exact, "tokens_vs_oracle": len(errs),
-                       "max_err_over_rms": max(errs), "tolerance": 2e-3, "ok": bool(exact and max(errs) <= 2e-3)}}
+                       "max_err_over_rms": max(errs) if errs else None, "tolerance": 2e-3,
+                       "ok": bool(exact and (not errs or max(errs) <= 2e-3))}}
     cache.close()
     print(json.dumps(line), flush=True)
 
